@@ -1,0 +1,242 @@
+"""Benchmark: hybrid-batch attention microseconds per iteration on one MI355X, and the achieved
+fraction of the max(MFMA, HBM) roofline.
+
+    python bench.py [--steps K] [--warmup W] [--workload N] [--mode fused]
+
+One step = one pod_attn_run over the whole hybrid batch (prefill tiles + decode split-KV +
+combine), inputs resident in HBM.  Prints ONE JSON line.  The default workload is the
+Llama-2-7B-shaped layer (32 query / 32 KV heads, head_dim 128, bf16, 16-token pages): one
+1024-token prefill chunk at offset 3072 plus 64 decodes at context 4096, over a randomly
+permuted 40960-page pool.  The other workloads are parity-test cases; --workload selects them
+for manual runs.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "hybrid-batch attention µs/iter + fraction of max(MFMA,HBM) roofline, 1 GPU"
+PEAK_HBM = 8.0e12            # B/s, MI355X
+PEAK_MFMA = {"bf16": 2.5e15, "fp32": 157.3e12}   # dense FLOP/s, MI355X
+
+
+def algorithmic_work(spec):
+    """Bytes and FLOPs the method must move / do (not what a kernel happens to do):
+    K and V read once per KV head per live context token, q read and out written once, one
+    int32 block-table entry per live page; 4*D FLOPs per visible (query head, key) pair."""
+    eb = spec.elem_bytes
+    D, Hq, Hkv = spec.head_dim, spec.num_q_heads, spec.num_kv_heads
+    ctx = spec.seq_ctx()
+    kv = sum(ctx) * Hkv * D * eb * 2
+    qo = spec.total_q * Hq * D * eb * 2
+    bt = sum(-(-c // 16) for c in ctx) * 4
+    pairs_pf = 0
+    for L, c in zip(spec.prefill_q_len, spec.prefill_ctx_len):
+        o = c - L
+        pairs_pf += L * o + L * (L + 1) // 2
+    pairs_dc = sum(spec.decode_ctx_len)
+    pairs = Hq * (pairs_pf + pairs_dc)
+    return {"bytes": kv + qo + bt, "kv_bytes": kv, "flops": 4 * D * pairs, "pairs": pairs,
+            "pairs_prefill": Hq * pairs_pf, "pairs_decode": Hq * pairs_dc}
+
+
+def workload_desc(spec):
+    pre = ", ".join(f"{L}@{c - L}" for L, c in zip(spec.prefill_q_len, spec.prefill_ctx_len))
+    dc = spec.decode_ctx_len
+    dec = f"{len(dc)}x{dc[0]}" if len(set(dc)) == 1 else f"{len(dc)} (ctx {min(dc)}..{max(dc)}, mean {sum(dc) / len(dc):.0f})"
+    return {"workload": f"{spec.name}: hybrid batch, prefill chunks [{pre}] + {dec} decodes",
+            "heads_q_kv_dim": [spec.num_q_heads, spec.num_kv_heads, spec.head_dim],
+            "page_tokens": 16, "pool_pages": spec.num_pages, "pages": "random permutation",
+            "dtype": spec.dtype}
+
+
+def time_mode(torch, h, b, meta, out, ws, steps, warmup):
+    """Wall time of `steps` runs (events on the launch stream around the loop) and the mean
+    duration of the kernels of one run (one-shot events armed before each run)."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        h.run(b.q, b.k_pool, b.v_pool, b.block_tables, meta, out, ws)
+    torch.cuda.synchronize()
+    ks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        h.set_kernel_events(*ks[i])
+        h.run(b.q, b.k_pool, b.v_pool, b.block_tables, meta, out, ws)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    kern = [a.elapsed_time(z) for a, z in ks]
+    return total_ms / steps, sum(kern) / len(kern), min(kern)
+
+
+def cpu_baseline(b, budget_s=12.0):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload: whole decode
+    sequences (all heads) and blocks of 32 prefill rows (all heads), until about budget_s of
+    CPU work; scaled to the full workload by its visible (head, key) pair count."""
+    import numpy as np
+    import torch
+    from oracle import attention as orc
+
+    spec = b.spec
+
+    class Pages:
+        def __init__(self, t):
+            self.t = t
+
+        def __getitem__(self, idx):
+            sel = self.t[torch.as_tensor(np.asarray(idx, dtype=np.int64), device=self.t.device)].cpu()
+            return sel.view(torch.int16).numpy() if spec.dtype == "bf16" else sel.numpy()
+
+    q = b.q.cpu()
+    qraw = q.view(torch.int16).numpy() if spec.dtype == "bf16" else q.numpy()
+    prob = orc.HybridProblem(qraw, Pages(b.k_pool), Pages(b.v_pool), b.block_tables_host, b.prefill_q_start,
+                             b.prefill_ctx_len, b.decode_ctx_len, spec.num_q_heads, spec.num_kv_heads,
+                             spec.dtype, spec.softmax_scale)
+    Hq = spec.num_q_heads
+    t_dc = t_pf = 0.0
+    pairs_dc = pairs_pf = 0
+    n_dc = n_pf_rows = 0
+    start = time.perf_counter()
+    i = 0
+    while i < spec.num_decode and time.perf_counter() - start < budget_s / 2:
+        s = spec.num_prefill + i
+        t = time.perf_counter()
+        prob.sequence_output(s)
+        t_dc += time.perf_counter() - t
+        pairs_dc += Hq * spec.decode_ctx_len[i]
+        n_dc += 1
+        i += 1
+    start = time.perf_counter()
+    for p in range(spec.num_prefill):
+        rows = prob.seq_rows(p)
+        for a in range(0, len(rows), 32):
+            if time.perf_counter() - start >= budget_s / 2:
+                break
+            blk = rows[a:a + 32]
+            t = time.perf_counter()
+            prob.rows_output(p, blk)
+            t_pf += time.perf_counter() - t
+            pairs_pf += Hq * sum(prob.row_info(int(r))[1] + 1 for r in blk)
+            n_pf_rows += len(blk)
+    w = algorithmic_work(spec)
+    est = 0.0
+    if pairs_dc:
+        est += t_dc / pairs_dc * w["pairs_decode"]
+    if pairs_pf:
+        est += t_pf / pairs_pf * w["pairs_prefill"]
+    threads = os.cpu_count()
+    try:
+        from threadpoolctl import threadpool_info
+        nt = [d.get("num_threads", 0) for d in threadpool_info() if d.get("user_api") == "blas"]
+        if nt:
+            threads = max(nt)
+    except Exception:
+        pass
+    return {"value": round(est * 1e6, 1), "unit": "us/iter", "cores": threads, "kind": "oracle",
+            "sample": (f"{n_dc} whole decode sequences + {n_pf_rows} prefill rows, all {Hq} heads "
+                       f"({t_dc + t_pf:.1f} s of fp64 numpy incl. page copies to host), "
+                       f"scaled by visible (head,key) pairs to the full batch")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2, help="1..5; 2 is the measured workload")
+    ap.add_argument("--mode", default="fused", choices=["fused", "separate", "streams"])
+    ap.add_argument("--no-compare", action="store_true", help="skip timing the other two modes")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(the hybrid batch shards by sequence or KV head with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from hybrid_prefill_decode_paged_amd import binding
+    from hybrid_prefill_decode_paged_amd import inputs as gen
+
+    binding.load()
+    torch.cuda.set_device(0)
+    spec = gen.config_spec(args.workload)
+    print(f"[bench] generating {spec.name}: {spec.num_pages} pages", file=sys.stderr, flush=True)
+    b = gen.make_batch(spec, "cuda")
+    torch.cuda.synchronize()
+    meta = binding.BatchMeta.from_batch(b)
+    work = algorithmic_work(spec)
+    peak_mfma = PEAK_MFMA[spec.dtype]
+    t_roof_s = max(work["flops"] / peak_mfma, work["bytes"] / PEAK_HBM)
+    bound = "hbm" if work["bytes"] / PEAK_HBM >= work["flops"] / peak_mfma else "mfma"
+
+    results = {}
+    stats = {}
+    modes = [args.mode] + ([] if args.no_compare else [m for m in ("fused", "separate", "streams") if m != args.mode])
+    for mode in modes:
+        h = binding.PodAttention(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.dtype, mode,
+                                 scale=spec.softmax_scale)
+        ws = torch.empty(h.workspace_size(meta), dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(b.q)
+        steps = args.steps if mode == args.mode else max(5, args.steps // 2)
+        print(f"[bench] timing mode={mode} steps={steps}", file=sys.stderr, flush=True)
+        ms, kern_ms, kern_min = time_mode(torch, h, b, meta, out, ws, steps, args.warmup)
+        results[mode] = {"us_per_iter": round(ms * 1e3, 2), "kernel_us_mean": round(kern_ms * 1e3, 2),
+                         "kernel_us_min": round(kern_min * 1e3, 2)}
+        stats[mode] = h.stats()
+        del ws, out
+        h.close()
+
+    main_ms = results[args.mode]["us_per_iter"] / 1e3
+    kern_s = results[args.mode]["kernel_us_mean"] / 1e6
+    if bound == "hbm":
+        achieved, peak, unit = work["bytes"] / kern_s / 1e9, PEAK_HBM / 1e9, "GB/s"
+    else:
+        achieved, peak, unit = work["flops"] / kern_s / 1e12, peak_mfma / 1e12, "TFLOP/s"
+    st = stats[args.mode]
+    line = {
+        "metric": METRIC,
+        "value": results[args.mode]["us_per_iter"],
+        "unit": "us/iter",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_ms, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic (seeded N(0,1)*0.5 values, seeded page permutation)",
+        "config": workload_desc(spec),
+        "roofline": {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": "pod_fused_kernel" if args.mode == "fused" else f"{args.mode} kernels",
+                     "algorithmic_bytes": work["bytes"], "algorithmic_flops": work["flops"],
+                     "t_roof_us": round(t_roof_s * 1e6, 2),
+                     "roof_fraction_of_step": round(t_roof_s / main_ms * 1e3, 4)},
+        "modes": results,
+        "fused_vs_separate": (round(results["separate"]["us_per_iter"] / results["fused"]["us_per_iter"], 4)
+                              if "separate" in results and "fused" in results else None),
+        "plan": {k: st[k] for k in ("num_prefill_items", "num_decode_items", "num_combine_groups",
+                                    "decode_split_tokens", "prefill_max_splits", "grid_wgs", "wgs_per_cu",
+                                    "num_cus", "vgprs_per_lane", "lds_bytes_per_wg", "mode_used",
+                                    "fallback_reason")},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(b, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

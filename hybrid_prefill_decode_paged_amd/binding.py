@@ -1,0 +1,245 @@
+"""ctypes binding of libpod_attn.so: argument marshalling only, same names as the C ABI.
+
+Every step of the attention runs in the library's HIP kernels; nothing here computes.  If the
+library is missing, ``load()`` raises -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+from typing import Optional
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpod_attn.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "pod_attn.h")
+
+BF16, FP32 = 0, 1
+MODE_FUSED, MODE_SEPARATE, MODE_STREAMS = 0, 1, 2
+MODES = {"fused": MODE_FUSED, "separate": MODE_SEPARATE, "streams": MODE_STREAMS}
+FLAG_DEBUG_CLAIMS = 1
+DEVICE_ERR_BAD_PAGE = 1
+
+STATUS = {0: "OK", -1: "ERR_INVALID_ARG", -2: "ERR_UNSUPPORTED", -3: "ERR_WORKSPACE",
+          -4: "ERR_HIP", -5: "ERR_NO_DEVICE"}
+
+
+class PodAttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class Config(C.Structure):
+    _fields_ = [("num_q_heads", C.c_int), ("num_kv_heads", C.c_int), ("head_dim", C.c_int),
+                ("page_size", C.c_int), ("dtype", C.c_int), ("mode", C.c_int), ("scale", C.c_float),
+                ("decode_split_tokens", C.c_int), ("prefill_split_cap", C.c_int),
+                ("wgs_per_cu", C.c_int), ("flags", C.c_int)]
+
+
+class Batch(C.Structure):
+    _fields_ = [("num_prefill", C.c_int), ("prefill_q_start", C.POINTER(C.c_int32)),
+                ("prefill_ctx_len", C.POINTER(C.c_int32)), ("num_decode", C.c_int),
+                ("decode_ctx_len", C.POINTER(C.c_int32)), ("block_table_stride", C.c_int),
+                ("num_pages_in_pool", C.c_int)]
+
+
+class Stats(C.Structure):
+    _fields_ = [(n, C.c_int) for n in (
+        "mode_requested", "mode_used", "fallback_reason", "num_prefill_items", "num_decode_items",
+        "num_combine_groups", "prefill_tile_cols", "prefill_tile_queries", "prefill_kv_tile",
+        "prefill_max_splits", "decode_split_tokens", "decode_max_splits", "grid_wgs", "wgs_per_cu",
+        "num_cus", "lds_bytes_per_wg", "vgprs_per_lane")] + [
+        ("workspace_bytes", C.c_size_t), ("host_plan_us", C.c_double)]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load the library once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise FileNotFoundError(f"{path} is missing: build it with `python -m hybrid_prefill_decode_paged_amd.build`")
+    lib = C.CDLL(path)
+    P, I, VP = C.POINTER, C.c_int, C.c_void_p
+    lib.pod_attn_create.argtypes = [P(Config), P(VP)]
+    lib.pod_attn_workspace_size.argtypes = [VP, P(Batch), P(C.c_size_t)]
+    lib.pod_attn_run.argtypes = [VP, VP, VP, VP, VP, P(Batch), VP, VP, C.c_size_t, VP]
+    lib.pod_attn_get_stats.argtypes = [VP, P(Stats)]
+    lib.pod_attn_gather_kv.argtypes = [VP, VP, I, VP, I, I, P(Batch), VP, VP]
+    lib.pod_attn_read_device_status.argtypes = [VP, VP, VP, P(C.c_int32), P(C.c_int32), I, P(I),
+                                                P(C.c_int32), P(C.c_int32), I]
+    lib.pod_attn_plan_inspect.argtypes = [P(Config), P(Batch), I, I, P(C.c_int32), I, P(I), P(Stats)]
+    lib.pod_attn_set_kernel_events.argtypes = [VP, VP, VP]
+    lib.pod_attn_last_error.restype = C.c_char_p
+    lib.pod_attn_destroy.argtypes = [VP]
+    lib.pod_attn_destroy.restype = None
+    for name in ("pod_attn_create", "pod_attn_workspace_size", "pod_attn_run", "pod_attn_get_stats",
+                 "pod_attn_gather_kv", "pod_attn_read_device_status", "pod_attn_plan_inspect",
+                 "pod_attn_set_kernel_events"):
+        getattr(lib, name).restype = C.c_int
+    _lib = lib
+    return lib
+
+
+def header_functions(header: str = HEADER):
+    """Names of the functions include/pod_attn.h declares."""
+    text = open(header).read()
+    return sorted(set(re.findall(r"^\s*(?:pod_attn_status|void|const char\*)\s+(pod_attn_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def _check(status: int):
+    if status != 0:
+        msg = load().pod_attn_last_error()
+        raise PodAttnError(status, msg.decode() if msg else "")
+
+
+def make_config(num_q_heads, num_kv_heads, head_dim, dtype="bf16", mode="fused", scale=0.0,
+                decode_split_tokens=0, prefill_split_cap=0, wgs_per_cu=0, flags=0) -> Config:
+    return Config(num_q_heads, num_kv_heads, head_dim, 16, BF16 if dtype == "bf16" else FP32,
+                  MODES[mode] if isinstance(mode, str) else int(mode), float(scale),
+                  int(decode_split_tokens), int(prefill_split_cap), int(wgs_per_cu), int(flags))
+
+
+class BatchMeta:
+    """Host metadata of one batch, kept alive while the C structure points into it."""
+
+    def __init__(self, prefill_q_start, prefill_ctx_len, decode_ctx_len, block_table_stride,
+                 num_pages_in_pool):
+        self.q_start = np.ascontiguousarray(prefill_q_start, dtype=np.int32)
+        self.p_ctx = np.ascontiguousarray(prefill_ctx_len, dtype=np.int32)
+        self.d_ctx = np.ascontiguousarray(decode_ctx_len, dtype=np.int32)
+        if len(self.q_start) == 0:
+            self.q_start = np.zeros(1, dtype=np.int32)
+        ptr = lambda a: a.ctypes.data_as(C.POINTER(C.c_int32))
+        self.c = Batch(len(self.p_ctx), ptr(self.q_start), ptr(self.p_ctx), len(self.d_ctx),
+                       ptr(self.d_ctx), int(block_table_stride), int(num_pages_in_pool))
+
+    @property
+    def total_q(self):
+        return int(self.q_start[len(self.p_ctx)]) + len(self.d_ctx)
+
+    @classmethod
+    def from_batch(cls, b):
+        return cls(b.prefill_q_start, b.prefill_ctx_len, b.decode_ctx_len,
+                   b.block_tables_host.shape[1], b.spec.num_pages)
+
+
+def plan_inspect(cfg: Config, meta: BatchMeta, num_cus: int, wgs_per_cu: int):
+    """Host-only planning (no GPU): (items [n, 16] int32, stats dict)."""
+    lib = load()
+    n = C.c_int(0)
+    st = Stats()
+    _check(lib.pod_attn_plan_inspect(C.byref(cfg), C.byref(meta.c), num_cus, wgs_per_cu, None, 0,
+                                     C.byref(n), C.byref(st)))
+    items = np.zeros((max(1, n.value), 16), dtype=np.int32)
+    _check(lib.pod_attn_plan_inspect(C.byref(cfg), C.byref(meta.c), num_cus, wgs_per_cu,
+                                     items.ctypes.data_as(C.POINTER(C.c_int32)), n.value,
+                                     C.byref(n), None))
+    return items[: n.value], st.as_dict()
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _stream_handle(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+class PodAttention:
+    """One library handle (one head configuration) on the current HIP device."""
+
+    def __init__(self, num_q_heads, num_kv_heads, head_dim, dtype="bf16", mode="fused", scale=0.0,
+                 decode_split_tokens=0, prefill_split_cap=0, wgs_per_cu=0, flags=0):
+        self.lib = load()
+        self.cfg = make_config(num_q_heads, num_kv_heads, head_dim, dtype, mode, scale,
+                               decode_split_tokens, prefill_split_cap, wgs_per_cu, flags)
+        h = C.c_void_p()
+        _check(self.lib.pod_attn_create(C.byref(self.cfg), C.byref(h)))
+        self.h = h
+        self.dtype = dtype
+
+    def close(self):
+        if getattr(self, "h", None):
+            self.lib.pod_attn_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace_size(self, meta: BatchMeta) -> int:
+        n = C.c_size_t(0)
+        _check(self.lib.pod_attn_workspace_size(self.h, C.byref(meta.c), C.byref(n)))
+        return n.value
+
+    def check_buffers(self, q, k_cache, v_cache, block_tables, meta: BatchMeta, out):
+        """Host-side shape checks of the caller's tensors against what the kernels will read."""
+        c = self.cfg
+        elem = 2 if c.dtype == BF16 else 4
+        want_q = meta.total_q * c.num_q_heads * c.head_dim
+        pool = meta.c.num_pages_in_pool * c.num_kv_heads * 16 * c.head_dim
+        n_seq = len(meta.p_ctx) + len(meta.d_ctx)
+        for name, t, n in (("q", q, want_q), ("out", out, want_q), ("k_cache", k_cache, pool),
+                           ("v_cache", v_cache, pool)):
+            if t.element_size() != elem or t.numel() < n or not t.is_contiguous():
+                raise PodAttnError(-1, f"{name}: need a contiguous tensor of >= {n} {elem}-byte elements, "
+                                       f"got {tuple(t.shape)} {t.dtype}")
+        if block_tables.element_size() != 4 or block_tables.numel() < n_seq * meta.c.block_table_stride \
+                or not block_tables.is_contiguous():
+            raise PodAttnError(-1, f"block_tables: need >= {n_seq}x{meta.c.block_table_stride} int32")
+
+    def run(self, q, k_cache, v_cache, block_tables, meta: BatchMeta, out, workspace, stream=None):
+        """pod_attn_run on device tensors; asynchronous on ``stream`` (default: torch's current)."""
+        if meta.total_q:
+            self.check_buffers(q, k_cache, v_cache, block_tables, meta, out)
+        _check(self.lib.pod_attn_run(self.h, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                     C.byref(meta.c), _ptr(out), _ptr(workspace),
+                                     0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                     _stream_handle(stream)))
+        return out
+
+    def set_kernel_events(self, ev_start, ev_end):
+        """Arm the one-shot profiling events (torch.cuda.Event objects) for the next run."""
+        _check(self.lib.pod_attn_set_kernel_events(self.h, C.c_void_p(ev_start.cuda_event),
+                                                   C.c_void_p(ev_end.cuda_event)))
+
+    def stats(self) -> dict:
+        st = Stats()
+        _check(self.lib.pod_attn_get_stats(self.h, C.byref(st)))
+        return st.as_dict()
+
+    def gather_kv(self, cache, which: int, block_tables, seq: int, ctx: int, meta: BatchMeta, out, stream=None):
+        _check(self.lib.pod_attn_gather_kv(self.h, _ptr(cache), int(which), _ptr(block_tables), int(seq),
+                                           int(ctx), C.byref(meta.c), _ptr(out), _stream_handle(stream)))
+        return out
+
+    def read_device_status(self, workspace, n_items_cap: int = 0, cu_cap: int = 0, stream=None):
+        """(status_word, claims[n] or None, (prefill_per_cu, decode_per_cu) or None)."""
+        status = C.c_int32(0)
+        n = C.c_int(0)
+        claims = np.zeros(max(1, n_items_cap), dtype=np.int32)
+        pf = np.zeros(max(1, cu_cap), dtype=np.int32)
+        dc = np.zeros(max(1, cu_cap), dtype=np.int32)
+        ip = lambda a: a.ctypes.data_as(C.POINTER(C.c_int32))
+        _check(self.lib.pod_attn_read_device_status(
+            self.h, _ptr(workspace), _stream_handle(stream), C.byref(status),
+            ip(claims) if n_items_cap else None, n_items_cap, C.byref(n),
+            ip(pf) if cu_cap else None, ip(dc) if cu_cap else None, cu_cap))
+        return (status.value, claims[: min(n.value, n_items_cap)] if n_items_cap else None,
+                (pf[:cu_cap], dc[:cu_cap]) if cu_cap else None)

@@ -1,0 +1,77 @@
+"""Build the C-ABI library libpod_attn.so (gfx950 code objects + host planner) in-tree.
+
+    python -m hybrid_prefill_decode_paged_amd.build
+
+Every call compiles from source with hipcc; nothing is cached between calls.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+OUT_DIR = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libpod_attn.so")
+ARCH = "gfx950"
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
+          "-I" + os.path.join(ROOT, "include")]
+# Device code: gfx950 only; packed-FP32 instructions disabled (see DESIGN notes on packed fp32).
+DEVICE = ["-x", "hip", f"--offload-arch={ARCH}", "-Xclang", "-target-feature",
+          "-Xclang", "-packed-fp32-ops", "-munsafe-fp-atomics"]
+
+SOURCES = [
+    ("pod_kernels.hip", True),
+    ("pod_api.cpp", False),
+    ("plan.cpp", False),
+]
+
+
+def _run(cmd):
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in p.stdout.splitlines()
+                    if "packed-fp32-ops" not in l and "is not a recognized feature" not in l)
+    if p.returncode != 0:
+        raise RuntimeError(f"build step failed ({p.returncode}): {' '.join(cmd)}\n{out}")
+    return out
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(OUT_DIR, exist_ok=True)
+    jobs = []
+    for src, device in SOURCES:
+        obj = os.path.join(OUT_DIR, src + ".o")
+        cmd = [HIPCC, *COMMON]
+        if device:
+            cmd += DEVICE
+        else:
+            cmd += ["-D__HIP_PLATFORM_AMD__"]
+        cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
+        jobs.append((cmd, obj))
+    with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        outs = list(ex.map(lambda j: _run(j[0]), jobs))
+    if verbose:
+        for o in outs:
+            if o.strip():
+                print(o)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp] + [o for _, o in jobs])
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+def clean():
+    shutil.rmtree(OUT_DIR, ignore_errors=True)
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

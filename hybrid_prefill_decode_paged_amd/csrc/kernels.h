@@ -1,0 +1,19 @@
+// Kernel entry points of one (dtype, head_dim) instantiation, as launchable function handles.
+#pragma once
+
+namespace pod {
+
+struct KernelSet {
+  const void* fused = nullptr;     // persistent fused prefill + decode kernel (KernelParams)
+  const void* prefill = nullptr;   // one workgroup per prefill item (KernelParams)
+  const void* decode = nullptr;    // one workgroup per decode item (KernelParams)
+  const void* combine = nullptr;   // one workgroup per combine group (KernelParams)
+  const void* gather = nullptr;    // debug gather (cache, which, bt_row, ctx, hkv, num_pages, out, status)
+  int fused_lds = 0;               // static LDS bytes of the fused kernel
+  int prefill_kv_tile = 0;         // keys per prefill inner iteration
+};
+
+// dtype: 0 bf16, 1 fp32; head_dim: 64 or 128.
+KernelSet kernel_set(int dtype, int head_dim);
+
+}  // namespace pod

@@ -1,0 +1,239 @@
+// Host planner: validation of the configuration and batch, and the split of the hybrid batch
+// into work items.
+//
+// Prefill: each chunk is cut into query tiles of floor(128 / group) rows, so that one tile is
+// 128 (query, head) columns sharing one KV head; a tile needs the keys up to its last query's
+// position.  Long tiles are split along the keys into at most `prefill_split_cap` ranges, the
+// cap that keeps one prefill chunk from flooding the machine with work items and pushing
+// decode out (Silicon & Systems, "POD-Attention hybrid batching", section "Virtual CTAs and
+// per-SM balance").
+// Decode: each (sequence, KV head) is split along its context into ranges of about
+// `decode_split_tokens` keys whose partial results are merged by log-sum-exp ("LLMSO - W4 -
+// Optimization & Frameworks", section "FlashDecoding -- decode 단계의 병렬성 확보"); the split
+// length is chosen from the total decode work and the number of persistent workgroups so that
+// every workgroup gets many small items and the last wave of work stays short (the wave
+// quantization loss of the same digest, section "Why concurrency alone is not enough").
+// Work is ordered longest first within each kind.
+#include "plan.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <numeric>
+
+namespace pod {
+
+namespace {
+int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+int round_up_int(int a, int m) { return ceil_div(a, m) * m; }
+}  // namespace
+
+pod_attn_status validate_config(const pod_attn_config* c, Config* out, std::string* err) {
+  if (!c || !out) { *err = "null config"; return POD_ATTN_ERR_INVALID_ARG; }
+  if (c->num_q_heads < 1 || c->num_kv_heads < 1) {
+    *err = "num_q_heads and num_kv_heads must be >= 1"; return POD_ATTN_ERR_INVALID_ARG;
+  }
+  if (c->num_q_heads % c->num_kv_heads != 0) {
+    *err = "num_q_heads must be a multiple of num_kv_heads"; return POD_ATTN_ERR_INVALID_ARG;
+  }
+  if (c->num_q_heads / c->num_kv_heads > kMaxGroup) {
+    *err = "query heads per KV head above 16 are not supported"; return POD_ATTN_ERR_UNSUPPORTED;
+  }
+  if (c->page_size != kPage) { *err = "page_size must be 16"; return POD_ATTN_ERR_UNSUPPORTED; }
+  if (c->head_dim != 64 && c->head_dim != 128) {
+    *err = "head_dim must be 64 or 128"; return POD_ATTN_ERR_UNSUPPORTED;
+  }
+  if (c->dtype != POD_ATTN_BF16 && c->dtype != POD_ATTN_FP32) {
+    *err = "dtype must be POD_ATTN_BF16 or POD_ATTN_FP32"; return POD_ATTN_ERR_INVALID_ARG;
+  }
+  if (c->mode < POD_ATTN_MODE_FUSED || c->mode > POD_ATTN_MODE_STREAMS) {
+    *err = "unknown mode"; return POD_ATTN_ERR_INVALID_ARG;
+  }
+  if (!(c->scale >= 0.f) || std::isinf(c->scale)) {
+    *err = "scale must be finite and >= 0"; return POD_ATTN_ERR_INVALID_ARG;
+  }
+  if (c->decode_split_tokens < 0 || (c->decode_split_tokens % 128) != 0) {
+    *err = "decode_split_tokens must be 0 or a positive multiple of 128"; return POD_ATTN_ERR_INVALID_ARG;
+  }
+  if (c->prefill_split_cap < 0 || c->wgs_per_cu < 0 || c->wgs_per_cu > 8) {
+    *err = "prefill_split_cap must be >= 0 and wgs_per_cu in [0, 8]"; return POD_ATTN_ERR_INVALID_ARG;
+  }
+  Config k;
+  k.hq = c->num_q_heads; k.hkv = c->num_kv_heads; k.d = c->head_dim; k.page = c->page_size;
+  k.dtype = c->dtype; k.mode = c->mode;
+  k.scale = c->scale > 0.f ? c->scale : 1.0f / std::sqrt((float)c->head_dim);
+  k.decode_split_tokens = c->decode_split_tokens; k.prefill_split_cap = c->prefill_split_cap;
+  k.wgs_per_cu = c->wgs_per_cu; k.flags = c->flags;
+  *out = k;
+  return POD_ATTN_OK;
+}
+
+pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus, int wgs_per_cu,
+                           Plan* out, std::string* err) {
+  if (!b) { *err = "null batch"; return POD_ATTN_ERR_INVALID_ARG; }
+  if (b->num_prefill < 0 || b->num_decode < 0) { *err = "negative sequence count"; return POD_ATTN_ERR_INVALID_ARG; }
+  if (b->num_prefill > 0 && (!b->prefill_q_start || !b->prefill_ctx_len)) {
+    *err = "prefill arrays are null"; return POD_ATTN_ERR_INVALID_ARG;
+  }
+  if (b->num_decode > 0 && !b->decode_ctx_len) { *err = "decode_ctx_len is null"; return POD_ATTN_ERR_INVALID_ARG; }
+  if (b->block_table_stride < 1) { *err = "block_table_stride must be >= 1"; return POD_ATTN_ERR_INVALID_ARG; }
+  if (b->num_pages_in_pool < 1) { *err = "num_pages_in_pool must be >= 1"; return POD_ATTN_ERR_INVALID_ARG; }
+  if (num_cus < 1 || wgs_per_cu < 1) { *err = "bad device shape"; return POD_ATTN_ERR_INVALID_ARG; }
+  const long max_ctx = (long)b->block_table_stride * kPage;
+  if (b->num_prefill > 0 && b->prefill_q_start[0] != 0) {
+    *err = "prefill_q_start[0] must be 0"; return POD_ATTN_ERR_INVALID_ARG;
+  }
+  for (int i = 0; i < b->num_prefill; ++i) {
+    long L = (long)b->prefill_q_start[i + 1] - b->prefill_q_start[i];
+    long ctx = b->prefill_ctx_len[i];
+    if (L < 0) { *err = "prefill_q_start must be non-decreasing (chunk " + std::to_string(i) + ")"; return POD_ATTN_ERR_INVALID_ARG; }
+    if (ctx < L) { *err = "prefill chunk " + std::to_string(i) + ": q_len exceeds ctx"; return POD_ATTN_ERR_INVALID_ARG; }
+    if (ctx > max_ctx) { *err = "prefill chunk " + std::to_string(i) + ": ctx exceeds block_table_stride*16"; return POD_ATTN_ERR_INVALID_ARG; }
+    if (ctx > (1L << 30)) { *err = "context too long"; return POD_ATTN_ERR_INVALID_ARG; }
+  }
+  for (int i = 0; i < b->num_decode; ++i) {
+    long ctx = b->decode_ctx_len[i];
+    if (ctx < 1) { *err = "decode " + std::to_string(i) + ": ctx must be >= 1"; return POD_ATTN_ERR_INVALID_ARG; }
+    if (ctx > max_ctx) { *err = "decode " + std::to_string(i) + ": ctx exceeds block_table_stride*16"; return POD_ATTN_ERR_INVALID_ARG; }
+    if (ctx > (1L << 30)) { *err = "context too long"; return POD_ATTN_ERR_INVALID_ARG; }
+  }
+  const long prefill_rows = b->num_prefill > 0 ? (long)b->prefill_q_start[b->num_prefill] : 0;
+  if (prefill_rows + b->num_decode > (1L << 30)) { *err = "too many query rows"; return POD_ATTN_ERR_INVALID_ARG; }
+
+  Plan p;
+  const int G = c.group();
+  p.tile_queries = kTileCols / G;
+  p.tile_cols = p.tile_queries * G;
+  p.prefill_rows = (int)prefill_rows;
+  p.total_q = (int)prefill_rows + b->num_decode;
+
+  // ---------------- prefill tiles
+  struct Tile { int seq, q_row, n_q, q_pos, kv_len; };
+  std::vector<Tile> tiles;
+  for (int i = 0; i < b->num_prefill; ++i) {
+    int L = b->prefill_q_start[i + 1] - b->prefill_q_start[i];
+    int ctx = b->prefill_ctx_len[i];
+    for (int t = 0; t < L; t += p.tile_queries) {
+      Tile tl;
+      tl.seq = i;
+      tl.q_row = b->prefill_q_start[i] + t;
+      tl.n_q = std::min(p.tile_queries, L - t);
+      tl.q_pos = ctx - L + t;
+      tl.kv_len = tl.q_pos + tl.n_q;
+      tiles.push_back(tl);
+    }
+  }
+  std::stable_sort(tiles.begin(), tiles.end(), [](const Tile& a, const Tile& b2) {
+    return (long)a.kv_len * a.n_q > (long)b2.kv_len * b2.n_q;
+  });
+  const int cap = c.prefill_split_cap > 0 ? c.prefill_split_cap : 8;
+  int item = 0, group = 0, slot = 0;
+  p.prefill_max_splits = 0;
+  for (const Tile& tl : tiles) {
+    int ns = std::max(1, std::min(cap, ceil_div(tl.kv_len, 4096)));
+    int st = round_up_int(ceil_div(tl.kv_len, ns), kPrefillKvTile);
+    ns = ceil_div(tl.kv_len, st);
+    std::vector<int32_t> d(kDescInts, 0);
+    d[kDSeq] = tl.seq; d[kDQRow] = tl.q_row; d[kDNq] = tl.n_q; d[kDQPos] = tl.q_pos;
+    d[kDKvLen] = tl.kv_len; d[kDNSplit] = ns; d[kDSplitTok] = st; d[kDItemBegin] = item;
+    d[kDGroupBegin] = group; d[kDPartBase] = slot; d[kDNcols] = tl.n_q * G;
+    item += c.hkv * ns;
+    if (ns > 1) { group += c.hkv; slot += c.hkv * ns * tl.n_q * G; }
+    p.prefill_max_splits = std::max(p.prefill_max_splits, ns);
+    p.pdesc.insert(p.pdesc.end(), d.begin(), d.end());
+  }
+  p.n_pdesc = (int)tiles.size();
+  p.n_pf_items = item;
+  p.n_pf_groups = group;
+
+  // ---------------- decode sequences
+  long total_tok = 0;
+  for (int i = 0; i < b->num_decode; ++i) total_tok += (long)b->decode_ctx_len[i] * c.hkv;
+  int st_target;
+  if (c.decode_split_tokens > 0) {
+    st_target = c.decode_split_tokens;
+  } else {
+    long target_items = (long)num_cus * wgs_per_cu * 16;
+    long st = (total_tok + target_items - 1) / std::max(1L, target_items);
+    st = std::max(512L, std::min(4096L, st));
+    st_target = round_up_int((int)st, 128);
+  }
+  p.decode_split_tokens = st_target;
+  std::vector<int> order(b->num_decode);
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(), [&](int x, int y) {
+    return b->decode_ctx_len[x] > b->decode_ctx_len[y];
+  });
+  int ditem = 0;
+  p.decode_max_splits = 0;
+  for (int i : order) {
+    int ctx = b->decode_ctx_len[i];
+    int ns = ceil_div(ctx, st_target);
+    int st = round_up_int(ceil_div(ctx, ns), 128);
+    ns = ceil_div(ctx, st);
+    std::vector<int32_t> d(kDescInts, 0);
+    d[kDSeq] = b->num_prefill + i; d[kDQRow] = (int)prefill_rows + i; d[kDNq] = 1;
+    d[kDQPos] = ctx - 1; d[kDKvLen] = ctx; d[kDNSplit] = ns; d[kDSplitTok] = st;
+    d[kDItemBegin] = ditem; d[kDGroupBegin] = group; d[kDPartBase] = slot; d[kDNcols] = G;
+    ditem += c.hkv * ns;
+    if (ns > 1) { group += c.hkv; slot += c.hkv * ns * G; }
+    p.decode_max_splits = std::max(p.decode_max_splits, ns);
+    p.ddesc.insert(p.ddesc.end(), d.begin(), d.end());
+  }
+  p.n_ddesc = b->num_decode;
+  p.n_dc_items = ditem;
+  p.n_groups = group;
+  p.n_slots = slot;
+
+  // ---------------- workspace map
+  WorkspaceMap m{};
+  size_t off = 0;
+  m.ctrl = off; off = align_up(off + sizeof(int32_t) * kCtrlInts, 256);
+  m.tickets = off; off = align_up(off + sizeof(int32_t) * std::max(1, p.n_groups), 256);
+  m.claims = off;
+  if (c.flags & POD_ATTN_FLAG_DEBUG_CLAIMS)
+    off = align_up(off + sizeof(int32_t) * std::max(1, p.n_pf_items + p.n_dc_items), 256);
+  m.pdesc = off; off = align_up(off + sizeof(int32_t) * std::max<size_t>(1, p.pdesc.size()), 256);
+  m.ddesc = off; off = align_up(off + sizeof(int32_t) * std::max<size_t>(1, p.ddesc.size()), 256);
+  m.copy_bytes = off;
+  m.part_o = off; off = align_up(off + sizeof(float) * (size_t)p.n_slots * c.d, 256);
+  m.part_lse = off; off = align_up(off + sizeof(float) * (size_t)std::max(1, p.n_slots), 256);
+  m.total = off;
+  p.map = m;
+  *out = std::move(p);
+  return POD_ATTN_OK;
+}
+
+void stage_plan(const Plan& p, const Config& c, uint8_t* dst) {
+  std::memset(dst, 0, p.map.copy_bytes);
+  if (!p.pdesc.empty()) std::memcpy(dst + p.map.pdesc, p.pdesc.data(), p.pdesc.size() * 4);
+  if (!p.ddesc.empty()) std::memcpy(dst + p.map.ddesc, p.ddesc.data(), p.ddesc.size() * 4);
+  (void)c;
+}
+
+void expand_items(const Plan& p, const Config& c, std::vector<int32_t>* items) {
+  items->clear();
+  const int G = c.group();
+  for (int kind = 0; kind < 2; ++kind) {
+    const std::vector<int32_t>& D = kind == 0 ? p.pdesc : p.ddesc;
+    const int n = kind == 0 ? p.n_pdesc : p.n_ddesc;
+    for (int di = 0; di < n; ++di) {
+      const int32_t* d = &D[(size_t)di * kDescInts];
+      const int ns = d[kDNSplit], st = d[kDSplitTok];
+      for (int h = 0; h < c.hkv; ++h) {
+        for (int s = 0; s < ns; ++s) {
+          int32_t it[16] = {0};
+          it[0] = d[kDSeq]; it[1] = d[kDQRow]; it[2] = d[kDNq]; it[3] = d[kDQPos];
+          it[4] = h; it[5] = s * st; it[6] = std::min(d[kDKvLen], (s + 1) * st);
+          it[7] = ns > 1 ? d[kDGroupBegin] + h : -1;
+          it[8] = s;
+          it[9] = ns > 1 ? d[kDPartBase] + (h * ns + s) * d[kDNq] * G : -1;
+          it[10] = kind;
+          items->insert(items->end(), it, it + 16);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace pod

@@ -1,0 +1,40 @@
+// Host planner for one hybrid batch: validates the metadata and splits the work into prefill
+// tile items and decode split-KV items (host-only code, no HIP calls).
+#pragma once
+#include <string>
+#include <vector>
+
+#include "../../include/pod_attn.h"
+#include "pod_internal.h"
+
+namespace pod {
+
+struct Config {
+  int hq = 0, hkv = 0, d = 0, page = 16, dtype = 0, mode = 0;
+  float scale = 0.f;
+  int decode_split_tokens = 0, prefill_split_cap = 0, wgs_per_cu = 0, flags = 0;
+  int group() const { return hq / hkv; }
+  int elem_bytes() const { return dtype == POD_ATTN_BF16 ? 2 : 4; }
+};
+
+struct Plan {
+  std::vector<int32_t> pdesc, ddesc;   // kDescInts each
+  int n_pdesc = 0, n_ddesc = 0;
+  int n_pf_items = 0, n_dc_items = 0;
+  int n_pf_groups = 0, n_groups = 0, n_slots = 0;
+  int tile_queries = 0, tile_cols = 0;
+  int prefill_max_splits = 0, decode_split_tokens = 0, decode_max_splits = 0;
+  int total_q = 0, prefill_rows = 0;
+  WorkspaceMap map{};
+};
+
+// Returns POD_ATTN_OK or an error status with *err set.
+pod_attn_status validate_config(const pod_attn_config* c, Config* out, std::string* err);
+pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus, int wgs_per_cu,
+                           Plan* out, std::string* err);
+// Write the host-staged prefix of the workspace ([0, map.copy_bytes)) into dst.
+void stage_plan(const Plan& p, const Config& c, uint8_t* dst);
+// Expand descriptor-encoded items to the 16-int form of pod_attn_plan_inspect.
+void expand_items(const Plan& p, const Config& c, std::vector<int32_t>* items);
+
+}  // namespace pod

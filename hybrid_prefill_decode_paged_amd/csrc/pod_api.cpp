@@ -1,0 +1,385 @@
+// C ABI of the hybrid-batch attention library: handle, planning, staging of the plan into the
+// caller's workspace, and the three launch modes (fused, separate, two streams) that the
+// Silicon & Systems digest "POD-Attention hybrid batching" compares (sections "Why
+// concurrency alone is not enough" and "Reproduction and hardware evaluation"), with the
+// diagnostics its section "Predictable latency and diagnostics" asks a runtime to expose.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <chrono>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/pod_attn.h"
+#include "kernels.h"
+#include "plan.h"
+
+using namespace pod;
+
+namespace {
+thread_local std::string g_err;
+
+pod_attn_status fail(pod_attn_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+#define POD_HIP(x)                                                                      \
+  do {                                                                                  \
+    hipError_t e_ = (x);                                                                \
+    if (e_ != hipSuccess) return fail(POD_ATTN_ERR_HIP, std::string(#x) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+int env_int(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  if (!v || !*v) return dflt;
+  return std::atoi(v);
+}
+
+bool log_on() { return env_int("POD_ATTN_LOG", 0) != 0; }
+
+struct StagingSlot {
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t done = nullptr;
+  bool pending = false;
+};
+constexpr int kRing = 4;
+}  // namespace
+
+struct pod_attn_handle {
+  Config cfg;
+  int device = 0;
+  int num_cus = 0;
+  int wgs_per_cu = 0;
+  int fused_occupancy = 0;
+  int fused_vgprs = 0;
+  KernelSet ks;
+  hipStream_t sA = nullptr, sB = nullptr;
+  hipEvent_t evStart = nullptr, evA = nullptr, evB = nullptr;
+  StagingSlot ring[kRing];
+  int ring_next = 0;
+  pod_attn_stats stats{};
+  Plan last_plan;
+  int mode_env = -1;
+  hipEvent_t prof_start = nullptr, prof_end = nullptr;   // one-shot profiling events
+};
+
+extern "C" {
+
+const char* pod_attn_last_error(void) { return g_err.c_str(); }
+
+pod_attn_status pod_attn_create(const pod_attn_config* cfg, pod_attn_handle** out) {
+  if (!out) return fail(POD_ATTN_ERR_INVALID_ARG, "null output handle pointer");
+  *out = nullptr;
+  Config c;
+  std::string err;
+  pod_attn_status st = validate_config(cfg, &c, &err);
+  if (st != POD_ATTN_OK) return fail(st, err);
+
+  int dev = 0, ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return fail(POD_ATTN_ERR_NO_DEVICE, "no HIP device");
+  POD_HIP(hipGetDevice(&dev));
+  hipDeviceProp_t prop;
+  POD_HIP(hipGetDeviceProperties(&prop, dev));
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(POD_ATTN_ERR_NO_DEVICE, std::string("device is ") + prop.gcnArchName + ", built for gfx950");
+
+  pod_attn_handle* h = new pod_attn_handle();
+  h->cfg = c;
+  h->device = dev;
+  h->num_cus = prop.multiProcessorCount;
+  h->ks = kernel_set(c.dtype, c.d);
+
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, h->ks.fused, kThreads, 0) != hipSuccess) occ = 0;
+  h->fused_occupancy = occ;
+  hipFuncAttributes fa;
+  if (hipFuncGetAttributes(&fa, h->ks.fused) == hipSuccess) h->fused_vgprs = fa.numRegs;
+  int w = c.wgs_per_cu > 0 ? c.wgs_per_cu : env_int("POD_ATTN_WGS_PER_CU", 0);
+  if (w <= 0) w = std::min(occ, 2);
+  h->wgs_per_cu = std::max(1, std::min(w, std::max(1, occ)));
+  if (c.decode_split_tokens == 0) h->cfg.decode_split_tokens = env_int("POD_ATTN_DECODE_SPLIT_TOKENS", 0) / 128 * 128;
+  if (c.prefill_split_cap == 0) h->cfg.prefill_split_cap = std::max(0, env_int("POD_ATTN_PREFILL_SPLIT_CAP", 0));
+  if (const char* m = std::getenv("POD_ATTN_MODE")) {
+    if (!std::strcmp(m, "fused")) h->mode_env = POD_ATTN_MODE_FUSED;
+    else if (!std::strcmp(m, "separate")) h->mode_env = POD_ATTN_MODE_SEPARATE;
+    else if (!std::strcmp(m, "streams")) h->mode_env = POD_ATTN_MODE_STREAMS;
+  }
+
+  hipError_t e = hipSuccess;
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&h->sA, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&h->sB, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&h->evStart, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&h->evA, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&h->evB, hipEventDisableTiming);
+  for (int i = 0; i < kRing && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&h->ring[i].done, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    pod_attn_destroy(h);
+    return fail(POD_ATTN_ERR_HIP, std::string("stream/event creation: ") + hipGetErrorString(e));
+  }
+  h->stats.num_cus = h->num_cus;
+  h->stats.wgs_per_cu = h->wgs_per_cu;
+  h->stats.lds_bytes_per_wg = h->ks.fused_lds;
+  h->stats.vgprs_per_lane = h->fused_vgprs;
+  h->stats.prefill_kv_tile = h->ks.prefill_kv_tile;
+  if (log_on())
+    std::fprintf(stderr, "[pod_attn] create: Hq=%d Hkv=%d D=%d dtype=%d mode=%d cus=%d occ=%d wgs/cu=%d vgprs=%d lds=%d\n",
+                 c.hq, c.hkv, c.d, c.dtype, c.mode, h->num_cus, occ, h->wgs_per_cu, h->fused_vgprs, h->ks.fused_lds);
+  *out = h;
+  return POD_ATTN_OK;
+}
+
+void pod_attn_destroy(pod_attn_handle* h) {
+  if (!h) return;
+  for (int i = 0; i < kRing; ++i) {
+    if (h->ring[i].done) {
+      if (h->ring[i].pending) (void)hipEventSynchronize(h->ring[i].done);
+      (void)hipEventDestroy(h->ring[i].done);
+    }
+    if (h->ring[i].host) (void)hipHostFree(h->ring[i].host);
+  }
+  if (h->evStart) (void)hipEventDestroy(h->evStart);
+  if (h->evA) (void)hipEventDestroy(h->evA);
+  if (h->evB) (void)hipEventDestroy(h->evB);
+  if (h->sA) (void)hipStreamDestroy(h->sA);
+  if (h->sB) (void)hipStreamDestroy(h->sB);
+  delete h;
+}
+
+pod_attn_status pod_attn_workspace_size(pod_attn_handle* h, const pod_attn_batch* b, size_t* bytes) {
+  if (!h || !bytes) return fail(POD_ATTN_ERR_INVALID_ARG, "null handle or output");
+  Plan p;
+  std::string err;
+  pod_attn_status st = plan_batch(h->cfg, b, h->num_cus, h->wgs_per_cu, &p, &err);
+  if (st != POD_ATTN_OK) return fail(st, err);
+  *bytes = p.map.total;
+  return POD_ATTN_OK;
+}
+
+static hipError_t launch(const void* fn, int grid, KernelParams& p, hipStream_t s) {
+  void* args[] = {&p};
+  return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
+}
+
+pod_attn_status pod_attn_run(pod_attn_handle* h, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, const pod_attn_batch* b, void* out,
+                             void* workspace, size_t workspace_bytes, void* stream_) {
+  if (!h) return fail(POD_ATTN_ERR_INVALID_ARG, "null handle");
+  hipStream_t stream = (hipStream_t)stream_;
+  const auto t0 = std::chrono::steady_clock::now();
+  Plan p;
+  std::string err;
+  pod_attn_status st = plan_batch(h->cfg, b, h->num_cus, h->wgs_per_cu, &p, &err);
+  if (st != POD_ATTN_OK) return fail(st, err);
+  const double plan_us = std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t0).count();
+  if (p.total_q == 0) return POD_ATTN_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !out)
+    return fail(POD_ATTN_ERR_INVALID_ARG, "null device buffer (q, k_cache, v_cache, block_tables or out)");
+  if (!workspace) return fail(POD_ATTN_ERR_WORKSPACE, "null workspace");
+  if (workspace_bytes < p.map.total)
+    return fail(POD_ATTN_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) + " bytes, needs " +
+                                            std::to_string(p.map.total));
+  if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out | (uintptr_t)workspace) & 15)
+    return fail(POD_ATTN_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+
+  // mode
+  const int requested = h->mode_env >= 0 ? h->mode_env : h->cfg.mode;
+  int mode = requested;
+  int reason = h->mode_env >= 0 && h->mode_env != h->cfg.mode ? POD_ATTN_FALLBACK_ENV : POD_ATTN_FALLBACK_NONE;
+  if (mode == POD_ATTN_MODE_FUSED) {
+    if (h->fused_occupancy < 1) {
+      mode = POD_ATTN_MODE_SEPARATE;
+      reason = POD_ATTN_FALLBACK_OCCUPANCY;
+    } else if (p.n_pf_items == 0) {
+      reason = POD_ATTN_FALLBACK_NO_PREFILL;
+    } else if (p.n_dc_items == 0) {
+      reason = POD_ATTN_FALLBACK_NO_DECODE;
+    }
+  }
+
+  // stage the plan (descriptors + zeroed counters) through a pinned ring and copy it in
+  StagingSlot& slot = h->ring[h->ring_next];
+  h->ring_next = (h->ring_next + 1) % kRing;
+  if (slot.pending) {
+    POD_HIP(hipEventSynchronize(slot.done));
+    slot.pending = false;
+  }
+  if (slot.cap < p.map.copy_bytes) {
+    if (slot.host) POD_HIP(hipHostFree(slot.host));
+    slot.host = nullptr;
+    slot.cap = 0;
+    size_t cap = std::max<size_t>(p.map.copy_bytes * 2, 1 << 16);
+    POD_HIP(hipHostMalloc(&slot.host, cap, hipHostMallocDefault));
+    slot.cap = cap;
+  }
+  stage_plan(p, h->cfg, (uint8_t*)slot.host);
+  POD_HIP(hipMemcpyAsync(workspace, slot.host, p.map.copy_bytes, hipMemcpyHostToDevice, stream));
+  POD_HIP(hipEventRecord(slot.done, stream));
+  slot.pending = true;
+
+  uint8_t* ws = (uint8_t*)workspace;
+  KernelParams kp{};
+  kp.q = q; kp.k = k_cache; kp.v = v_cache; kp.bt = block_tables; kp.out = out;
+  kp.ctrl = (int32_t*)(ws + p.map.ctrl);
+  kp.tickets = (int32_t*)(ws + p.map.tickets);
+  kp.claims = (h->cfg.flags & POD_ATTN_FLAG_DEBUG_CLAIMS) ? (int32_t*)(ws + p.map.claims) : nullptr;
+  kp.pdesc = (const int32_t*)(ws + p.map.pdesc);
+  kp.ddesc = (const int32_t*)(ws + p.map.ddesc);
+  kp.part_o = (float*)(ws + p.map.part_o);
+  kp.part_lse = (float*)(ws + p.map.part_lse);
+  kp.n_pdesc = p.n_pdesc; kp.n_ddesc = p.n_ddesc;
+  kp.n_pf_items = p.n_pf_items; kp.n_dc_items = p.n_dc_items;
+  kp.n_pf_groups = p.n_pf_groups; kp.n_groups = p.n_groups;
+  kp.hq = h->cfg.hq; kp.hkv = h->cfg.hkv; kp.group = h->cfg.group();
+  kp.bt_stride = b->block_table_stride; kp.num_pages = b->num_pages_in_pool;
+  kp.scale_log2 = h->cfg.scale * 1.4426950408889634f;
+  kp.prefill_cap_per_cu = std::max(1, h->wgs_per_cu / 2);
+
+  hipEvent_t prof_start = h->prof_start, prof_end = h->prof_end;
+  h->prof_start = h->prof_end = nullptr;
+  if (prof_start) POD_HIP(hipEventRecord(prof_start, stream));
+  int grid = 0;
+  if (mode == POD_ATTN_MODE_FUSED) {
+    kp.inline_combine = 1;
+    grid = h->num_cus * h->wgs_per_cu;
+    POD_HIP(launch(h->ks.fused, grid, kp, stream));
+  } else if (mode == POD_ATTN_MODE_SEPARATE) {
+    kp.inline_combine = 0;
+    if (p.n_pf_items) POD_HIP(launch(h->ks.prefill, p.n_pf_items, kp, stream));
+    if (p.n_dc_items) POD_HIP(launch(h->ks.decode, p.n_dc_items, kp, stream));
+    if (p.n_groups) {
+      kp.group_begin = 0; kp.group_end = p.n_groups;
+      POD_HIP(launch(h->ks.combine, p.n_groups, kp, stream));
+    }
+  } else {
+    kp.inline_combine = 0;
+    POD_HIP(hipEventRecord(h->evStart, stream));
+    POD_HIP(hipStreamWaitEvent(h->sA, h->evStart, 0));
+    POD_HIP(hipStreamWaitEvent(h->sB, h->evStart, 0));
+    if (p.n_pf_items) POD_HIP(launch(h->ks.prefill, p.n_pf_items, kp, h->sA));
+    if (p.n_pf_groups) {
+      KernelParams c = kp;
+      c.group_begin = 0; c.group_end = p.n_pf_groups;
+      POD_HIP(launch(h->ks.combine, p.n_pf_groups, c, h->sA));
+    }
+    if (p.n_dc_items) POD_HIP(launch(h->ks.decode, p.n_dc_items, kp, h->sB));
+    if (p.n_groups > p.n_pf_groups) {
+      KernelParams c = kp;
+      c.group_begin = p.n_pf_groups; c.group_end = p.n_groups;
+      POD_HIP(launch(h->ks.combine, p.n_groups - p.n_pf_groups, c, h->sB));
+    }
+    POD_HIP(hipEventRecord(h->evA, h->sA));
+    POD_HIP(hipEventRecord(h->evB, h->sB));
+    POD_HIP(hipStreamWaitEvent(stream, h->evA, 0));
+    POD_HIP(hipStreamWaitEvent(stream, h->evB, 0));
+  }
+  if (prof_end) POD_HIP(hipEventRecord(prof_end, stream));
+
+  pod_attn_stats& s = h->stats;
+  s.mode_requested = requested;
+  s.mode_used = mode;
+  s.fallback_reason = reason;
+  s.num_prefill_items = p.n_pf_items;
+  s.num_decode_items = p.n_dc_items;
+  s.num_combine_groups = p.n_groups;
+  s.prefill_tile_cols = p.tile_cols;
+  s.prefill_tile_queries = p.tile_queries;
+  s.prefill_max_splits = p.prefill_max_splits;
+  s.decode_split_tokens = p.decode_split_tokens;
+  s.decode_max_splits = p.decode_max_splits;
+  s.grid_wgs = grid;
+  s.workspace_bytes = p.map.total;
+  s.host_plan_us = plan_us;
+  if (log_on())
+    std::fprintf(stderr, "[pod_attn] run: mode=%d reason=%d pf_items=%d dc_items=%d groups=%d split=%d grid=%d plan=%.1fus\n",
+                 mode, reason, p.n_pf_items, p.n_dc_items, p.n_groups, p.decode_split_tokens, grid, plan_us);
+  h->last_plan = std::move(p);
+  return POD_ATTN_OK;
+}
+
+pod_attn_status pod_attn_set_kernel_events(pod_attn_handle* h, void* ev_start, void* ev_end) {
+  if (!h) return fail(POD_ATTN_ERR_INVALID_ARG, "null handle");
+  h->prof_start = (hipEvent_t)ev_start;
+  h->prof_end = (hipEvent_t)ev_end;
+  return POD_ATTN_OK;
+}
+
+pod_attn_status pod_attn_get_stats(pod_attn_handle* h, pod_attn_stats* st) {
+  if (!h || !st) return fail(POD_ATTN_ERR_INVALID_ARG, "null handle or stats");
+  *st = h->stats;
+  return POD_ATTN_OK;
+}
+
+pod_attn_status pod_attn_gather_kv(pod_attn_handle* h, const void* cache, int which, const int32_t* block_tables,
+                                   int seq, int ctx, const pod_attn_batch* b, void* out_contig, void* stream) {
+  if (!h || !cache || !block_tables || !b || !out_contig) return fail(POD_ATTN_ERR_INVALID_ARG, "null argument");
+  if (which != 0 && which != 1) return fail(POD_ATTN_ERR_INVALID_ARG, "which must be 0 (K) or 1 (V)");
+  if (seq < 0 || seq >= b->num_prefill + b->num_decode) return fail(POD_ATTN_ERR_INVALID_ARG, "seq out of range");
+  if (ctx < 1 || (long)ctx > (long)b->block_table_stride * kPage) return fail(POD_ATTN_ERR_INVALID_ARG, "ctx out of range");
+  const size_t total = (size_t)ctx * h->cfg.hkv * h->cfg.d;
+  const int grid = (int)((total + kThreads - 1) / kThreads);
+  const int32_t* row = block_tables + (size_t)seq * b->block_table_stride;
+  int hkv = h->cfg.hkv, np = b->num_pages_in_pool;
+  int32_t* status = nullptr;
+  void* args[] = {(void*)&cache, &which, (void*)&row, &ctx, &hkv, &np, &out_contig, (void*)&status};
+  POD_HIP(hipLaunchKernel(h->ks.gather, dim3(grid), dim3(kThreads), args, 0, (hipStream_t)stream));
+  return POD_ATTN_OK;
+}
+
+pod_attn_status pod_attn_read_device_status(pod_attn_handle* h, const void* workspace, void* stream,
+                                            int32_t* status_word, int32_t* claims, int claims_cap, int* n_items,
+                                            int32_t* pf_cu, int32_t* dc_cu, int cu_cap) {
+  if (!h || !workspace) return fail(POD_ATTN_ERR_INVALID_ARG, "null handle or workspace");
+  POD_HIP(hipStreamSynchronize((hipStream_t)stream));
+  const uint8_t* ws = (const uint8_t*)workspace;
+  const Plan& p = h->last_plan;
+  if (status_word) POD_HIP(hipMemcpy(status_word, ws + p.map.ctrl + 4 * kCStatus, 4, hipMemcpyDeviceToHost));
+  const int n = p.n_pf_items + p.n_dc_items;
+  if (n_items) *n_items = n;
+  if (claims && claims_cap > 0 && (h->cfg.flags & POD_ATTN_FLAG_DEBUG_CLAIMS))
+    POD_HIP(hipMemcpy(claims, ws + p.map.claims, 4 * (size_t)std::min(n, claims_cap), hipMemcpyDeviceToHost));
+  const int m = std::min(cu_cap, (int)kCuSlots);
+  if (pf_cu && m > 0) POD_HIP(hipMemcpy(pf_cu, ws + p.map.ctrl + 4 * kCClaimsPrefillCu, 4 * (size_t)m, hipMemcpyDeviceToHost));
+  if (dc_cu && m > 0) POD_HIP(hipMemcpy(dc_cu, ws + p.map.ctrl + 4 * kCClaimsDecodeCu, 4 * (size_t)m, hipMemcpyDeviceToHost));
+  return POD_ATTN_OK;
+}
+
+pod_attn_status pod_attn_plan_inspect(const pod_attn_config* cfg, const pod_attn_batch* b, int num_cus, int wgs_per_cu,
+                                      int32_t* items, int items_cap, int* n_items, pod_attn_stats* stats) {
+  Config c;
+  std::string err;
+  pod_attn_status st = validate_config(cfg, &c, &err);
+  if (st != POD_ATTN_OK) return fail(st, err);
+  Plan p;
+  st = plan_batch(c, b, num_cus, wgs_per_cu, &p, &err);
+  if (st != POD_ATTN_OK) return fail(st, err);
+  std::vector<int32_t> all;
+  expand_items(p, c, &all);
+  const int n = (int)(all.size() / 16);
+  if (n_items) *n_items = n;
+  if (items && items_cap > 0) std::memcpy(items, all.data(), 4 * 16 * (size_t)std::min(n, items_cap));
+  if (stats) {
+    pod_attn_stats s{};
+    s.mode_requested = c.mode;
+    s.mode_used = c.mode;
+    s.num_prefill_items = p.n_pf_items;
+    s.num_decode_items = p.n_dc_items;
+    s.num_combine_groups = p.n_groups;
+    s.prefill_tile_cols = p.tile_cols;
+    s.prefill_tile_queries = p.tile_queries;
+    s.prefill_max_splits = p.prefill_max_splits;
+    s.decode_split_tokens = p.decode_split_tokens;
+    s.decode_max_splits = p.decode_max_splits;
+    s.num_cus = num_cus;
+    s.wgs_per_cu = wgs_per_cu;
+    s.workspace_bytes = p.map.total;
+    *stats = s;
+  }
+  return POD_ATTN_OK;
+}
+
+}  // extern "C"

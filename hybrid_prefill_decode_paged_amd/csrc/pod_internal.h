@@ -1,0 +1,79 @@
+// Internal layout shared by the host planner and the gfx950 kernels: work descriptors,
+// workspace map and kernel parameter block.  Not part of the public ABI.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pod {
+
+constexpr int kPage = 16;            // tokens per KV page
+constexpr int kWaves = 4;            // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTileCols = 128;       // (query, head) columns of one prefill tile: 4 waves x 32
+constexpr int kMaxGroup = 16;        // decode columns = group size, one 16-wide MFMA block
+constexpr int kPrefillKvTile = 64;   // keys per prefill inner iteration (4 pages)
+constexpr int kDecodeStep = 32;      // keys per decode wave step (2 pages)
+constexpr int kCuSlots = 1024;       // hashed (XCC, SE, CU) slots for per-CU scheduler state
+
+// A descriptor covers one prefill query tile or one decode sequence; it expands to
+// Hkv * n_split work items (item = (kv head, KV split)), head-major.
+enum DescField {
+  kDSeq = 0,        // block-table row
+  kDQRow,           // first q/out row
+  kDNq,             // query rows (decode: 1)
+  kDQPos,           // absolute position of the first query row
+  kDKvLen,          // keys the tile needs: last query position + 1 (decode: ctx)
+  kDNSplit,         // KV splits per head (>= 1)
+  kDSplitTok,       // tokens per split (multiple of the kind's key step)
+  kDItemBegin,      // first item index within the kind's item list
+  kDGroupBegin,     // first combine group (one per head) when n_split > 1, else -1
+  kDPartBase,       // first partial slot when n_split > 1
+  kDNcols,          // columns = n_q * group
+  kDescInts = 16
+};
+
+// Control block (int32 words at the start of the workspace), zeroed by every run.
+enum CtrlWord {
+  kCQueuePrefill = 0,
+  kCQueueDecode = 64,
+  kCStatus = 128,
+  kCActivePrefill = 256,                    // [kCuSlots] prefill-role WGs now on each CU
+  kCClaimsPrefillCu = 256 + kCuSlots,       // [kCuSlots] prefill items claimed per CU
+  kCClaimsDecodeCu = 256 + 2 * kCuSlots,    // [kCuSlots] decode items claimed per CU
+  kCtrlInts = 256 + 3 * kCuSlots
+};
+
+enum StatusBits { kStatusBadPage = 1 };
+
+struct KernelParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* bt;
+  void* out;
+  int32_t* ctrl;
+  int32_t* tickets;          // [n_groups]
+  int32_t* claims;           // [n_pf_items + n_dc_items] or null
+  const int32_t* pdesc;      // prefill descriptors
+  const int32_t* ddesc;      // decode descriptors
+  float* part_o;             // [slots][D]
+  float* part_lse;           // [slots], log2-domain log-sum-exp
+  int n_pdesc, n_ddesc;
+  int n_pf_items, n_dc_items;
+  int n_pf_groups, n_groups; // groups [0, n_pf_groups) are prefill, the rest decode
+  int hq, hkv, group, bt_stride, num_pages;
+  float scale_log2;          // softmax scale * log2(e)
+  int prefill_cap_per_cu;    // fused: prefill-role workgroups allowed per CU while decode remains
+  int inline_combine;        // 1: last-arriving split combines in-kernel (fused)
+  int group_begin, group_end;// combine kernel range
+};
+
+// Workspace map (byte offsets), computed by the planner.
+struct WorkspaceMap {
+  size_t ctrl, tickets, claims, pdesc, ddesc, copy_bytes;  // [0, copy_bytes) is host-staged
+  size_t part_o, part_lse, total;
+};
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace pod

@@ -1,0 +1,820 @@
+// gfx950 (MI355X, CDNA4) kernels for fused hybrid-batch paged attention.
+//
+// Sources (web pages; sections as printed on them):
+//   [POD] Silicon & Systems digest "POD-Attention hybrid batching"
+//   [W6]  "Week 6: Beyond PyTorch: Custom Kernel과 vLLM"
+//   [W4]  "LLMSO - W4 - Optimization & Frameworks"
+//
+// What every kernel computes is exact attention, softmax(scale * q K^T, causal by absolute
+// position) V, over K/V read through block tables ([W6] "Attention에 적용하기",
+// "Non-Causal vs. Causal Attention", "PagedAttention").  The kernels evaluate it with the
+// online softmax: a running maximum m and running sum l per query column, the running output
+// rescaled by exp(m_old - m_new) whenever the maximum grows, one division at the end ([W6]
+// "FlashAttention의 single-pass 트릭"; [W4] "FlashAttention -- I/O를 줄이는 방향").  Key
+// ranges that are split over several work items are merged by log-sum-exp ([W4]
+// "FlashDecoding -- decode 단계의 병렬성 확보").  Exponentials are taken base 2 with
+// log2(e) folded into the scale, which is the same function.
+//
+// Matrix layout on the MFMA units.  Both products run as 16x16 MFMA blocks with the keys on
+// the M side and the (query, head) columns on the N side:
+//   S^T[key][col]  = K[key][:] . Q[col][:]          (A = K rows, B = Q^T)
+//   O^T[d][col]   += V^T[d][key] . P^T[key][col]     (A = V^T rows, B = P^T)
+// so that the score block leaves the first MFMA in exactly the register layout the second one
+// takes as its B operand (lane l holds column l%16 and keys 4*(l/16)+i), with no shuffles.
+// The contraction index of an MFMA may be assigned to (lane group, register slot) in any way,
+// as long as A and B agree; the KV page layout is chosen so that each lane's operand is one
+// contiguous 16-byte (K) or 8-byte (V, bf16) load: K pages are [D/x][16][x] (16-byte chunks of
+// x dims per token), V pages are [D][16] (tokens contiguous per dim).
+//
+// Decode items stream K/V straight from HBM into registers (no reuse, so no LDS staging), two
+// pages per wave step with the next step's loads in flight; prefill tiles stage 64 keys of K
+// and V in LDS (double-buffered) and share them across the four waves, each wave owning 32 of
+// the tile's 128 query columns.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+#include "pod_internal.h"
+
+namespace pod {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define CPTR(T) const __attribute__((address_space(4))) T*
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+template <typename T> struct ElemTraits;
+template <> struct ElemTraits<__bf16> { static constexpr int kBytes = 2; };
+template <> struct ElemTraits<float> { static constexpr int kBytes = 4; };
+
+// Compile-time geometry of one (dtype, head_dim) instantiation.
+template <typename T, int D> struct Geo {
+  static constexpr int kBytes = ElemTraits<T>::kBytes;
+  static constexpr int kEpc = 16 / kBytes;              // elements per 16-byte chunk
+  static constexpr int kNch = D / kEpc;                 // 16-byte chunks per K row
+  static constexpr int kNs = kNch / 4;                  // QK steps: one chunk per lane group
+  static constexpr int kSlab = kPage * D * kBytes;      // bytes of one (page, KV head) slab
+  static constexpr int kCps = kSlab / 16;               // 16-byte chunks per slab
+  static constexpr int kTp = kSlab <= 4096 ? 4 : 2;     // pages per prefill KV tile
+  static constexpr int kTileKeys = kTp * kPage;
+  static constexpr int kDb = D / 16;                    // 16-row blocks of O^T
+  static constexpr int kStageChunks = 2 * kTp * kCps;   // K + V chunks of one prefill tile
+  static constexpr int kStageR = kStageChunks / kThreads;
+  static constexpr int kPrefillLds = 2 * 2 * kTp * kSlab;              // 2 buffers x (K, V)
+  static constexpr int kMergeRow = D + 4;                              // padded floats
+  static constexpr int kMergeLds = kWaves * 16 * kMergeRow * 4 + kWaves * 16 * 2 * 4;
+  static constexpr int kFusedLds = kPrefillLds > kMergeLds ? kPrefillLds : kMergeLds;
+  static_assert(kStageChunks % kThreads == 0, "tile must split evenly over the workgroup");
+  static_assert(kTp % 2 == 0, "bf16 PV pairs pages");
+};
+
+// ------------------------------------------------------------------ page addressing
+// One address generator for every reader of the paged cache (attention kernels and gather).
+template <typename T, int D>
+__device__ __forceinline__ const char* slab_ptr(const void* base, int page, int hkv, int g) {
+  return (const char*)base + ((size_t)page * hkv + g) * Geo<T, D>::kSlab;
+}
+// byte offset, inside a K slab, of the 16-byte chunk c (dims c*x .. c*x+x-1) of token slot t
+__device__ __forceinline__ int k_chunk_off(int c, int t) { return (c * kPage + t) * 16; }
+// byte offset, inside a V slab, of dim d, token slot t
+template <typename T>
+__device__ __forceinline__ int v_elem_off(int d, int t) { return (d * kPage + t) * ElemTraits<T>::kBytes; }
+
+// Reads block-table entry `pi` of row `btr` when the page holds keys (lim > 0); an entry
+// outside the pool is never dereferenced: it is reported and its page counts as empty.
+__device__ __forceinline__ int page_or_empty(CPTR(int32_t) btr, int pi, int& lim, int num_pages,
+                                             int32_t* status) {
+  int pg = 0;
+  if (lim > 0) {
+    pg = btr[pi];
+    if ((unsigned)pg >= (unsigned)num_pages) {
+      if ((threadIdx.x & 63) == 0) atomicOr(status, (int)kStatusBadPage);
+      pg = 0;
+      lim = 0;
+    }
+  } else {
+    lim = 0;
+  }
+  return pg;
+}
+
+// ------------------------------------------------------------------ small primitives
+__device__ __forceinline__ u32x4 ld16(const char* p) { return *(const u32x4*)p; }
+__device__ __forceinline__ u32x2 ld8(const char* p) { return *(const u32x2*)p; }
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float max_over_groups(float v) {   // over lanes l, l^16, l^32, l^48
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float sum_over_groups(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));   // RNE
+}
+
+// One 16-byte chunk of contraction per lane: bf16 -> one 16x16x32 MFMA; fp32 -> four
+// 16x16x4 MFMAs, element e of both chunks feeding the e-th.
+__device__ __forceinline__ f32x4 mfma_chunk(u32x4 a, u32x4 b, f32x4 c, __bf16) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_chunk(u32x4 a, u32x4 b, f32x4 c, float) {
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+  return c;
+}
+
+// V^T operand of one page for one lane: 4 tokens (4q .. 4q+3) of dim d.
+template <typename T> struct VOp;
+template <> struct VOp<__bf16> { typedef u32x2 type; };
+template <> struct VOp<float> { typedef u32x4 type; };
+
+template <typename T>
+__device__ __forceinline__ typename VOp<T>::type load_vop(const char* p);
+template <> __device__ __forceinline__ u32x2 load_vop<__bf16>(const char* p) { return ld8(p); }
+template <> __device__ __forceinline__ u32x4 load_vop<float>(const char* p) { return ld16(p); }
+
+// Zero the V^T elements of slots >= lim (tokens 4q .. 4q+3), so that 0 * (NaN in an unused
+// slot) never enters the sum: masking selects, it does not multiply.
+__device__ __forceinline__ u32x2 mask_vop(u32x2 v, int q, int lim) {
+  const int t0 = 4 * q;
+  uint32_t m0 = (t0 + 0 < lim ? 0x0000FFFFu : 0u) | (t0 + 1 < lim ? 0xFFFF0000u : 0u);
+  uint32_t m1 = (t0 + 2 < lim ? 0x0000FFFFu : 0u) | (t0 + 3 < lim ? 0xFFFF0000u : 0u);
+  return u32x2{v.x & m0, v.y & m1};
+}
+__device__ __forceinline__ u32x4 mask_vop(u32x4 v, int q, int lim) {
+  const int t0 = 4 * q;
+  return u32x4{t0 + 0 < lim ? v.x : 0u, t0 + 1 < lim ? v.y : 0u, t0 + 2 < lim ? v.z : 0u,
+               t0 + 3 < lim ? v.w : 0u};
+}
+
+// PV for one pair of pages (bf16: one 16x16x32 MFMA; keys = 4 of each page per lane group).
+__device__ __forceinline__ f32x4 pv_pair(u32x2 va, u32x2 vb, u32x4 pb, f32x4 c) {
+  u32x4 a = {va.x, va.y, vb.x, vb.y};
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, pb), c, 0, 0, 0);
+}
+// PV for one page in fp32: four 16x16x4 MFMAs, key 4q+i in the i-th.
+__device__ __forceinline__ f32x4 pv_page_f32(u32x4 v, f32x4 p, f32x4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.x), p.x, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.y), p.y, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.z), p.z, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.w), p.w, c, 0, 0, 0);
+  return c;
+}
+
+template <typename T>
+__device__ __forceinline__ void store4(T* dst, f32x4 v);
+template <> __device__ __forceinline__ void store4<__bf16>(__bf16* dst, f32x4 v) {
+  u32x2 w = {pack_bf16(v.x, v.y), pack_bf16(v.z, v.w)};
+  *(u32x2*)dst = w;
+}
+template <> __device__ __forceinline__ void store4<float>(float* dst, f32x4 v) { *(f32x4*)dst = v; }
+
+// Descriptor lookup: last descriptor whose first item (or group) is <= key.
+__device__ __forceinline__ int find_desc(CPTR(int32_t) descs, int n, int field, int key) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (descs[mid * kDescInts + field] <= key) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// ------------------------------------------------------------------ online-softmax update
+// Per query column (lane l holds column l%16): x = masked scaled scores of this block (log2
+// domain, -inf where masked), NV values per lane.  Updates m (column max, identical in the 4
+// lane groups), l (this lane's partial sum) and returns the rescale factor for the output.
+template <int NV>
+__device__ __forceinline__ float softmax_update(float (&x)[NV], float& m, float& l) {
+  float mloc = x[0];
+#pragma unroll
+  for (int i = 1; i < NV; ++i) mloc = fmaxf(mloc, x[i]);
+  mloc = max_over_groups(mloc);
+  const float m_new = fmaxf(m, mloc);
+  const float m_use = m_new == kNegInf ? 0.f : m_new;
+  const float alpha = exp2_fast(m - m_use);
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    x[i] = exp2_fast(x[i] - m_use);
+    sum += x[i];
+  }
+  l = l * alpha + sum;
+  m = m_new;
+  return alpha;
+}
+
+// ------------------------------------------------------------------ decode item
+// One (decode sequence, KV head, key split): the G query heads of the KV head are the
+// columns of one 16-wide block.  The four waves take interleaved 32-key steps of the split and
+// merge through LDS at the end.
+template <typename T, int D>
+__device__ void decode_item(const KernelParams& P, CPTR(int32_t) dsc, int head, int split, char* lds) {
+  using Gm = Geo<T, D>;
+  typedef typename VOp<T>::type VT;
+  const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+  const int w = wave_index();
+  const int G = P.group;
+  const int seq = dsc[kDSeq], q_row = dsc[kDQRow], kv_len = dsc[kDKvLen];
+  const int ns = dsc[kDNSplit], st = dsc[kDSplitTok];
+  const int kv_begin = split * st;
+  const int kv_end = min(kv_len, kv_begin + st);
+  const int n_steps = (kv_end - kv_begin + kDecodeStep - 1) / kDecodeStep;
+  CPTR(int32_t) btr = (CPTR(int32_t))P.bt + (size_t)seq * P.bt_stride;
+  const float sl2 = P.scale_log2;
+
+  // Q^T operand: column n is query head head*G+n (zero when n >= G).
+  u32x4 qop[Gm::kNs];
+  {
+    const int hcol = head * G + (n < G ? n : 0);
+    const char* qp = (const char*)P.q + ((size_t)q_row * P.hq + hcol) * (D * Gm::kBytes);
+#pragma unroll
+    for (int s = 0; s < Gm::kNs; ++s) {
+      u32x4 v = ld16(qp + (4 * s + q) * 16);
+      qop[s] = n < G ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  f32x4 o[Gm::kDb];
+#pragma unroll
+  for (int b = 0; b < Gm::kDb; ++b) o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegInf, l_run = 0.f;
+
+  u32x4 kA[2][Gm::kNs], kB[2][Gm::kNs];
+  VT vA[2][Gm::kDb], vB[2][Gm::kDb];
+  int limA[2], limB[2];
+
+  auto load_step = [&](int step, u32x4 (&kr)[2][Gm::kNs], VT (&vr)[2][Gm::kDb], int (&lim)[2]) {
+    const int tok0 = kv_begin + step * kDecodeStep;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int pi = (tok0 >> 4) + p;
+      int l = min(kPage, kv_end - pi * kPage);
+      const int pg = page_or_empty(btr, pi, l, P.num_pages, P.ctrl + kCStatus);
+      lim[p] = l;
+      const char* kp = slab_ptr<T, D>(P.k, pg, P.hkv, head);
+      const char* vp = slab_ptr<T, D>(P.v, pg, P.hkv, head);
+#pragma unroll
+      for (int s = 0; s < Gm::kNs; ++s) kr[p][s] = ld16(kp + k_chunk_off(4 * s + q, n));
+#pragma unroll
+      for (int b = 0; b < Gm::kDb; ++b) vr[p][b] = load_vop<T>(vp + v_elem_off<T>(16 * b + n, 4 * q));
+    }
+  };
+
+  auto compute_step = [&](u32x4 (&kr)[2][Gm::kNs], VT (&vr)[2][Gm::kDb], const int (&lim)[2]) {
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < Gm::kNs; ++s) {
+      s0 = mfma_chunk(kr[0][s], qop[s], s0, T());
+      s1 = mfma_chunk(kr[1][s], qop[s], s1, T());
+    }
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = (4 * q + i < lim[0]) ? s0[i] * sl2 : kNegInf;
+      x[4 + i] = (4 * q + i < lim[1]) ? s1[i] * sl2 : kNegInf;
+    }
+    const float alpha = softmax_update<8>(x, m_run, l_run);
+#pragma unroll
+    for (int b = 0; b < Gm::kDb; ++b) o[b] *= alpha;
+    if (lim[0] < kPage || lim[1] < kPage) {
+#pragma unroll
+      for (int b = 0; b < Gm::kDb; ++b) {
+        vr[0][b] = mask_vop(vr[0][b], q, lim[0]);
+        vr[1][b] = mask_vop(vr[1][b], q, lim[1]);
+      }
+    }
+    if constexpr (Gm::kBytes == 2) {
+      const u32x4 pb = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]),
+                        pack_bf16(x[6], x[7])};
+#pragma unroll
+      for (int b = 0; b < Gm::kDb; ++b) o[b] = pv_pair(vr[0][b], vr[1][b], pb, o[b]);
+    } else {
+      const f32x4 p0 = {x[0], x[1], x[2], x[3]}, p1 = {x[4], x[5], x[6], x[7]};
+#pragma unroll
+      for (int b = 0; b < Gm::kDb; ++b) {
+        o[b] = pv_page_f32(vr[0][b], p0, o[b]);
+        o[b] = pv_page_f32(vr[1][b], p1, o[b]);
+      }
+    }
+  };
+
+  // Two register sets: the next step's loads are issued before the current step's math.
+  // Past the last step the prefetch re-reads the current step (cache hits, results unused).
+  int step = w;
+  if (step < n_steps) {
+    load_step(step, kA, vA, limA);
+    for (;;) {
+      int nxt = step + kWaves;
+      load_step(nxt < n_steps ? nxt : step, kB, vB, limB);
+      compute_step(kA, vA, limA);
+      if (nxt >= n_steps) break;
+      step = nxt;
+      nxt = step + kWaves;
+      load_step(nxt < n_steps ? nxt : step, kA, vA, limA);
+      compute_step(kB, vB, limB);
+      if (nxt >= n_steps) break;
+      step = nxt;
+    }
+  }
+
+  // ---- merge the four waves' states through LDS
+  float* lo = (float*)lds;                                   // [4][16][D+4]
+  float* lm = lo + kWaves * 16 * Gm::kMergeRow;              // [4][16]
+  float* ll = lm + kWaves * 16;                              // [4][16]
+  const float l_tot = sum_over_groups(l_run);
+#pragma unroll
+  for (int b = 0; b < Gm::kDb; ++b)
+    *(f32x4*)(lo + (w * 16 + n) * Gm::kMergeRow + 16 * b + 4 * q) = o[b];
+  if (q == 0) {
+    lm[w * 16 + n] = m_run;
+    ll[w * 16 + n] = l_tot;
+  }
+  __syncthreads();
+  {
+    const int tid = threadIdx.x;
+    const int c = tid & 15, dg = tid >> 4;                   // 16 columns x 16 dim groups
+    constexpr int kPer = D / 16;
+    float M = kNegInf;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, lm[ww * 16 + c]);
+    float wt[kWaves], L = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      wt[ww] = M == kNegInf ? 0.f : exp2_fast(lm[ww * 16 + c] - M);
+      L += wt[ww] * ll[ww * 16 + c];
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    float res[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      float a = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) a += wt[ww] * lo[(ww * 16 + c) * Gm::kMergeRow + dg * kPer + j];
+      res[j] = a * inv;
+    }
+    if (c < G) {
+      if (ns == 1) {
+        T* dst = (T*)P.out + ((size_t)q_row * P.hq + head * G + c) * D + dg * kPer;
+#pragma unroll
+        for (int j = 0; j < kPer; j += 4) store4<T>(dst + j, f32x4{res[j], res[j + 1], res[j + 2], res[j + 3]});
+      } else {
+        const size_t slot = (size_t)dsc[kDPartBase] + ((size_t)head * ns + split) * G + c;
+        float* dst = P.part_o + slot * D + dg * kPer;
+#pragma unroll
+        for (int j = 0; j < kPer; j += 4) *(f32x4*)(dst + j) = f32x4{res[j], res[j + 1], res[j + 2], res[j + 3]};
+        if (dg == 0) P.part_lse[slot] = L > 0.f ? M + __log2f(L) : kNegInf;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ prefill tile item
+// One (query tile, KV head, key split): 128 columns = floor(128/G) queries x G heads; wave w
+// owns columns 32w .. 32w+31 (two 16-wide blocks).  Keys advance 64 (or 32) at a time,
+// staged in LDS by all 256 threads with the next tile's global loads in flight.
+template <typename T, int D>
+__device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head, int split, char* lds) {
+  using Gm = Geo<T, D>;
+  const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, q = lane >> 4;
+  const int w = wave_index();
+  const int G = P.group;
+  const int seq = dsc[kDSeq], q_row = dsc[kDQRow], n_q = dsc[kDNq], q_pos = dsc[kDQPos];
+  const int kv_len = dsc[kDKvLen], ns = dsc[kDNSplit], st = dsc[kDSplitTok];
+  const int ncols = n_q * G;
+  const int kv_begin = split * st;
+  const int kv_end = min(kv_len, kv_begin + st);
+  const int n_tiles = (kv_end - kv_begin + Gm::kTileKeys - 1) / Gm::kTileKeys;
+  CPTR(int32_t) btr = (CPTR(int32_t))P.bt + (size_t)seq * P.bt_stride;
+  const float sl2 = P.scale_log2;
+
+  // columns of this lane
+  int pos[2];
+  bool cval[2];
+  u32x4 qop[2][Gm::kNs];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int c = 32 * w + 16 * nb + n;
+    cval[nb] = c < ncols;
+    const int cc = cval[nb] ? c : 0;
+    const int qi = cc / G, hh = cc - qi * G;
+    pos[nb] = q_pos + qi;
+    const char* qp = (const char*)P.q + ((size_t)(q_row + qi) * P.hq + head * G + hh) * (D * Gm::kBytes);
+#pragma unroll
+    for (int s = 0; s < Gm::kNs; ++s) {
+      u32x4 v = ld16(qp + (4 * s + q) * 16);
+      qop[nb][s] = cval[nb] ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  const int wc0 = 32 * w;
+  const bool wave_active = wc0 < ncols;
+  const int pmin = q_pos + wc0 / G;
+  const int pmax = q_pos + (min(ncols, wc0 + 32) - 1) / G;
+
+  f32x4 o[2][Gm::kDb];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int b = 0; b < Gm::kDb; ++b) o[nb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {kNegInf, kNegInf}, l_run[2] = {0.f, 0.f};
+
+  // ---- staging: chunk r of this thread is linear chunk r*256+tid of [K pages][V pages]
+  u32x4 stg[Gm::kStageR];
+  int lim_cur[Gm::kTp], lim_nxt[Gm::kTp];
+  auto tile_pages = [&](int j, int (&lim)[Gm::kTp], int (&pg)[Gm::kTp]) {
+    const int tb = kv_begin + j * Gm::kTileKeys;
+#pragma unroll
+    for (int p = 0; p < Gm::kTp; ++p) {
+      const int pi = (tb >> 4) + p;
+      int l = min(kPage, kv_end - pi * kPage);
+      pg[p] = page_or_empty(btr, pi, l, P.num_pages, P.ctrl + kCStatus);
+      lim[p] = l;
+    }
+  };
+  auto load_tile = [&](int j, int (&lim)[Gm::kTp]) {
+    int pg[Gm::kTp];
+    tile_pages(j, lim, pg);
+#pragma unroll
+    for (int r = 0; r < Gm::kStageR; ++r) {
+      const int L = r * kThreads + tid;
+      const int half = L / (Gm::kTp * Gm::kCps);
+      const int rem = L - half * (Gm::kTp * Gm::kCps);
+      const int p = rem / Gm::kCps, c = rem - p * Gm::kCps;
+      int page = pg[0];
+#pragma unroll
+      for (int pp = 1; pp < Gm::kTp; ++pp) page = p == pp ? pg[pp] : page;
+      const char* base = slab_ptr<T, D>(half ? P.v : P.k, page, P.hkv, head);
+      stg[r] = ld16(base + c * 16);
+    }
+  };
+  auto kbuf = [&](int b) { return lds + b * (2 * Gm::kTp * Gm::kSlab); };
+  auto vbuf = [&](int b) { return lds + b * (2 * Gm::kTp * Gm::kSlab) + Gm::kTp * Gm::kSlab; };
+  // bf16 V rows are 32 bytes (two 16-byte halves); rows 8..15 of each 16-row block swap their
+  // halves so that a wave's 8-byte reads of 16 consecutive rows spread over all LDS banks.
+  auto vswz = [&](int c) {
+    if constexpr (Gm::kBytes == 2) {
+      const int d = c >> 1, h = c & 1;
+      return d * 2 + (h ^ ((d >> 3) & 1));
+    } else {
+      return c;
+    }
+  };
+  auto store_tile = [&](int b) {
+#pragma unroll
+    for (int r = 0; r < Gm::kStageR; ++r) {
+      const int L = r * kThreads + tid;
+      const int half = L / (Gm::kTp * Gm::kCps);
+      const int rem = L - half * (Gm::kTp * Gm::kCps);
+      const int p = rem / Gm::kCps, c = rem - p * Gm::kCps;
+      char* dst = half ? vbuf(b) + p * Gm::kSlab + vswz(c) * 16 : kbuf(b) + p * Gm::kSlab + c * 16;
+      *(u32x4*)dst = stg[r];
+    }
+  };
+
+  auto compute_tile = [&](int b, int j, const int (&lim)[Gm::kTp]) {
+    const int tb = kv_begin + j * Gm::kTileKeys;
+    if (!wave_active || tb > pmax) return;                    // every key after every query
+    bool full = tb + Gm::kTileKeys - 1 <= pmin;
+#pragma unroll
+    for (int p = 0; p < Gm::kTp; ++p) full = full && lim[p] == kPage;
+    const char* kb = kbuf(b);
+    const char* vb = vbuf(b);
+    f32x4 S[2][Gm::kTp];
+#pragma unroll
+    for (int mb = 0; mb < Gm::kTp; ++mb) {
+      u32x4 kop[Gm::kNs];
+#pragma unroll
+      for (int s = 0; s < Gm::kNs; ++s) kop[s] = *(const u32x4*)(kb + mb * Gm::kSlab + k_chunk_off(4 * s + q, n));
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < Gm::kNs; ++s) acc = mfma_chunk(kop[s], qop[nb][s], acc, T());
+        S[nb][mb] = acc;
+      }
+    }
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      float x[4 * Gm::kTp];
+#pragma unroll
+      for (int mb = 0; mb < Gm::kTp; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int slot = 4 * q + i;
+          const int t = tb + mb * kPage + slot;
+          const bool ok = full || (slot < lim[mb] && t <= pos[nb]);
+          x[4 * mb + i] = ok ? S[nb][mb][i] * sl2 : kNegInf;
+        }
+      const float alpha = softmax_update<4 * Gm::kTp>(x, m_run[nb], l_run[nb]);
+#pragma unroll
+      for (int b2 = 0; b2 < Gm::kDb; ++b2) o[nb][b2] *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < Gm::kTp; ++mb)
+        S[nb][mb] = f32x4{x[4 * mb], x[4 * mb + 1], x[4 * mb + 2], x[4 * mb + 3]};
+    }
+    bool vmask = false;
+#pragma unroll
+    for (int p = 0; p < Gm::kTp; ++p) vmask = vmask || lim[p] < kPage;
+    if constexpr (Gm::kBytes == 2) {
+#pragma unroll
+      for (int pp = 0; pp < Gm::kTp / 2; ++pp) {
+        u32x4 pb[2];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const f32x4 a = S[nb][2 * pp], c = S[nb][2 * pp + 1];
+          pb[nb] = u32x4{pack_bf16(a.x, a.y), pack_bf16(a.z, a.w), pack_bf16(c.x, c.y), pack_bf16(c.z, c.w)};
+        }
+#pragma unroll
+        for (int b2 = 0; b2 < Gm::kDb; ++b2) {
+          const int d = 16 * b2 + n;
+          const int off = vswz(d * 2 + (q >> 1)) * 16 + (q & 1) * 8;
+          u32x2 va = *(const u32x2*)(vb + (2 * pp) * Gm::kSlab + off);
+          u32x2 vc = *(const u32x2*)(vb + (2 * pp + 1) * Gm::kSlab + off);
+          if (vmask) {
+            va = mask_vop(va, q, lim[2 * pp]);
+            vc = mask_vop(vc, q, lim[2 * pp + 1]);
+          }
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) o[nb][b2] = pv_pair(va, vc, pb[nb], o[nb][b2]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < Gm::kTp; ++mb)
+#pragma unroll
+        for (int b2 = 0; b2 < Gm::kDb; ++b2) {
+          const int d = 16 * b2 + n;
+          u32x4 v = *(const u32x4*)(vb + mb * Gm::kSlab + v_elem_off<T>(d, 4 * q));
+          if (vmask) v = mask_vop(v, q, lim[mb]);
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) o[nb][b2] = pv_page_f32(v, S[nb][mb], o[nb][b2]);
+        }
+    }
+  };
+
+  if (n_tiles > 0) {
+    load_tile(0, lim_cur);
+    store_tile(0);
+    __syncthreads();
+    for (int j = 0; j < n_tiles; ++j) {
+      const bool more = j + 1 < n_tiles;
+      if (more) load_tile(j + 1, lim_nxt);
+      compute_tile(j & 1, j, lim_cur);
+      if (more) store_tile((j + 1) & 1);
+      __syncthreads();
+#pragma unroll
+      for (int p = 0; p < Gm::kTp; ++p) lim_cur[p] = lim_nxt[p];
+    }
+  }
+
+  // ---- epilogue: normalise and write the output, or the split partial (o, lse)
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const float l_tot = sum_over_groups(l_run[nb]);
+    if (!cval[nb]) continue;
+    const int c = 32 * w + 16 * nb + n;
+    const int qi = c / G, hh = c - qi * G;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (ns == 1) {
+      T* dst = (T*)P.out + ((size_t)(q_row + qi) * P.hq + head * G + hh) * D + 4 * q;
+#pragma unroll
+      for (int b2 = 0; b2 < Gm::kDb; ++b2) store4<T>(dst + 16 * b2, o[nb][b2] * inv);
+    } else {
+      const size_t slot = (size_t)dsc[kDPartBase] + ((size_t)head * ns + split) * ncols + c;
+      float* dst = P.part_o + slot * D + 4 * q;
+#pragma unroll
+      for (int b2 = 0; b2 < Gm::kDb; ++b2) *(f32x4*)(dst + 16 * b2) = o[nb][b2] * inv;
+      if (q == 0) P.part_lse[slot] = l_tot > 0.f ? m_run[nb] + __log2f(l_tot) : kNegInf;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ log-sum-exp combine
+// out = sum_s w_s o_s / sum_s w_s with w_s = 2^(lse_s - max lse); empty splits weigh zero.
+template <typename T, int D>
+__device__ void combine_group(const KernelParams& P, CPTR(int32_t) dsc, int head) {
+  const int ns = dsc[kDNSplit], ncols = dsc[kDNcols], q_row = dsc[kDQRow];
+  const size_t base = (size_t)dsc[kDPartBase] + (size_t)head * ns * ncols;
+  const int G = P.group;
+  constexpr int kQ = D / 4;
+  for (int idx = threadIdx.x; idx < ncols * kQ; idx += kThreads) {
+    const int c = idx / kQ, d4 = idx - c * kQ;
+    float M = kNegInf;
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, P.part_lse[base + (size_t)s * ncols + c]);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+    if (M != kNegInf) {
+      for (int s = 0; s < ns; ++s) {
+        const size_t slot = base + (size_t)s * ncols + c;
+        const float wgt = exp2_fast(P.part_lse[slot] - M);
+        if (wgt > 0.f) acc += wgt * *(const f32x4*)(P.part_o + slot * D + 4 * d4);
+        wsum += wgt;
+      }
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    const int qi = c / G, hh = c - qi * G;
+    T* dst = (T*)P.out + ((size_t)(q_row + qi) * P.hq + head * G + hh) * D + 4 * d4;
+    store4<T>(dst, acc * inv);
+  }
+}
+
+// ------------------------------------------------------------------ item dispatch
+template <typename T, int D>
+__device__ void run_item(const KernelParams& P, int kind, int item, char* lds, int* s_flag) {
+  CPTR(int32_t) descs = (CPTR(int32_t))(kind == 0 ? P.pdesc : P.ddesc);
+  const int nd = kind == 0 ? P.n_pdesc : P.n_ddesc;
+  const int di = find_desc(descs, nd, kDItemBegin, item);
+  CPTR(int32_t) dsc = descs + (size_t)di * kDescInts;
+  const int ns = dsc[kDNSplit];
+  const int local = item - dsc[kDItemBegin];
+  const int head = local / ns, split = local - head * ns;
+  if (kind == 0) prefill_item<T, D>(P, dsc, head, split, lds);
+  else decode_item<T, D>(P, dsc, head, split, lds);
+  if (ns > 1 && P.inline_combine) {
+    // Last arriver combines: each wave's partial stores complete, one agent-scope release
+    // makes them visible device-wide, the ticket counts arrivals; the last one acquires and
+    // merges.  No workgroup ever waits for another ([POD], "Virtual CTAs and per-SM balance":
+    // exact synchronisation where partial results meet, no deadlock between the two kinds).
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's stores have reached L2
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      __threadfence();
+      const int prev = atomicAdd(P.tickets + dsc[kDGroupBegin] + head, 1);
+      const int last = prev == ns - 1;
+      if (last) __threadfence();
+      *s_flag = last;
+    }
+    __syncthreads();
+    if (*s_flag) combine_group<T, D>(P, dsc, head);
+  }
+  __syncthreads();   // LDS and the flag are reused by the next item
+}
+
+__device__ __forceinline__ int cu_slot() {
+  const unsigned hw = __builtin_amdgcn_s_getreg((4) | (0 << 6) | (31 << 11));     // HW_ID
+  const unsigned xcc = __builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11));    // XCC_ID[3:0]
+  const unsigned cu = (hw >> 8) & 15u, sh = (hw >> 12) & 1u, se = (hw >> 13) & 3u;
+  return (int)(((xcc & 7u) << 7) | (se << 5) | (sh << 4) | cu);
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void note_claim(const KernelParams& P, int kind, int item, int cu) {
+  if (P.claims) {
+    atomicAdd(P.claims + (kind == 0 ? 0 : P.n_pf_items) + item, 1);
+    atomicAdd(P.ctrl + (kind == 0 ? kCClaimsPrefillCu : kCClaimsDecodeCu) + cu, 1);
+  }
+}
+
+// ------------------------------------------------------------------ kernels
+// Fused persistent kernel: every workgroup loops, taking a role per CU and claiming items of
+// that kind through one atomic counter per kind; at most `prefill_cap_per_cu` workgroups of a
+// CU hold the prefill role while decode work remains, so every CU keeps streaming decode while
+// its prefill tiles run ([POD], "Virtual CTAs and per-SM balance").  A workgroup whose queue is
+// drained takes the other kind; the kernel ends when both are drained.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads, 2) void pod_fused_kernel(KernelParams P) {
+  __shared__ __attribute__((aligned(16))) char lds[Geo<T, D>::kFusedLds];
+  __shared__ int s_role, s_item, s_flag;
+  const int tid = threadIdx.x;
+  const int cu = cu_slot();
+  int* active = P.ctrl + kCActivePrefill + cu;
+  bool pf_open = P.n_pf_items > 0, dc_open = P.n_dc_items > 0;
+  bool counted = false;                       // thread 0: holds a prefill slot of its CU
+  for (;;) {
+    if (tid == 0) {
+      int role = -1;
+      if (pf_open && dc_open) {
+        const int a = atomicAdd(active, 1);
+        if (a < P.prefill_cap_per_cu) { role = 0; counted = true; }
+        else { atomicSub(active, 1); role = 1; }
+      } else if (dc_open) {
+        role = 1;
+      } else if (pf_open) {
+        role = 0;
+      }
+      s_role = role;
+      if (role >= 0) s_item = atomicAdd(P.ctrl + (role == 0 ? kCQueuePrefill : kCQueueDecode), 1);
+    }
+    __syncthreads();
+    const int role = s_role;
+    int item = s_item;
+    __syncthreads();
+    if (role < 0) break;
+    const int n_items = role == 0 ? P.n_pf_items : P.n_dc_items;
+    int* counter = P.ctrl + (role == 0 ? kCQueuePrefill : kCQueueDecode);
+    while (item < n_items) {
+      int next = 0;
+      if (tid == 0) {
+        next = atomicAdd(counter, 1);          // claim ahead; consumed after this item
+        note_claim<T, D>(P, role, item, cu);
+      }
+      run_item<T, D>(P, role, item, lds, &s_flag);
+      if (tid == 0) s_item = next;
+      __syncthreads();
+      item = s_item;
+      __syncthreads();
+    }
+    if (role == 0) {
+      pf_open = false;
+      if (tid == 0 && counted) { atomicSub(active, 1); counted = false; }
+    } else {
+      dc_open = false;
+    }
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads, 2) void pod_prefill_kernel(KernelParams P) {
+  __shared__ __attribute__((aligned(16))) char lds[Geo<T, D>::kPrefillLds];
+  __shared__ int s_flag;
+  if (threadIdx.x == 0) note_claim<T, D>(P, 0, blockIdx.x, cu_slot());
+  run_item<T, D>(P, 0, blockIdx.x, lds, &s_flag);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads, 2) void pod_decode_kernel(KernelParams P) {
+  __shared__ __attribute__((aligned(16))) char lds[Geo<T, D>::kMergeLds];
+  __shared__ int s_flag;
+  if (threadIdx.x == 0) note_claim<T, D>(P, 1, blockIdx.x, cu_slot());
+  run_item<T, D>(P, 1, blockIdx.x, lds, &s_flag);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void pod_combine_kernel(KernelParams P) {
+  const int g = P.group_begin + (int)blockIdx.x;
+  if (g >= P.group_end) return;
+  const bool pf = g < P.n_pf_groups;
+  CPTR(int32_t) descs = (CPTR(int32_t))(pf ? P.pdesc : P.ddesc);
+  const int nd = pf ? P.n_pdesc : P.n_ddesc;
+  const int di = find_desc(descs, nd, kDGroupBegin, g);
+  CPTR(int32_t) dsc = descs + (size_t)di * kDescInts;
+  combine_group<T, D>(P, dsc, g - dsc[kDGroupBegin]);
+}
+
+// Debug gather: element (t, g, d) of one sequence, through the kernels' page addressing.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void pod_gather_kernel(const void* cache, int which,
+                                                             const int32_t* bt_row, int ctx, int hkv,
+                                                             int num_pages, void* out, int32_t* status) {
+  using Gm = Geo<T, D>;
+  const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  const size_t total = (size_t)ctx * hkv * D;
+  if (idx >= total) return;
+  const int d = (int)(idx % D);
+  const int g = (int)((idx / D) % hkv);
+  const int t = (int)(idx / ((size_t)D * hkv));
+  const int pg = bt_row[t >> 4];
+  T val = T(0);
+  if ((unsigned)pg < (unsigned)num_pages) {
+    const char* sp = slab_ptr<T, D>(cache, pg, hkv, g);
+    const int slot = t & 15;
+    const char* p = which == 0 ? sp + k_chunk_off(d / Gm::kEpc, slot) + (d % Gm::kEpc) * Gm::kBytes
+                               : sp + v_elem_off<T>(d, slot);
+    val = *(const T*)p;
+  } else if (status) {
+    atomicOr(status, (int)kStatusBadPage);
+  }
+  ((T*)out)[idx] = val;
+}
+
+template <typename T, int D>
+KernelSet make_set() {
+  KernelSet s;
+  s.fused = (const void*)&pod_fused_kernel<T, D>;
+  s.prefill = (const void*)&pod_prefill_kernel<T, D>;
+  s.decode = (const void*)&pod_decode_kernel<T, D>;
+  s.combine = (const void*)&pod_combine_kernel<T, D>;
+  s.gather = (const void*)&pod_gather_kernel<T, D>;
+  s.fused_lds = Geo<T, D>::kFusedLds;
+  s.prefill_kv_tile = Geo<T, D>::kTileKeys;
+  return s;
+}
+
+}  // namespace
+
+KernelSet kernel_set(int dtype, int head_dim) {
+  if (dtype == 0 && head_dim == 128) return make_set<__bf16, 128>();
+  if (dtype == 0 && head_dim == 64) return make_set<__bf16, 64>();
+  if (dtype == 1 && head_dim == 128) return make_set<float, 128>();
+  return make_set<float, 64>();
+}
+
+}  // namespace pod

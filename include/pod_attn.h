@@ -1,0 +1,215 @@
+/*
+ * pod_attn.h -- C ABI of the fused hybrid-batch paged attention library for MI355X (gfx950).
+ *
+ * One call computes, for a mixed batch, exact causal chunked-prefill attention (a query chunk
+ * over its cached prefix plus itself) and decode attention (one query token over its whole
+ * context), reading K and V from a paged KV cache through per-sequence block tables.
+ *
+ * Sources (web pages; sections as printed on them):
+ *   [POD] Silicon & Systems digest "POD-Attention hybrid batching": one fused launch whose
+ *         software scheduler hands prefill or decode work to each compute unit (section
+ *         "Virtual CTAs and per-SM balance"); comparison against separate and stream-concurrent
+ *         launches (sections "Why concurrency alone is not enough", "Reproduction and hardware
+ *         evaluation"); unsupported shapes fall back and the runtime reports tile choice,
+ *         occupancy and fallback reasons (section "Predictable latency and diagnostics").
+ *   [W6]  "Week 6: Beyond PyTorch: Custom Kernel과 vLLM": attention equation (section
+ *         "Attention에 적용하기"), causal rule ("Non-Causal vs. Causal Attention"), prefill /
+ *         extend / decode kinds ("한 스텝에 여러 종류의 request 섞기"), paged blocks and block
+ *         tables ("PagedAttention"), padding-free packed batches ("vLLM 내부 구조").
+ *   [W4]  "LLMSO - W4 - Optimization & Frameworks": online softmax, split-KV decoding with a
+ *         max/sum combine, block-table gather, GQA (section "1-2. 어텐션 최적화").
+ *
+ * Definition of the result (exact; no approximation):
+ *   For query row r of sequence s at absolute position i, query head h, KV head
+ *   g = floor(h / (Hq / Hkv)):
+ *       out[r][h] = sum_{j <= i} softmax_j(scale * <q[r][h], k_s[j][g]>) * v_s[j][g]
+ *   with j running over the sequence's logical tokens 0 .. ctx-1.  A prefill (extend) chunk of
+ *   L rows with context ctx holds positions ctx-L .. ctx-1 (its own K/V are already in the
+ *   cache); a decode row is at position ctx-1.
+ *
+ * Buffer formats (all row-major, element type bf16 or fp32 as configured, same for all):
+ *   q, out   [total_q][Hq][D]; rows 0 .. P-1 are the prefill chunks back to back in batch order
+ *            (P = prefill_q_start[num_prefill]), rows P .. P+num_decode-1 the decode queries.
+ *   k_cache  [num_pages][Hkv][D/x][16][x]  with x = 16 bytes / element size (8 for bf16, 4 for
+ *            fp32): element (page, g, slot t, dim d) at (((page*Hkv+g)*(D/x) + d/x)*16 + t)*x + d%x.
+ *            One (page, head) slab is 16*D*elem bytes, contiguous; every 16-byte chunk holds x
+ *            consecutive dims of one token.
+ *   v_cache  [num_pages][Hkv][D][16]: element (page, g, t, d) at ((page*Hkv+g)*D + d)*16 + t.
+ *            Each 16-byte chunk holds 8 (bf16) or 4 (fp32) consecutive tokens of one dim.
+ *   block_tables  int32 [num_prefill + num_decode][block_table_stride], device memory.  Row s
+ *            maps logical page t/16 of sequence s to a physical page; rows for the prefill
+ *            sequences come first, then one row per decode.  Only entries 0 .. ceil(ctx/16)-1
+ *            of a row are read; slots past ctx in the last page are never used in the result.
+ *
+ * Ownership: the caller owns every device buffer (q, caches, block tables, out, workspace) and
+ * every host array.  The handle owns host state only (plus, in STREAMS mode, two HIP streams
+ * and events, and a small pinned host staging ring).  No call allocates device memory.
+ *
+ * Errors: every call returns a pod_attn_status; on a non-OK status pod_attn_last_error()
+ * returns a message for the calling thread.  pod_attn_run is asynchronous on `stream`;
+ * argument and launch errors are returned synchronously; device faults surface at the
+ * caller's next synchronisation, as for any HIP launch.  A block-table entry outside
+ * [0, num_pages_in_pool) is never dereferenced: the kernels read nothing for that page,
+ * treat its tokens as absent and set POD_ATTN_DEVICE_ERR_BAD_PAGE in the workspace status word
+ * (see pod_attn_read_device_status).
+ */
+#ifndef POD_ATTN_H
+#define POD_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  POD_ATTN_OK = 0,
+  POD_ATTN_ERR_INVALID_ARG = -1,   /* null pointer, inconsistent metadata, bad sizes          */
+  POD_ATTN_ERR_UNSUPPORTED = -2,   /* valid but unsupported shape (head_dim, group size, ...) */
+  POD_ATTN_ERR_WORKSPACE = -3,     /* workspace missing or smaller than pod_attn_workspace_size */
+  POD_ATTN_ERR_HIP = -4,           /* a HIP runtime call failed (message has the HIP error)    */
+  POD_ATTN_ERR_NO_DEVICE = -5      /* no usable gfx950 device for create()                     */
+} pod_attn_status;
+
+typedef enum { POD_ATTN_BF16 = 0, POD_ATTN_FP32 = 1 } pod_attn_dtype;
+
+/* FUSED: one persistent launch, prefill and decode work claimed per compute unit.
+ * SEPARATE: prefill kernel, then decode kernel, then the split combine, serially on `stream`.
+ * STREAMS: prefill on one internal stream concurrently with decode (+combine) on another;
+ * both wait for `stream` and `stream` waits for both.  All modes give the same result up to
+ * floating-point rounding order ([POD], "Why concurrency alone is not enough"). */
+typedef enum { POD_ATTN_MODE_FUSED = 0, POD_ATTN_MODE_SEPARATE = 1, POD_ATTN_MODE_STREAMS = 2 } pod_attn_mode;
+
+/* Fallback reasons reported in pod_attn_stats.fallback_reason ([POD], "Predictable latency
+ * and diagnostics": unsupported-but-valid work is routed to separate kernels, with a reason). */
+typedef enum {
+  POD_ATTN_FALLBACK_NONE = 0,
+  POD_ATTN_FALLBACK_NO_PREFILL = 1,    /* nothing to overlap: fused kernel runs decode only    */
+  POD_ATTN_FALLBACK_NO_DECODE = 2,     /* nothing to overlap: fused kernel runs prefill only   */
+  POD_ATTN_FALLBACK_OCCUPANCY = 3,     /* fused kernel cannot keep 2 workgroups per CU; ran SEPARATE */
+  POD_ATTN_FALLBACK_ENV = 4            /* mode overridden by POD_ATTN_MODE                      */
+} pod_attn_fallback;
+
+/* Flags */
+#define POD_ATTN_FLAG_DEBUG_CLAIMS 1   /* count every work-item claim in the workspace (tests) */
+
+typedef struct pod_attn_config {
+  int num_q_heads;          /* Hq >= 1                                                        */
+  int num_kv_heads;         /* Hkv >= 1, Hq % Hkv == 0, group Hq/Hkv <= 16                     */
+  int head_dim;             /* D: 64 or 128                                                   */
+  int page_size;            /* tokens per page: must be 16                                    */
+  int dtype;                /* pod_attn_dtype                                                 */
+  int mode;                 /* pod_attn_mode                                                  */
+  float scale;              /* softmax scale; 0 means 1/sqrt(head_dim)                        */
+  int decode_split_tokens;  /* 0: automatic; else tokens per decode work item (multiple of 128) */
+  int prefill_split_cap;    /* 0: automatic; else max KV splits of one prefill tile (>= 1)     */
+  int wgs_per_cu;           /* 0: automatic; else persistent workgroups per CU in FUSED mode  */
+  int flags;                /* POD_ATTN_FLAG_*                                                */
+} pod_attn_config;
+
+/* Batch metadata: host arrays ([W6] "vLLM 내부 구조": padding-free packing with offsets). */
+typedef struct pod_attn_batch {
+  int num_prefill;                 /* prefill (extend) chunks, >= 0                           */
+  const int32_t* prefill_q_start;  /* host [num_prefill+1]: row offsets, [0] = 0, non-decreasing */
+  const int32_t* prefill_ctx_len;  /* host [num_prefill]: ctx = chunk offset + chunk length     */
+  int num_decode;                  /* decode sequences, >= 0                                   */
+  const int32_t* decode_ctx_len;   /* host [num_decode]: context length (>= 1), query at ctx-1  */
+  int block_table_stride;          /* int32 entries per block-table row, >= ceil(max ctx / 16) */
+  int num_pages_in_pool;           /* pages in k_cache / v_cache                               */
+} pod_attn_batch;
+
+typedef struct pod_attn_handle pod_attn_handle;   /* opaque, host-side */
+
+/* Diagnostics of the last pod_attn_run on a handle ([POD], "Predictable latency and
+ * diagnostics": virtual-CTA ratio, tile choice, occupancy, fallback reason). */
+typedef struct pod_attn_stats {
+  int mode_requested;
+  int mode_used;
+  int fallback_reason;          /* pod_attn_fallback                                          */
+  int num_prefill_items;        /* prefill work items (tile x KV head x KV split)             */
+  int num_decode_items;         /* decode work items (sequence x KV head x split)             */
+  int num_combine_groups;       /* (query tile, KV head) groups whose splits are combined     */
+  int prefill_tile_cols;        /* query-head columns per prefill tile (queries x group)      */
+  int prefill_tile_queries;     /* query rows per prefill tile                                */
+  int prefill_kv_tile;          /* keys per prefill inner iteration                           */
+  int prefill_max_splits;       /* largest KV split count of a prefill tile                   */
+  int decode_split_tokens;      /* tokens per decode work item                                */
+  int decode_max_splits;        /* largest split count of a decode (sequence, KV head)        */
+  int grid_wgs;                 /* workgroups launched by the fused kernel (0 otherwise)      */
+  int wgs_per_cu;               /* persistent workgroups per CU in FUSED mode                 */
+  int num_cus;                  /* compute units of the device                                */
+  int lds_bytes_per_wg;         /* LDS of the fused kernel per workgroup                      */
+  int vgprs_per_lane;           /* registers of the fused kernel per lane (arch + acc)        */
+  size_t workspace_bytes;       /* workspace needed by this batch                             */
+  double host_plan_us;          /* host planning time of the last run                         */
+} pod_attn_stats;
+
+/* Create a handle for one attention configuration on the current HIP device.  Validates the
+ * configuration (ERR_INVALID_ARG / ERR_UNSUPPORTED) and queries the device (ERR_NO_DEVICE if
+ * it is not a gfx950).  Launches nothing. */
+pod_attn_status pod_attn_create(const pod_attn_config* cfg, pod_attn_handle** out);
+
+/* Bytes of device workspace pod_attn_run needs for this batch (work lists, counters, split
+ * partials).  Validates the batch metadata. */
+pod_attn_status pod_attn_workspace_size(pod_attn_handle* h, const pod_attn_batch* batch, size_t* bytes);
+
+/* Compute the hybrid batch.  q, k_cache, v_cache, block_tables, out and workspace are device
+ * pointers in the formats above; `stream` is a hipStream_t (NULL = null stream).  Plans the
+ * work on the host, copies the plan into `workspace` and launches on `stream` (FUSED: one
+ * kernel; SEPARATE: up to three; STREAMS: as SEPARATE on two internal streams joined by
+ * events).  Returns before the GPU finishes.  `out` rows are each written exactly once; no
+ * other memory than `out` and `workspace` is written. */
+pod_attn_status pod_attn_run(pod_attn_handle* h, const void* q, const void* k_cache,
+                             const void* v_cache, const int32_t* block_tables,
+                             const pod_attn_batch* batch, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Copy the diagnostics of the last run into *st. */
+pod_attn_status pod_attn_get_stats(pod_attn_handle* h, pod_attn_stats* st);
+
+/* Debug/test: gather one sequence's K (which = 0) or V (which = 1) for all KV heads into
+ * out_contig [ctx][Hkv][D] (same element type), through the same page-address arithmetic the
+ * attention kernels use.  Bit-exact copy; asynchronous on `stream`. */
+pod_attn_status pod_attn_gather_kv(pod_attn_handle* h, const void* cache, int which,
+                                   const int32_t* block_tables, int seq, int ctx,
+                                   const pod_attn_batch* batch, void* out_contig, void* stream);
+
+/* Debug/test: synchronise `stream` and read the workspace status word written by the last run
+ * (bit POD_ATTN_DEVICE_ERR_BAD_PAGE) and, if the handle has POD_ATTN_FLAG_DEBUG_CLAIMS, the
+ * per-item claim counts (claims[i] for prefill items first, then decode items; up to
+ * claims_cap entries) and per-CU claim totals of each kind (up to cu_cap entries each; may be
+ * NULL).  Returns the number of items in *n_items. */
+#define POD_ATTN_DEVICE_ERR_BAD_PAGE 1
+pod_attn_status pod_attn_read_device_status(pod_attn_handle* h, const void* workspace,
+                                            void* stream, int32_t* status_word,
+                                            int32_t* claims, int claims_cap, int* n_items,
+                                            int32_t* prefill_claims_per_cu,
+                                            int32_t* decode_claims_per_cu, int cu_cap);
+
+/* Host-only (no GPU needed): plan a batch for a device with num_cus compute units and
+ * wgs_per_cu persistent workgroups, and return the work items as 16 int32 each
+ * {seq, q_row, n_q, q_pos, kv_head, kv_begin, kv_end, group, split, partial_slot, kind
+ * (0 prefill, 1 decode), 0...}, prefill items first.  *n_items receives the count; at most
+ * items_cap items are written.  stats (may be NULL) receives the planning diagnostics. */
+pod_attn_status pod_attn_plan_inspect(const pod_attn_config* cfg, const pod_attn_batch* batch,
+                                      int num_cus, int wgs_per_cu, int32_t* items,
+                                      int items_cap, int* n_items, pod_attn_stats* stats);
+
+/* Profiling hook: when ev_start / ev_end (hipEvent_t, may be NULL) are set, the next
+ * pod_attn_run records ev_start on the launch stream right after the plan copy, before the
+ * first kernel, and ev_end after the last kernel (STREAMS mode: after the join), so that the
+ * kernels' own duration can be read with hipEventElapsedTime.  The hook is consumed by that
+ * run (one-shot); the events stay owned by the caller. */
+pod_attn_status pod_attn_set_kernel_events(pod_attn_handle* h, void* ev_start, void* ev_end);
+
+/* Thread-local message for the last non-OK status returned on this thread. */
+const char* pod_attn_last_error(void);
+
+/* Release the handle (internal streams and events included).  NULL is ignored. */
+void pod_attn_destroy(pod_attn_handle* h);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* POD_ATTN_H */

@@ -245,7 +245,11 @@ class HybridProblem:
 
     def sequence_output(self, s: int, heads: Iterable[int] | None = None) -> np.ndarray:
         """Reference output for every row of sequence s: [rows, len(heads), D]."""
-        rows = self.seq_rows(s)
+        return self.rows_output(s, self.seq_rows(s), heads)
+
+    def rows_output(self, s: int, rows, heads: Iterable[int] | None = None) -> np.ndarray:
+        """Reference output for the given q rows (all of sequence s): [rows, len(heads), D]."""
+        rows = np.asarray(rows, dtype=np.int64)
         if len(rows) == 0:
             return np.zeros((0, self.Hq, self.D))
         _, _, ctx = self.row_info(int(rows[0]))

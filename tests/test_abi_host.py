@@ -1,0 +1,229 @@
+"""Host-side checks of the C ABI (no GPU): the library loads and exports every declared
+function, the planner covers every (query row, head, visible key) exactly once, the
+validator rejects bad metadata with the documented status codes, and a host model of the
+fused kernel's claim policy terminates with every item claimed once."""
+import heapq
+
+import numpy as np
+import pytest
+import torch
+
+from hybrid_prefill_decode_paged_amd import binding as B
+from hybrid_prefill_decode_paged_amd import inputs as gen
+
+
+def test_library_exports_every_declared_function():
+    lib = B.load()
+    names = B.header_functions()
+    assert len(names) >= 9, names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/pod_attn.h but not exported"
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
+def test_create_without_device_reports_no_device():
+    with pytest.raises(B.PodAttnError) as e:
+        B.PodAttention(4, 4, 64, "fp32")
+    assert e.value.status == -5
+
+
+def _meta(spec):
+    bt = gen.block_tables_for(spec)
+    qs = np.zeros(spec.num_prefill + 1, np.int32)
+    qs[1:] = np.cumsum(spec.prefill_q_len)
+    return B.BatchMeta(qs, spec.prefill_ctx_len, spec.decode_ctx_len, bt.shape[1], spec.num_pages)
+
+
+def _check_coverage(spec, items, G):
+    """Every (row, head) covered by exactly one group; the group's key ranges tile [0, kv_len)
+    with kv_len = last query position + 1 >= every row's position + 1."""
+    Hkv = spec.num_kv_heads
+    qs = np.concatenate([[0], np.cumsum(spec.prefill_q_len)]).astype(int)
+    P = int(qs[-1])
+    covered = np.zeros((P + spec.num_decode, Hkv), dtype=np.int64)
+    groups = {}
+    for it in items:
+        seq, q_row, n_q, q_pos, g, a, z, grp, split, slot, kind = it[:11]
+        key = (kind, q_row, g)
+        groups.setdefault(key, []).append((split, a, z, n_q, q_pos, grp, slot, seq))
+    for (kind, q_row, g), parts in groups.items():
+        parts.sort()
+        n_q, q_pos, seq = parts[0][3], parts[0][4], parts[0][7]
+        assert [p[0] for p in parts] == list(range(len(parts)))
+        assert parts[0][1] == 0
+        for x, y in zip(parts[:-1], parts[1:]):
+            assert x[2] == y[1], "split ranges must be contiguous"
+        kv_len = parts[-1][2]
+        assert kv_len == q_pos + n_q
+        assert all(p[2] > p[1] for p in parts)
+        if len(parts) == 1:
+            assert parts[0][5] == -1
+        else:
+            assert len({p[5] for p in parts}) == 1 and parts[0][5] >= 0
+        covered[q_row:q_row + n_q, g] += 1
+        if kind == 0:
+            i = int(np.searchsorted(qs, q_row, side="right") - 1)
+            assert seq == i
+            L, ctx = spec.prefill_q_len[i], spec.prefill_ctx_len[i]
+            assert q_pos == ctx - L + (q_row - qs[i])
+        else:
+            i = q_row - P
+            assert seq == spec.num_prefill + i and n_q == 1
+            assert kv_len == spec.decode_ctx_len[i]
+    assert np.all(covered == 1)
+    # partial slots of split groups never overlap
+    slots = []
+    for it in items:
+        if it[7] >= 0:
+            ncols = it[2] * G
+            slots.append((int(it[9]), int(it[9]) + ncols))
+    slots.sort()
+    for (a0, a1), (b0, b1) in zip(slots[:-1], slots[1:]):
+        assert a1 <= b0
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+def test_plan_covers_every_row_head_key_once(idx):
+    spec = gen.config_spec(idx)
+    cfg = B.make_config(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.dtype)
+    items, st = B.plan_inspect(cfg, _meta(spec), 256, 2)
+    assert st["num_prefill_items"] + st["num_decode_items"] == len(items)
+    _check_coverage(spec, items, spec.num_q_heads // spec.num_kv_heads)
+
+
+@pytest.mark.parametrize("G,D,split,cap", [(1, 128, 0, 0), (2, 64, 128, 1), (3, 128, 256, 3),
+                                           (8, 64, 512, 0), (16, 128, 0, 2)])
+def test_plan_ragged_batches(G, D, split, cap):
+    rng = np.random.default_rng(G * 100 + D)
+    pre = [(int(L), int(L + o)) for L, o in zip(rng.integers(1, 300, 5), rng.integers(0, 3000, 5))]
+    pre.append((0, 17))                       # an empty chunk
+    dec = rng.integers(1, 5000, 9).tolist() + [1, 16, 17]
+    spec = gen.custom_spec("bf16", Hq=2 * G, Hkv=2, D=D, prefill=pre, decode=dec)
+    cfg = B.make_config(2 * G, 2, D, "bf16", decode_split_tokens=split, prefill_split_cap=cap)
+    items, st = B.plan_inspect(cfg, _meta(spec), 80, 2)
+    _check_coverage(spec, items, G)
+    if cap:
+        assert st["prefill_max_splits"] <= cap
+    if split:
+        assert st["decode_split_tokens"] == split
+
+
+def test_longest_first_order():
+    spec = gen.config_spec(4)
+    cfg = B.make_config(32, 4, 128)
+    items, _ = B.plan_inspect(cfg, _meta(spec), 256, 2)
+    pf = items[items[:, 10] == 0]
+    work = [(it[6] - it[5]) for it in pf[:: max(1, 1)]]
+    # descriptors are ordered by tile work; the first item belongs to the longest chunk
+    assert pf[0][3] + pf[0][2] == max(spec.prefill_ctx_len)
+    dc = items[items[:, 10] == 1]
+    kv = [int(it[3]) + 1 for it in dc]
+    assert kv[0] == max(spec.decode_ctx_len)
+    assert len(work) == len(pf)
+
+
+def _expect(status, **batch_kw):
+    cfg_kw = batch_kw.pop("cfg", {})
+    base = dict(num_q_heads=4, num_kv_heads=2, head_dim=128, dtype="bf16")
+    base.update(cfg_kw)
+    cfg = B.make_config(**base)
+    m = dict(prefill_q_start=[0, 8], prefill_ctx_len=[20], decode_ctx_len=[5, 33],
+             block_table_stride=4, num_pages_in_pool=100)
+    m.update(batch_kw)
+    meta = B.BatchMeta(**m)
+    with pytest.raises(B.PodAttnError) as e:
+        B.plan_inspect(cfg, meta, 256, 2)
+    assert e.value.status == status, str(e.value)
+    assert len(str(e.value)) > len("ERR_INVALID_ARG: ")
+
+
+def test_validator_rejects_bad_metadata():
+    INV, UNS = -1, -2
+    _expect(INV, cfg=dict(num_q_heads=6, num_kv_heads=4))          # Hq % Hkv != 0
+    _expect(UNS, cfg=dict(head_dim=96))                             # head_dim not 64/128
+    _expect(UNS, cfg=dict(num_q_heads=64, num_kv_heads=2))          # group 32 > 16
+    _expect(INV, prefill_q_start=[0, 30])                           # q_len > ctx
+    _expect(INV, prefill_q_start=[3, 8])                            # q_start[0] != 0
+    _expect(INV, decode_ctx_len=[0, 5])                             # decode ctx 0
+    _expect(INV, decode_ctx_len=[5, 65])                            # ctx > stride*16
+    _expect(INV, block_table_stride=0)
+    _expect(INV, num_pages_in_pool=0)
+    _expect(INV, cfg=dict(decode_split_tokens=100))                 # not a multiple of 128
+    cfg = B.make_config(4, 2, 128)
+    cfg.page_size = 32
+    with pytest.raises(B.PodAttnError) as e:
+        B.plan_inspect(cfg, B.BatchMeta([0], [], [4], 1, 4), 256, 2)
+    assert e.value.status == UNS
+
+
+def test_empty_batch_plans_nothing():
+    cfg = B.make_config(4, 2, 128)
+    items, st = B.plan_inspect(cfg, B.BatchMeta([0], [], [], 1, 1), 256, 2)
+    assert len(items) == 0 and st["num_decode_items"] == 0
+
+
+# ------------------------------------------------------------------ claim-policy model
+def simulate_fused(n_pf, n_dc, pf_time, dc_time, num_cus, wgs, cap, seed=0):
+    """Event simulation of the fused kernel's scheduler: each workgroup picks a role (prefill
+    only while its CU holds fewer than `cap` prefill-role workgroups, unless decode is drained),
+    claims items of that kind until the counter passes the end, then re-picks; returns the
+    claim log and the finish time."""
+    rng = np.random.default_rng(seed)
+    counters = [0, 0]
+    n_items = [n_pf, n_dc]
+    active = [0] * num_cus
+    claimed = [[], []]
+    events = []
+    state = {}
+    t_end = 0.0
+    for wg in range(num_cus * wgs):
+        cu = wg % num_cus
+        state[wg] = dict(cu=cu, pf_open=n_pf > 0, dc_open=n_dc > 0, role=None, counted=False)
+        heapq.heappush(events, (rng.uniform(0, 1e-3), wg))
+    while events:
+        t, wg = heapq.heappop(events)
+        s = state[wg]
+        t_end = max(t_end, t)
+        if s["role"] is not None:
+            i = counters[s["role"]]
+            counters[s["role"]] += 1
+            if i < n_items[s["role"]]:
+                claimed[s["role"]].append(i)
+                dt = (pf_time if s["role"] == 0 else dc_time) * rng.uniform(0.8, 1.2)
+                heapq.heappush(events, (t + dt, wg))
+                continue
+            if s["role"] == 0:
+                s["pf_open"] = False
+                if s["counted"]:
+                    active[s["cu"]] -= 1
+                    s["counted"] = False
+            else:
+                s["dc_open"] = False
+            s["role"] = None
+        role = None
+        if s["pf_open"] and s["dc_open"]:
+            if active[s["cu"]] < cap:
+                active[s["cu"]] += 1
+                s["counted"] = True
+                role = 0
+            else:
+                role = 1
+        elif s["dc_open"]:
+            role = 1
+        elif s["pf_open"]:
+            role = 0
+        if role is None:
+            continue
+        assert not (role == 0 and s["dc_open"] and active[s["cu"]] > cap)
+        s["role"] = role
+        heapq.heappush(events, (t, wg))
+    return claimed, t_end, active
+
+
+@pytest.mark.parametrize("n_pf,n_dc", [(0, 500), (300, 0), (256, 4096), (2000, 64), (1, 1)])
+def test_claim_policy_terminates_and_claims_each_item_once(n_pf, n_dc):
+    claimed, t, active = simulate_fused(n_pf, n_dc, 5.0, 1.0, num_cus=64, wgs=2, cap=1)
+    assert sorted(claimed[0]) == list(range(n_pf))
+    assert sorted(claimed[1]) == list(range(n_dc))
+    assert all(a == 0 for a in active)
+    assert np.isfinite(t)

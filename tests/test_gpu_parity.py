@@ -1,0 +1,222 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the same seeded
+inputs, element by element, in every launch mode; plus the bit-exact and structural checks
+(gather, page permutation, unused-slot NaNs, claim counts, determinism, bad page ids)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from hybrid_prefill_decode_paged_amd import binding as B
+from hybrid_prefill_decode_paged_amd import inputs as gen
+from oracle import attention as orc
+
+from helpers import check_close, problem, run_library, sample_pairs, to_f64
+
+pytestmark = pytest.mark.gpu
+MODES = ["fused", "separate", "streams"]
+
+
+def _say(msg):
+    print(f"[gpu-test] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.load()
+
+
+def _full_check(b, mode, what, **kw):
+    _say(f"{what} mode={mode} {kw}")
+    out, h, ws = run_library(b, mode=mode, **kw)
+    want = problem(b).full_output()
+    err = check_close(to_f64(out), want, b.spec.dtype, f"{what}/{mode}")
+    return out, h, ws, err
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_config1_fp32_all_modes(mode):
+    b = gen.make_batch(gen.config_spec(1), "cuda")
+    _full_check(b, mode, "cfg1")
+
+
+SMALL = [
+    # (dtype, Hq, Hkv, D, prefill (q_len, ctx) pairs, decode ctx list)
+    ("bf16", 4, 4, 128, [(64, 192)], [37, 100, 256, 257]),
+    ("bf16", 8, 2, 128, [(100, 100), (33, 290), (1, 17)], [1, 15, 16, 17, 600]),
+    ("bf16", 16, 2, 64, [(130, 700)], [2000, 31, 5]),
+    ("bf16", 16, 1, 128, [(40, 1000), (17, 17)], [1, 4097]),
+    ("bf16", 6, 2, 128, [(77, 200)], [999, 64]),
+    ("fp32", 8, 4, 128, [(50, 130)], [300, 1]),
+    ("fp32", 4, 1, 64, [(200, 480)], [77, 1025]),
+    ("bf16", 4, 2, 128, [], [4096, 1000, 3]),
+    ("bf16", 4, 2, 128, [(256, 3000), (0, 10)], []),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SMALL)))
+@pytest.mark.parametrize("mode", MODES)
+def test_small_batches_all_modes(case, mode):
+    dt, hq, hkv, d, pre, dec = SMALL[case]
+    spec = gen.custom_spec(dt, Hq=hq, Hkv=hkv, D=d, prefill=pre, decode=dec, seed=100 + case)
+    b = gen.make_batch(spec, "cuda")
+    _full_check(b, mode, f"small{case}")
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_forced_splits_use_the_combine(mode):
+    """Short split lengths force multi-split prefill tiles and decode sequences, so the
+    log-sum-exp combine (in-kernel last arriver, or the combine kernel) is exercised."""
+    spec = gen.custom_spec("bf16", Hq=8, Hkv=2, D=128, prefill=[(150, 1500), (64, 64)],
+                           decode=[1, 129, 700, 3000], seed=7)
+    b = gen.make_batch(spec, "cuda")
+    _, h, _, _ = _full_check(b, mode, "splits", decode_split_tokens=128, prefill_split_cap=16)
+    st = h.stats()
+    assert st["decode_max_splits"] > 1 and st["num_combine_groups"] > 0
+
+
+def test_nan_in_unused_slots_changes_nothing():
+    spec = gen.custom_spec("bf16", Hq=8, Hkv=2, D=128, prefill=[(45, 301)], decode=[17, 33, 250], seed=3)
+    for mode in MODES:
+        b = gen.make_batch(spec, "cuda")
+        _say(f"nan-poison mode={mode}")
+        ref, _, _ = run_library(b, mode=mode)
+        gen.poison_unused(b, float("nan"))
+        out, _, _ = run_library(b, mode=mode)
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+def test_permuted_and_identity_tables_bitwise_equal():
+    spec = gen.custom_spec("bf16", Hq=8, Hkv=2, D=128, prefill=[(70, 500)], decode=[900, 31], seed=5,
+                           identity_pages=True)
+    b = gen.make_batch(spec, "cuda")
+    perm = torch.randperm(spec.num_pages, generator=torch.Generator().manual_seed(0))
+    b2 = gen.HybridBatch(**{**b.__dict__})
+    b2.k_pool = torch.empty_like(b.k_pool)
+    b2.v_pool = torch.empty_like(b.v_pool)
+    b2.k_pool[perm.cuda()] = b.k_pool
+    b2.v_pool[perm.cuda()] = b.v_pool
+    bt2 = b.block_tables_host.copy()
+    used = bt2 != gen.UNUSED_PAGE_ID
+    bt2[used] = perm.numpy()[bt2[used]]
+    b2.block_tables_host = bt2
+    b2.block_tables = torch.from_numpy(bt2).cuda()
+    for mode in MODES:
+        _say(f"permuted-vs-identity mode={mode}")
+        o1, _, _ = run_library(b, mode=mode)
+        o2, _, _ = run_library(b2, mode=mode)
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp32", 64), ("bf16", 64)])
+def test_gather_is_bit_exact(dtype, D):
+    spec = gen.custom_spec(dtype, Hq=4, Hkv=2, D=D, prefill=[(10, 77)], decode=[1, 16, 33, 300], seed=9)
+    b = gen.make_batch(spec, "cuda")
+    h = B.PodAttention(4, 2, D, dtype)
+    meta = B.BatchMeta.from_batch(b)
+    prob = problem(b)
+    for seq, ctx in enumerate(spec.seq_ctx()):
+        for which, pool in ((0, b.k_pool), (1, b.v_pool)):
+            _say(f"gather {dtype} D={D} seq={seq} which={which}")
+            out = torch.empty(ctx, 2, D, dtype=spec.torch_dtype, device="cuda")
+            h.gather_kv(pool, which, b.block_tables, seq, ctx, meta, out)
+            torch.cuda.synchronize()
+            got = out.cpu()
+            for g in range(2):
+                K, V = orc.gather_kv(prob.k_pool, prob.v_pool, b.block_tables_host[seq], ctx, g, dtype)
+                want = K if which == 0 else V
+                np.testing.assert_array_equal(got[:, g].to(torch.float64).numpy(), want)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_every_item_claimed_exactly_once(mode):
+    spec = gen.custom_spec("bf16", Hq=8, Hkv=2, D=128, prefill=[(300, 2000), (50, 60)],
+                           decode=list(range(1, 3000, 97)), seed=12)
+    b = gen.make_batch(spec, "cuda")
+    _say(f"claims mode={mode}")
+    out, h, ws = run_library(b, mode=mode, flags=B.FLAG_DEBUG_CLAIMS, decode_split_tokens=256)
+    st = h.stats()
+    n = st["num_prefill_items"] + st["num_decode_items"]
+    status, claims, per_cu = h.read_device_status(ws, n_items_cap=n, cu_cap=1024)
+    assert status == 0
+    assert len(claims) == n and np.all(claims == 1), np.unique(claims, return_counts=True)
+    pf, dc = per_cu
+    assert pf.sum() == st["num_prefill_items"] and dc.sum() == st["num_decode_items"]
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_run_to_run_bitwise_determinism(mode):
+    spec = gen.custom_spec("bf16", Hq=32, Hkv=8, D=128, prefill=[(256, 2000)],
+                           decode=[3000, 1500, 700, 40], seed=21)
+    b = gen.make_batch(spec, "cuda")
+    _say(f"determinism mode={mode}")
+    o1, h, ws = run_library(b, mode=mode, decode_split_tokens=256)
+    o2 = torch.empty_like(o1)
+    run_library(b, handle=h, out=o2, workspace=ws)
+    o3 = torch.empty_like(o1)
+    run_library(b, handle=h, out=o3, workspace=ws)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
+
+
+def test_out_of_pool_page_id_is_reported_not_read():
+    """A used block-table entry outside the pool is never dereferenced: the kernels flag it in
+    the workspace status word and treat that page as holding no keys."""
+    spec = gen.custom_spec("bf16", Hq=4, Hkv=2, D=128, prefill=[(16, 64)], decode=[40, 20], seed=4)
+    b = gen.make_batch(spec, "cuda")
+    bt = b.block_tables_host.copy()
+    bt[2, 1] = spec.num_pages + 1000            # row 2 = second decode (ctx 20): its second page
+    b.block_tables_host = bt
+    b.block_tables = torch.from_numpy(bt).cuda()
+    for mode in MODES:
+        _say(f"bad-page mode={mode}")
+        out, h, ws = run_library(b, mode=mode)
+        status, _, _ = h.read_device_status(ws)
+        assert status & B.DEVICE_ERR_BAD_PAGE
+        # sequences without a bad entry are unaffected
+        prob = problem(b)
+        want = np.stack([prob.sequence_output(s) for s in (0,)])[0]
+        check_close(to_f64(out[:16]), want, "bf16", "bad-page/clean rows")
+        assert not torch.isnan(out[16:]).any()
+
+
+def test_empty_batch_is_a_no_op():
+    h = B.PodAttention(4, 2, 128, "bf16")
+    meta = B.BatchMeta([0], [], [], 1, 1)
+    q = torch.zeros(1, 4, 128, dtype=torch.bfloat16, device="cuda")
+    h.run(q, q, q, torch.zeros(1, 1, dtype=torch.int32, device="cuda"), meta, q, None)
+    torch.cuda.synchronize()
+
+
+def test_workspace_too_small_is_rejected():
+    spec = gen.custom_spec("bf16", Hq=4, Hkv=2, D=128, prefill=[(16, 64)], decode=[40], seed=4)
+    b = gen.make_batch(spec, "cuda")
+    h = B.PodAttention(4, 2, 128, "bf16")
+    meta = B.BatchMeta.from_batch(b)
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(B.PodAttnError) as e:
+        h.run(b.q, b.k_pool, b.v_pool, b.block_tables, meta, torch.empty_like(b.q), ws)
+    assert e.value.status == -3
+
+
+# ------------------------------------------------------------------ full-size workloads
+@pytest.mark.parametrize("idx", [2, 3, 4, 5])
+def test_full_size_workloads_sampled(idx):
+    spec = gen.config_spec(idx)
+    _say(f"cfg{idx}: generating {spec.num_pages} pages")
+    b = gen.make_batch(spec, "cuda")
+    prob = problem(b)
+    pairs = sample_pairs(b, n_prefill=6, n_decode=6, seed=idx)
+    want = prob.sampled_output(pairs)
+    for mode in ("fused", "separate"):
+        _say(f"cfg{idx} mode={mode}")
+        out, h, ws = run_library(b, mode=mode)
+        got = np.stack([to_f64(out[r, hh]) for r, hh in pairs])
+        check_close(got, want, "bf16", f"cfg{idx}/{mode}")
+        assert not torch.isnan(out).any()
+        del out, ws
+    del b, prob
+    torch.cuda.empty_cache()
