@@ -65,6 +65,9 @@ def time_mode(torch, h, b, meta, out, ws, steps, warmup):
         h.run(b.q, b.k_pool, b.v_pool, b.block_tables, meta, out, ws)
     torch.cuda.synchronize()
     ks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, z in ks:             # torch creates the HIP events on first record; the library re-records them
+        a.record(stream)
+        z.record(stream)
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)

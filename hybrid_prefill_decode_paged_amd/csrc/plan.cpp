@@ -153,7 +153,7 @@ pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus
   if (c.decode_split_tokens > 0) {
     st_target = c.decode_split_tokens;
   } else {
-    long target_items = (long)num_cus * wgs_per_cu * 16;
+    long target_items = (long)num_cus * wgs_per_cu * kWaves * 4;   // ~4 items per decode wave
     long st = (total_tok + target_items - 1) / std::max(1L, target_items);
     st = std::max(512L, std::min(4096L, st));
     st_target = round_up_int((int)st, 128);
@@ -220,8 +220,8 @@ void expand_items(const Plan& p, const Config& c, std::vector<int32_t>* items) {
     for (int di = 0; di < n; ++di) {
       const int32_t* d = &D[(size_t)di * kDescInts];
       const int ns = d[kDNSplit], st = d[kDSplitTok];
-      for (int h = 0; h < c.hkv; ++h) {
-        for (int s = 0; s < ns; ++s) {
+      for (int s = 0; s < ns; ++s) {           // split-major, as the kernels decode items
+        for (int h = 0; h < c.hkv; ++h) {
           int32_t it[16] = {0};
           it[0] = d[kDSeq]; it[1] = d[kDQRow]; it[2] = d[kDNq]; it[3] = d[kDQPos];
           it[4] = h; it[5] = s * st; it[6] = std::min(d[kDKvLen], (s + 1) * st);

@@ -165,6 +165,17 @@ static hipError_t launch(const void* fn, int grid, KernelParams& p, hipStream_t 
   return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
 }
 
+// Combine groups [g0, g1), whose groups have at most max_cols columns: one workgroup per
+// (group, 16 columns).
+static hipError_t launch_combine(pod_attn_handle* h, const KernelParams& base, int g0, int g1, int max_cols,
+                                 hipStream_t s) {
+  KernelParams c = base;
+  c.group_begin = g0;
+  c.group_end = g1;
+  c.combine_col_blocks = (max_cols + 15) / 16;
+  return launch(h->ks.combine, (g1 - g0) * c.combine_col_blocks, c, s);
+}
+
 pod_attn_status pod_attn_run(pod_attn_handle* h, const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* block_tables, const pod_attn_batch* b, void* out,
                              void* workspace, size_t workspace_bytes, void* stream_) {
@@ -250,28 +261,18 @@ pod_attn_status pod_attn_run(pod_attn_handle* h, const void* q, const void* k_ca
   } else if (mode == POD_ATTN_MODE_SEPARATE) {
     kp.inline_combine = 0;
     if (p.n_pf_items) POD_HIP(launch(h->ks.prefill, p.n_pf_items, kp, stream));
-    if (p.n_dc_items) POD_HIP(launch(h->ks.decode, p.n_dc_items, kp, stream));
-    if (p.n_groups) {
-      kp.group_begin = 0; kp.group_end = p.n_groups;
-      POD_HIP(launch(h->ks.combine, p.n_groups, kp, stream));
-    }
+    if (p.n_dc_items) POD_HIP(launch(h->ks.decode, (p.n_dc_items + kWaves - 1) / kWaves, kp, stream));
+    if (p.n_pf_groups) POD_HIP(launch_combine(h, kp, 0, p.n_pf_groups, p.tile_cols, stream));
+    if (p.n_groups > p.n_pf_groups) POD_HIP(launch_combine(h, kp, p.n_pf_groups, p.n_groups, h->cfg.group(), stream));
   } else {
     kp.inline_combine = 0;
     POD_HIP(hipEventRecord(h->evStart, stream));
     POD_HIP(hipStreamWaitEvent(h->sA, h->evStart, 0));
     POD_HIP(hipStreamWaitEvent(h->sB, h->evStart, 0));
     if (p.n_pf_items) POD_HIP(launch(h->ks.prefill, p.n_pf_items, kp, h->sA));
-    if (p.n_pf_groups) {
-      KernelParams c = kp;
-      c.group_begin = 0; c.group_end = p.n_pf_groups;
-      POD_HIP(launch(h->ks.combine, p.n_pf_groups, c, h->sA));
-    }
-    if (p.n_dc_items) POD_HIP(launch(h->ks.decode, p.n_dc_items, kp, h->sB));
-    if (p.n_groups > p.n_pf_groups) {
-      KernelParams c = kp;
-      c.group_begin = p.n_pf_groups; c.group_end = p.n_groups;
-      POD_HIP(launch(h->ks.combine, p.n_groups - p.n_pf_groups, c, h->sB));
-    }
+    if (p.n_pf_groups) POD_HIP(launch_combine(h, kp, 0, p.n_pf_groups, p.tile_cols, h->sA));
+    if (p.n_dc_items) POD_HIP(launch(h->ks.decode, (p.n_dc_items + kWaves - 1) / kWaves, kp, h->sB));
+    if (p.n_groups > p.n_pf_groups) POD_HIP(launch_combine(h, kp, p.n_pf_groups, p.n_groups, h->cfg.group(), h->sB));
     POD_HIP(hipEventRecord(h->evA, h->sA));
     POD_HIP(hipEventRecord(h->evB, h->sB));
     POD_HIP(hipStreamWaitEvent(stream, h->evA, 0));

@@ -14,9 +14,11 @@ constexpr int kMaxGroup = 16;        // decode columns = group size, one 16-wide
 constexpr int kPrefillKvTile = 64;   // keys per prefill inner iteration (4 pages)
 constexpr int kDecodeStep = 32;      // keys per decode wave step (2 pages)
 constexpr int kCuSlots = 1024;       // hashed (XCC, SE, CU) slots for per-CU scheduler state
+constexpr int kMaxCombineSplits = 256;  // splits merged through the LDS weight table
 
 // A descriptor covers one prefill query tile or one decode sequence; it expands to
-// Hkv * n_split work items (item = (kv head, KV split)), head-major.
+// Hkv * n_split work items, split-major: item = split * Hkv + kv_head, so that items taken
+// one after another read the adjacent (page, head) slabs of the same pages.
 enum DescField {
   kDSeq = 0,        // block-table row
   kDQRow,           // first q/out row
@@ -66,6 +68,7 @@ struct KernelParams {
   int prefill_cap_per_cu;    // fused: prefill-role workgroups allowed per CU while decode remains
   int inline_combine;        // 1: last-arriving split combines in-kernel (fused)
   int group_begin, group_end;// combine kernel range
+  int combine_col_blocks;     // combine kernel: workgroups per group (16 columns each)
 };
 
 // Workspace map (byte offsets), computed by the planner.

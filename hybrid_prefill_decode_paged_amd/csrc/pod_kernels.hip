@@ -68,9 +68,7 @@ template <typename T, int D> struct Geo {
   static constexpr int kStageChunks = 2 * kTp * kCps;   // K + V chunks of one prefill tile
   static constexpr int kStageR = kStageChunks / kThreads;
   static constexpr int kPrefillLds = 2 * 2 * kTp * kSlab;              // 2 buffers x (K, V)
-  static constexpr int kMergeRow = D + 4;                              // padded floats
-  static constexpr int kMergeLds = kWaves * 16 * kMergeRow * 4 + kWaves * 16 * 2 * 4;
-  static constexpr int kFusedLds = kPrefillLds > kMergeLds ? kPrefillLds : kMergeLds;
+  static constexpr int kFusedLds = kPrefillLds;                        // decode uses no LDS
   static_assert(kStageChunks % kThreads == 0, "tile must split evenly over the workgroup");
   static_assert(kTp % 2 == 0, "bf16 PV pairs pages");
 };
@@ -222,19 +220,95 @@ __device__ __forceinline__ float softmax_update(float (&x)[NV], float& m, float&
   return alpha;
 }
 
-// ------------------------------------------------------------------ decode item
-// One (decode sequence, KV head, key split): the G query heads of the KV head are the
-// columns of one 16-wide block.  The four waves take interleaved 32-key steps of the split and
-// merge through LDS at the end.
+// ------------------------------------------------------------------ split partials
+// Partials that another workgroup merges inside the same launch are written and read with
+// device-scope (write-through / L2-bypassing) accesses: the writer's stores are complete once
+// its vmcnt drains, so no cache-wide write-back is needed before the ticket is taken, and the
+// merging wave never sees a stale line from its own L2.
+__device__ __forceinline__ void store_part4(float* dst, f32x4 v, bool coherent) {
+  if (coherent) {
+    __hip_atomic_store(dst + 0, v.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(dst + 1, v.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(dst + 2, v.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(dst + 3, v.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    *(f32x4*)dst = v;
+  }
+}
+__device__ __forceinline__ void store_part1(float* dst, float v, bool coherent) {
+  if (coherent) __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *dst = v;
+}
+__device__ __forceinline__ f32x4 load_part4_coherent(const float* src) {
+  return f32x4{__hip_atomic_load(src + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+               __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+               __hip_atomic_load(src + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+               __hip_atomic_load(src + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)};
+}
+__device__ __forceinline__ float load_part1_coherent(const float* src) {
+  return __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Arrival of one split: every store of the calling wave has completed (vmcnt 0); one lane takes
+// the group's ticket.  Returns, wave-uniformly, whether this split arrived last.
+__device__ __forceinline__ int arrive_last(int32_t* ticket, int ns) {
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  int last = 0;
+  if ((threadIdx.x & 63) == 0) last = atomicAdd(ticket, 1) == ns - 1;
+  return __builtin_amdgcn_readfirstlane(last);
+}
+
+// ------------------------------------------------------------------ log-sum-exp combine
+// out = sum_s w_s o_s / sum_s w_s with w_s = 2^(lse_s - max lse); empty splits weigh zero.
+// In-kernel form (the last-arriving split merges its group): work is spread over `nthreads`
+// threads starting at `tid`, partials are read with device-scope loads.
 template <typename T, int D>
-__device__ void decode_item(const KernelParams& P, CPTR(int32_t) dsc, int head, int split, char* lds) {
+__device__ void combine_group(const KernelParams& P, CPTR(int32_t) dsc, int head, int tid, int nthreads) {
+  const int ns = dsc[kDNSplit], ncols = dsc[kDNcols], q_row = dsc[kDQRow];
+  const size_t base = (size_t)dsc[kDPartBase] + (size_t)head * ns * ncols;
+  const int G = P.group;
+  constexpr int kQ = D / 4;
+  for (int idx = tid; idx < ncols * kQ; idx += nthreads) {
+    const int c = idx / kQ, d4 = idx - c * kQ;
+    float M = kNegInf;
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, load_part1_coherent(P.part_lse + base + (size_t)s * ncols + c));
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+    if (M != kNegInf) {
+      for (int s = 0; s < ns; ++s) {
+        const size_t slot = base + (size_t)s * ncols + c;
+        const float wgt = exp2_fast(load_part1_coherent(P.part_lse + slot) - M);
+        if (wgt > 0.f) acc += wgt * load_part4_coherent(P.part_o + slot * D + 4 * d4);
+        wsum += wgt;
+      }
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    const int qi = c / G, hh = c - qi * G;
+    T* dst = (T*)P.out + ((size_t)(q_row + qi) * P.hq + head * G + hh) * D + 4 * d4;
+    store4<T>(dst, acc * inv);
+  }
+}
+
+// ------------------------------------------------------------------ decode item (one wave)
+// One (decode sequence, KV head, key split) streamed by a single wave: the G query heads of
+// the KV head are the columns of one 16-wide MFMA block; 32 keys (two pages) per step, with
+// the next step's K/V loads in flight while the current step is computed.  Waves run their
+// decode items independently (no workgroup barrier, no LDS).
+template <typename T, int D>
+__device__ void decode_wave_item(const KernelParams& P, int item) {
   using Gm = Geo<T, D>;
   typedef typename VOp<T>::type VT;
+  CPTR(int32_t) descs = (CPTR(int32_t))P.ddesc;
+  const int di = find_desc(descs, P.n_ddesc, kDItemBegin, item);
+  CPTR(int32_t) dsc = descs + (size_t)di * kDescInts;
+  const int ns = dsc[kDNSplit];
+  const int local = item - dsc[kDItemBegin];
+  const int split = local / P.hkv, head = local - split * P.hkv;   // adjacent items: adjacent heads
+
   const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
-  const int w = wave_index();
   const int G = P.group;
   const int seq = dsc[kDSeq], q_row = dsc[kDQRow], kv_len = dsc[kDKvLen];
-  const int ns = dsc[kDNSplit], st = dsc[kDSplitTok];
+  const int st = dsc[kDSplitTok];
   const int kv_begin = split * st;
   const int kv_end = min(kv_len, kv_begin + st);
   const int n_steps = (kv_end - kv_begin + kDecodeStep - 1) / kDecodeStep;
@@ -317,74 +391,44 @@ __device__ void decode_item(const KernelParams& P, CPTR(int32_t) dsc, int head, 
     }
   };
 
-  // Two register sets: the next step's loads are issued before the current step's math.
-  // Past the last step the prefetch re-reads the current step (cache hits, results unused).
-  int step = w;
-  if (step < n_steps) {
-    load_step(step, kA, vA, limA);
-    for (;;) {
-      int nxt = step + kWaves;
-      load_step(nxt < n_steps ? nxt : step, kB, vB, limB);
-      compute_step(kA, vA, limA);
-      if (nxt >= n_steps) break;
-      step = nxt;
-      nxt = step + kWaves;
-      load_step(nxt < n_steps ? nxt : step, kA, vA, limA);
-      compute_step(kB, vB, limB);
-      if (nxt >= n_steps) break;
-      step = nxt;
-    }
+  // Two register sets; past the last step the prefetch re-reads the current step (cache hits,
+  // results unused) so that every load is unconditional.
+  int step = 0;
+  load_step(0, kA, vA, limA);
+  for (;;) {
+    int nxt = step + 1;
+    load_step(nxt < n_steps ? nxt : step, kB, vB, limB);
+    compute_step(kA, vA, limA);
+    if (nxt >= n_steps) break;
+    step = nxt;
+    nxt = step + 1;
+    load_step(nxt < n_steps ? nxt : step, kA, vA, limA);
+    compute_step(kB, vB, limB);
+    if (nxt >= n_steps) break;
+    step = nxt;
   }
 
-  // ---- merge the four waves' states through LDS
-  float* lo = (float*)lds;                                   // [4][16][D+4]
-  float* lm = lo + kWaves * 16 * Gm::kMergeRow;              // [4][16]
-  float* ll = lm + kWaves * 16;                              // [4][16]
+  // ---- epilogue: lane (n, q) holds O^T[16b + 4q + i][n]
   const float l_tot = sum_over_groups(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (n < G) {
+    if (ns == 1) {
+      T* dst = (T*)P.out + ((size_t)q_row * P.hq + head * G + n) * D + 4 * q;
 #pragma unroll
-  for (int b = 0; b < Gm::kDb; ++b)
-    *(f32x4*)(lo + (w * 16 + n) * Gm::kMergeRow + 16 * b + 4 * q) = o[b];
-  if (q == 0) {
-    lm[w * 16 + n] = m_run;
-    ll[w * 16 + n] = l_tot;
-  }
-  __syncthreads();
-  {
-    const int tid = threadIdx.x;
-    const int c = tid & 15, dg = tid >> 4;                   // 16 columns x 16 dim groups
-    constexpr int kPer = D / 16;
-    float M = kNegInf;
+      for (int b = 0; b < Gm::kDb; ++b) store4<T>(dst + 16 * b, o[b] * inv);
+    } else {
+      const size_t slot = (size_t)dsc[kDPartBase] + ((size_t)head * ns + split) * G + n;
+      float* dst = P.part_o + slot * D + 4 * q;
+      const bool coh = P.inline_combine != 0;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, lm[ww * 16 + c]);
-    float wt[kWaves], L = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
-      wt[ww] = M == kNegInf ? 0.f : exp2_fast(lm[ww * 16 + c] - M);
-      L += wt[ww] * ll[ww * 16 + c];
-    }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    float res[kPer];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      float a = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) a += wt[ww] * lo[(ww * 16 + c) * Gm::kMergeRow + dg * kPer + j];
-      res[j] = a * inv;
-    }
-    if (c < G) {
-      if (ns == 1) {
-        T* dst = (T*)P.out + ((size_t)q_row * P.hq + head * G + c) * D + dg * kPer;
-#pragma unroll
-        for (int j = 0; j < kPer; j += 4) store4<T>(dst + j, f32x4{res[j], res[j + 1], res[j + 2], res[j + 3]});
-      } else {
-        const size_t slot = (size_t)dsc[kDPartBase] + ((size_t)head * ns + split) * G + c;
-        float* dst = P.part_o + slot * D + dg * kPer;
-#pragma unroll
-        for (int j = 0; j < kPer; j += 4) *(f32x4*)(dst + j) = f32x4{res[j], res[j + 1], res[j + 2], res[j + 3]};
-        if (dg == 0) P.part_lse[slot] = L > 0.f ? M + __log2f(L) : kNegInf;
-      }
+      for (int b = 0; b < Gm::kDb; ++b) store_part4(dst + 16 * b, o[b] * inv, coh);
+      if (q == 0) store_part1(P.part_lse + slot, l_tot > 0.f ? m_run + __log2f(l_tot) : kNegInf, coh);
     }
   }
+  // Last arriver combines ([POD], "Virtual CTAs and per-SM balance": exact synchronisation
+  // where partial results meet, and no wave ever waits for another).
+  if (ns > 1 && P.inline_combine && arrive_last(P.tickets + dsc[kDGroupBegin] + head, ns))
+    combine_group<T, D>(P, dsc, head, lane, 64);
 }
 
 // ------------------------------------------------------------------ prefill tile item
@@ -436,8 +480,9 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
     for (int b = 0; b < Gm::kDb; ++b) o[nb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run[2] = {kNegInf, kNegInf}, l_run[2] = {0.f, 0.f};
 
-  // ---- staging: chunk r of this thread is linear chunk r*256+tid of [K pages][V pages]
-  u32x4 stg[Gm::kStageR];
+  // ---- staging: K and V pages of a key tile go HBM -> LDS directly (global_load_lds, no
+  // registers); instruction r of wave w moves linear chunks r*256 + 64w .. +63 of
+  // [K pages][V pages], one 16-byte chunk per lane, into consecutive LDS.
   int lim_cur[Gm::kTp], lim_nxt[Gm::kTp];
   auto tile_pages = [&](int j, int (&lim)[Gm::kTp], int (&pg)[Gm::kTp]) {
     const int tb = kv_begin + j * Gm::kTileKeys;
@@ -449,26 +494,11 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
       lim[p] = l;
     }
   };
-  auto load_tile = [&](int j, int (&lim)[Gm::kTp]) {
-    int pg[Gm::kTp];
-    tile_pages(j, lim, pg);
-#pragma unroll
-    for (int r = 0; r < Gm::kStageR; ++r) {
-      const int L = r * kThreads + tid;
-      const int half = L / (Gm::kTp * Gm::kCps);
-      const int rem = L - half * (Gm::kTp * Gm::kCps);
-      const int p = rem / Gm::kCps, c = rem - p * Gm::kCps;
-      int page = pg[0];
-#pragma unroll
-      for (int pp = 1; pp < Gm::kTp; ++pp) page = p == pp ? pg[pp] : page;
-      const char* base = slab_ptr<T, D>(half ? P.v : P.k, page, P.hkv, head);
-      stg[r] = ld16(base + c * 16);
-    }
-  };
   auto kbuf = [&](int b) { return lds + b * (2 * Gm::kTp * Gm::kSlab); };
   auto vbuf = [&](int b) { return lds + b * (2 * Gm::kTp * Gm::kSlab) + Gm::kTp * Gm::kSlab; };
   // bf16 V rows are 32 bytes (two 16-byte halves); rows 8..15 of each 16-row block swap their
   // halves so that a wave's 8-byte reads of 16 consecutive rows spread over all LDS banks.
+  // The swap is its own inverse, so LDS chunk c is loaded from source chunk vswz(c).
   auto vswz = [&](int c) {
     if constexpr (Gm::kBytes == 2) {
       const int d = c >> 1, h = c & 1;
@@ -477,15 +507,22 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
       return c;
     }
   };
-  auto store_tile = [&](int b) {
+  auto issue_tile = [&](int j, int b, int (&lim)[Gm::kTp]) {
+    int pg[Gm::kTp];
+    tile_pages(j, lim, pg);
 #pragma unroll
     for (int r = 0; r < Gm::kStageR; ++r) {
-      const int L = r * kThreads + tid;
-      const int half = L / (Gm::kTp * Gm::kCps);
-      const int rem = L - half * (Gm::kTp * Gm::kCps);
-      const int p = rem / Gm::kCps, c = rem - p * Gm::kCps;
-      char* dst = half ? vbuf(b) + p * Gm::kSlab + vswz(c) * 16 : kbuf(b) + p * Gm::kSlab + c * 16;
-      *(u32x4*)dst = stg[r];
+      const int L0 = r * kThreads + 64 * w;                 // wave-uniform first chunk
+      const int half = L0 / (Gm::kTp * Gm::kCps);
+      const int rem0 = L0 - half * (Gm::kTp * Gm::kCps);
+      const int p = rem0 / Gm::kCps, c0 = rem0 - p * Gm::kCps;
+      int page = pg[0];
+#pragma unroll
+      for (int pp = 1; pp < Gm::kTp; ++pp) page = p == pp ? pg[pp] : page;
+      const int c = c0 + lane;
+      const char* src = slab_ptr<T, D>(half ? P.v : P.k, page, P.hkv, head) + (half ? vswz(c) : c) * 16;
+      char* dst = (half ? vbuf(b) : kbuf(b)) + p * Gm::kSlab + c0 * 16;
+      __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
     }
   };
 
@@ -514,15 +551,22 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       float x[4 * Gm::kTp];
+      if (full) {                                  // wave-uniform: no key of the tile is masked
 #pragma unroll
-      for (int mb = 0; mb < Gm::kTp; ++mb)
+        for (int mb = 0; mb < Gm::kTp; ++mb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int slot = 4 * q + i;
-          const int t = tb + mb * kPage + slot;
-          const bool ok = full || (slot < lim[mb] && t <= pos[nb]);
-          x[4 * mb + i] = ok ? S[nb][mb][i] * sl2 : kNegInf;
-        }
+          for (int i = 0; i < 4; ++i) x[4 * mb + i] = S[nb][mb][i] * sl2;
+      } else {
+#pragma unroll
+        for (int mb = 0; mb < Gm::kTp; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int slot = 4 * q + i;
+            const int t = tb + mb * kPage + slot;
+            const bool ok = (slot < lim[mb]) & (t <= pos[nb]);   // select, never multiply
+            x[4 * mb + i] = ok ? S[nb][mb][i] * sl2 : kNegInf;
+          }
+      }
       const float alpha = softmax_update<4 * Gm::kTp>(x, m_run[nb], l_run[nb]);
 #pragma unroll
       for (int b2 = 0; b2 < Gm::kDb; ++b2) o[nb][b2] *= alpha;
@@ -571,14 +615,14 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
   };
 
   if (n_tiles > 0) {
-    load_tile(0, lim_cur);
-    store_tile(0);
+    issue_tile(0, 0, lim_cur);
+    __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): this wave's LDS loads landed
     __syncthreads();
     for (int j = 0; j < n_tiles; ++j) {
       const bool more = j + 1 < n_tiles;
-      if (more) load_tile(j + 1, lim_nxt);
+      if (more) issue_tile(j + 1, (j + 1) & 1, lim_nxt);
       compute_tile(j & 1, j, lim_cur);
-      if (more) store_tile((j + 1) & 1);
+      __builtin_amdgcn_s_waitcnt(0x0F70);
       __syncthreads();
 #pragma unroll
       for (int p = 0; p < Gm::kTp; ++p) lim_cur[p] = lim_nxt[p];
@@ -600,70 +644,34 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
     } else {
       const size_t slot = (size_t)dsc[kDPartBase] + ((size_t)head * ns + split) * ncols + c;
       float* dst = P.part_o + slot * D + 4 * q;
+      const bool coh = P.inline_combine != 0;
 #pragma unroll
-      for (int b2 = 0; b2 < Gm::kDb; ++b2) *(f32x4*)(dst + 16 * b2) = o[nb][b2] * inv;
-      if (q == 0) P.part_lse[slot] = l_tot > 0.f ? m_run[nb] + __log2f(l_tot) : kNegInf;
+      for (int b2 = 0; b2 < Gm::kDb; ++b2) store_part4(dst + 16 * b2, o[nb][b2] * inv, coh);
+      if (q == 0) store_part1(P.part_lse + slot, l_tot > 0.f ? m_run[nb] + __log2f(l_tot) : kNegInf, coh);
     }
-  }
-}
-
-// ------------------------------------------------------------------ log-sum-exp combine
-// out = sum_s w_s o_s / sum_s w_s with w_s = 2^(lse_s - max lse); empty splits weigh zero.
-template <typename T, int D>
-__device__ void combine_group(const KernelParams& P, CPTR(int32_t) dsc, int head) {
-  const int ns = dsc[kDNSplit], ncols = dsc[kDNcols], q_row = dsc[kDQRow];
-  const size_t base = (size_t)dsc[kDPartBase] + (size_t)head * ns * ncols;
-  const int G = P.group;
-  constexpr int kQ = D / 4;
-  for (int idx = threadIdx.x; idx < ncols * kQ; idx += kThreads) {
-    const int c = idx / kQ, d4 = idx - c * kQ;
-    float M = kNegInf;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, P.part_lse[base + (size_t)s * ncols + c]);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float wsum = 0.f;
-    if (M != kNegInf) {
-      for (int s = 0; s < ns; ++s) {
-        const size_t slot = base + (size_t)s * ncols + c;
-        const float wgt = exp2_fast(P.part_lse[slot] - M);
-        if (wgt > 0.f) acc += wgt * *(const f32x4*)(P.part_o + slot * D + 4 * d4);
-        wsum += wgt;
-      }
-    }
-    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-    const int qi = c / G, hh = c - qi * G;
-    T* dst = (T*)P.out + ((size_t)(q_row + qi) * P.hq + head * G + hh) * D + 4 * d4;
-    store4<T>(dst, acc * inv);
   }
 }
 
 // ------------------------------------------------------------------ item dispatch
+// Prefill item: the whole workgroup.  Split partials are merged by the workgroup that
+// arrives last when the combine runs in-kernel.
 template <typename T, int D>
-__device__ void run_item(const KernelParams& P, int kind, int item, char* lds, int* s_flag) {
-  CPTR(int32_t) descs = (CPTR(int32_t))(kind == 0 ? P.pdesc : P.ddesc);
-  const int nd = kind == 0 ? P.n_pdesc : P.n_ddesc;
-  const int di = find_desc(descs, nd, kDItemBegin, item);
+__device__ void run_prefill_item(const KernelParams& P, int item, char* lds, int* s_flag) {
+  CPTR(int32_t) descs = (CPTR(int32_t))P.pdesc;
+  const int di = find_desc(descs, P.n_pdesc, kDItemBegin, item);
   CPTR(int32_t) dsc = descs + (size_t)di * kDescInts;
   const int ns = dsc[kDNSplit];
   const int local = item - dsc[kDItemBegin];
-  const int head = local / ns, split = local - head * ns;
-  if (kind == 0) prefill_item<T, D>(P, dsc, head, split, lds);
-  else decode_item<T, D>(P, dsc, head, split, lds);
+  const int split = local / P.hkv, head = local - split * P.hkv;
+  prefill_item<T, D>(P, dsc, head, split, lds);
   if (ns > 1 && P.inline_combine) {
-    // Last arriver combines: each wave's partial stores complete, one agent-scope release
-    // makes them visible device-wide, the ticket counts arrivals; the last one acquires and
-    // merges.  No workgroup ever waits for another ([POD], "Virtual CTAs and per-SM balance":
-    // exact synchronisation where partial results meet, no deadlock between the two kinds).
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's stores have reached L2
+    // Each wave's partial stores complete before the barrier; thread 0 takes the ticket; the
+    // workgroup holding the last split merges the group.  No workgroup waits for another.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    if (threadIdx.x == 0) {
-      __threadfence();
-      const int prev = atomicAdd(P.tickets + dsc[kDGroupBegin] + head, 1);
-      const int last = prev == ns - 1;
-      if (last) __threadfence();
-      *s_flag = last;
-    }
+    if (threadIdx.x == 0) *s_flag = atomicAdd(P.tickets + dsc[kDGroupBegin] + head, 1) == ns - 1;
     __syncthreads();
-    if (*s_flag) combine_group<T, D>(P, dsc, head);
+    if (*s_flag) combine_group<T, D>(P, dsc, head, threadIdx.x, kThreads);
   }
   __syncthreads();   // LDS and the flag are reused by the next item
 }
@@ -675,7 +683,6 @@ __device__ __forceinline__ int cu_slot() {
   return (int)(((xcc & 7u) << 7) | (se << 5) | (sh << 4) | cu);
 }
 
-template <typename T, int D>
 __device__ __forceinline__ void note_claim(const KernelParams& P, int kind, int item, int cu) {
   if (P.claims) {
     atomicAdd(P.claims + (kind == 0 ? 0 : P.n_pf_items) + item, 1);
@@ -683,12 +690,34 @@ __device__ __forceinline__ void note_claim(const KernelParams& P, int kind, int 
   }
 }
 
+// Decode stream of one wave: claim items one at a time from the decode counter (the next
+// claim is issued before the current item is processed) until the counter passes the end.
+template <typename T, int D>
+__device__ void decode_wave_stream(const KernelParams& P, int cu) {
+  const int lane = threadIdx.x & 63;
+  int* counter = P.ctrl + kCQueueDecode;
+  int item = 0;
+  if (lane == 0) item = atomicAdd(counter, 1);
+  item = __builtin_amdgcn_readfirstlane(item);
+  while (item < P.n_dc_items) {
+    int next = 0;
+    if (lane == 0) {
+      next = atomicAdd(counter, 1);
+      note_claim(P, 1, item, cu);
+    }
+    decode_wave_item<T, D>(P, item);
+    item = __builtin_amdgcn_readfirstlane(next);
+  }
+}
+
 // ------------------------------------------------------------------ kernels
-// Fused persistent kernel: every workgroup loops, taking a role per CU and claiming items of
-// that kind through one atomic counter per kind; at most `prefill_cap_per_cu` workgroups of a
-// CU hold the prefill role while decode work remains, so every CU keeps streaming decode while
-// its prefill tiles run ([POD], "Virtual CTAs and per-SM balance").  A workgroup whose queue is
-// drained takes the other kind; the kernel ends when both are drained.
+// Fused persistent kernel: every workgroup loops, taking a role for its CU and claiming work
+// of that kind through one atomic counter per kind.  At most `prefill_cap_per_cu` workgroups of
+// a CU hold the prefill role while decode work remains, so every CU keeps streaming decode while
+// its prefill tiles run ([POD], "Virtual CTAs and per-SM balance").  A prefill-role workgroup
+// works on one tile at a time with all four waves; a decode-role workgroup's four waves each
+// stream their own decode items.  A workgroup whose kind is drained takes the other kind; the
+// kernel ends when both are drained.
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 2) void pod_fused_kernel(KernelParams P) {
   __shared__ __attribute__((aligned(16))) char lds[Geo<T, D>::kFusedLds];
@@ -711,33 +740,33 @@ __global__ __launch_bounds__(kThreads, 2) void pod_fused_kernel(KernelParams P) 
         role = 0;
       }
       s_role = role;
-      if (role >= 0) s_item = atomicAdd(P.ctrl + (role == 0 ? kCQueuePrefill : kCQueueDecode), 1);
+      if (role == 0) s_item = atomicAdd(P.ctrl + kCQueuePrefill, 1);
     }
     __syncthreads();
     const int role = s_role;
     int item = s_item;
     __syncthreads();
     if (role < 0) break;
-    const int n_items = role == 0 ? P.n_pf_items : P.n_dc_items;
-    int* counter = P.ctrl + (role == 0 ? kCQueuePrefill : kCQueueDecode);
-    while (item < n_items) {
+    if (role == 1) {
+      decode_wave_stream<T, D>(P, cu);
+      __syncthreads();
+      dc_open = false;
+      continue;
+    }
+    while (item < P.n_pf_items) {
       int next = 0;
       if (tid == 0) {
-        next = atomicAdd(counter, 1);          // claim ahead; consumed after this item
-        note_claim<T, D>(P, role, item, cu);
+        next = atomicAdd(P.ctrl + kCQueuePrefill, 1);     // claim ahead; consumed after this item
+        note_claim(P, 0, item, cu);
       }
-      run_item<T, D>(P, role, item, lds, &s_flag);
+      run_prefill_item<T, D>(P, item, lds, &s_flag);
       if (tid == 0) s_item = next;
       __syncthreads();
       item = s_item;
       __syncthreads();
     }
-    if (role == 0) {
-      pf_open = false;
-      if (tid == 0 && counted) { atomicSub(active, 1); counted = false; }
-    } else {
-      dc_open = false;
-    }
+    pf_open = false;
+    if (tid == 0 && counted) { atomicSub(active, 1); counted = false; }
   }
 }
 
@@ -745,28 +774,75 @@ template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 2) void pod_prefill_kernel(KernelParams P) {
   __shared__ __attribute__((aligned(16))) char lds[Geo<T, D>::kPrefillLds];
   __shared__ int s_flag;
-  if (threadIdx.x == 0) note_claim<T, D>(P, 0, blockIdx.x, cu_slot());
-  run_item<T, D>(P, 0, blockIdx.x, lds, &s_flag);
+  if (threadIdx.x == 0) note_claim(P, 0, blockIdx.x, cu_slot());
+  run_prefill_item<T, D>(P, blockIdx.x, lds, &s_flag);
 }
 
+// Separate decode kernel: wave w of workgroup b takes decode item 4b + w.
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 2) void pod_decode_kernel(KernelParams P) {
-  __shared__ __attribute__((aligned(16))) char lds[Geo<T, D>::kMergeLds];
-  __shared__ int s_flag;
-  if (threadIdx.x == 0) note_claim<T, D>(P, 1, blockIdx.x, cu_slot());
-  run_item<T, D>(P, 1, blockIdx.x, lds, &s_flag);
+  const int item = (int)blockIdx.x * kWaves + wave_index();
+  if (item >= P.n_dc_items) return;
+  if ((threadIdx.x & 63) == 0) note_claim(P, 1, item, cu_slot());
+  decode_wave_item<T, D>(P, item);
 }
 
+// Separate-mode combine: one workgroup per (group, block of 16 columns); the split weights of
+// the block's columns are computed once into LDS, then every (column, 4 dims) is merged.
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void pod_combine_kernel(KernelParams P) {
-  const int g = P.group_begin + (int)blockIdx.x;
+  __shared__ float s_w[16][kMaxCombineSplits];
+  __shared__ float s_inv[16];
+  const int cb = P.combine_col_blocks;
+  const int g = P.group_begin + (int)blockIdx.x / cb;
+  const int blk = (int)blockIdx.x - ((int)blockIdx.x / cb) * cb;
   if (g >= P.group_end) return;
   const bool pf = g < P.n_pf_groups;
   CPTR(int32_t) descs = (CPTR(int32_t))(pf ? P.pdesc : P.ddesc);
   const int nd = pf ? P.n_pdesc : P.n_ddesc;
   const int di = find_desc(descs, nd, kDGroupBegin, g);
   CPTR(int32_t) dsc = descs + (size_t)di * kDescInts;
-  combine_group<T, D>(P, dsc, g - dsc[kDGroupBegin]);
+  const int head = g - dsc[kDGroupBegin];
+  const int ns = dsc[kDNSplit], ncols = dsc[kDNcols], q_row = dsc[kDQRow];
+  const int c0 = blk * 16;
+  if (c0 >= ncols) return;
+  const int nc = min(16, ncols - c0);
+  const size_t base = (size_t)dsc[kDPartBase] + (size_t)head * ns * ncols;
+  const int tid = threadIdx.x;
+  if (ns > kMaxCombineSplits) {                       // rare: merge without the LDS table
+    combine_group<T, D>(P, dsc, head, tid, kThreads);
+    return;
+  }
+  for (int i = tid; i < nc * ns; i += kThreads) {
+    const int c = i / ns, sp = i - c * ns;
+    s_w[c][sp] = P.part_lse[base + (size_t)sp * ncols + c0 + c];
+  }
+  __syncthreads();
+  if (tid < nc) {
+    float M = kNegInf;
+    for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, s_w[tid][sp]);
+    float sum = 0.f;
+    for (int sp = 0; sp < ns; ++sp) {
+      const float wgt = M == kNegInf ? 0.f : exp2_fast(s_w[tid][sp] - M);
+      s_w[tid][sp] = wgt;
+      sum += wgt;
+    }
+    s_inv[tid] = sum > 0.f ? 1.f / sum : 0.f;
+  }
+  __syncthreads();
+  constexpr int kQ = D / 4;
+  const int G = P.group;
+  for (int idx = tid; idx < nc * kQ; idx += kThreads) {
+    const int c = idx / kQ, d4 = idx - c * kQ;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < ns; ++sp) {
+      const float wgt = s_w[c][sp];
+      if (wgt > 0.f) acc += wgt * *(const f32x4*)(P.part_o + (base + (size_t)sp * ncols + c0 + c) * D + 4 * d4);
+    }
+    const int cc = c0 + c, qi = cc / G, hh = cc - qi * G;
+    T* dst = (T*)P.out + ((size_t)(q_row + qi) * P.hq + head * G + hh) * D + 4 * d4;
+    store4<T>(dst, acc * s_inv[c]);
+  }
 }
 
 // Debug gather: element (t, g, d) of one sequence, through the kernels' page addressing.
