@@ -81,6 +81,19 @@ def time_mode(torch, h, b, meta, out, ws, steps, warmup):
     return total_ms / steps, sum(kern) / len(kern), min(kern)
 
 
+def measured_traffic(kernel_name, workload_name):
+    """HBM bytes per launch from the committed counter record (FETCH_SIZE + WRITE_SIZE, each
+    calibrated on a plain copy), or None when absent or taken on different kernel sources."""
+    from hybrid_prefill_decode_paged_amd.profiling import kernel_source_hash
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_name}_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec["traffic_bytes_per_dispatch"]
+
+
 def cpu_baseline(b, budget_s=12.0):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload: whole decode
     sequences (all heads) and blocks of 32 prefill rows (all heads), until about budget_s of
@@ -160,7 +173,18 @@ def main():
     ap.add_argument("--no-compare", action="store_true", help="skip timing the other two modes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy 3 times (counter calibration)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        x = torch.full((1 << 30,), 3, dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print("copied 3 x 1 GiB", flush=True)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(the hybrid batch shards by sequence or KV head with no exchange; see DESIGN.md)",
@@ -207,6 +231,8 @@ def main():
     else:
         achieved, peak, unit = work["flops"] / kern_s / 1e12, peak_mfma / 1e12, "TFLOP/s"
     st = stats[args.mode]
+    kernel_name = "pod_fused_kernel" if args.mode == "fused" else f"{args.mode} kernels"
+    traffic = measured_traffic(kernel_name, spec.name)
     line = {
         "metric": METRIC,
         "value": results[args.mode]["us_per_iter"],
@@ -222,8 +248,8 @@ def main():
         "data": "synthetic (seeded N(0,1)*0.5 values, seeded page permutation)",
         "config": workload_desc(spec),
         "roofline": {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
-                     "frac": round(achieved / peak, 4), "traffic": None,
-                     "kernel": "pod_fused_kernel" if args.mode == "fused" else f"{args.mode} kernels",
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "kernel": kernel_name,
                      "algorithmic_bytes": work["bytes"], "algorithmic_flops": work["flops"],
                      "t_roof_us": round(t_roof_s * 1e6, 2),
                      "roof_fraction_of_step": round(t_roof_s / main_ms * 1e3, 4)},

@@ -55,8 +55,8 @@ pod_attn_status validate_config(const pod_attn_config* c, Config* out, std::stri
   if (c->decode_split_tokens < 0 || (c->decode_split_tokens % 128) != 0) {
     *err = "decode_split_tokens must be 0 or a positive multiple of 128"; return POD_ATTN_ERR_INVALID_ARG;
   }
-  if (c->prefill_split_cap < 0 || c->wgs_per_cu < 0 || c->wgs_per_cu > 8) {
-    *err = "prefill_split_cap must be >= 0 and wgs_per_cu in [0, 8]"; return POD_ATTN_ERR_INVALID_ARG;
+  if (c->prefill_split_cap < 0 || c->prefill_split_cap > kMaxCombineSplits || c->wgs_per_cu < 0 || c->wgs_per_cu > 8) {
+    *err = "prefill_split_cap must be in [0, 128] and wgs_per_cu in [0, 8]"; return POD_ATTN_ERR_INVALID_ARG;
   }
   Config k;
   k.hq = c->num_q_heads; k.hkv = c->num_kv_heads; k.d = c->head_dim; k.page = c->page_size;
@@ -130,7 +130,7 @@ pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus
   int item = 0, group = 0, slot = 0;
   p.prefill_max_splits = 0;
   for (const Tile& tl : tiles) {
-    int ns = std::max(1, std::min(cap, ceil_div(tl.kv_len, 4096)));
+    int ns = std::max(1, std::min(std::min(cap, kMaxCombineSplits), ceil_div(tl.kv_len, 4096)));
     int st = round_up_int(ceil_div(tl.kv_len, ns), kPrefillKvTile);
     ns = ceil_div(tl.kv_len, st);
     std::vector<int32_t> d(kDescInts, 0);
@@ -168,7 +168,7 @@ pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus
   p.decode_max_splits = 0;
   for (int i : order) {
     int ctx = b->decode_ctx_len[i];
-    int ns = ceil_div(ctx, st_target);
+    int ns = std::min(kMaxCombineSplits, ceil_div(ctx, st_target));
     int st = round_up_int(ceil_div(ctx, ns), 128);
     ns = ceil_div(ctx, st);
     std::vector<int32_t> d(kDescInts, 0);

@@ -14,7 +14,8 @@ constexpr int kMaxGroup = 16;        // decode columns = group size, one 16-wide
 constexpr int kPrefillKvTile = 64;   // keys per prefill inner iteration (4 pages)
 constexpr int kDecodeStep = 32;      // keys per decode wave step (2 pages)
 constexpr int kCuSlots = 1024;       // hashed (XCC, SE, CU) slots for per-CU scheduler state
-constexpr int kMaxCombineSplits = 256;  // splits merged through the LDS weight table
+constexpr int kMaxCombineSplits = 128;  // max KV splits of one group (LDS weight table rows)
+constexpr int kCombineLdsPerWave = 16 * kMaxCombineSplits * 4;   // [16 columns][splits] floats
 
 // A descriptor covers one prefill query tile or one decode sequence; it expands to
 // Hkv * n_split work items, split-major: item = split * Hkv + kv_head, so that items taken

@@ -68,7 +68,8 @@ template <typename T, int D> struct Geo {
   static constexpr int kStageChunks = 2 * kTp * kCps;   // K + V chunks of one prefill tile
   static constexpr int kStageR = kStageChunks / kThreads;
   static constexpr int kPrefillLds = 2 * 2 * kTp * kSlab;              // 2 buffers x (K, V)
-  static constexpr int kFusedLds = kPrefillLds;                        // decode uses no LDS
+  static constexpr int kCombineLds = kWaves * kCombineLdsPerWave;    // in-kernel split combine tables
+  static constexpr int kFusedLds = kPrefillLds > kCombineLds ? kPrefillLds : kCombineLds;
   static_assert(kStageChunks % kThreads == 0, "tile must split evenly over the workgroup");
   static_assert(kTp % 2 == 0, "bf16 PV pairs pages");
 };
@@ -197,27 +198,39 @@ __device__ __forceinline__ int find_desc(CPTR(int32_t) descs, int n, int field, 
 __device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // ------------------------------------------------------------------ online-softmax update
-// Per query column (lane l holds column l%16): x = masked scaled scores of this block (log2
-// domain, -inf where masked), NV values per lane.  Updates m (column max, identical in the 4
-// lane groups), l (this lane's partial sum) and returns the rescale factor for the output.
+// Per query column (lane l holds column l%16): x = raw scores of this block, -inf where masked,
+// NV values per lane.  The running max m is kept in the log2 domain (scores times sl2 =
+// scale*log2 e, sl2 > 0, so the max commutes with the scaling); updates m (identical in the 4
+// lane groups) and l (this lane's partial sum), turns x into probabilities 2^(x*sl2 - m) and
+// returns the rescale factor 2^(m_old - m_new) for the running output.
 template <int NV>
-__device__ __forceinline__ float softmax_update(float (&x)[NV], float& m, float& l) {
+__device__ __forceinline__ float softmax_update(float (&x)[NV], float sl2, float& m, float& l) {
   float mloc = x[0];
 #pragma unroll
   for (int i = 1; i < NV; ++i) mloc = fmaxf(mloc, x[i]);
-  mloc = max_over_groups(mloc);
+  mloc = max_over_groups(mloc) * sl2;
   const float m_new = fmaxf(m, mloc);
   const float m_use = m_new == kNegInf ? 0.f : m_new;
   const float alpha = exp2_fast(m - m_use);
   float sum = 0.f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    x[i] = exp2_fast(x[i] - m_use);
+    x[i] = exp2_fast(__builtin_fmaf(x[i], sl2, -m_use));
     sum += x[i];
   }
   l = l * alpha + sum;
   m = m_new;
   return alpha;
+}
+
+// Rescale a running output only when some column's maximum moved (alpha == 1 exactly
+// otherwise, so skipping the multiply changes nothing).
+template <int N>
+__device__ __forceinline__ void rescale(f32x4 (&o)[N], float alpha) {
+  if (__any(alpha != 1.f)) {
+#pragma unroll
+    for (int b = 0; b < N; ++b) o[b] *= alpha;
+  }
 }
 
 // ------------------------------------------------------------------ split partials
@@ -260,32 +273,60 @@ __device__ __forceinline__ int arrive_last(int32_t* ticket, int ns) {
 
 // ------------------------------------------------------------------ log-sum-exp combine
 // out = sum_s w_s o_s / sum_s w_s with w_s = 2^(lse_s - max lse); empty splits weigh zero.
-// In-kernel form (the last-arriving split merges its group): work is spread over `nthreads`
-// threads starting at `tid`, partials are read with device-scope loads.
+// In-kernel form, run by one wave for up to 16 columns of a group: the splits' lse values go to
+// an LDS table `sw` ([16][ns] floats) with all loads in flight at once, the weights are formed
+// once per column, then every (column, 4 dims) output sums its splits with 8 partial loads in
+// flight.  Partials are read with device-scope loads.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <typename T, int D>
-__device__ void combine_group(const KernelParams& P, CPTR(int32_t) dsc, int head, int tid, int nthreads) {
+__device__ void combine_block_wave(const KernelParams& P, CPTR(int32_t) dsc, int head, int c0, float* sw) {
+  const int lane = threadIdx.x & 63;
   const int ns = dsc[kDNSplit], ncols = dsc[kDNcols], q_row = dsc[kDQRow];
+  const int nc = min(16, ncols - c0);
   const size_t base = (size_t)dsc[kDPartBase] + (size_t)head * ns * ncols;
   const int G = P.group;
   constexpr int kQ = D / 4;
-  for (int idx = tid; idx < ncols * kQ; idx += nthreads) {
-    const int c = idx / kQ, d4 = idx - c * kQ;
+  for (int i = lane; i < nc * ns; i += 64) {
+    const int c = i / ns, sp = i - c * ns;
+    sw[c * ns + sp] = load_part1_coherent(P.part_lse + base + (size_t)sp * ncols + c0 + c);
+  }
+  wave_lds_sync();
+  if (lane < nc) {
     float M = kNegInf;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, load_part1_coherent(P.part_lse + base + (size_t)s * ncols + c));
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float wsum = 0.f;
-    if (M != kNegInf) {
-      for (int s = 0; s < ns; ++s) {
-        const size_t slot = base + (size_t)s * ncols + c;
-        const float wgt = exp2_fast(load_part1_coherent(P.part_lse + slot) - M);
-        if (wgt > 0.f) acc += wgt * load_part4_coherent(P.part_o + slot * D + 4 * d4);
-        wsum += wgt;
-      }
+    for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, sw[lane * ns + sp]);
+    float sum = 0.f;
+    for (int sp = 0; sp < ns; ++sp) {
+      const float wgt = M == kNegInf ? 0.f : exp2_fast(sw[lane * ns + sp] - M);
+      sw[lane * ns + sp] = wgt;
+      sum += wgt;
     }
-    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-    const int qi = c / G, hh = c - qi * G;
+    const float inv = sum > 0.f ? 1.f / sum : 0.f;
+    for (int sp = 0; sp < ns; ++sp) sw[lane * ns + sp] *= inv;
+  }
+  wave_lds_sync();
+  const size_t sstride = (size_t)ncols * D;             // floats between consecutive splits
+  for (int pidx = lane; pidx < nc * kQ; pidx += 64) {
+    const int c = pidx / kQ, d4 = pidx - c * kQ;
+    const float* src = P.part_o + (base + c0 + c) * D + 4 * d4;
+    const float* wc = sw + c * ns;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    int sp = 0;
+    for (; sp + 8 <= ns; sp += 8) {
+      f32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = load_part4_coherent(src + (size_t)(sp + u) * sstride);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += wc[sp + u] * v[u];
+    }
+    for (; sp < ns; ++sp) acc += wc[sp] * load_part4_coherent(src + (size_t)sp * sstride);
+    const int cc = c0 + c, qi = cc / G, hh = cc - qi * G;
     T* dst = (T*)P.out + ((size_t)(q_row + qi) * P.hq + head * G + hh) * D + 4 * d4;
-    store4<T>(dst, acc * inv);
+    store4<T>(dst, acc);
   }
 }
 
@@ -295,7 +336,7 @@ __device__ void combine_group(const KernelParams& P, CPTR(int32_t) dsc, int head
 // the next step's K/V loads in flight while the current step is computed.  Waves run their
 // decode items independently (no workgroup barrier, no LDS).
 template <typename T, int D>
-__device__ void decode_wave_item(const KernelParams& P, int item) {
+__device__ void decode_wave_item(const KernelParams& P, int item, float* sw) {
   using Gm = Geo<T, D>;
   typedef typename VOp<T>::type VT;
   CPTR(int32_t) descs = (CPTR(int32_t))P.ddesc;
@@ -342,8 +383,8 @@ __device__ void decode_wave_item(const KernelParams& P, int item) {
     for (int p = 0; p < 2; ++p) {
       const int pi = (tok0 >> 4) + p;
       int l = min(kPage, kv_end - pi * kPage);
-      const int pg = page_or_empty(btr, pi, l, P.num_pages, P.ctrl + kCStatus);
-      lim[p] = l;
+      const int pg = __builtin_amdgcn_readfirstlane(page_or_empty(btr, pi, l, P.num_pages, P.ctrl + kCStatus));
+      lim[p] = __builtin_amdgcn_readfirstlane(l);
       const char* kp = slab_ptr<T, D>(P.k, pg, P.hkv, head);
       const char* vp = slab_ptr<T, D>(P.v, pg, P.hkv, head);
 #pragma unroll
@@ -363,12 +404,10 @@ __device__ void decode_wave_item(const KernelParams& P, int item) {
     float x[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      x[i] = (4 * q + i < lim[0]) ? s0[i] * sl2 : kNegInf;
-      x[4 + i] = (4 * q + i < lim[1]) ? s1[i] * sl2 : kNegInf;
+      x[i] = (4 * q + i < lim[0]) ? s0[i] : kNegInf;
+      x[4 + i] = (4 * q + i < lim[1]) ? s1[i] : kNegInf;
     }
-    const float alpha = softmax_update<8>(x, m_run, l_run);
-#pragma unroll
-    for (int b = 0; b < Gm::kDb; ++b) o[b] *= alpha;
+    rescale(o, softmax_update<8>(x, sl2, m_run, l_run));
     if (lim[0] < kPage || lim[1] < kPage) {
 #pragma unroll
       for (int b = 0; b < Gm::kDb; ++b) {
@@ -428,7 +467,7 @@ __device__ void decode_wave_item(const KernelParams& P, int item) {
   // Last arriver combines ([POD], "Virtual CTAs and per-SM balance": exact synchronisation
   // where partial results meet, and no wave ever waits for another).
   if (ns > 1 && P.inline_combine && arrive_last(P.tickets + dsc[kDGroupBegin] + head, ns))
-    combine_group<T, D>(P, dsc, head, lane, 64);
+    combine_block_wave<T, D>(P, dsc, head, 0, sw);
 }
 
 // ------------------------------------------------------------------ prefill tile item
@@ -490,8 +529,8 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
     for (int p = 0; p < Gm::kTp; ++p) {
       const int pi = (tb >> 4) + p;
       int l = min(kPage, kv_end - pi * kPage);
-      pg[p] = page_or_empty(btr, pi, l, P.num_pages, P.ctrl + kCStatus);
-      lim[p] = l;
+      pg[p] = __builtin_amdgcn_readfirstlane(page_or_empty(btr, pi, l, P.num_pages, P.ctrl + kCStatus));
+      lim[p] = __builtin_amdgcn_readfirstlane(l);
     }
   };
   auto kbuf = [&](int b) { return lds + b * (2 * Gm::kTp * Gm::kSlab); };
@@ -555,21 +594,18 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
 #pragma unroll
         for (int mb = 0; mb < Gm::kTp; ++mb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) x[4 * mb + i] = S[nb][mb][i] * sl2;
+          for (int i = 0; i < 4; ++i) x[4 * mb + i] = S[nb][mb][i];
       } else {
+        const int rel = pos[nb] - tb - 4 * q;      // key slot 4q+i of page mb visible iff 16mb+i <= rel
 #pragma unroll
         for (int mb = 0; mb < Gm::kTp; ++mb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int slot = 4 * q + i;
-            const int t = tb + mb * kPage + slot;
-            const bool ok = (slot < lim[mb]) & (t <= pos[nb]);   // select, never multiply
-            x[4 * mb + i] = ok ? S[nb][mb][i] * sl2 : kNegInf;
+            const bool ok = (4 * q + i < lim[mb]) & (mb * kPage + i <= rel);   // select, never multiply
+            x[4 * mb + i] = ok ? S[nb][mb][i] : kNegInf;
           }
       }
-      const float alpha = softmax_update<4 * Gm::kTp>(x, m_run[nb], l_run[nb]);
-#pragma unroll
-      for (int b2 = 0; b2 < Gm::kDb; ++b2) o[nb][b2] *= alpha;
+      rescale(o[nb], softmax_update<4 * Gm::kTp>(x, sl2, m_run[nb], l_run[nb]));
 #pragma unroll
       for (int mb = 0; mb < Gm::kTp; ++mb)
         S[nb][mb] = f32x4{x[4 * mb], x[4 * mb + 1], x[4 * mb + 2], x[4 * mb + 3]};
@@ -671,7 +707,11 @@ __device__ void run_prefill_item(const KernelParams& P, int item, char* lds, int
     __syncthreads();
     if (threadIdx.x == 0) *s_flag = atomicAdd(P.tickets + dsc[kDGroupBegin] + head, 1) == ns - 1;
     __syncthreads();
-    if (*s_flag) combine_group<T, D>(P, dsc, head, threadIdx.x, kThreads);
+    if (*s_flag) {
+      const int w = wave_index();
+      float* sw = (float*)(lds + w * kCombineLdsPerWave);
+      for (int c0 = 16 * w; c0 < dsc[kDNcols]; c0 += 16 * kWaves) combine_block_wave<T, D>(P, dsc, head, c0, sw);
+    }
   }
   __syncthreads();   // LDS and the flag are reused by the next item
 }
@@ -693,7 +733,7 @@ __device__ __forceinline__ void note_claim(const KernelParams& P, int kind, int 
 // Decode stream of one wave: claim items one at a time from the decode counter (the next
 // claim is issued before the current item is processed) until the counter passes the end.
 template <typename T, int D>
-__device__ void decode_wave_stream(const KernelParams& P, int cu) {
+__device__ void decode_wave_stream(const KernelParams& P, int cu, float* sw) {
   const int lane = threadIdx.x & 63;
   int* counter = P.ctrl + kCQueueDecode;
   int item = 0;
@@ -705,7 +745,7 @@ __device__ void decode_wave_stream(const KernelParams& P, int cu) {
       next = atomicAdd(counter, 1);
       note_claim(P, 1, item, cu);
     }
-    decode_wave_item<T, D>(P, item);
+    decode_wave_item<T, D>(P, item, sw);
     item = __builtin_amdgcn_readfirstlane(next);
   }
 }
@@ -748,7 +788,7 @@ __global__ __launch_bounds__(kThreads, 2) void pod_fused_kernel(KernelParams P) 
     __syncthreads();
     if (role < 0) break;
     if (role == 1) {
-      decode_wave_stream<T, D>(P, cu);
+      decode_wave_stream<T, D>(P, cu, (float*)(lds + wave_index() * kCombineLdsPerWave));
       __syncthreads();
       dc_open = false;
       continue;
@@ -784,7 +824,7 @@ __global__ __launch_bounds__(kThreads, 2) void pod_decode_kernel(KernelParams P)
   const int item = (int)blockIdx.x * kWaves + wave_index();
   if (item >= P.n_dc_items) return;
   if ((threadIdx.x & 63) == 0) note_claim(P, 1, item, cu_slot());
-  decode_wave_item<T, D>(P, item);
+  decode_wave_item<T, D>(P, item, nullptr);   // no in-kernel combine here: the combine kernel merges
 }
 
 // Separate-mode combine: one workgroup per (group, block of 16 columns); the split weights of
@@ -809,10 +849,6 @@ __global__ __launch_bounds__(kThreads) void pod_combine_kernel(KernelParams P) {
   const int nc = min(16, ncols - c0);
   const size_t base = (size_t)dsc[kDPartBase] + (size_t)head * ns * ncols;
   const int tid = threadIdx.x;
-  if (ns > kMaxCombineSplits) {                       // rare: merge without the LDS table
-    combine_group<T, D>(P, dsc, head, tid, kThreads);
-    return;
-  }
   for (int i = tid; i < nc * ns; i += kThreads) {
     const int c = i / ns, sp = i - c * ns;
     s_w[c][sp] = P.part_lse[base + (size_t)sp * ncols + c0 + c];

@@ -1,0 +1,93 @@
+"""Turn rocprofv3 CSV output into the short text summaries kept under profiles/.
+
+    python -m hybrid_prefill_decode_paged_amd.profiling stats  <kernel_stats.csv> <out.md> <command...>
+    python -m hybrid_prefill_decode_paged_amd.profiling traffic <copy_fetch_dir> <copy_write_dir> \
+        <fetch_dir> <write_dir> <kernel-substring> <out.json> <command...>
+
+Traffic: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the kernel, each scaled by the ratio of
+the true byte count to what the same counter reads for a plain 1 GiB device copy
+(``python bench.py --calibrate-copy``: 1 GiB read + 1 GiB written per dispatch).  The record
+carries the SHA-256 of the kernel sources so that bench.py reports it only while the kernels
+are unchanged.
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ("csrc/pod_kernels.hip", "csrc/pod_internal.h", "csrc/plan.cpp")
+COPY_BYTES = 1 << 30
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(PKG, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _counter_csv(d: str) -> str:
+    files = glob.glob(os.path.join(d, "*counter_collection.csv"))
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {d}")
+    return files[0]
+
+
+def per_dispatch(d: str, kernel_substr: str, counter: str):
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(_counter_csv(d)))
+            if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter]
+    if not vals:
+        raise ValueError(f"{counter} for '{kernel_substr}' not found in {d}")
+    return statistics.mean(vals), len(vals)
+
+
+def traffic_record(copy_fetch, copy_write, fetch, write, kernel_substr, command):
+    cf, _ = per_dispatch(copy_fetch, "copyBuffer", "FETCH_SIZE")
+    cw, _ = per_dispatch(copy_write, "copyBuffer", "WRITE_SIZE")
+    f, nf = per_dispatch(fetch, kernel_substr, "FETCH_SIZE")
+    w, nw = per_dispatch(write, kernel_substr, "WRITE_SIZE")
+    fs, ws = (COPY_BYTES / 1024) / cf, (COPY_BYTES / 1024) / cw
+    return {
+        "kernel": kernel_substr,
+        "fetch_kib_per_dispatch": round(f, 1), "write_kib_per_dispatch": round(w, 1),
+        "dispatches": [nf, nw],
+        "copy_fetch_kib": round(cf, 1), "copy_write_kib": round(cw, 1),
+        "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+        "traffic_bytes_per_dispatch": int(round((f * fs + w * ws) * 1024)),
+        "kernel_source_sha256": kernel_source_hash(),
+        "command": command,
+    }
+
+
+def stats_summary(path: str, command: str) -> str:
+    rows = list(csv.DictReader(open(path)))
+    out = ["# rocprofv3 kernel statistics", "", f"Command: `{command}`", "",
+           "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"]
+        short = name.split("(")[0][:90]
+        out.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} |")
+    return "\n".join(out) + "\n"
+
+
+def main(argv):
+    if argv[0] == "stats":
+        open(argv[2], "w").write(stats_summary(argv[1], " ".join(argv[3:])))
+    elif argv[0] == "traffic":
+        rec = traffic_record(*argv[1:6], " ".join(argv[7:]))
+        json.dump(rec, open(argv[6], "w"), indent=1)
+        print(json.dumps(rec))
+    else:
+        raise SystemExit(__doc__)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])

@@ -48,6 +48,7 @@ def _check_coverage(spec, items, G):
         groups.setdefault(key, []).append((split, a, z, n_q, q_pos, grp, slot, seq))
     for (kind, q_row, g), parts in groups.items():
         parts.sort()
+        assert len(parts) <= 128, "at most 128 KV splits per group"
         n_q, q_pos, seq = parts[0][3], parts[0][4], parts[0][7]
         assert [p[0] for p in parts] == list(range(len(parts)))
         assert parts[0][1] == 0
@@ -92,7 +93,7 @@ def test_plan_covers_every_row_head_key_once(idx):
 
 
 @pytest.mark.parametrize("G,D,split,cap", [(1, 128, 0, 0), (2, 64, 128, 1), (3, 128, 256, 3),
-                                           (8, 64, 512, 0), (16, 128, 0, 2)])
+                                           (8, 64, 512, 0), (16, 128, 0, 2), (1, 64, 128, 128)])
 def test_plan_ragged_batches(G, D, split, cap):
     rng = np.random.default_rng(G * 100 + D)
     pre = [(int(L), int(L + o)) for L, o in zip(rng.integers(1, 300, 5), rng.integers(0, 3000, 5))]
