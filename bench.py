@@ -258,7 +258,7 @@ def main():
                               if "separate" in results and "fused" in results else None),
         "plan": {k: st[k] for k in ("num_prefill_items", "num_decode_items", "num_combine_groups",
                                     "decode_split_tokens", "prefill_max_splits", "grid_wgs", "wgs_per_cu",
-                                    "num_cus", "vgprs_per_lane", "lds_bytes_per_wg", "mode_used",
+                                    "num_cus", "vgprs_per_lane", "lds_bytes_per_wg", "mode_used", "prefill_wg_budget",
                                     "fallback_reason")},
     }
     if not args.no_cpu_baseline:

@@ -52,7 +52,7 @@ class Stats(C.Structure):
         "num_combine_groups", "prefill_tile_cols", "prefill_tile_queries", "prefill_kv_tile",
         "prefill_max_splits", "decode_split_tokens", "decode_max_splits", "grid_wgs", "wgs_per_cu",
         "num_cus", "lds_bytes_per_wg", "vgprs_per_lane")] + [
-        ("workspace_bytes", C.c_size_t), ("host_plan_us", C.c_double)]
+        ("workspace_bytes", C.c_size_t), ("host_plan_us", C.c_double), ("prefill_wg_budget", C.c_int)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

@@ -140,6 +140,8 @@ pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus
     item += c.hkv * ns;
     if (ns > 1) { group += c.hkv; slot += c.hkv * ns * tl.n_q * G; }
     p.prefill_max_splits = std::max(p.prefill_max_splits, ns);
+    p.prefill_flops += 4.0 * c.d * G * c.hkv *
+                       ((double)tl.n_q * tl.q_pos + (double)tl.n_q * (tl.n_q + 1) / 2.0);
     p.pdesc.insert(p.pdesc.end(), d.begin(), d.end());
   }
   p.n_pdesc = (int)tiles.size();
@@ -178,6 +180,7 @@ pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus
     ditem += c.hkv * ns;
     if (ns > 1) { group += c.hkv; slot += c.hkv * ns * G; }
     p.decode_max_splits = std::max(p.decode_max_splits, ns);
+    p.decode_bytes += 2.0 * ctx * c.hkv * c.d * c.elem_bytes();
     p.ddesc.insert(p.ddesc.end(), d.begin(), d.end());
   }
   p.n_ddesc = b->num_decode;

@@ -25,6 +25,8 @@ struct Plan {
   int tile_queries = 0, tile_cols = 0;
   int prefill_max_splits = 0, decode_split_tokens = 0, decode_max_splits = 0;
   int total_q = 0, prefill_rows = 0;
+  double prefill_flops = 0.0;   // 4*D per visible (query head, key) pair of the prefill share
+  double decode_bytes = 0.0;    // K+V bytes of the decode share
   WorkspaceMap map{};
 };
 

@@ -40,6 +40,7 @@ enum CtrlWord {
   kCQueuePrefill = 0,
   kCQueueDecode = 64,
   kCStatus = 128,
+  kCActivePrefillAll = 192,                 // prefill-role workgroups now active, device-wide
   kCActivePrefill = 256,                    // [kCuSlots] prefill-role WGs now on each CU
   kCClaimsPrefillCu = 256 + kCuSlots,       // [kCuSlots] prefill items claimed per CU
   kCClaimsDecodeCu = 256 + 2 * kCuSlots,    // [kCuSlots] decode items claimed per CU
@@ -67,9 +68,11 @@ struct KernelParams {
   int hq, hkv, group, bt_stride, num_pages;
   float scale_log2;          // softmax scale * log2(e)
   int prefill_cap_per_cu;    // fused: prefill-role workgroups allowed per CU while decode remains
+  int prefill_wg_budget;     // fused: prefill-role workgroups allowed device-wide while decode remains
   int inline_combine;        // 1: last-arriving split combines in-kernel (fused)
   int group_begin, group_end;// combine kernel range
   int combine_col_blocks;     // combine kernel: workgroups per group (16 columns each)
+  int decode_block_claim;     // fused: a decode-role workgroup claims 4 consecutive items at once
 };
 
 // Workspace map (byte offsets), computed by the planner.

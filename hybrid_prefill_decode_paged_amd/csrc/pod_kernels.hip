@@ -736,28 +736,28 @@ template <typename T, int D>
 __device__ void decode_wave_stream(const KernelParams& P, int cu, float* sw) {
   const int lane = threadIdx.x & 63;
   int* counter = P.ctrl + kCQueueDecode;
-  int item = 0;
-  if (lane == 0) item = atomicAdd(counter, 1);
-  item = __builtin_amdgcn_readfirstlane(item);
-  while (item < P.n_dc_items) {
-    int next = 0;
-    if (lane == 0) {
-      next = atomicAdd(counter, 1);
-      note_claim(P, 1, item, cu);
-    }
+  for (;;) {
+    // Claim after the previous item is done: items run for tens of microseconds, so claiming
+    // ahead would reserve work that idle waves could otherwise take at the end.
+    int item = 0;
+    if (lane == 0) item = atomicAdd(counter, 1);
+    item = __builtin_amdgcn_readfirstlane(item);
+    if (item >= P.n_dc_items) break;
+    if (lane == 0) note_claim(P, 1, item, cu);
     decode_wave_item<T, D>(P, item, sw);
-    item = __builtin_amdgcn_readfirstlane(next);
   }
 }
 
 // ------------------------------------------------------------------ kernels
-// Fused persistent kernel: every workgroup loops, taking a role for its CU and claiming work
-// of that kind through one atomic counter per kind.  At most `prefill_cap_per_cu` workgroups of
-// a CU hold the prefill role while decode work remains, so every CU keeps streaming decode while
-// its prefill tiles run ([POD], "Virtual CTAs and per-SM balance").  A prefill-role workgroup
-// works on one tile at a time with all four waves; a decode-role workgroup's four waves each
-// stream their own decode items.  A workgroup whose kind is drained takes the other kind; the
-// kernel ends when both are drained.
+// Fused persistent kernel: every workgroup loops, taking a role and claiming work of that kind
+// through one atomic counter per kind.  While decode work remains, at most `prefill_wg_budget`
+// workgroups device-wide and `prefill_cap_per_cu` per CU hold the prefill role: the budget is
+// sized on the host so that the prefill share finishes about when the HBM-bound decode stream
+// does, and the rest of the machine keeps enough decode loads in flight to fill HBM ([POD],
+// "Virtual CTAs and per-SM balance": the scheduler places complementary work per SM).  A
+// prefill-role workgroup works on one tile at a time with all four waves; a decode-role
+// workgroup's four waves stream four adjacent decode items.  A workgroup whose kind is drained
+// takes the other kind; the kernel ends when both are drained.
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 2) void pod_fused_kernel(KernelParams P) {
   __shared__ __attribute__((aligned(16))) char lds[Geo<T, D>::kFusedLds];
@@ -765,15 +765,23 @@ __global__ __launch_bounds__(kThreads, 2) void pod_fused_kernel(KernelParams P) 
   const int tid = threadIdx.x;
   const int cu = cu_slot();
   int* active = P.ctrl + kCActivePrefill + cu;
+  int* active_all = P.ctrl + kCActivePrefillAll;
   bool pf_open = P.n_pf_items > 0, dc_open = P.n_dc_items > 0;
-  bool counted = false;                       // thread 0: holds a prefill slot of its CU
+  bool counted = false;                       // thread 0: holds a prefill slot
   for (;;) {
     if (tid == 0) {
       int role = -1;
       if (pf_open && dc_open) {
         const int a = atomicAdd(active, 1);
-        if (a < P.prefill_cap_per_cu) { role = 0; counted = true; }
-        else { atomicSub(active, 1); role = 1; }
+        const int g = atomicAdd(active_all, 1);
+        if (a < P.prefill_cap_per_cu && g < P.prefill_wg_budget) {
+          role = 0;
+          counted = true;
+        } else {
+          atomicSub(active, 1);
+          atomicSub(active_all, 1);
+          role = 1;
+        }
       } else if (dc_open) {
         role = 1;
       } else if (pf_open) {
@@ -788,25 +796,43 @@ __global__ __launch_bounds__(kThreads, 2) void pod_fused_kernel(KernelParams P) 
     __syncthreads();
     if (role < 0) break;
     if (role == 1) {
-      decode_wave_stream<T, D>(P, cu, (float*)(lds + wave_index() * kCombineLdsPerWave));
-      __syncthreads();
+      if (P.decode_block_claim) {
+        // The workgroup claims 4 consecutive items (adjacent KV heads of one key range) and each
+        // wave streams one of them; the next block is claimed once the current one is done.
+        float* sw = (float*)(lds + wave_index() * kCombineLdsPerWave);
+        for (;;) {
+          if (tid == 0) s_item = atomicAdd(P.ctrl + kCQueueDecode, kWaves);
+          __syncthreads();
+          const int base = s_item;
+          __syncthreads();
+          if (base >= P.n_dc_items) break;
+          const int item = base + wave_index();
+          if (item < P.n_dc_items) {
+            if ((tid & 63) == 0) note_claim(P, 1, item, cu);
+            decode_wave_item<T, D>(P, item, sw);
+          }
+        }
+      } else {
+        decode_wave_stream<T, D>(P, cu, (float*)(lds + wave_index() * kCombineLdsPerWave));
+        __syncthreads();
+      }
       dc_open = false;
       continue;
     }
     while (item < P.n_pf_items) {
-      int next = 0;
-      if (tid == 0) {
-        next = atomicAdd(P.ctrl + kCQueuePrefill, 1);     // claim ahead; consumed after this item
-        note_claim(P, 0, item, cu);
-      }
-      run_prefill_item<T, D>(P, item, lds, &s_flag);
-      if (tid == 0) s_item = next;
+      if (tid == 0) note_claim(P, 0, item, cu);
+      run_prefill_item<T, D>(P, item, lds, &s_flag);   // ends with a barrier
+      if (tid == 0) s_item = atomicAdd(P.ctrl + kCQueuePrefill, 1);   // claim once idle
       __syncthreads();
       item = s_item;
       __syncthreads();
     }
     pf_open = false;
-    if (tid == 0 && counted) { atomicSub(active, 1); counted = false; }
+    if (tid == 0 && counted) {
+      atomicSub(active, 1);
+      atomicSub(active_all, 1);
+      counted = false;
+    }
   }
 }
 

@@ -143,6 +143,7 @@ typedef struct pod_attn_stats {
   int vgprs_per_lane;           /* registers of the fused kernel per lane (arch + acc)        */
   size_t workspace_bytes;       /* workspace needed by this batch                             */
   double host_plan_us;          /* host planning time of the last run                         */
+  int prefill_wg_budget;        /* FUSED: prefill-role workgroups allowed while decode remains */
 } pod_attn_stats;
 
 /* Create a handle for one attention configuration on the current HIP device.  Validates the
