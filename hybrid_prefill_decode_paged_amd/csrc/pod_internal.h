@@ -14,6 +14,7 @@ constexpr int kMaxGroup = 16;        // decode columns = group size, one 16-wide
 constexpr int kPrefillKvTile = 64;   // keys per prefill inner iteration (4 pages)
 constexpr int kDecodeStep = 32;      // keys per decode wave step (2 pages)
 constexpr int kCuSlots = 1024;       // hashed (XCC, SE, CU) slots for per-CU scheduler state
+constexpr int kXcds = 8;             // accelerator complex dies (one L2 each)
 constexpr int kMaxCombineSplits = 128;  // max KV splits of one group (LDS weight table rows)
 constexpr int kCombineLdsPerWave = 16 * kMaxCombineSplits * 4;   // [16 columns][splits] floats
 
@@ -44,7 +45,8 @@ enum CtrlWord {
   kCActivePrefill = 256,                    // [kCuSlots] prefill-role WGs now on each CU
   kCClaimsPrefillCu = 256 + kCuSlots,       // [kCuSlots] prefill items claimed per CU
   kCClaimsDecodeCu = 256 + 2 * kCuSlots,    // [kCuSlots] decode items claimed per CU
-  kCtrlInts = 256 + 3 * kCuSlots
+  kCQueuePrefillXcd = 256 + 3 * kCuSlots,   // [kXcds] prefill queues, one 128-byte line each
+  kCtrlInts = 256 + 3 * kCuSlots + kXcds * 32
 };
 
 enum StatusBits { kStatusBadPage = 1 };

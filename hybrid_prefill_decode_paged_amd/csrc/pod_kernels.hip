@@ -109,15 +109,21 @@ __device__ __forceinline__ u32x4 ld16(const char* p) { return *(const u32x4*)p; 
 __device__ __forceinline__ u32x2 ld8(const char* p) { return *(const u32x2*)p; }
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float max_over_groups(float v) {   // over lanes l, l^16, l^32, l^48
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+// Reductions over lanes l, l^16, l^32, l^48 with the gfx950 lane-swap instructions (VALU, no
+// LDS round trip): v_permlane16_swap applied to (v, v) hands every lane the values of lanes
+// l&~16 and l|16, i.e. its own and its partner's, in the same order on both partners, so the
+// results are bit-identical across the four lanes.
+__device__ __forceinline__ float max_over_groups(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float sum_over_groups(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   f32x2 v = {a, b};
@@ -212,12 +218,16 @@ __device__ __forceinline__ float softmax_update(float (&x)[NV], float sl2, float
   const float m_new = fmaxf(m, mloc);
   const float m_use = m_new == kNegInf ? 0.f : m_new;
   const float alpha = exp2_fast(m - m_use);
-  float sum = 0.f;
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    x[i] = exp2_fast(__builtin_fmaf(x[i], sl2, -m_use));
-    sum += x[i];
-  }
+  for (int i = 0; i < NV; ++i) x[i] = exp2_fast(__builtin_fmaf(x[i], sl2, -m_use));
+  float part[NV];                                // pairwise sum: short dependency chain
+#pragma unroll
+  for (int i = 0; i < NV; ++i) part[i] = x[i];
+#pragma unroll
+  for (int w = NV / 2; w >= 1; w /= 2)
+#pragma unroll
+    for (int i = 0; i < w; ++i) part[i] = part[i] + part[i + w];
+  const float sum = part[0];
   l = l * alpha + sum;
   m = m_new;
   return alpha;
@@ -730,6 +740,20 @@ __device__ __forceinline__ void note_claim(const KernelParams& P, int kind, int 
   }
 }
 
+// Prefill claim for a workgroup on XCC `xcc`: queue x holds items x, x+8, x+16, ... (the
+// order in which the hardware spreads a plain grid over the 8 dies), so the tiles that share a
+// KV head's keys run on one die and reuse its L2; a workgroup whose queue is drained takes
+// work from the other dies' queues.  Returns n_pf_items when every queue is drained.
+__device__ __forceinline__ int claim_prefill(const KernelParams& P, int xcc) {
+  for (int k = 0; k < kXcds; ++k) {
+    const int x = (xcc + k) & (kXcds - 1);
+    const int c = atomicAdd(P.ctrl + kCQueuePrefillXcd + 32 * x, 1);
+    const long item = (long)c * kXcds + x;
+    if (item < P.n_pf_items) return (int)item;
+  }
+  return P.n_pf_items;
+}
+
 // Decode stream of one wave: claim items one at a time from the decode counter (the next
 // claim is issued before the current item is processed) until the counter passes the end.
 template <typename T, int D>
@@ -764,6 +788,7 @@ __global__ __launch_bounds__(kThreads, 2) void pod_fused_kernel(KernelParams P) 
   __shared__ int s_role, s_item, s_flag;
   const int tid = threadIdx.x;
   const int cu = cu_slot();
+  const int xcc = cu >> 7;
   int* active = P.ctrl + kCActivePrefill + cu;
   int* active_all = P.ctrl + kCActivePrefillAll;
   bool pf_open = P.n_pf_items > 0, dc_open = P.n_dc_items > 0;
@@ -788,7 +813,7 @@ __global__ __launch_bounds__(kThreads, 2) void pod_fused_kernel(KernelParams P) 
         role = 0;
       }
       s_role = role;
-      if (role == 0) s_item = atomicAdd(P.ctrl + kCQueuePrefill, 1);
+      if (role == 0) s_item = claim_prefill(P, xcc);
     }
     __syncthreads();
     const int role = s_role;
@@ -822,7 +847,7 @@ __global__ __launch_bounds__(kThreads, 2) void pod_fused_kernel(KernelParams P) 
     while (item < P.n_pf_items) {
       if (tid == 0) note_claim(P, 0, item, cu);
       run_prefill_item<T, D>(P, item, lds, &s_flag);   // ends with a barrier
-      if (tid == 0) s_item = atomicAdd(P.ctrl + kCQueuePrefill, 1);   // claim once idle
+      if (tid == 0) s_item = claim_prefill(P, xcc);   // claim once idle
       __syncthreads();
       item = s_item;
       __syncthreads();
