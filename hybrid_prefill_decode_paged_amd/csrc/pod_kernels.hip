@@ -698,6 +698,293 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
   }
 }
 
+// ------------------------------------------------------------------ prefill tile, bf16
+// Same item, same arithmetic, laid out for gfx950's LDS: every MFMA operand is one
+// conflict-free 16-byte LDS read per lane, and the softmax spends as few VALU cycles per score
+// as the method allows (the row sum runs on the matrix unit).
+//
+// Key -> row assignment of QK.  A 32-key pair of pages (pp) is scored as two 16-row blocks:
+// block a holds keys 8r+i and block b keys 8r+4+i (r = row/4, i = row%4).  The MFMA output
+// then gives lane group q the keys 8q .. 8q+7 of the pair (4 from a, 4 from b), i.e. one
+// 16-byte chunk of a V row, so P^T feeds the PV product unshuffled and the V^T operand is a
+// single b128 read.
+//
+// LDS tile (64 keys = 4 pages), one 1 KB unit per (page, group):
+//   K unit (page p, chunk group s): the page's dim chunks 4s .. 4s+3 for its 16 tokens,
+//     [chunk][slot][16 B], token t at slot kslot(p&1, t);
+//   V unit (page p, dim group g): dims 32g .. 32g+31, [dim][half][16 B] (half h = tokens
+//     8h .. 8h+7), half h of dim d at position h ^ bit2(d) ^ bit3(d).
+// Both permutations make any 8 or 16 consecutive lanes of an operand read touch distinct banks;
+// each is its own inverse, so the staging lane at slot i fetches the source chunk of index
+// perm(i).  Wave w stages page w of every tile: contiguous 1 KB HBM reads straight into LDS.
+constexpr float kRescaleLog2 = 8.f;   // keep a stale running max while scores exceed it by < 2^8
+
+__device__ __forceinline__ int kslot(int par, int t) { return t ^ ((((t >> 3) & 1) ^ par) << 2); }
+
+// Zero the bf16 V^T elements k >= lt of one lane's 8 token slots.
+__device__ __forceinline__ u32x4 mask_v8(u32x4 v, int lt) {
+  u32x4 r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int t = 2 * k;
+    const uint32_t m = (t < lt ? 0x0000FFFFu : 0u) | (t + 1 < lt ? 0xFFFF0000u : 0u);
+    r[k] = v[k] & m;
+  }
+  return r;
+}
+
+template <int D>
+__device__ void prefill_item_bf16(const KernelParams& P, CPTR(int32_t) dsc, int head, int split, char* lds) {
+  constexpr int kNs = D / 32;                  // QK steps of 32 dims = K units per page
+  constexpr int kVg = D / 32;                  // V units per page
+  constexpr int kDb = D / 16;                  // 16-dim blocks of O^T
+  constexpr int kTp = 4, kTileKeys = kTp * kPage;
+  constexpr int kKBytes = kTp * kNs * 1024;
+  constexpr int kBufBytes = kKBytes + kTp * kVg * 1024;
+  static_assert(kBufBytes * 2 == Geo<__bf16, D>::kPrefillLds, "two staged tiles fill the prefill LDS");
+  const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+  const int w = wave_index();
+  const int G = P.group;
+  const int seq = dsc[kDSeq], q_row = dsc[kDQRow], n_q = dsc[kDNq], q_pos = dsc[kDQPos];
+  const int kv_len = dsc[kDKvLen], ns = dsc[kDNSplit], st = dsc[kDSplitTok];
+  const int ncols = n_q * G;
+  const int kv_begin = split * st;
+  const int kv_end = min(kv_len, kv_begin + st);
+  const int n_tiles = (kv_end - kv_begin + kTileKeys - 1) / kTileKeys;
+  CPTR(int32_t) btr = (CPTR(int32_t))P.bt + (size_t)seq * P.bt_stride;
+  const float sl2 = P.scale_log2;
+
+  // Q^T operand: lane (column n, group q) holds dims 8(4s+q) .. +7 of its column.
+  int pos[2];
+  bool cval[2];
+  u32x4 qop[2][kNs];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int c = 32 * w + 16 * nb + n;
+    cval[nb] = c < ncols;
+    const int cc = cval[nb] ? c : 0;
+    const int qi = cc / G, hh = cc - qi * G;
+    pos[nb] = q_pos + qi;
+    const char* qp = (const char*)P.q + ((size_t)(q_row + qi) * P.hq + head * G + hh) * (D * 2);
+#pragma unroll
+    for (int s = 0; s < kNs; ++s) {
+      u32x4 v = ld16(qp + (4 * s + q) * 16);
+      qop[nb][s] = cval[nb] ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  const int wc0 = 32 * w;
+  const bool wave_active = wc0 < ncols;
+  const int pmin = q_pos + wc0 / G;
+  const int pmax = q_pos + (min(ncols, wc0 + 32) - 1) / G;
+
+  f32x4 o[2][kDb], lsum[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    lsum[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < kDb; ++b) o[nb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float m_run[2] = {kNegInf, kNegInf};
+
+  // lane-constant LDS offsets of the operand reads and of the staging sources
+  const int par = n >> 3;
+  const int t_a = 8 * ((n >> 2) & 1) + (n & 3);
+  const int koff_a = par * 1024 + (q * 16 + kslot(par, t_a)) * 16;
+  const int koff_b = par * 1024 + (q * 16 + kslot(par, t_a + 4)) * 16;
+  const int voff = (q >> 1) * 1024 + (2 * n + ((q & 1) ^ ((n >> 2) & 1) ^ ((n >> 3) & 1))) * 16;
+  const int src_k = ((lane >> 4) * 16 + kslot(w & 1, lane & 15)) * 16;
+  const int rv = lane >> 1;
+  const int src_v = (2 * rv + ((lane & 1) ^ ((rv >> 2) & 1) ^ ((rv >> 3) & 1))) * 16;
+
+  int lim_cur[kTp], lim_nxt[kTp];
+  // Stages tile j into buffer b (this wave: page w of the tile); returns that page's key count.
+  auto issue_tile = [&](int j, int b, int (&lim)[kTp]) -> int {
+    const int tb = kv_begin + j * kTileKeys;
+    int own = 0, own_lim = 0;
+#pragma unroll
+    for (int p = 0; p < kTp; ++p) {
+      const int pi = (tb >> 4) + p;
+      int l = min(kPage, kv_end - pi * kPage);
+      const int pg = __builtin_amdgcn_readfirstlane(page_or_empty(btr, pi, l, P.num_pages, P.ctrl + kCStatus));
+      lim[p] = __builtin_amdgcn_readfirstlane(l);
+      own = p == w ? pg : own;
+      own_lim = p == w ? lim[p] : own_lim;
+    }
+    if (own_lim <= 0) return 0;               // absent page: nothing is read
+    const char* kp = slab_ptr<__bf16, D>(P.k, own, P.hkv, head) + src_k;
+    const char* vp = slab_ptr<__bf16, D>(P.v, own, P.hkv, head) + src_v;
+    char* dst = lds + b * kBufBytes + w * 1024;
+#pragma unroll
+    for (int s = 0; s < kNs; ++s)
+      __builtin_amdgcn_global_load_lds((const void*)(kp + s * 1024),
+                                       (__attribute__((address_space(3))) void*)(dst + s * 4096), 16, 0, 0);
+#pragma unroll
+    for (int g = 0; g < kVg; ++g)
+      __builtin_amdgcn_global_load_lds((const void*)(vp + g * 1024),
+                                       (__attribute__((address_space(3))) void*)(dst + kKBytes + g * 4096), 16, 0, 0);
+    return own_lim;
+  };
+  // After this wave's staging loads have landed: zero the V slots of tokens >= lim of its page
+  // (all of them for an absent page), so that a zero probability never meets a NaN or stale
+  // value in the PV product.  Scores of those slots are masked by select.
+  auto zero_v_tail = [&](int b, int lim_own) {
+    char* vu = lds + b * kBufBytes + kKBytes + w * 1024;
+#pragma unroll
+    for (int g = 0; g < kVg; ++g) {
+      const int r = lane >> 1;
+      const int h = (lane & 1) ^ ((r >> 2) & 1) ^ ((r >> 3) & 1);   // stored chunk holds tokens 8h .. 8h+7
+      u32x4* cp = (u32x4*)(vu + g * 4096 + lane * 16);
+      const u32x4 v = lim_own > 0 ? *cp : u32x4{0u, 0u, 0u, 0u};
+      *cp = mask_v8(v, lim_own - 8 * h);
+    }
+  };
+
+  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};   // bf16 1.0 pairs
+
+  // `masked` (wave-uniform): some key of the tile lies after a query of the wave, or some page
+  // of the tile is partial or absent.
+  auto tile_body = [&](bool masked, const char* kb, int tb, const int (&lim)[kTp]) {
+    const char* vb = kb + kKBytes;
+    // S^T blocks [nb][pp][blk]; the K operands of step k+1 are read while step k multiplies
+    // (one step of lookahead, pinned with scheduling barriers so that the reads are not all
+    // hoisted ahead of the products).
+    f32x4 S[2][2][2];
+    auto kread = [&](int k, u32x4 (&kop)[kNs]) {
+      const int pp = k >> 1, blk = k & 1;
+#pragma unroll
+      for (int s = 0; s < kNs; ++s)
+        kop[s] = *(const u32x4*)(kb + (s * 4 + 2 * pp) * 1024 + (blk ? koff_b : koff_a));
+    };
+    u32x4 kop0[kNs], kop1[kNs];
+    kread(0, kop0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      u32x4 (&cur)[kNs] = (k & 1) ? kop1 : kop0;
+      u32x4 (&nxt)[kNs] = (k & 1) ? kop0 : kop1;
+      if (k + 1 < 4) kread(k + 1, nxt);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < kNs; ++s) acc = mfma_chunk(cur[s], qop[nb][s], acc, __bf16());
+        S[nb][k >> 1][k & 1] = acc;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    u32x4 pb[2][2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      float x[16];                             // x[8pp + 4blk + i]: key 32pp + 8q + 4blk + i
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[8 * pp + 4 * blk + i] = S[nb][pp][blk][i];
+      if (masked) {
+        // slot (pp, blk, i) of this lane is key 32pp + 8q + 4blk + i of the tile, token
+        // 8(q&1) + 4blk + i of page 2pp + q/2: visible iff 4blk + i <= bound(pp)
+        const int rel = pos[nb] - tb - 8 * q;
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          const int lt = ((q >> 1) ? lim[2 * pp + 1] : lim[2 * pp]) - 8 * (q & 1);
+          const int bound = min(rel - 32 * pp, lt - 1);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) x[8 * pp + k] = k <= bound ? x[8 * pp + k] : kNegInf;   // select, never multiply
+        }
+      }
+      float mx = x[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
+      mx = max_over_groups(mx) * sl2;
+      // The running max only moves when a score exceeds it by more than 2^kRescaleLog2; any
+      // reference value gives the same softmax as long as numerator and denominator share it,
+      // and the bound keeps every probability <= 2^kRescaleLog2.
+      const bool grow = mx > m_run[nb] + kRescaleLog2;
+      if (__any(grow)) {
+        const float alpha = grow ? exp2_fast(m_run[nb] - mx) : 1.f;
+        m_run[nb] = grow ? mx : m_run[nb];
+#pragma unroll
+        for (int b = 0; b < kDb; ++b) o[nb][b] *= alpha;
+        lsum[nb] *= alpha;
+      }
+      const float m_use = m_run[nb] == kNegInf ? 0.f : m_run[nb];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] = exp2_fast(__builtin_fmaf(x[i], sl2, -m_use));
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp)
+        pb[nb][pp] = u32x4{pack_bf16(x[8 * pp + 0], x[8 * pp + 1]), pack_bf16(x[8 * pp + 2], x[8 * pp + 3]),
+                           pack_bf16(x[8 * pp + 4], x[8 * pp + 5]), pack_bf16(x[8 * pp + 6], x[8 * pp + 7])};
+    }
+    // PV: V^T operands two blocks ahead of the products that use them
+    auto vread = [&](int k) {
+      const int pp = k / kDb, b2 = k % kDb;
+      return *(const u32x4*)(vb + ((b2 >> 1) * 4 + 2 * pp) * 1024 + (b2 & 1) * 512 + voff);
+    };
+    constexpr int kPv = 2 * kDb;
+    u32x4 vq[3];
+    vq[0] = vread(0);
+    vq[1] = vread(1);
+#pragma unroll
+    for (int k = 0; k < kPv; ++k) {
+      const int pp = k / kDb, b2 = k % kDb;
+      if (k + 2 < kPv) vq[(k + 2) % 3] = vread(k + 2);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) o[nb][b2] = mfma_chunk(vq[k % 3], pb[nb][pp], o[nb][b2], __bf16());
+      if (b2 == kDb - 1) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) lsum[nb] = mfma_chunk(ones, pb[nb][pp], lsum[nb], __bf16());
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  if (n_tiles > 0) {
+    const int own0 = issue_tile(0, 0, lim_cur);
+    __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): this wave's LDS loads landed
+    if (own0 < kPage) zero_v_tail(0, own0);
+    __syncthreads();
+    for (int j = 0; j < n_tiles; ++j) {
+      const bool more = j + 1 < n_tiles;
+      int own_nxt = kPage;
+      if (more) own_nxt = issue_tile(j + 1, (j + 1) & 1, lim_nxt);
+      const int tb = kv_begin + j * kTileKeys;
+      if (wave_active && tb <= pmax) {        // else every key follows every query of the wave
+        const bool full = (tb + kTileKeys - 1 <= pmin) & (lim_cur[0] == kPage) & (lim_cur[1] == kPage) &
+                          (lim_cur[2] == kPage) & (lim_cur[3] == kPage);
+        tile_body(!full, lds + (j & 1) * kBufBytes, tb, lim_cur);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      if (own_nxt < kPage) zero_v_tail((j + 1) & 1, own_nxt);
+      __syncthreads();
+#pragma unroll
+      for (int p = 0; p < kTp; ++p) lim_cur[p] = lim_nxt[p];
+    }
+  }
+
+  // ---- epilogue: normalise and write the output, or the split partial (o, lse)
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const float l_tot = lsum[nb][0];           // every row of the ones-product holds the column sum
+    if (!cval[nb]) continue;
+    const int c = 32 * w + 16 * nb + n;
+    const int qi = c / G, hh = c - qi * G;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (ns == 1) {
+      __bf16* dst = (__bf16*)P.out + ((size_t)(q_row + qi) * P.hq + head * G + hh) * D + 4 * q;
+#pragma unroll
+      for (int b2 = 0; b2 < kDb; ++b2) store4<__bf16>(dst + 16 * b2, o[nb][b2] * inv);
+    } else {
+      const size_t slot = (size_t)dsc[kDPartBase] + ((size_t)head * ns + split) * ncols + c;
+      float* dst = P.part_o + slot * D + 4 * q;
+      const bool coh = P.inline_combine != 0;
+#pragma unroll
+      for (int b2 = 0; b2 < kDb; ++b2) store_part4(dst + 16 * b2, o[nb][b2] * inv, coh);
+      if (q == 0) store_part1(P.part_lse + slot, l_tot > 0.f ? m_run[nb] + __log2f(l_tot) : kNegInf, coh);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ item dispatch
 // Prefill item: the whole workgroup.  Split partials are merged by the workgroup that
 // arrives last when the combine runs in-kernel.
@@ -709,7 +996,8 @@ __device__ void run_prefill_item(const KernelParams& P, int item, char* lds, int
   const int ns = dsc[kDNSplit];
   const int local = item - dsc[kDItemBegin];
   const int split = local / P.hkv, head = local - split * P.hkv;
-  prefill_item<T, D>(P, dsc, head, split, lds);
+  if constexpr (sizeof(T) == 2) prefill_item_bf16<D>(P, dsc, head, split, lds);
+  else prefill_item<T, D>(P, dsc, head, split, lds);
   if (ns > 1 && P.inline_combine) {
     // Each wave's partial stores complete before the barrier; thread 0 takes the ticket; the
     // workgroup holding the last split merges the group.  No workgroup waits for another.
