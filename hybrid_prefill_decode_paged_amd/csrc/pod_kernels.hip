@@ -713,10 +713,12 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
 //   K unit (page p, chunk group s): the page's dim chunks 4s .. 4s+3 for its 16 tokens,
 //     [chunk][slot][16 B], token t at slot kslot(p&1, t);
 //   V unit (page p, dim group g): dims 32g .. 32g+31, [dim][half][16 B] (half h = tokens
-//     8h .. 8h+7), half h of dim d at position h ^ bit2(d) ^ bit3(d).
-// Both permutations make any 8 or 16 consecutive lanes of an operand read touch distinct banks;
-// each is its own inverse, so the staging lane at slot i fetches the source chunk of index
-// perm(i).  Wave w stages page w of every tile: contiguous 1 KB HBM reads straight into LDS.
+//     8h .. 8h+7), i.e. the page's own byte order.
+// Measured on gfx950 (LDS bank-conflict counter, one b128 read per lane): the K operand read
+// conflicts two-way in the page's own order and not at all with the slot permutation, which is
+// its own inverse, so the staging lane at slot i fetches source chunk kslot(p&1, i); the V
+// operand read is conflict-free unpermuted.  Wave w stages page w of every tile: contiguous
+// 1 KB HBM reads straight into LDS.
 constexpr float kRescaleLog2 = 8.f;   // keep a stale running max while scores exceed it by < 2^8
 
 __device__ __forceinline__ int kslot(int par, int t) { return t ^ ((((t >> 3) & 1) ^ par) << 2); }
@@ -791,10 +793,9 @@ __device__ void prefill_item_bf16(const KernelParams& P, CPTR(int32_t) dsc, int 
   const int t_a = 8 * ((n >> 2) & 1) + (n & 3);
   const int koff_a = par * 1024 + (q * 16 + kslot(par, t_a)) * 16;
   const int koff_b = par * 1024 + (q * 16 + kslot(par, t_a + 4)) * 16;
-  const int voff = (q >> 1) * 1024 + (2 * n + ((q & 1) ^ ((n >> 2) & 1) ^ ((n >> 3) & 1))) * 16;
+  const int voff = (q >> 1) * 1024 + (2 * n + (q & 1)) * 16;
   const int src_k = ((lane >> 4) * 16 + kslot(w & 1, lane & 15)) * 16;
-  const int rv = lane >> 1;
-  const int src_v = (2 * rv + ((lane & 1) ^ ((rv >> 2) & 1) ^ ((rv >> 3) & 1))) * 16;
+  const int src_v = lane * 16;
 
   int lim_cur[kTp], lim_nxt[kTp];
   // Stages tile j into buffer b (this wave: page w of the tile); returns that page's key count.
@@ -831,8 +832,7 @@ __device__ void prefill_item_bf16(const KernelParams& P, CPTR(int32_t) dsc, int 
     char* vu = lds + b * kBufBytes + kKBytes + w * 1024;
 #pragma unroll
     for (int g = 0; g < kVg; ++g) {
-      const int r = lane >> 1;
-      const int h = (lane & 1) ^ ((r >> 2) & 1) ^ ((r >> 3) & 1);   // stored chunk holds tokens 8h .. 8h+7
+      const int h = lane & 1;                  // the chunk holds tokens 8h .. 8h+7
       u32x4* cp = (u32x4*)(vu + g * 4096 + lane * 16);
       const u32x4 v = lim_own > 0 ? *cp : u32x4{0u, 0u, 0u, 0u};
       *cp = mask_v8(v, lim_own - 8 * h);
@@ -871,16 +871,18 @@ __device__ void prefill_item_bf16(const KernelParams& P, CPTR(int32_t) dsc, int 
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    u32x4 pb[2][2];
+    // softmax of both column blocks: maxima first (two independent reduction chains), one
+    // rescale branch, then the probabilities
+    float x[2][16];                            // x[nb][8pp + 4blk + i]: key 32pp + 8q + 4blk + i
+    float mx[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      float x[16];                             // x[8pp + 4blk + i]: key 32pp + 8q + 4blk + i
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) x[8 * pp + 4 * blk + i] = S[nb][pp][blk][i];
+          for (int i = 0; i < 4; ++i) x[nb][8 * pp + 4 * blk + i] = S[nb][pp][blk][i];
       if (masked) {
         // slot (pp, blk, i) of this lane is key 32pp + 8q + 4blk + i of the tile, token
         // 8(q&1) + 4blk + i of page 2pp + q/2: visible iff 4blk + i <= bound(pp)
@@ -890,31 +892,41 @@ __device__ void prefill_item_bf16(const KernelParams& P, CPTR(int32_t) dsc, int 
           const int lt = ((q >> 1) ? lim[2 * pp + 1] : lim[2 * pp]) - 8 * (q & 1);
           const int bound = min(rel - 32 * pp, lt - 1);
 #pragma unroll
-          for (int k = 0; k < 8; ++k) x[8 * pp + k] = k <= bound ? x[8 * pp + k] : kNegInf;   // select, never multiply
+          for (int k = 0; k < 8; ++k) x[nb][8 * pp + k] = k <= bound ? x[nb][8 * pp + k] : kNegInf;   // select, never multiply
         }
       }
-      float mx = x[0];
+      float m = x[nb][0];
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
-      mx = max_over_groups(mx) * sl2;
-      // The running max only moves when a score exceeds it by more than 2^kRescaleLog2; any
-      // reference value gives the same softmax as long as numerator and denominator share it,
-      // and the bound keeps every probability <= 2^kRescaleLog2.
-      const bool grow = mx > m_run[nb] + kRescaleLog2;
-      if (__any(grow)) {
-        const float alpha = grow ? exp2_fast(m_run[nb] - mx) : 1.f;
-        m_run[nb] = grow ? mx : m_run[nb];
+      for (int i = 1; i < 16; ++i) m = fmaxf(m, x[nb][i]);
+      mx[nb] = m;
+    }
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) mx[nb] = max_over_groups(mx[nb]) * sl2;
+    // The running max only moves when a score exceeds it by more than 2^kRescaleLog2; any
+    // reference value gives the same softmax as long as numerator and denominator share it,
+    // and the bound keeps every probability <= 2^kRescaleLog2.
+    const bool grow0 = mx[0] > m_run[0] + kRescaleLog2, grow1 = mx[1] > m_run[1] + kRescaleLog2;
+    if (__any(grow0 | grow1)) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const bool grow = nb ? grow1 : grow0;
+        const float alpha = grow ? exp2_fast(m_run[nb] - mx[nb]) : 1.f;
+        m_run[nb] = grow ? mx[nb] : m_run[nb];
 #pragma unroll
         for (int b = 0; b < kDb; ++b) o[nb][b] *= alpha;
         lsum[nb] *= alpha;
       }
+    }
+    u32x4 pb[2][2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
       const float m_use = m_run[nb] == kNegInf ? 0.f : m_run[nb];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = exp2_fast(__builtin_fmaf(x[i], sl2, -m_use));
+      for (int i = 0; i < 16; ++i) x[nb][i] = exp2_fast(__builtin_fmaf(x[nb][i], sl2, -m_use));
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp)
-        pb[nb][pp] = u32x4{pack_bf16(x[8 * pp + 0], x[8 * pp + 1]), pack_bf16(x[8 * pp + 2], x[8 * pp + 3]),
-                           pack_bf16(x[8 * pp + 4], x[8 * pp + 5]), pack_bf16(x[8 * pp + 6], x[8 * pp + 7])};
+        pb[nb][pp] = u32x4{pack_bf16(x[nb][8 * pp + 0], x[nb][8 * pp + 1]), pack_bf16(x[nb][8 * pp + 2], x[nb][8 * pp + 3]),
+                           pack_bf16(x[nb][8 * pp + 4], x[nb][8 * pp + 5]), pack_bf16(x[nb][8 * pp + 6], x[nb][8 * pp + 7])};
     }
     // PV: V^T operands two blocks ahead of the products that use them
     auto vread = [&](int k) {
