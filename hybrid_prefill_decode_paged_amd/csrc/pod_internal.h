@@ -71,7 +71,7 @@ struct KernelParams {
   float scale_log2;          // softmax scale * log2(e)
   int prefill_cap_per_cu;    // fused: prefill-role workgroups allowed per CU while decode remains
   int prefill_wg_budget;     // fused: prefill-role workgroups allowed device-wide while decode remains
-  int inline_combine;        // 1: last-arriving split combines in-kernel (fused)
+  int inline_combine;        // 1: the last-arriving decode split merges its group in-kernel (fused)
   int group_begin, group_end;// combine kernel range
   int combine_col_blocks;     // combine kernel: workgroups per group (16 columns each)
   int decode_block_claim;     // fused: a decode-role workgroup claims 4 consecutive items at once

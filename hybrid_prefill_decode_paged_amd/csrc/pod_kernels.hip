@@ -690,7 +690,7 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
     } else {
       const size_t slot = (size_t)dsc[kDPartBase] + ((size_t)head * ns + split) * ncols + c;
       float* dst = P.part_o + slot * D + 4 * q;
-      const bool coh = P.inline_combine != 0;
+      const bool coh = false;                  // merged by the combine kernel
 #pragma unroll
       for (int b2 = 0; b2 < Gm::kDb; ++b2) store_part4(dst + 16 * b2, o[nb][b2] * inv, coh);
       if (q == 0) store_part1(P.part_lse + slot, l_tot > 0.f ? m_run[nb] + __log2f(l_tot) : kNegInf, coh);
@@ -989,7 +989,7 @@ __device__ void prefill_item_bf16(const KernelParams& P, CPTR(int32_t) dsc, int 
     } else {
       const size_t slot = (size_t)dsc[kDPartBase] + ((size_t)head * ns + split) * ncols + c;
       float* dst = P.part_o + slot * D + 4 * q;
-      const bool coh = P.inline_combine != 0;
+      const bool coh = false;                  // merged by the combine kernel
 #pragma unroll
       for (int b2 = 0; b2 < kDb; ++b2) store_part4(dst + 16 * b2, o[nb][b2] * inv, coh);
       if (q == 0) store_part1(P.part_lse + slot, l_tot > 0.f ? m_run[nb] + __log2f(l_tot) : kNegInf, coh);
@@ -998,10 +998,12 @@ __device__ void prefill_item_bf16(const KernelParams& P, CPTR(int32_t) dsc, int 
 }
 
 // ------------------------------------------------------------------ item dispatch
-// Prefill item: the whole workgroup.  Split partials are merged by the workgroup that
-// arrives last when the combine runs in-kernel.
+// Prefill item: the whole workgroup.  Split partials (up to 128 columns x D floats per item)
+// go out with plain 16-byte stores and are merged by the combine kernel after the launch: in
+// the fused kernel, merging them in the last-arriving workgroup needed device-coherent stores
+// and loads and measured 20-30% slower on the prefill share than one combine launch.
 template <typename T, int D>
-__device__ void run_prefill_item(const KernelParams& P, int item, char* lds, int* s_flag) {
+__device__ void run_prefill_item(const KernelParams& P, int item, char* lds) {
   CPTR(int32_t) descs = (CPTR(int32_t))P.pdesc;
   const int di = find_desc(descs, P.n_pdesc, kDItemBegin, item);
   CPTR(int32_t) dsc = descs + (size_t)di * kDescInts;
@@ -1010,19 +1012,6 @@ __device__ void run_prefill_item(const KernelParams& P, int item, char* lds, int
   const int split = local / P.hkv, head = local - split * P.hkv;
   if constexpr (sizeof(T) == 2) prefill_item_bf16<D>(P, dsc, head, split, lds);
   else prefill_item<T, D>(P, dsc, head, split, lds);
-  if (ns > 1 && P.inline_combine) {
-    // Each wave's partial stores complete before the barrier; thread 0 takes the ticket; the
-    // workgroup holding the last split merges the group.  No workgroup waits for another.
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    if (threadIdx.x == 0) *s_flag = atomicAdd(P.tickets + dsc[kDGroupBegin] + head, 1) == ns - 1;
-    __syncthreads();
-    if (*s_flag) {
-      const int w = wave_index();
-      float* sw = (float*)(lds + w * kCombineLdsPerWave);
-      for (int c0 = 16 * w; c0 < dsc[kDNcols]; c0 += 16 * kWaves) combine_block_wave<T, D>(P, dsc, head, c0, sw);
-    }
-  }
   __syncthreads();   // LDS and the flag are reused by the next item
 }
 
@@ -1085,7 +1074,7 @@ __device__ void decode_wave_stream(const KernelParams& P, int cu, float* sw) {
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 2) void pod_fused_kernel(KernelParams P) {
   __shared__ __attribute__((aligned(16))) char lds[Geo<T, D>::kFusedLds];
-  __shared__ int s_role, s_item, s_flag;
+  __shared__ int s_role, s_item;
   const int tid = threadIdx.x;
   const int cu = cu_slot();
   const int xcc = cu >> 7;
@@ -1146,7 +1135,7 @@ __global__ __launch_bounds__(kThreads, 2) void pod_fused_kernel(KernelParams P) 
     }
     while (item < P.n_pf_items) {
       if (tid == 0) note_claim(P, 0, item, cu);
-      run_prefill_item<T, D>(P, item, lds, &s_flag);   // ends with a barrier
+      run_prefill_item<T, D>(P, item, lds);   // ends with a barrier
       if (tid == 0) s_item = claim_prefill(P, xcc);   // claim once idle
       __syncthreads();
       item = s_item;
@@ -1164,9 +1153,8 @@ __global__ __launch_bounds__(kThreads, 2) void pod_fused_kernel(KernelParams P) 
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 2) void pod_prefill_kernel(KernelParams P) {
   __shared__ __attribute__((aligned(16))) char lds[Geo<T, D>::kPrefillLds];
-  __shared__ int s_flag;
   if (threadIdx.x == 0) note_claim(P, 0, blockIdx.x, cu_slot());
-  run_prefill_item<T, D>(P, blockIdx.x, lds, &s_flag);
+  run_prefill_item<T, D>(P, blockIdx.x, lds);
 }
 
 // Separate decode kernel: wave w of workgroup b takes decode item 4b + w.
