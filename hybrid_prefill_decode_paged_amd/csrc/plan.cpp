@@ -13,7 +13,7 @@
 // length is chosen from the total decode work and the number of persistent workgroups so that
 // every workgroup gets many small items and the last wave of work stays short (the wave
 // quantization loss of the same digest, section "Why concurrency alone is not enough").
-// Work is ordered longest first within each kind.
+// Decode work is ordered longest first; prefill work is dealt to per-XCD queues (below).
 #include "plan.h"
 
 #include <algorithm>
@@ -108,11 +108,24 @@ pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus
   p.total_q = (int)prefill_rows + b->num_decode;
 
   // ---------------- prefill tiles
+  // Tiles of one chunk share their split boundaries (one split length per chunk), so that the
+  // tiles reading the same key range of the same KV head form a group.  Groups are dealt whole
+  // to the kXcds per-XCD claim queues, largest first onto the least-loaded queue, so that a
+  // group's tiles run together under one L2 and every XCD gets about the same work.
   struct Tile { int seq, q_row, n_q, q_pos, kv_len; };
-  std::vector<Tile> tiles;
+  const int cap = c.prefill_split_cap > 0 ? c.prefill_split_cap : 8;
+  int group = 0, slot = 0;
+  p.prefill_max_splits = 0;
+  struct PGroup { double work; std::vector<int32_t> items; };   // items: (desc, split << 16 | head)
+  std::vector<PGroup> pgroups;
   for (int i = 0; i < b->num_prefill; ++i) {
-    int L = b->prefill_q_start[i + 1] - b->prefill_q_start[i];
-    int ctx = b->prefill_ctx_len[i];
+    const int L = b->prefill_q_start[i + 1] - b->prefill_q_start[i];
+    const int ctx = b->prefill_ctx_len[i];
+    if (L == 0) continue;
+    int ns_c = std::max(1, std::min(std::min(cap, kMaxCombineSplits), ceil_div(ctx, 4096)));
+    const int st = round_up_int(ceil_div(ctx, ns_c), kPrefillKvTile);
+    ns_c = ceil_div(ctx, st);
+    std::vector<Tile> tiles;
     for (int t = 0; t < L; t += p.tile_queries) {
       Tile tl;
       tl.seq = i;
@@ -122,30 +135,51 @@ pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus
       tl.kv_len = tl.q_pos + tl.n_q;
       tiles.push_back(tl);
     }
+    std::reverse(tiles.begin(), tiles.end());  // last (longest) tile first
+    const size_t g0 = pgroups.size();
+    pgroups.resize(g0 + (size_t)ns_c * c.hkv);
+    for (const Tile& tl : tiles) {
+      const int ns = ceil_div(tl.kv_len, st);
+      const int di = (int)(p.pdesc.size() / kDescInts);
+      std::vector<int32_t> d(kDescInts, 0);
+      d[kDSeq] = tl.seq; d[kDQRow] = tl.q_row; d[kDNq] = tl.n_q; d[kDQPos] = tl.q_pos;
+      d[kDKvLen] = tl.kv_len; d[kDNSplit] = ns; d[kDSplitTok] = st;
+      d[kDGroupBegin] = group; d[kDPartBase] = slot; d[kDNcols] = tl.n_q * G;
+      if (ns > 1) { group += c.hkv; slot += c.hkv * ns * tl.n_q * G; }
+      p.prefill_max_splits = std::max(p.prefill_max_splits, ns);
+      p.prefill_flops += 4.0 * c.d * G * c.hkv *
+                         ((double)tl.n_q * tl.q_pos + (double)tl.n_q * (tl.n_q + 1) / 2.0);
+      p.pdesc.insert(p.pdesc.end(), d.begin(), d.end());
+      for (int sp = 0; sp < ns; ++sp) {
+        const double keys = std::min(tl.kv_len, (sp + 1) * st) - sp * st;
+        for (int h = 0; h < c.hkv; ++h) {
+          PGroup& pg = pgroups[g0 + (size_t)sp * c.hkv + h];
+          pg.work += keys * tl.n_q;
+          pg.items.push_back(di);
+          pg.items.push_back((sp << 16) | h);
+        }
+      }
+    }
   }
-  std::stable_sort(tiles.begin(), tiles.end(), [](const Tile& a, const Tile& b2) {
-    return (long)a.kv_len * a.n_q > (long)b2.kv_len * b2.n_q;
-  });
-  const int cap = c.prefill_split_cap > 0 ? c.prefill_split_cap : 8;
-  int item = 0, group = 0, slot = 0;
-  p.prefill_max_splits = 0;
-  for (const Tile& tl : tiles) {
-    int ns = std::max(1, std::min(std::min(cap, kMaxCombineSplits), ceil_div(tl.kv_len, 4096)));
-    int st = round_up_int(ceil_div(tl.kv_len, ns), kPrefillKvTile);
-    ns = ceil_div(tl.kv_len, st);
-    std::vector<int32_t> d(kDescInts, 0);
-    d[kDSeq] = tl.seq; d[kDQRow] = tl.q_row; d[kDNq] = tl.n_q; d[kDQPos] = tl.q_pos;
-    d[kDKvLen] = tl.kv_len; d[kDNSplit] = ns; d[kDSplitTok] = st; d[kDItemBegin] = item;
-    d[kDGroupBegin] = group; d[kDPartBase] = slot; d[kDNcols] = tl.n_q * G;
-    item += c.hkv * ns;
-    if (ns > 1) { group += c.hkv; slot += c.hkv * ns * tl.n_q * G; }
-    p.prefill_max_splits = std::max(p.prefill_max_splits, ns);
-    p.prefill_flops += 4.0 * c.d * G * c.hkv *
-                       ((double)tl.n_q * tl.q_pos + (double)tl.n_q * (tl.n_q + 1) / 2.0);
-    p.pdesc.insert(p.pdesc.end(), d.begin(), d.end());
+  p.n_pdesc = (int)(p.pdesc.size() / kDescInts);
+  std::vector<int> gorder(pgroups.size());
+  std::iota(gorder.begin(), gorder.end(), 0);
+  std::stable_sort(gorder.begin(), gorder.end(), [&](int x, int y) { return pgroups[x].work > pgroups[y].work; });
+  std::vector<int32_t> per_xcd[kXcds];
+  double load[kXcds] = {0};
+  for (int gi : gorder) {
+    if (pgroups[gi].items.empty()) continue;
+    const int x = (int)(std::min_element(load, load + kXcds) - load);
+    load[x] += pgroups[gi].work;
+    per_xcd[x].insert(per_xcd[x].end(), pgroups[gi].items.begin(), pgroups[gi].items.end());
   }
-  p.n_pdesc = (int)tiles.size();
-  p.n_pf_items = item;
+  p.pitems.assign(kPItemHeader, 0);
+  for (int x = 0; x < kXcds; ++x) {
+    p.pitems[x] = (int32_t)((p.pitems.size() - kPItemHeader) / 2);
+    p.pitems.insert(p.pitems.end(), per_xcd[x].begin(), per_xcd[x].end());
+  }
+  p.n_pf_items = (int)((p.pitems.size() - kPItemHeader) / 2);
+  p.pitems[kXcds] = p.n_pf_items;
   p.n_pf_groups = group;
 
   // ---------------- decode sequences
@@ -197,6 +231,7 @@ pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus
   if (c.flags & POD_ATTN_FLAG_DEBUG_CLAIMS)
     off = align_up(off + sizeof(int32_t) * std::max(1, p.n_pf_items + p.n_dc_items), 256);
   m.pdesc = off; off = align_up(off + sizeof(int32_t) * std::max<size_t>(1, p.pdesc.size()), 256);
+  m.pitems = off; off = align_up(off + sizeof(int32_t) * p.pitems.size(), 256);
   m.ddesc = off; off = align_up(off + sizeof(int32_t) * std::max<size_t>(1, p.ddesc.size()), 256);
   m.copy_bytes = off;
   m.part_o = off; off = align_up(off + sizeof(float) * (size_t)p.n_slots * c.d, 256);
@@ -210,6 +245,7 @@ pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus
 void stage_plan(const Plan& p, const Config& c, uint8_t* dst) {
   std::memset(dst, 0, p.map.copy_bytes);
   if (!p.pdesc.empty()) std::memcpy(dst + p.map.pdesc, p.pdesc.data(), p.pdesc.size() * 4);
+  std::memcpy(dst + p.map.pitems, p.pitems.data(), p.pitems.size() * 4);
   if (!p.ddesc.empty()) std::memcpy(dst + p.map.ddesc, p.ddesc.data(), p.ddesc.size() * 4);
   (void)c;
 }
@@ -217,25 +253,30 @@ void stage_plan(const Plan& p, const Config& c, uint8_t* dst) {
 void expand_items(const Plan& p, const Config& c, std::vector<int32_t>* items) {
   items->clear();
   const int G = c.group();
-  for (int kind = 0; kind < 2; ++kind) {
-    const std::vector<int32_t>& D = kind == 0 ? p.pdesc : p.ddesc;
-    const int n = kind == 0 ? p.n_pdesc : p.n_ddesc;
-    for (int di = 0; di < n; ++di) {
-      const int32_t* d = &D[(size_t)di * kDescInts];
-      const int ns = d[kDNSplit], st = d[kDSplitTok];
-      for (int s = 0; s < ns; ++s) {           // split-major, as the kernels decode items
-        for (int h = 0; h < c.hkv; ++h) {
-          int32_t it[16] = {0};
-          it[0] = d[kDSeq]; it[1] = d[kDQRow]; it[2] = d[kDNq]; it[3] = d[kDQPos];
-          it[4] = h; it[5] = s * st; it[6] = std::min(d[kDKvLen], (s + 1) * st);
-          it[7] = ns > 1 ? d[kDGroupBegin] + h : -1;
-          it[8] = s;
-          it[9] = ns > 1 ? d[kDPartBase] + (h * ns + s) * d[kDNq] * G : -1;
-          it[10] = kind;
-          items->insert(items->end(), it, it + 16);
-        }
-      }
-    }
+  auto emit = [&](const int32_t* d, int s, int h, int kind, int queue) {
+    const int ns = d[kDNSplit], st = d[kDSplitTok];
+    int32_t it[16] = {0};
+    it[0] = d[kDSeq]; it[1] = d[kDQRow]; it[2] = d[kDNq]; it[3] = d[kDQPos];
+    it[4] = h; it[5] = s * st; it[6] = std::min(d[kDKvLen], (s + 1) * st);
+    it[7] = ns > 1 ? d[kDGroupBegin] + h : -1;
+    it[8] = s;
+    it[9] = ns > 1 ? d[kDPartBase] + (h * ns + s) * d[kDNq] * G : -1;
+    it[10] = kind;
+    it[11] = queue;
+    items->insert(items->end(), it, it + 16);
+  };
+  // prefill: in item-table order (the per-XCD queues back to back)
+  int queue = 0;
+  for (int i = 0; i < p.n_pf_items; ++i) {
+    while (queue + 1 < kXcds && i >= p.pitems[queue + 1]) ++queue;
+    const int32_t* e = &p.pitems[kPItemHeader + 2 * (size_t)i];
+    emit(&p.pdesc[(size_t)e[0] * kDescInts], e[1] >> 16, e[1] & 0xFFFF, 0, queue);
+  }
+  // decode: descriptor order, split-major, as the kernels decode items
+  for (int di = 0; di < p.n_ddesc; ++di) {
+    const int32_t* d = &p.ddesc[(size_t)di * kDescInts];
+    for (int s = 0; s < d[kDNSplit]; ++s)
+      for (int h = 0; h < c.hkv; ++h) emit(d, s, h, 1, -1);
   }
 }
 

@@ -19,6 +19,7 @@ struct Config {
 
 struct Plan {
   std::vector<int32_t> pdesc, ddesc;   // kDescInts each
+  std::vector<int32_t> pitems;         // prefill item table: kPItemHeader ints, then (desc, split << 16 | head)
   int n_pdesc = 0, n_ddesc = 0;
   int n_pf_items = 0, n_dc_items = 0;
   int n_pf_groups = 0, n_groups = 0, n_slots = 0;

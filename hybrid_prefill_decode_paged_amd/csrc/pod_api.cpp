@@ -255,6 +255,7 @@ pod_attn_status pod_attn_run(pod_attn_handle* h, const void* q, const void* k_ca
   kp.tickets = (int32_t*)(ws + p.map.tickets);
   kp.claims = (h->cfg.flags & POD_ATTN_FLAG_DEBUG_CLAIMS) ? (int32_t*)(ws + p.map.claims) : nullptr;
   kp.pdesc = (const int32_t*)(ws + p.map.pdesc);
+  kp.pitems = (const int32_t*)(ws + p.map.pitems);
   kp.ddesc = (const int32_t*)(ws + p.map.ddesc);
   kp.part_o = (float*)(ws + p.map.part_o);
   kp.part_lse = (float*)(ws + p.map.part_lse);

@@ -15,6 +15,7 @@ constexpr int kPrefillKvTile = 64;   // keys per prefill inner iteration (4 page
 constexpr int kDecodeStep = 32;      // keys per decode wave step (2 pages)
 constexpr int kCuSlots = 1024;       // hashed (XCC, SE, CU) slots for per-CU scheduler state
 constexpr int kXcds = 8;             // accelerator complex dies (one L2 each)
+constexpr int kPItemHeader = 16;     // prefill item table header: queue x = items [hdr[x], hdr[x+1])
 constexpr int kMaxCombineSplits = 128;  // max KV splits of one group (LDS weight table rows)
 constexpr int kCombineLdsPerWave = 16 * kMaxCombineSplits * 4;   // [16 columns][splits] floats
 
@@ -29,7 +30,7 @@ enum DescField {
   kDKvLen,          // keys the tile needs: last query position + 1 (decode: ctx)
   kDNSplit,         // KV splits per head (>= 1)
   kDSplitTok,       // tokens per split (multiple of the kind's key step)
-  kDItemBegin,      // first item index within the kind's item list
+  kDItemBegin,      // decode: first item index of the descriptor
   kDGroupBegin,     // first combine group (one per head) when n_split > 1, else -1
   kDPartBase,       // first partial slot when n_split > 1
   kDNcols,          // columns = n_q * group
@@ -61,6 +62,7 @@ struct KernelParams {
   int32_t* tickets;          // [n_groups]
   int32_t* claims;           // [n_pf_items + n_dc_items] or null
   const int32_t* pdesc;      // prefill descriptors
+  const int32_t* pitems;     // prefill item table (header, then (desc, split << 16 | head) per item)
   const int32_t* ddesc;      // decode descriptors
   float* part_o;             // [slots][D]
   float* part_lse;           // [slots], log2-domain log-sum-exp
@@ -79,7 +81,7 @@ struct KernelParams {
 
 // Workspace map (byte offsets), computed by the planner.
 struct WorkspaceMap {
-  size_t ctrl, tickets, claims, pdesc, ddesc, copy_bytes;  // [0, copy_bytes) is host-staged
+  size_t ctrl, tickets, claims, pdesc, pitems, ddesc, copy_bytes;  // [0, copy_bytes) is host-staged
   size_t part_o, part_lse, total;
 };
 

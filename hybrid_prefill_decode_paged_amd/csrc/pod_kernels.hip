@@ -797,10 +797,29 @@ __device__ void prefill_item_bf16(const KernelParams& P, CPTR(int32_t) dsc, int 
   const int src_k = ((lane >> 4) * 16 + kslot(w & 1, lane & 15)) * 16;
   const int src_v = lane * 16;
 
-  int lim_cur[kTp], lim_nxt[kTp];
-  // Stages tile j into buffer b (this wave: page w of the tile); returns that page's key count.
-  auto issue_tile = [&](int j, int b, int (&lim)[kTp]) -> int {
-    const int tb = kv_begin + j * kTileKeys;
+  // LDS: K buffers [2][kKBytes], then V buffers [2][kVBytes].  K(t) (tile t) lives in K buffer
+  // t&1 and is staged two tiles ahead of the QK product that reads it, V(t) in V buffer t&1 one
+  // tile ahead of its PV product, so that tile t's softmax can run beside tile t+1's QK.
+  constexpr int kVBytes = kTp * kVg * 1024;
+  auto kbuf = [&](int b) { return lds + b * kKBytes; };
+  auto vbuf = [&](int b) { return lds + 2 * kKBytes + b * kVBytes; };
+
+  // K(t): this wave stages page w of tile t.
+  auto stage_k = [&](int t) {
+    const int pi = ((kv_begin + t * kTileKeys) >> 4) + w;
+    int l = min(kPage, kv_end - pi * kPage);
+    const int pg = __builtin_amdgcn_readfirstlane(page_or_empty(btr, pi, l, P.num_pages, P.ctrl + kCStatus));
+    if (__builtin_amdgcn_readfirstlane(l) <= 0) return;    // absent page: nothing is read
+    const char* kp = slab_ptr<__bf16, D>(P.k, pg, P.hkv, head) + src_k;
+    char* dst = kbuf(t & 1) + w * 1024;
+#pragma unroll
+    for (int s = 0; s < kNs; ++s)
+      __builtin_amdgcn_global_load_lds((const void*)(kp + s * 1024),
+                                       (__attribute__((address_space(3))) void*)(dst + s * 4096), 16, 0, 0);
+  };
+  // V(t): key counts of the tile's pages into lim; this wave stages page w; returns its count.
+  auto stage_v = [&](int t, int (&lim)[kTp]) -> int {
+    const int tb = kv_begin + t * kTileKeys;
     int own = 0, own_lim = 0;
 #pragma unroll
     for (int p = 0; p < kTp; ++p) {
@@ -811,25 +830,20 @@ __device__ void prefill_item_bf16(const KernelParams& P, CPTR(int32_t) dsc, int 
       own = p == w ? pg : own;
       own_lim = p == w ? lim[p] : own_lim;
     }
-    if (own_lim <= 0) return 0;               // absent page: nothing is read
-    const char* kp = slab_ptr<__bf16, D>(P.k, own, P.hkv, head) + src_k;
+    if (own_lim <= 0) return 0;
     const char* vp = slab_ptr<__bf16, D>(P.v, own, P.hkv, head) + src_v;
-    char* dst = lds + b * kBufBytes + w * 1024;
-#pragma unroll
-    for (int s = 0; s < kNs; ++s)
-      __builtin_amdgcn_global_load_lds((const void*)(kp + s * 1024),
-                                       (__attribute__((address_space(3))) void*)(dst + s * 4096), 16, 0, 0);
+    char* dst = vbuf(t & 1) + w * 1024;
 #pragma unroll
     for (int g = 0; g < kVg; ++g)
       __builtin_amdgcn_global_load_lds((const void*)(vp + g * 1024),
-                                       (__attribute__((address_space(3))) void*)(dst + kKBytes + g * 4096), 16, 0, 0);
+                                       (__attribute__((address_space(3))) void*)(dst + g * 4096), 16, 0, 0);
     return own_lim;
   };
   // After this wave's staging loads have landed: zero the V slots of tokens >= lim of its page
   // (all of them for an absent page), so that a zero probability never meets a NaN or stale
   // value in the PV product.  Scores of those slots are masked by select.
-  auto zero_v_tail = [&](int b, int lim_own) {
-    char* vu = lds + b * kBufBytes + kKBytes + w * 1024;
+  auto zero_v_tail = [&](int t, int lim_own) {
+    char* vu = vbuf(t & 1) + w * 1024;
 #pragma unroll
     for (int g = 0; g < kVg; ++g) {
       const int h = lane & 1;                  // the chunk holds tokens 8h .. 8h+7
@@ -840,15 +854,10 @@ __device__ void prefill_item_bf16(const KernelParams& P, CPTR(int32_t) dsc, int 
   };
 
   const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};   // bf16 1.0 pairs
+  typedef f32x4 Scores[2][2][2];               // S^T blocks [nb][pp][blk]
 
-  // `masked` (wave-uniform): some key of the tile lies after a query of the wave, or some page
-  // of the tile is partial or absent.
-  auto tile_body = [&](bool masked, const char* kb, int tb, const int (&lim)[kTp]) {
-    const char* vb = kb + kKBytes;
-    // S^T blocks [nb][pp][blk]; the K operands of step k+1 are read while step k multiplies
-    // (one step of lookahead, pinned with scheduling barriers so that the reads are not all
-    // hoisted ahead of the products).
-    f32x4 S[2][2][2];
+  // QK of one staged tile; the K operands of step k+1 are read while step k multiplies.
+  auto qk = [&](const char* kb, Scores& S) {
     auto kread = [&](int k, u32x4 (&kop)[kNs]) {
       const int pp = k >> 1, blk = k & 1;
 #pragma unroll
@@ -869,66 +878,56 @@ __device__ void prefill_item_bf16(const KernelParams& P, CPTR(int32_t) dsc, int 
         for (int s = 0; s < kNs; ++s) acc = mfma_chunk(cur[s], qop[nb][s], acc, __bf16());
         S[nb][k >> 1][k & 1] = acc;
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
-    // softmax of both column blocks: maxima first (two independent reduction chains), one
-    // rescale branch, then the probabilities
-    float x[2][16];                            // x[nb][8pp + 4blk + i]: key 32pp + 8q + 4blk + i
-    float mx[2];
+  };
+  // Causal and range mask of a tile that needs one: slot (pp, blk, i) of this lane is key
+  // 32pp + 8q + 4blk + i of the tile, token 8(q&1) + 4blk + i of page 2pp + q/2, visible iff
+  // 4blk + i <= bound(pp).  A select, never a multiply.
+  auto apply_mask = [&](Scores& S, int tb, const int (&lim)[kTp]) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
+      const int rel = pos[nb] - tb - 8 * q;
 #pragma unroll
-      for (int pp = 0; pp < 2; ++pp)
+      for (int pp = 0; pp < 2; ++pp) {
+        const int lt = ((q >> 1) ? lim[2 * pp + 1] : lim[2 * pp]) - 8 * (q & 1);
+        const int bound = min(rel - 32 * pp, lt - 1);
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) x[nb][8 * pp + 4 * blk + i] = S[nb][pp][blk][i];
-      if (masked) {
-        // slot (pp, blk, i) of this lane is key 32pp + 8q + 4blk + i of the tile, token
-        // 8(q&1) + 4blk + i of page 2pp + q/2: visible iff 4blk + i <= bound(pp)
-        const int rel = pos[nb] - tb - 8 * q;
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-          const int lt = ((q >> 1) ? lim[2 * pp + 1] : lim[2 * pp]) - 8 * (q & 1);
-          const int bound = min(rel - 32 * pp, lt - 1);
-#pragma unroll
-          for (int k = 0; k < 8; ++k) x[nb][8 * pp + k] = k <= bound ? x[nb][8 * pp + k] : kNegInf;   // select, never multiply
-        }
-      }
-      float m = x[nb][0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) m = fmaxf(m, x[nb][i]);
-      mx[nb] = m;
-    }
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) mx[nb] = max_over_groups(mx[nb]) * sl2;
-    // The running max only moves when a score exceeds it by more than 2^kRescaleLog2; any
-    // reference value gives the same softmax as long as numerator and denominator share it,
-    // and the bound keeps every probability <= 2^kRescaleLog2.
-    const bool grow0 = mx[0] > m_run[0] + kRescaleLog2, grow1 = mx[1] > m_run[1] + kRescaleLog2;
-    if (__any(grow0 | grow1)) {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const bool grow = nb ? grow1 : grow0;
-        const float alpha = grow ? exp2_fast(m_run[nb] - mx[nb]) : 1.f;
-        m_run[nb] = grow ? mx[nb] : m_run[nb];
-#pragma unroll
-        for (int b = 0; b < kDb; ++b) o[nb][b] *= alpha;
-        lsum[nb] *= alpha;
+          for (int i = 0; i < 4; ++i) S[nb][pp][blk][i] = 4 * blk + i <= bound ? S[nb][pp][blk][i] : kNegInf;
       }
     }
-    u32x4 pb[2][2];
+  };
+  // Probabilities of a scored tile.  The running max only moves when a score exceeds it by more
+  // than 2^kRescaleLog2: any reference value gives the same softmax as long as numerator and
+  // denominator share it, and the bound keeps every probability <= 2^kRescaleLog2.  Returns
+  // (per lane) whether the running output must be rescaled by alpha before the PV product.
+  auto softmax = [&](Scores& S, u32x4 (&pb)[2][2], float (&alpha)[2]) -> bool {
+    bool grow_any = false;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      const float m_use = m_run[nb] == kNegInf ? 0.f : m_run[nb];
+      float m = S[nb][0][0][0];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) x[nb][i] = exp2_fast(__builtin_fmaf(x[nb][i], sl2, -m_use));
+      for (int k = 1; k < 16; ++k) m = fmaxf(m, S[nb][k >> 3][(k >> 2) & 1][k & 3]);
+      const float mx = max_over_groups(m) * sl2;
+      const bool grow = mx > m_run[nb] + kRescaleLog2;
+      alpha[nb] = grow ? exp2_fast(m_run[nb] - mx) : 1.f;
+      m_run[nb] = grow ? mx : m_run[nb];
+      grow_any = grow_any | grow;
+      const float m_use = m_run[nb] == kNegInf ? 0.f : m_run[nb];
+      float x[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) x[k] = exp2_fast(__builtin_fmaf(S[nb][k >> 3][(k >> 2) & 1][k & 3], sl2, -m_use));
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp)
-        pb[nb][pp] = u32x4{pack_bf16(x[nb][8 * pp + 0], x[nb][8 * pp + 1]), pack_bf16(x[nb][8 * pp + 2], x[nb][8 * pp + 3]),
-                           pack_bf16(x[nb][8 * pp + 4], x[nb][8 * pp + 5]), pack_bf16(x[nb][8 * pp + 6], x[nb][8 * pp + 7])};
+        pb[nb][pp] = u32x4{pack_bf16(x[8 * pp + 0], x[8 * pp + 1]), pack_bf16(x[8 * pp + 2], x[8 * pp + 3]),
+                           pack_bf16(x[8 * pp + 4], x[8 * pp + 5]), pack_bf16(x[8 * pp + 6], x[8 * pp + 7])};
     }
-    // PV: V^T operands two blocks ahead of the products that use them
+    return grow_any;
+  };
+  // PV of one staged tile: V^T operands two blocks ahead of the products that use them; the
+  // row sums come from the same P^T against a ones operand.
+  auto pv = [&](const char* vb, const u32x4 (&pb)[2][2]) {
     auto vread = [&](int k) {
       const int pp = k / kDb, b2 = k % kDb;
       return *(const u32x4*)(vb + ((b2 >> 1) * 4 + 2 * pp) * 1024 + (b2 & 1) * 512 + voff);
@@ -947,30 +946,56 @@ __device__ void prefill_item_bf16(const KernelParams& P, CPTR(int32_t) dsc, int 
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) lsum[nb] = mfma_chunk(ones, pb[nb][pp], lsum[nb], __bf16());
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
+  int lim_cur[kTp], lim_nxt[kTp];
+  // Iteration j: stage K(j+2) and V(j+1); QK(j+1) beside softmax(j) (one basic block, so the
+  // matrix and vector units overlap); PV(j).  The product for tile j+1 past the last tile reads
+  // a stale buffer and is discarded.
+  auto iteration = [&](int j, Scores& Sc, Scores& Sn) {
+    const int tb = kv_begin + j * kTileKeys;
+    const bool more1 = j + 1 < n_tiles;
+    if (j + 2 < n_tiles) stage_k(j + 2);
+    int own_nv = kPage;
+    if (more1) own_nv = stage_v(j + 1, lim_nxt);
+    if (wave_active && tb <= pmax) {          // else every key follows every query of the wave
+      const bool full = (tb + kTileKeys - 1 <= pmin) & (lim_cur[0] == kPage) & (lim_cur[1] == kPage) &
+                        (lim_cur[2] == kPage) & (lim_cur[3] == kPage);
+      if (!full) apply_mask(Sc, tb, lim_cur);
+      qk(kbuf((j + 1) & 1), Sn);
+      u32x4 pb[2][2];
+      float alpha[2];
+      if (__any(softmax(Sc, pb, alpha))) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+          for (int b = 0; b < kDb; ++b) o[nb][b] *= alpha[nb];
+          lsum[nb] *= alpha[nb];
+        }
+      }
+      pv(vbuf(j & 1), pb);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): this wave's staging loads landed
+    if (own_nv < kPage) zero_v_tail(j + 1, own_nv);
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < kTp; ++p) lim_cur[p] = lim_nxt[p];
+  };
+
   if (n_tiles > 0) {
-    const int own0 = issue_tile(0, 0, lim_cur);
-    __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): this wave's LDS loads landed
+    Scores SA, SB;
+    stage_k(0);
+    if (n_tiles > 1) stage_k(1);
+    const int own0 = stage_v(0, lim_cur);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     if (own0 < kPage) zero_v_tail(0, own0);
     __syncthreads();
-    for (int j = 0; j < n_tiles; ++j) {
-      const bool more = j + 1 < n_tiles;
-      int own_nxt = kPage;
-      if (more) own_nxt = issue_tile(j + 1, (j + 1) & 1, lim_nxt);
-      const int tb = kv_begin + j * kTileKeys;
-      if (wave_active && tb <= pmax) {        // else every key follows every query of the wave
-        const bool full = (tb + kTileKeys - 1 <= pmin) & (lim_cur[0] == kPage) & (lim_cur[1] == kPage) &
-                          (lim_cur[2] == kPage) & (lim_cur[3] == kPage);
-        tile_body(!full, lds + (j & 1) * kBufBytes, tb, lim_cur);
-      }
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-      if (own_nxt < kPage) zero_v_tail((j + 1) & 1, own_nxt);
-      __syncthreads();
-#pragma unroll
-      for (int p = 0; p < kTp; ++p) lim_cur[p] = lim_nxt[p];
+    if (wave_active && kv_begin <= pmax) qk(kbuf(0), SA);
+    __syncthreads();                           // K buffer 0 is restaged by the first iteration
+    for (int j = 0; j < n_tiles; j += 2) {
+      iteration(j, SA, SB);
+      if (j + 1 < n_tiles) iteration(j + 1, SB, SA);
     }
   }
 
@@ -1004,15 +1029,12 @@ __device__ void prefill_item_bf16(const KernelParams& P, CPTR(int32_t) dsc, int 
 // and loads and measured 20-30% slower on the prefill share than one combine launch.
 template <typename T, int D>
 __device__ void run_prefill_item(const KernelParams& P, int item, char* lds) {
-  CPTR(int32_t) descs = (CPTR(int32_t))P.pdesc;
-  const int di = find_desc(descs, P.n_pdesc, kDItemBegin, item);
-  CPTR(int32_t) dsc = descs + (size_t)di * kDescInts;
-  const int ns = dsc[kDNSplit];
-  const int local = item - dsc[kDItemBegin];
-  const int split = local / P.hkv, head = local - split * P.hkv;
+  CPTR(int32_t) e = (CPTR(int32_t))P.pitems + kPItemHeader + 2 * (size_t)item;
+  CPTR(int32_t) dsc = (CPTR(int32_t))P.pdesc + (size_t)e[0] * kDescInts;
+  const int split = e[1] >> 16, head = e[1] & 0xFFFF;
   if constexpr (sizeof(T) == 2) prefill_item_bf16<D>(P, dsc, head, split, lds);
   else prefill_item<T, D>(P, dsc, head, split, lds);
-  __syncthreads();   // LDS and the flag are reused by the next item
+  __syncthreads();   // LDS is reused by the next item
 }
 
 __device__ __forceinline__ int cu_slot() {
@@ -1029,16 +1051,18 @@ __device__ __forceinline__ void note_claim(const KernelParams& P, int kind, int 
   }
 }
 
-// Prefill claim for a workgroup on XCC `xcc`: queue x holds items x, x+8, x+16, ... (the
-// order in which the hardware spreads a plain grid over the 8 dies), so the tiles that share a
-// KV head's keys run on one die and reuse its L2; a workgroup whose queue is drained takes
-// work from the other dies' queues.  Returns n_pf_items when every queue is drained.
+// Prefill claim for a workgroup on XCC `xcc`: queue x is the item range [hdr[x], hdr[x+1]) of
+// the item table, whole groups of tiles that read the same keys of the same KV head, so such
+// tiles run on one die and reuse its L2; a workgroup whose queue is drained takes work from
+// the other dies' queues.  Returns n_pf_items when every queue is drained.
 __device__ __forceinline__ int claim_prefill(const KernelParams& P, int xcc) {
+  CPTR(int32_t) hdr = (CPTR(int32_t))P.pitems;
   for (int k = 0; k < kXcds; ++k) {
     const int x = (xcc + k) & (kXcds - 1);
+    const int b = hdr[x], n = hdr[x + 1] - b;
+    if (n <= 0) continue;
     const int c = atomicAdd(P.ctrl + kCQueuePrefillXcd + 32 * x, 1);
-    const long item = (long)c * kXcds + x;
-    if (item < P.n_pf_items) return (int)item;
+    if (c < n) return b + c;
   }
   return P.n_pf_items;
 }
@@ -1153,8 +1177,16 @@ __global__ __launch_bounds__(kThreads, 2) void pod_fused_kernel(KernelParams P) 
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 2) void pod_prefill_kernel(KernelParams P) {
   __shared__ __attribute__((aligned(16))) char lds[Geo<T, D>::kPrefillLds];
-  if (threadIdx.x == 0) note_claim(P, 0, blockIdx.x, cu_slot());
-  run_prefill_item<T, D>(P, blockIdx.x, lds);
+  __shared__ int s_item;
+  // one item per workgroup (the grid has n_pf_items workgroups), taken from this die's queue
+  if (threadIdx.x == 0) {
+    const int cu = cu_slot();
+    s_item = claim_prefill(P, cu >> 7);
+    if (s_item < P.n_pf_items) note_claim(P, 0, s_item, cu);
+  }
+  __syncthreads();
+  const int item = s_item;
+  if (item < P.n_pf_items) run_prefill_item<T, D>(P, item, lds);
 }
 
 // Separate decode kernel: wave w of workgroup b takes decode item 4b + w.

@@ -191,8 +191,10 @@ pod_attn_status pod_attn_read_device_status(pod_attn_handle* h, const void* work
 /* Host-only (no GPU needed): plan a batch for a device with num_cus compute units and
  * wgs_per_cu persistent workgroups, and return the work items as 16 int32 each
  * {seq, q_row, n_q, q_pos, kv_head, kv_begin, kv_end, group, split, partial_slot, kind
- * (0 prefill, 1 decode), 0...}, prefill items first.  *n_items receives the count; at most
- * items_cap items are written.  stats (may be NULL) receives the planning diagnostics. */
+ * (0 prefill, 1 decode), queue, 0...}, prefill items first, in the order the kernels index
+ * them.  queue is the per-XCD claim queue (0..7) of a prefill item and -1 for decode.
+ * *n_items receives the count; at most items_cap items are written.  stats (may be NULL)
+ * receives the planning diagnostics. */
 pod_attn_status pod_attn_plan_inspect(const pod_attn_config* cfg, const pod_attn_batch* batch,
                                       int num_cus, int wgs_per_cu, int32_t* items,
                                       int items_cap, int* n_items, pod_attn_stats* stats);

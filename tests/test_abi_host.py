@@ -228,3 +228,29 @@ def test_claim_policy_terminates_and_claims_each_item_once(n_pf, n_dc):
     assert sorted(claimed[1]) == list(range(n_dc))
     assert all(a == 0 for a in active)
     assert np.isfinite(t)
+
+
+@pytest.mark.parametrize("idx", [2, 3, 4, 5])
+def test_prefill_queues_hold_whole_key_range_groups(idx):
+    """Prefill items are dealt to the 8 per-XCD claim queues in whole groups (same chunk, KV
+    head and key range), the queues are contiguous in item order, the tiles of a chunk share
+    their split boundaries, and no queue carries much more key work than the average."""
+    spec = gen.config_spec(idx)
+    cfg = B.make_config(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.dtype)
+    items, _ = B.plan_inspect(cfg, _meta(spec), 256, 2)
+    pf = items[items[:, 10] == 0]
+    q = pf[:, 11]
+    assert np.all(np.diff(q) >= 0) and q.min() >= 0 and q.max() < 8
+    owner, work = {}, np.zeros(8)
+    bounds = {}
+    for it in pf:
+        seq, n_q, head, a, z, queue = int(it[0]), int(it[2]), int(it[4]), int(it[5]), int(it[6]), int(it[11])
+        key = (seq, head, a)
+        assert owner.setdefault(key, queue) == queue, "a key-range group spans two queues"
+        bounds.setdefault(seq, set()).add(a)
+        work[queue] += (z - a) * n_q
+    for seq, starts in bounds.items():
+        st = sorted(starts)
+        if len(st) > 1:
+            assert len({y - x for x, y in zip(st[:-1], st[1:])}) == 1, "tiles of a chunk share split boundaries"
+    assert work.max() <= 1.35 * work.mean(), work
