@@ -68,6 +68,7 @@ struct pod_attn_handle {
   hipEvent_t prof_start = nullptr, prof_end = nullptr;   // one-shot profiling events
   int decode_block_claim = 1;
   int prefill_wgs_override = 0;     // POD_ATTN_PREFILL_WGS
+  int prefill_per_cu_override = 0;  // POD_ATTN_PREFILL_PER_CU
 };
 
 extern "C" {
@@ -108,6 +109,7 @@ pod_attn_status pod_attn_create(const pod_attn_config* cfg, pod_attn_handle** ou
   if (c.prefill_split_cap == 0) h->cfg.prefill_split_cap = std::max(0, env_int("POD_ATTN_PREFILL_SPLIT_CAP", 0));
   h->decode_block_claim = env_int("POD_ATTN_DECODE_BLOCK_CLAIM", 1);
   h->prefill_wgs_override = env_int("POD_ATTN_PREFILL_WGS", 0);
+  h->prefill_per_cu_override = env_int("POD_ATTN_PREFILL_PER_CU", 0);
   if (const char* m = std::getenv("POD_ATTN_MODE")) {
     if (!std::strcmp(m, "fused")) h->mode_env = POD_ATTN_MODE_FUSED;
     else if (!std::strcmp(m, "separate")) h->mode_env = POD_ATTN_MODE_SEPARATE;
@@ -169,16 +171,21 @@ static hipError_t launch(const void* fn, int grid, KernelParams& p, hipStream_t 
   return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
 }
 
-// Prefill-role workgroups allowed while decode work remains (fused mode): three quarters of
-// the grid.  Prefill tiles run for tens to hundreds of microseconds each, so starting them
-// early on most workgroups keeps them from forming the tail, while the remaining quarter (plus
-// every workgroup that finds no prefill tile left) keeps decode loads in flight; measured on
-// the five workloads, smaller budgets lost 5-15% and larger ones serialise the two kinds.
+// Prefill-role workgroups allowed while decode work remains (fused mode).  The binding limit is
+// the per-CU cap (one prefill workgroup per CU, so every CU keeps a decode workgroup streaming
+// beside its matrix work); the device-wide budget is the whole grid unless overridden.  Measured
+// on the four bf16 workloads (interleaved A/B runs): one per CU beat three quarters of the grid
+// with two per CU by 1-8%, and adding a device-wide budget of one per CU on top only lost (its
+// counter rejects transiently).
 static int prefill_budget(const pod_attn_handle* h, const Plan& p) {
   const int total = h->num_cus * h->wgs_per_cu;
   if (h->prefill_wgs_override > 0) return std::min(h->prefill_wgs_override, total);
-  if (p.n_pf_items == 0 || p.n_dc_items == 0) return total;
-  return std::max(1, (3 * total) / 4);
+  (void)p;
+  return total;
+}
+static int prefill_per_cu(const pod_attn_handle* h) {
+  if (h->prefill_per_cu_override > 0) return std::min(h->prefill_per_cu_override, h->wgs_per_cu);
+  return 1;
 }
 
 // Combine groups [g0, g1), whose groups have at most max_cols columns: one workgroup per
@@ -265,7 +272,7 @@ pod_attn_status pod_attn_run(pod_attn_handle* h, const void* q, const void* k_ca
   kp.hq = h->cfg.hq; kp.hkv = h->cfg.hkv; kp.group = h->cfg.group();
   kp.bt_stride = b->block_table_stride; kp.num_pages = b->num_pages_in_pool;
   kp.scale_log2 = h->cfg.scale * 1.4426950408889634f;
-  kp.prefill_cap_per_cu = h->wgs_per_cu;
+  kp.prefill_cap_per_cu = prefill_per_cu(h);
   kp.prefill_wg_budget = prefill_budget(h, p);
   kp.decode_block_claim = h->decode_block_claim;
 
