@@ -284,6 +284,8 @@ pod_attn_status pod_attn_run(pod_attn_handle* h, const void* q, const void* k_ca
     kp.inline_combine = 1;                    // decode splits merge in-kernel
     grid = h->num_cus * h->wgs_per_cu;
     POD_HIP(launch(h->ks.fused, grid, kp, stream));
+    if (prof_end) POD_HIP(hipEventRecord(prof_end, stream));   // the fused kernel alone
+    prof_end = nullptr;
     if (p.n_pf_groups) POD_HIP(launch_combine(h, kp, 0, p.n_pf_groups, p.tile_cols, stream));
   } else if (mode == POD_ATTN_MODE_SEPARATE) {
     kp.inline_combine = 0;

@@ -247,28 +247,29 @@ __device__ __forceinline__ void rescale(f32x4 (&o)[N], float alpha) {
 // device-scope (write-through / L2-bypassing) accesses: the writer's stores are complete once
 // its vmcnt drains, so no cache-wide write-back is needed before the ticket is taken, and the
 // merging wave never sees a stale line from its own L2.
-__device__ __forceinline__ void store_part4(float* dst, f32x4 v, bool coherent) {
-  if (coherent) {
-    __hip_atomic_store(dst + 0, v.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(dst + 1, v.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(dst + 2, v.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(dst + 3, v.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  } else {
-    *(f32x4*)dst = v;
-  }
-}
+__device__ __forceinline__ void store_part4(float* dst, f32x4 v) { *(f32x4*)dst = v; }
 __device__ __forceinline__ void store_part1(float* dst, float v, bool coherent) {
   if (coherent) __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   else *dst = v;
 }
-__device__ __forceinline__ f32x4 load_part4_coherent(const float* src) {
-  return f32x4{__hip_atomic_load(src + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-               __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-               __hip_atomic_load(src + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-               __hip_atomic_load(src + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)};
-}
 __device__ __forceinline__ float load_part1_coherent(const float* src) {
   return __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 16-byte device-coherent accesses to a run of partials, through a buffer resource over it:
+// one 128-bit store or load per lane with the sc1 cache policy (written through past the
+// writer's L2, read past the reader's), where 32-bit atomics would take four accesses and
+// write partial memory lines four times.  Offsets are bytes from the resource base; the
+// hardware drops accesses outside [0, bytes).
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+constexpr int kCachePolicyCoherent = 16;   // sc1
+__device__ __forceinline__ BufRsrc part_rsrc(const float* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, bytes, 0x00020000);   // 32-bit data format
+}
+__device__ __forceinline__ void store_coherent4(BufRsrc r, int off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCachePolicyCoherent);
+}
+__device__ __forceinline__ f32x4 load_coherent4(BufRsrc r, int off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCachePolicyCoherent));
 }
 
 // Arrival of one split: every store of the calling wave has completed (vmcnt 0); one lane takes
@@ -318,21 +319,22 @@ __device__ void combine_block_wave(const KernelParams& P, CPTR(int32_t) dsc, int
     for (int sp = 0; sp < ns; ++sp) sw[lane * ns + sp] *= inv;
   }
   wave_lds_sync();
-  const size_t sstride = (size_t)ncols * D;             // floats between consecutive splits
+  const int sstride = ncols * D * 4;                   // bytes between consecutive splits
+  const BufRsrc grp = part_rsrc(P.part_o + base * D, ns * sstride);
   for (int pidx = lane; pidx < nc * kQ; pidx += 64) {
     const int c = pidx / kQ, d4 = pidx - c * kQ;
-    const float* src = P.part_o + (base + c0 + c) * D + 4 * d4;
+    const int src = ((c0 + c) * D + 4 * d4) * 4;
     const float* wc = sw + c * ns;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     int sp = 0;
     for (; sp + 8 <= ns; sp += 8) {
       f32x4 v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = load_part4_coherent(src + (size_t)(sp + u) * sstride);
+      for (int u = 0; u < 8; ++u) v[u] = load_coherent4(grp, src + (sp + u) * sstride);
 #pragma unroll
       for (int u = 0; u < 8; ++u) acc += wc[sp + u] * v[u];
     }
-    for (; sp < ns; ++sp) acc += wc[sp] * load_part4_coherent(src + (size_t)sp * sstride);
+    for (; sp < ns; ++sp) acc += wc[sp] * load_coherent4(grp, src + sp * sstride);
     const int cc = c0 + c, qi = cc / G, hh = cc - qi * G;
     T* dst = (T*)P.out + ((size_t)(q_row + qi) * P.hq + head * G + hh) * D + 4 * d4;
     store4<T>(dst, acc);
@@ -465,12 +467,18 @@ __device__ void decode_wave_item(const KernelParams& P, int item, float* sw) {
 #pragma unroll
       for (int b = 0; b < Gm::kDb; ++b) store4<T>(dst + 16 * b, o[b] * inv);
     } else {
-      const size_t slot = (size_t)dsc[kDPartBase] + ((size_t)head * ns + split) * G + n;
-      float* dst = P.part_o + slot * D + 4 * q;
+      const size_t run = (size_t)dsc[kDPartBase] + ((size_t)head * ns + split) * G;   // this split's G slots
       const bool coh = P.inline_combine != 0;
+      if (coh) {
+        const BufRsrc r = part_rsrc(P.part_o + run * D, G * D * 4);
 #pragma unroll
-      for (int b = 0; b < Gm::kDb; ++b) store_part4(dst + 16 * b, o[b] * inv, coh);
-      if (q == 0) store_part1(P.part_lse + slot, l_tot > 0.f ? m_run + __log2f(l_tot) : kNegInf, coh);
+        for (int b = 0; b < Gm::kDb; ++b) store_coherent4(r, (n * D + 4 * q + 16 * b) * 4, o[b] * inv);
+      } else {
+        float* dst = P.part_o + (run + n) * D + 4 * q;
+#pragma unroll
+        for (int b = 0; b < Gm::kDb; ++b) store_part4(dst + 16 * b, o[b] * inv);
+      }
+      if (q == 0) store_part1(P.part_lse + run + n, l_tot > 0.f ? m_run + __log2f(l_tot) : kNegInf, coh);
     }
   }
   // Last arriver combines ([POD], "Virtual CTAs and per-SM balance": exact synchronisation
@@ -689,10 +697,9 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
     } else {
       const size_t slot = (size_t)dsc[kDPartBase] + ((size_t)head * ns + split) * ncols + c;
       float* dst = P.part_o + slot * D + 4 * q;
-      const bool coh = false;                  // merged by the combine kernel
 #pragma unroll
-      for (int b2 = 0; b2 < Gm::kDb; ++b2) store_part4(dst + 16 * b2, o[nb][b2] * inv, coh);
-      if (q == 0) store_part1(P.part_lse + slot, l_tot > 0.f ? m_run[nb] + __log2f(l_tot) : kNegInf, coh);
+      for (int b2 = 0; b2 < Gm::kDb; ++b2) store_part4(dst + 16 * b2, o[nb][b2] * inv);   // merged by the combine kernel
+      if (q == 0) P.part_lse[slot] = l_tot > 0.f ? m_run[nb] + __log2f(l_tot) : kNegInf;
     }
   }
 }
@@ -1013,10 +1020,9 @@ __device__ void prefill_item_bf16(const KernelParams& P, CPTR(int32_t) dsc, int 
     } else {
       const size_t slot = (size_t)dsc[kDPartBase] + ((size_t)head * ns + split) * ncols + c;
       float* dst = P.part_o + slot * D + 4 * q;
-      const bool coh = false;                  // merged by the combine kernel
 #pragma unroll
-      for (int b2 = 0; b2 < kDb; ++b2) store_part4(dst + 16 * b2, o[nb][b2] * inv, coh);
-      if (q == 0) store_part1(P.part_lse + slot, l_tot > 0.f ? m_run[nb] + __log2f(l_tot) : kNegInf, coh);
+      for (int b2 = 0; b2 < kDb; ++b2) store_part4(dst + 16 * b2, o[nb][b2] * inv);   // merged by the combine kernel
+      if (q == 0) P.part_lse[slot] = l_tot > 0.f ? m_run[nb] + __log2f(l_tot) : kNegInf;
     }
   }
 }

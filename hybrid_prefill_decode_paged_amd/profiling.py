@@ -3,6 +3,10 @@
     python -m hybrid_prefill_decode_paged_amd.profiling stats  <kernel_stats.csv> <out.md> <command...>
     python -m hybrid_prefill_decode_paged_amd.profiling traffic <copy_fetch_dir> <copy_write_dir> \
         <fetch_dir> <write_dir> <kernel-substring> <out.json> <command...>
+    python -m hybrid_prefill_decode_paged_amd.profiling pmc <out.md> <title> <command> <dir>...
+
+pmc: per-kernel mean of every counter over its dispatches, for each counter-collection
+directory given (one rocprofv3 --pmc pass each), as one markdown table.
 
 Traffic: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the kernel, each scaled by the ratio of
 the true byte count to what the same counter reads for a plain 1 GiB device copy
@@ -21,7 +25,7 @@ import statistics
 import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ("csrc/pod_kernels.hip", "csrc/pod_internal.h", "csrc/plan.cpp")
+KERNEL_SOURCES = ("csrc/pod_kernels.hip", "csrc/pod_internal.h", "csrc/plan.cpp", "csrc/pod_api.cpp")
 COPY_BYTES = 1 << 30
 
 
@@ -78,9 +82,29 @@ def stats_summary(path: str, command: str) -> str:
     return "\n".join(out) + "\n"
 
 
+def pmc_summary(dirs, title: str, command: str) -> str:
+    rows = {}
+    for d in dirs:
+        for r in csv.DictReader(open(_counter_csv(d))):
+            name = r["Kernel_Name"].split("(")[0]
+            if "pod_" not in name:
+                continue
+            rows.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    counters = sorted({c for v in rows.values() for c in v})
+    out = [f"# {title}", "", f"Command: `{command}`", "",
+           "Per-dispatch mean of each counter (summed over the device by rocprofv3), dispatches in brackets.", "",
+           "| kernel | " + " | ".join(counters) + " |", "|---" * (len(counters) + 1) + "|"]
+    for name, d in rows.items():
+        cells = [f"{statistics.mean(d[c]):.4g} ({len(d[c])})" if c in d else "" for c in counters]
+        out.append(f"| {name[:70]} | " + " | ".join(cells) + " |")
+    return "\n".join(out) + "\n"
+
+
 def main(argv):
     if argv[0] == "stats":
         open(argv[2], "w").write(stats_summary(argv[1], " ".join(argv[3:])))
+    elif argv[0] == "pmc":
+        open(argv[1], "w").write(pmc_summary(argv[4:], argv[2], argv[3]))
     elif argv[0] == "traffic":
         rec = traffic_record(*argv[1:6], " ".join(argv[7:]))
         json.dump(rec, open(argv[6], "w"), indent=1)
