@@ -20,6 +20,7 @@ BF16, FP32 = 0, 1
 MODE_FUSED, MODE_SEPARATE, MODE_STREAMS = 0, 1, 2
 MODES = {"fused": MODE_FUSED, "separate": MODE_SEPARATE, "streams": MODE_STREAMS}
 FLAG_DEBUG_CLAIMS = 1
+FLAG_TRACE = 2
 DEVICE_ERR_BAD_PAGE = 1
 
 STATUS = {0: "OK", -1: "ERR_INVALID_ARG", -2: "ERR_UNSUPPORTED", -3: "ERR_WORKSPACE",
@@ -78,12 +79,13 @@ def load(path: str = LIB_PATH):
     lib.pod_attn_read_device_status.argtypes = [VP, VP, VP, P(C.c_int32), P(C.c_int32), I, P(I),
                                                 P(C.c_int32), P(C.c_int32), I]
     lib.pod_attn_plan_inspect.argtypes = [P(Config), P(Batch), I, I, P(C.c_int32), I, P(I), P(Stats)]
+    lib.pod_attn_read_trace.argtypes = [VP, VP, VP, P(C.c_uint32), I, P(I)]
     lib.pod_attn_set_kernel_events.argtypes = [VP, VP, VP]
     lib.pod_attn_last_error.restype = C.c_char_p
     lib.pod_attn_destroy.argtypes = [VP]
     lib.pod_attn_destroy.restype = None
     for name in ("pod_attn_create", "pod_attn_workspace_size", "pod_attn_run", "pod_attn_get_stats",
-                 "pod_attn_gather_kv", "pod_attn_read_device_status", "pod_attn_plan_inspect",
+                 "pod_attn_gather_kv", "pod_attn_read_device_status", "pod_attn_plan_inspect", "pod_attn_read_trace",
                  "pod_attn_set_kernel_events"):
         getattr(lib, name).restype = C.c_int
     _lib = lib
@@ -228,6 +230,16 @@ class PodAttention:
         _check(self.lib.pod_attn_gather_kv(self.h, _ptr(cache), int(which), _ptr(block_tables), int(seq),
                                            int(ctx), C.byref(meta.c), _ptr(out), _stream_handle(stream)))
         return out
+
+    def read_trace(self, workspace, stream=None) -> np.ndarray:
+        """Per-item timeline of the last run (handle created with FLAG_TRACE): uint32 [n, 4] rows
+        {start, end, cu_slot, kind} (100 MHz clock), prefill items first."""
+        n = C.c_int(0)
+        _check(self.lib.pod_attn_read_trace(self.h, _ptr(workspace), _stream_handle(stream), None, 0, C.byref(n)))
+        rec = np.zeros((max(1, n.value), 4), dtype=np.uint32)
+        _check(self.lib.pod_attn_read_trace(self.h, _ptr(workspace), _stream_handle(stream),
+                                            rec.ctypes.data_as(C.POINTER(C.c_uint32)), n.value, C.byref(n)))
+        return rec[: n.value]
 
     def read_device_status(self, workspace, n_items_cap: int = 0, cu_cap: int = 0, stream=None):
         """(status_word, claims[n] or None, (prefill_per_cu, decode_per_cu) or None)."""

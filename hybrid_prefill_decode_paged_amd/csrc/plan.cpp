@@ -236,6 +236,9 @@ pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus
   m.copy_bytes = off;
   m.part_o = off; off = align_up(off + sizeof(float) * (size_t)p.n_slots * c.d, 256);
   m.part_lse = off; off = align_up(off + sizeof(float) * (size_t)std::max(1, p.n_slots), 256);
+  m.trace = off;
+  if (c.flags & POD_ATTN_FLAG_TRACE)
+    off = align_up(off + 4 * sizeof(uint32_t) * (size_t)std::max(1, p.n_pf_items + p.n_dc_items), 256);
   m.total = off;
   p.map = m;
   *out = std::move(p);

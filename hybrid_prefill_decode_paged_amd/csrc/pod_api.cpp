@@ -261,6 +261,7 @@ pod_attn_status pod_attn_run(pod_attn_handle* h, const void* q, const void* k_ca
   kp.ctrl = (int32_t*)(ws + p.map.ctrl);
   kp.tickets = (int32_t*)(ws + p.map.tickets);
   kp.claims = (h->cfg.flags & POD_ATTN_FLAG_DEBUG_CLAIMS) ? (int32_t*)(ws + p.map.claims) : nullptr;
+  kp.trace = (h->cfg.flags & POD_ATTN_FLAG_TRACE) ? (uint32_t*)(ws + p.map.trace) : nullptr;
   kp.pdesc = (const int32_t*)(ws + p.map.pdesc);
   kp.pitems = (const int32_t*)(ws + p.map.pitems);
   kp.ddesc = (const int32_t*)(ws + p.map.ddesc);
@@ -376,6 +377,19 @@ pod_attn_status pod_attn_read_device_status(pod_attn_handle* h, const void* work
   const int m = std::min(cu_cap, (int)kCuSlots);
   if (pf_cu && m > 0) POD_HIP(hipMemcpy(pf_cu, ws + p.map.ctrl + 4 * kCClaimsPrefillCu, 4 * (size_t)m, hipMemcpyDeviceToHost));
   if (dc_cu && m > 0) POD_HIP(hipMemcpy(dc_cu, ws + p.map.ctrl + 4 * kCClaimsDecodeCu, 4 * (size_t)m, hipMemcpyDeviceToHost));
+  return POD_ATTN_OK;
+}
+
+pod_attn_status pod_attn_read_trace(pod_attn_handle* h, const void* workspace, void* stream, uint32_t* records,
+                                    int cap, int* n_items) {
+  if (!h || !workspace) return fail(POD_ATTN_ERR_INVALID_ARG, "null handle or workspace");
+  if (!(h->cfg.flags & POD_ATTN_FLAG_TRACE)) return fail(POD_ATTN_ERR_INVALID_ARG, "handle was created without POD_ATTN_FLAG_TRACE");
+  POD_HIP(hipStreamSynchronize((hipStream_t)stream));
+  const Plan& p = h->last_plan;
+  const int n = p.n_pf_items + p.n_dc_items;
+  if (n_items) *n_items = n;
+  if (records && cap > 0)
+    POD_HIP(hipMemcpy(records, (const uint8_t*)workspace + p.map.trace, 16 * (size_t)std::min(n, cap), hipMemcpyDeviceToHost));
   return POD_ATTN_OK;
 }
 

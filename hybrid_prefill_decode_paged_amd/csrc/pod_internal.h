@@ -61,6 +61,7 @@ struct KernelParams {
   int32_t* ctrl;
   int32_t* tickets;          // [n_groups]
   int32_t* claims;           // [n_pf_items + n_dc_items] or null
+  uint32_t* trace;           // [n_pf_items + n_dc_items][4] timeline records, or null
   const int32_t* pdesc;      // prefill descriptors
   const int32_t* pitems;     // prefill item table (header, then (desc, split << 16 | head) per item)
   const int32_t* ddesc;      // decode descriptors
@@ -82,7 +83,7 @@ struct KernelParams {
 // Workspace map (byte offsets), computed by the planner.
 struct WorkspaceMap {
   size_t ctrl, tickets, claims, pdesc, pitems, ddesc, copy_bytes;  // [0, copy_bytes) is host-staged
-  size_t part_o, part_lse, total;
+  size_t part_o, part_lse, trace, total;
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }

@@ -1056,6 +1056,17 @@ __device__ __forceinline__ void note_claim(const KernelParams& P, int kind, int 
   }
 }
 
+// Timeline record of one work item (POD_ATTN_FLAG_TRACE): low 32 bits of the 100 MHz constant
+// clock at the item's start and end, the CU slot that ran it, and its kind; one lane writes it.
+__device__ __forceinline__ uint32_t clock100() { return (uint32_t)__builtin_amdgcn_s_memrealtime(); }
+__device__ __forceinline__ uint32_t trace_start(const KernelParams& P) { return P.trace ? clock100() : 0u; }
+__device__ __forceinline__ void trace_item(const KernelParams& P, int kind, int item, uint32_t t0, int cu) {
+  if (P.trace) {
+    const uint32_t t1 = clock100();
+    *(u32x4*)(P.trace + 4 * ((size_t)(kind == 0 ? 0 : P.n_pf_items) + item)) = u32x4{t0, t1, (uint32_t)cu, (uint32_t)kind};
+  }
+}
+
 // Prefill claim for a workgroup on XCC `xcc`: queue x is the item range [hdr[x], hdr[x+1]) of
 // the item table, whole groups of tiles that read the same keys of the same KV head, so such
 // tiles run on one die and reuse its L2; a workgroup whose queue is drained takes work from
@@ -1086,20 +1097,21 @@ __device__ void decode_wave_stream(const KernelParams& P, int cu, float* sw) {
     item = __builtin_amdgcn_readfirstlane(item);
     if (item >= P.n_dc_items) break;
     if (lane == 0) note_claim(P, 1, item, cu);
+    const uint32_t t0 = trace_start(P);
     decode_wave_item<T, D>(P, item, sw);
+    if (lane == 0) trace_item(P, 1, item, t0, cu);
   }
 }
 
 // ------------------------------------------------------------------ kernels
-// Fused persistent kernel: every workgroup loops, taking a role and claiming work of that kind
-// through one atomic counter per kind.  While decode work remains, at most `prefill_wg_budget`
-// workgroups device-wide and `prefill_cap_per_cu` per CU hold the prefill role: the budget is
-// sized on the host so that the prefill share finishes about when the HBM-bound decode stream
-// does, and the rest of the machine keeps enough decode loads in flight to fill HBM ([POD],
-// "Virtual CTAs and per-SM balance": the scheduler places complementary work per SM).  A
-// prefill-role workgroup works on one tile at a time with all four waves; a decode-role
-// workgroup's four waves stream four adjacent decode items.  A workgroup whose kind is drained
-// takes the other kind; the kernel ends when both are drained.
+// Fused persistent kernel: every workgroup loops, taking a role and claiming work of that kind.
+// While decode work remains, at most `prefill_cap_per_cu` workgroups per CU (one by default) and
+// `prefill_wg_budget` device-wide hold the prefill role, so every CU keeps decode loads in
+// flight beside its matrix work ([POD], "Virtual CTAs and per-SM balance": the scheduler places
+// complementary work per SM).  A prefill-role workgroup works on one tile at a time with all
+// four waves, taking tiles from its die's queue; a decode-role workgroup's four waves stream four
+// adjacent decode items.  A workgroup whose kind is drained takes the other kind; the kernel
+// ends when both are drained.
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 2) void pod_fused_kernel(KernelParams P) {
   __shared__ __attribute__((aligned(16))) char lds[Geo<T, D>::kFusedLds];
@@ -1152,7 +1164,9 @@ __global__ __launch_bounds__(kThreads, 2) void pod_fused_kernel(KernelParams P) 
           const int item = base + wave_index();
           if (item < P.n_dc_items) {
             if ((tid & 63) == 0) note_claim(P, 1, item, cu);
+            const uint32_t t0 = trace_start(P);
             decode_wave_item<T, D>(P, item, sw);
+            if ((tid & 63) == 0) trace_item(P, 1, item, t0, cu);
           }
         }
       } else {
@@ -1164,7 +1178,9 @@ __global__ __launch_bounds__(kThreads, 2) void pod_fused_kernel(KernelParams P) 
     }
     while (item < P.n_pf_items) {
       if (tid == 0) note_claim(P, 0, item, cu);
+      const uint32_t t0 = trace_start(P);
       run_prefill_item<T, D>(P, item, lds);   // ends with a barrier
+      if (tid == 0) trace_item(P, 0, item, t0, cu);
       if (tid == 0) s_item = claim_prefill(P, xcc);   // claim once idle
       __syncthreads();
       item = s_item;
@@ -1184,14 +1200,17 @@ __global__ __launch_bounds__(kThreads, 2) void pod_prefill_kernel(KernelParams P
   __shared__ __attribute__((aligned(16))) char lds[Geo<T, D>::kPrefillLds];
   __shared__ int s_item;
   // one item per workgroup (the grid has n_pf_items workgroups), taken from this die's queue
+  const int cu = cu_slot();
   if (threadIdx.x == 0) {
-    const int cu = cu_slot();
     s_item = claim_prefill(P, cu >> 7);
     if (s_item < P.n_pf_items) note_claim(P, 0, s_item, cu);
   }
   __syncthreads();
   const int item = s_item;
-  if (item < P.n_pf_items) run_prefill_item<T, D>(P, item, lds);
+  if (item >= P.n_pf_items) return;
+  const uint32_t t0 = trace_start(P);
+  run_prefill_item<T, D>(P, item, lds);
+  if (threadIdx.x == 0) trace_item(P, 0, item, t0, cu);
 }
 
 // Separate decode kernel: wave w of workgroup b takes decode item 4b + w.
@@ -1199,8 +1218,11 @@ template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 2) void pod_decode_kernel(KernelParams P) {
   const int item = (int)blockIdx.x * kWaves + wave_index();
   if (item >= P.n_dc_items) return;
-  if ((threadIdx.x & 63) == 0) note_claim(P, 1, item, cu_slot());
+  const int cu = cu_slot();
+  if ((threadIdx.x & 63) == 0) note_claim(P, 1, item, cu);
+  const uint32_t t0 = trace_start(P);
   decode_wave_item<T, D>(P, item, nullptr);   // no in-kernel combine here: the combine kernel merges
+  if ((threadIdx.x & 63) == 0) trace_item(P, 1, item, t0, cu);
 }
 
 // Separate-mode combine: one workgroup per (group, block of 16 columns); the split weights of

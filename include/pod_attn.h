@@ -93,6 +93,7 @@ typedef enum {
 
 /* Flags */
 #define POD_ATTN_FLAG_DEBUG_CLAIMS 1   /* count every work-item claim in the workspace (tests) */
+#define POD_ATTN_FLAG_TRACE 2          /* record a timeline entry per work item (pod_attn_read_trace) */
 
 typedef struct pod_attn_config {
   int num_q_heads;          /* Hq >= 1                                                        */
@@ -187,6 +188,17 @@ pod_attn_status pod_attn_read_device_status(pod_attn_handle* h, const void* work
                                             int32_t* claims, int claims_cap, int* n_items,
                                             int32_t* prefill_claims_per_cu,
                                             int32_t* decode_claims_per_cu, int cu_cap);
+
+/* Debug/profiling: synchronise `stream` and copy the per-item timeline of the last run, for a
+ * handle created with POD_ATTN_FLAG_TRACE (else POD_ATTN_ERR_INVALID_ARG).  One record of 4
+ * uint32 per work item, prefill items first then decode items (the order of
+ * pod_attn_plan_inspect): {start, end, cu_slot, kind}, start/end being the low 32 bits of the
+ * device's 100 MHz constant clock when the item began and ended, cu_slot = XCC_ID*128 +
+ * SE*32 + SH*16 + CU of the compute unit that ran it, kind 0 prefill / 1 decode.  At most cap
+ * records are written; *n_items receives the item count.  The workspace must be the one
+ * passed to that run; tracing adds one 16-byte store per item. */
+pod_attn_status pod_attn_read_trace(pod_attn_handle* h, const void* workspace, void* stream,
+                                    uint32_t* records, int cap, int* n_items);
 
 /* Host-only (no GPU needed): plan a batch for a device with num_cus compute units and
  * wgs_per_cu persistent workgroups, and return the work items as 16 int32 each

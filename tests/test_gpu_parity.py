@@ -147,6 +147,37 @@ def test_every_item_claimed_exactly_once(mode):
     assert pf.sum() == st["num_prefill_items"] and dc.sum() == st["num_decode_items"]
 
 
+@pytest.mark.parametrize("mode", ["fused", "separate"])
+def test_trace_records_every_item(mode):
+    """POD_ATTN_FLAG_TRACE: one timeline record per item, ends after starts, CU slots in range,
+    kinds in item order, output unchanged by tracing.  Fused: prefill and decode items overlap in
+    time (the two kinds share the machine).  Separate: every prefill item ends before the first
+    decode item starts (one stream, prefill kernel first)."""
+    spec = gen.custom_spec("bf16", Hq=8, Hkv=2, D=128, prefill=[(600, 9000), (200, 4000)],
+                           decode=[3000 + 131 * i for i in range(40)], seed=21)
+    b = gen.make_batch(spec, "cuda")
+    _say(f"trace mode={mode}")
+    ref, _, _ = run_library(b, mode=mode)
+    out, h, ws = run_library(b, mode=mode, flags=B.FLAG_TRACE)
+    assert torch.equal(out, ref)
+    st = h.stats()
+    npf, ndc = st["num_prefill_items"], st["num_decode_items"]
+    rec = h.read_trace(ws).astype(np.int64)
+    assert rec.shape == (npf + ndc, 4)
+    t0 = rec[:, 0]
+    dur = (rec[:, 1] - t0) % (1 << 32)
+    assert np.all(dur < (1 << 31)), "an item ends before it starts"
+    assert np.all(rec[:, 2] < 1024)
+    assert np.all(rec[:npf, 3] == 0) and np.all(rec[npf:, 3] == 1)
+    start = (t0 - t0.min()) % (1 << 32)
+    end = start + dur
+    pf, dc = slice(0, npf), slice(npf, npf + ndc)
+    if mode == "fused":
+        assert end[pf].max() > start[dc].min() and end[dc].max() > start[pf].min(), "kinds never overlapped"
+    else:
+        assert end[pf].max() <= start[dc].min()
+
+
 @pytest.mark.parametrize("mode", MODES)
 def test_run_to_run_bitwise_determinism(mode):
     spec = gen.custom_spec("bf16", Hq=32, Hkv=8, D=128, prefill=[(256, 2000)],
