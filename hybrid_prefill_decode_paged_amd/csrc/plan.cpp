@@ -246,10 +246,11 @@ pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus
 }
 
 void stage_plan(const Plan& p, const Config& c, uint8_t* dst) {
-  std::memset(dst, 0, p.map.copy_bytes);
-  if (!p.pdesc.empty()) std::memcpy(dst + p.map.pdesc, p.pdesc.data(), p.pdesc.size() * 4);
-  std::memcpy(dst + p.map.pitems, p.pitems.data(), p.pitems.size() * 4);
-  if (!p.ddesc.empty()) std::memcpy(dst + p.map.ddesc, p.ddesc.data(), p.ddesc.size() * 4);
+  const size_t base = p.map.pdesc;             // [0, pdesc) is zero-filled on the device
+  std::memset(dst, 0, p.map.copy_bytes - base);
+  if (!p.pdesc.empty()) std::memcpy(dst + p.map.pdesc - base, p.pdesc.data(), p.pdesc.size() * 4);
+  std::memcpy(dst + p.map.pitems - base, p.pitems.data(), p.pitems.size() * 4);
+  if (!p.ddesc.empty()) std::memcpy(dst + p.map.ddesc - base, p.ddesc.data(), p.ddesc.size() * 4);
   (void)c;
 }
 

@@ -35,7 +35,8 @@ struct Plan {
 pod_attn_status validate_config(const pod_attn_config* c, Config* out, std::string* err);
 pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus, int wgs_per_cu,
                            Plan* out, std::string* err);
-// Write the host-staged prefix of the workspace ([0, map.copy_bytes)) into dst.
+// Write the host-staged part of the workspace, [map.pdesc, map.copy_bytes), into dst (from dst[0]);
+// [0, map.pdesc) (counters, tickets, claim counts) is zero-filled on the device.
 void stage_plan(const Plan& p, const Config& c, uint8_t* dst);
 // Expand descriptor-encoded items to the 16-int form of pod_attn_plan_inspect.
 void expand_items(const Plan& p, const Config& c, std::vector<int32_t>* items);

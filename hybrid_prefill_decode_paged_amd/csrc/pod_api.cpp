@@ -42,7 +42,8 @@ int env_int(const char* name, int dflt) {
 bool log_on() { return env_int("POD_ATTN_LOG", 0) != 0; }
 
 struct StagingSlot {
-  void* host = nullptr;
+  void* host = nullptr;            // pinned, fine-grained (read by the upload kernel over the host link)
+  void* dev = nullptr;             // its device address
   size_t cap = 0;
   hipEvent_t done = nullptr;
   bool pending = false;
@@ -69,6 +70,7 @@ struct pod_attn_handle {
   int decode_block_claim = 1;
   int prefill_wgs_override = 0;     // POD_ATTN_PREFILL_WGS
   int prefill_per_cu_override = 0;  // POD_ATTN_PREFILL_PER_CU
+  int prefill_cus_override = 0;     // POD_ATTN_PREFILL_CUS (-1: per-CU cap policy)
 };
 
 extern "C" {
@@ -110,6 +112,7 @@ pod_attn_status pod_attn_create(const pod_attn_config* cfg, pod_attn_handle** ou
   h->decode_block_claim = env_int("POD_ATTN_DECODE_BLOCK_CLAIM", 1);
   h->prefill_wgs_override = env_int("POD_ATTN_PREFILL_WGS", 0);
   h->prefill_per_cu_override = env_int("POD_ATTN_PREFILL_PER_CU", 0);
+  h->prefill_cus_override = env_int("POD_ATTN_PREFILL_CUS", 0);
   if (const char* m = std::getenv("POD_ATTN_MODE")) {
     if (!std::strcmp(m, "fused")) h->mode_env = POD_ATTN_MODE_FUSED;
     else if (!std::strcmp(m, "separate")) h->mode_env = POD_ATTN_MODE_SEPARATE;
@@ -183,6 +186,11 @@ static int prefill_budget(const pod_attn_handle* h, const Plan& p) {
   (void)p;
   return total;
 }
+static int prefill_cus(const pod_attn_handle* h, const Plan& p) {
+  if (h->prefill_cus_override != 0) return std::max(0, std::min(h->prefill_cus_override, h->num_cus));
+  (void)p;
+  return 0;
+}
 static int prefill_per_cu(const pod_attn_handle* h) {
   if (h->prefill_per_cu_override > 0) return std::min(h->prefill_per_cu_override, h->wgs_per_cu);
   return 1;
@@ -235,23 +243,32 @@ pod_attn_status pod_attn_run(pod_attn_handle* h, const void* q, const void* k_ca
     }
   }
 
-  // stage the plan (descriptors + zeroed counters) through a pinned ring and copy it in
+  // stage the plan through a pinned ring: the upload kernel zero-fills the counters and copies the
+  // descriptors in (slot i is rewritten only after its upload kernel has run)
   StagingSlot& slot = h->ring[h->ring_next];
   h->ring_next = (h->ring_next + 1) % kRing;
   if (slot.pending) {
     POD_HIP(hipEventSynchronize(slot.done));
     slot.pending = false;
   }
-  if (slot.cap < p.map.copy_bytes) {
+  const size_t staged = p.map.copy_bytes - p.map.pdesc;
+  if (slot.cap < staged) {
     if (slot.host) POD_HIP(hipHostFree(slot.host));
-    slot.host = nullptr;
+    slot.host = slot.dev = nullptr;
     slot.cap = 0;
-    size_t cap = std::max<size_t>(p.map.copy_bytes * 2, 1 << 16);
-    POD_HIP(hipHostMalloc(&slot.host, cap, hipHostMallocDefault));
+    size_t cap = std::max<size_t>(staged * 2, 1 << 16);
+    POD_HIP(hipHostMalloc(&slot.host, cap, hipHostMallocCoherent | hipHostMallocMapped));
+    POD_HIP(hipHostGetDevicePointer(&slot.dev, slot.host, 0));
     slot.cap = cap;
   }
   stage_plan(p, h->cfg, (uint8_t*)slot.host);
-  POD_HIP(hipMemcpyAsync(workspace, slot.host, p.map.copy_bytes, hipMemcpyHostToDevice, stream));
+  {
+    const void* src = slot.dev;
+    void* dst = workspace;
+    int nz = (int)(p.map.pdesc / 16), nc = (int)(staged / 16);
+    void* args[] = {(void*)&src, &dst, &nz, &nc};
+    POD_HIP(hipLaunchKernel(h->ks.stage, dim3((nz + nc + kThreads - 1) / kThreads), dim3(kThreads), args, 0, stream));
+  }
   POD_HIP(hipEventRecord(slot.done, stream));
   slot.pending = true;
 
@@ -275,6 +292,7 @@ pod_attn_status pod_attn_run(pod_attn_handle* h, const void* q, const void* k_ca
   kp.scale_log2 = h->cfg.scale * 1.4426950408889634f;
   kp.prefill_cap_per_cu = prefill_per_cu(h);
   kp.prefill_wg_budget = prefill_budget(h, p);
+  kp.prefill_cus = prefill_cus(h, p);
   kp.decode_block_claim = h->decode_block_claim;
 
   hipEvent_t prof_start = h->prof_start, prof_end = h->prof_end;

@@ -47,7 +47,9 @@ enum CtrlWord {
   kCClaimsPrefillCu = 256 + kCuSlots,       // [kCuSlots] prefill items claimed per CU
   kCClaimsDecodeCu = 256 + 2 * kCuSlots,    // [kCuSlots] decode items claimed per CU
   kCQueuePrefillXcd = 256 + 3 * kCuSlots,   // [kXcds] prefill queues, one 128-byte line each
-  kCtrlInts = 256 + 3 * kCuSlots + kXcds * 32
+  kCCuRole = 256 + 3 * kCuSlots + kXcds * 32,   // [kCuSlots] fused CU-partition role: 0 open, 1 prefill, 2 decode, 3 deciding
+  kCXcdPrefillCus = kCCuRole + kCuSlots,        // [kXcds] prefill CUs chosen on each die, one line each
+  kCtrlInts = kCXcdPrefillCus + kXcds * 32
 };
 
 enum StatusBits { kStatusBadPage = 1 };
@@ -74,6 +76,7 @@ struct KernelParams {
   float scale_log2;          // softmax scale * log2(e)
   int prefill_cap_per_cu;    // fused: prefill-role workgroups allowed per CU while decode remains
   int prefill_wg_budget;     // fused: prefill-role workgroups allowed device-wide while decode remains
+  int prefill_cus;           // fused: > 0: CUs (spread over the dies) whose workgroups all take prefill while decode remains
   int inline_combine;        // 1: the last-arriving decode split merges its group in-kernel (fused)
   int group_begin, group_end;// combine kernel range
   int combine_col_blocks;     // combine kernel: workgroups per group (16 columns each)
@@ -82,7 +85,7 @@ struct KernelParams {
 
 // Workspace map (byte offsets), computed by the planner.
 struct WorkspaceMap {
-  size_t ctrl, tickets, claims, pdesc, pitems, ddesc, copy_bytes;  // [0, copy_bytes) is host-staged
+  size_t ctrl, tickets, claims, pdesc, pitems, ddesc, copy_bytes;  // [0, pdesc) zeroed, [pdesc, copy_bytes) staged from the host
   size_t part_o, part_lse, trace, total;
 };
 

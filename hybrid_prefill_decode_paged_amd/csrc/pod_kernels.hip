@@ -1067,6 +1067,28 @@ __device__ __forceinline__ void trace_item(const KernelParams& P, int kind, int 
   }
 }
 
+// CU-partition role (fused kernel, prefill_cus > 0), called by thread 0: the first workgroup to
+// ask on a CU decides for the whole CU, taking one of its die's prefill-CU places while any is
+// left (prefill_cus spread evenly over the dies, so that every die's prefill queue keeps its
+// own CUs).  Returns 1 for a prefill CU, 2 for a decode CU.  A workgroup that finds its CU's
+// decision in progress (a few atomics by the other workgroup) polls with a bounded wait and
+// takes decode if it never settles.
+__device__ __forceinline__ int cu_role(const KernelParams& P, int cu, int xcc) {
+  int* slot = P.ctrl + kCCuRole + cu;
+  int prev = atomicCAS(slot, 0, 3);
+  if (prev == 0) {
+    const int quota = P.prefill_cus / kXcds + (xcc < P.prefill_cus % kXcds ? 1 : 0);
+    const int r = atomicAdd(P.ctrl + kCXcdPrefillCus + 32 * xcc, 1) < quota ? 1 : 2;
+    atomicExch(slot, r);
+    return r;
+  }
+  for (int i = 0; prev == 3 && i < 4096; ++i) {
+    __builtin_amdgcn_s_sleep(2);
+    prev = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return prev == 1 ? 1 : 2;
+}
+
 // Prefill claim for a workgroup on XCC `xcc`: queue x is the item range [hdr[x], hdr[x+1]) of
 // the item table, whole groups of tiles that read the same keys of the same KV head, so such
 // tiles run on one die and reuse its L2; a workgroup whose queue is drained takes work from
@@ -1126,7 +1148,9 @@ __global__ __launch_bounds__(kThreads, 2) void pod_fused_kernel(KernelParams P) 
   for (;;) {
     if (tid == 0) {
       int role = -1;
-      if (pf_open && dc_open) {
+      if (pf_open && dc_open && P.prefill_cus > 0) {
+        role = cu_role(P, cu, xcc) == 1 ? 0 : 1;
+      } else if (pf_open && dc_open) {
         const int a = atomicAdd(active, 1);
         const int g = atomicAdd(active_all, 1);
         if (a < P.prefill_cap_per_cu && g < P.prefill_wg_budget) {
@@ -1305,6 +1329,17 @@ __global__ __launch_bounds__(kThreads) void pod_gather_kernel(const void* cache,
   ((T*)out)[idx] = val;
 }
 
+// Plan upload, launched before the attention kernels on the same stream: the workspace's counter
+// region [0, 16 n_zero16) is zero-filled and the descriptor region after it is copied from the
+// pinned host staging buffer (read over the host link), one 16-byte word per thread.  A kernel
+// starts sooner after the previous kernel than a DMA copy's completion can release it.
+__global__ __launch_bounds__(kThreads) void pod_stage_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                             int n_zero16, int n_copy16) {
+  const int i = (int)blockIdx.x * kThreads + (int)threadIdx.x;
+  if (i < n_zero16) dst[i] = u32x4{0u, 0u, 0u, 0u};
+  else if (i < n_zero16 + n_copy16) dst[i] = src[i - n_zero16];
+}
+
 template <typename T, int D>
 KernelSet make_set() {
   KernelSet s;
@@ -1313,6 +1348,7 @@ KernelSet make_set() {
   s.decode = (const void*)&pod_decode_kernel<T, D>;
   s.combine = (const void*)&pod_combine_kernel<T, D>;
   s.gather = (const void*)&pod_gather_kernel<T, D>;
+  s.stage = (const void*)&pod_stage_kernel;
   s.fused_lds = Geo<T, D>::kFusedLds;
   s.prefill_kv_tile = Geo<T, D>::kTileKeys;
   return s;
