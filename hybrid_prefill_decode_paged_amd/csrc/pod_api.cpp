@@ -300,12 +300,9 @@ pod_attn_status pod_attn_run(pod_attn_handle* h, const void* q, const void* k_ca
   if (prof_start) POD_HIP(hipEventRecord(prof_start, stream));
   int grid = 0;
   if (mode == POD_ATTN_MODE_FUSED) {
-    kp.inline_combine = 1;                    // decode splits merge in-kernel
+    kp.inline_combine = 1;                    // split groups merge in-kernel (last arriver)
     grid = h->num_cus * h->wgs_per_cu;
     POD_HIP(launch(h->ks.fused, grid, kp, stream));
-    if (prof_end) POD_HIP(hipEventRecord(prof_end, stream));   // the fused kernel alone
-    prof_end = nullptr;
-    if (p.n_pf_groups) POD_HIP(launch_combine(h, kp, 0, p.n_pf_groups, p.tile_cols, stream));
   } else if (mode == POD_ATTN_MODE_SEPARATE) {
     kp.inline_combine = 0;
     if (p.n_pf_items) POD_HIP(launch(h->ks.prefill, p.n_pf_items, kp, stream));

@@ -1018,20 +1018,25 @@ __device__ void prefill_item_bf16(const KernelParams& P, CPTR(int32_t) dsc, int 
 #pragma unroll
       for (int b2 = 0; b2 < kDb; ++b2) store4<__bf16>(dst + 16 * b2, o[nb][b2] * inv);
     } else {
-      const size_t slot = (size_t)dsc[kDPartBase] + ((size_t)head * ns + split) * ncols + c;
-      float* dst = P.part_o + slot * D + 4 * q;
+      const size_t run = (size_t)dsc[kDPartBase] + ((size_t)head * ns + split) * ncols;   // this split's columns
+      if (P.inline_combine) {                  // merged in-kernel by the group's last split
+        const BufRsrc r = part_rsrc(P.part_o + run * D, ncols * D * 4);
 #pragma unroll
-      for (int b2 = 0; b2 < kDb; ++b2) store_part4(dst + 16 * b2, o[nb][b2] * inv);   // merged by the combine kernel
-      if (q == 0) P.part_lse[slot] = l_tot > 0.f ? m_run[nb] + __log2f(l_tot) : kNegInf;
+        for (int b2 = 0; b2 < kDb; ++b2) store_coherent4(r, (c * D + 4 * q + 16 * b2) * 4, o[nb][b2] * inv);
+      } else {                                 // merged by the combine kernel
+        float* dst = P.part_o + (run + c) * D + 4 * q;
+#pragma unroll
+        for (int b2 = 0; b2 < kDb; ++b2) store_part4(dst + 16 * b2, o[nb][b2] * inv);
+      }
+      if (q == 0) store_part1(P.part_lse + run + c, l_tot > 0.f ? m_run[nb] + __log2f(l_tot) : kNegInf, P.inline_combine != 0);
     }
   }
 }
 
 // ------------------------------------------------------------------ item dispatch
-// Prefill item: the whole workgroup.  Split partials (up to 128 columns x D floats per item)
-// go out with plain 16-byte stores and are merged by the combine kernel after the launch: in
-// the fused kernel, merging them in the last-arriving workgroup needed device-coherent stores
-// and loads and measured 20-30% slower on the prefill share than one combine launch.
+// Prefill item: the whole workgroup.  Split partials (up to 128 columns x D floats per item) are
+// merged in-kernel by the last-arriving split when inline_combine is set (fused mode; partials
+// written through with 16-byte device-coherent stores), else by the combine kernel.
 template <typename T, int D>
 __device__ void run_prefill_item(const KernelParams& P, int item, char* lds) {
   CPTR(int32_t) e = (CPTR(int32_t))P.pitems + kPItemHeader + 2 * (size_t)item;
@@ -1039,6 +1044,21 @@ __device__ void run_prefill_item(const KernelParams& P, int item, char* lds) {
   const int split = e[1] >> 16, head = e[1] & 0xFFFF;
   if constexpr (sizeof(T) == 2) prefill_item_bf16<D>(P, dsc, head, split, lds);
   else prefill_item<T, D>(P, dsc, head, split, lds);
+  const int ns = dsc[kDNSplit];
+  if (ns > 1 && P.inline_combine) {
+    // Each wave's partial stores (write-through) complete before the barrier; thread 0 takes the
+    // group's ticket; the workgroup holding the last split merges the group, each wave a block
+    // of 16 columns at a time.  No workgroup waits for another.
+    __shared__ int s_last;
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (threadIdx.x == 0) s_last = atomicAdd(P.tickets + dsc[kDGroupBegin] + head, 1) == ns - 1;
+    __syncthreads();
+    if (s_last) {
+      float* sw = (float*)(lds + wave_index() * kCombineLdsPerWave);
+      for (int c0 = 16 * wave_index(); c0 < dsc[kDNcols]; c0 += 16 * kWaves) combine_block_wave<T, D>(P, dsc, head, c0, sw);
+    }
+  }
   __syncthreads();   // LDS is reused by the next item
 }
 

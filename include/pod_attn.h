@@ -213,10 +213,9 @@ pod_attn_status pod_attn_plan_inspect(const pod_attn_config* cfg, const pod_attn
 
 /* Profiling hook: when ev_start / ev_end (hipEvent_t, may be NULL) are set, the next
  * pod_attn_run records ev_start on the launch stream right after the plan copy, before the
- * first kernel, and ev_end after the main kernels: FUSED mode, right after the fused kernel
- * (the short prefill split-combine kernel that follows it is outside the pair); SEPARATE mode,
- * after the last kernel; STREAMS mode, after the join.  The elapsed time between them, read
- * with hipEventElapsedTime, is then the duration of the fused kernel or of the kernel sequence.
+ * first attention kernel, and ev_end after the last one (FUSED mode: the fused kernel alone;
+ * SEPARATE mode: prefill, decode and combine kernels; STREAMS mode: after the join), so that
+ * the attention kernels' own duration can be read with hipEventElapsedTime.
  * The hook is consumed by that run (one-shot); the events stay owned by the caller. */
 pod_attn_status pod_attn_set_kernel_events(pod_attn_handle* h, void* ev_start, void* ev_end);
 
