@@ -75,7 +75,7 @@ def stats_summary(path: str, command: str) -> str:
     out = ["# rocprofv3 kernel statistics", "", f"Command: `{command}`", "",
            "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
     for r in rows:
-        name = r["Name"]
+        name = r["Name"].replace("(anonymous namespace)::", "")
         short = name.split("(")[0][:90]
         out.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                    f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} |")
@@ -86,7 +86,7 @@ def pmc_summary(dirs, title: str, command: str) -> str:
     rows = {}
     for d in dirs:
         for r in csv.DictReader(open(_counter_csv(d))):
-            name = r["Kernel_Name"].split("(")[0]
+            name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0]
             if "pod_" not in name:
                 continue
             rows.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
