@@ -810,13 +810,37 @@ __device__ void prefill_item_bf16(const KernelParams& P, CPTR(int32_t) dsc, int 
   auto kbuf = [&](int b) { return lds + b * kKBytes; };
   auto vbuf = [&](int b) { return lds + 2 * kKBytes + b * kVBytes; };
 
+  // Block-table entries of tile t: the four loads are issued together and checked afterwards
+  // (an entry outside the pool is reported and its page counts as absent); pages past kv_end
+  // are absent and read the tile's first entry, which exists.
+  auto tile_pages = [&](int t, int (&pg)[kTp], int (&lim)[kTp]) {
+    const int pi0 = (kv_begin + t * kTileKeys) >> 4;
+#pragma unroll
+    for (int p = 0; p < kTp; ++p) {
+      lim[p] = __builtin_amdgcn_readfirstlane(max(0, min(kPage, kv_end - (pi0 + p) * kPage)));
+      pg[p] = btr[lim[p] > 0 ? pi0 + p : pi0];
+    }
+    bool bad = false;
+#pragma unroll
+    for (int p = 0; p < kTp; ++p) {
+      const bool b = lim[p] > 0 && (unsigned)pg[p] >= (unsigned)P.num_pages;
+      lim[p] = b ? 0 : lim[p];
+      bad = bad | b;
+    }
+    if (bad && (threadIdx.x & 63) == 0) atomicOr(P.ctrl + kCStatus, (int)kStatusBadPage);
+  };
   // K(t): this wave stages page w of tile t.
   auto stage_k = [&](int t) {
-    const int pi = ((kv_begin + t * kTileKeys) >> 4) + w;
-    int l = min(kPage, kv_end - pi * kPage);
-    const int pg = __builtin_amdgcn_readfirstlane(page_or_empty(btr, pi, l, P.num_pages, P.ctrl + kCStatus));
-    if (__builtin_amdgcn_readfirstlane(l) <= 0) return;    // absent page: nothing is read
-    const char* kp = slab_ptr<__bf16, D>(P.k, pg, P.hkv, head) + src_k;
+    int pg[kTp], lim[kTp];
+    tile_pages(t, pg, lim);
+    int own = pg[0], own_lim = lim[0];
+#pragma unroll
+    for (int p = 1; p < kTp; ++p) {
+      own = p == w ? pg[p] : own;
+      own_lim = p == w ? lim[p] : own_lim;
+    }
+    if (own_lim <= 0) return;                  // absent page: nothing is read
+    const char* kp = slab_ptr<__bf16, D>(P.k, own, P.hkv, head) + src_k;
     char* dst = kbuf(t & 1) + w * 1024;
 #pragma unroll
     for (int s = 0; s < kNs; ++s)
@@ -825,15 +849,12 @@ __device__ void prefill_item_bf16(const KernelParams& P, CPTR(int32_t) dsc, int 
   };
   // V(t): key counts of the tile's pages into lim; this wave stages page w; returns its count.
   auto stage_v = [&](int t, int (&lim)[kTp]) -> int {
-    const int tb = kv_begin + t * kTileKeys;
-    int own = 0, own_lim = 0;
+    int pg[kTp];
+    tile_pages(t, pg, lim);
+    int own = pg[0], own_lim = lim[0];
 #pragma unroll
-    for (int p = 0; p < kTp; ++p) {
-      const int pi = (tb >> 4) + p;
-      int l = min(kPage, kv_end - pi * kPage);
-      const int pg = __builtin_amdgcn_readfirstlane(page_or_empty(btr, pi, l, P.num_pages, P.ctrl + kCStatus));
-      lim[p] = __builtin_amdgcn_readfirstlane(l);
-      own = p == w ? pg : own;
+    for (int p = 1; p < kTp; ++p) {
+      own = p == w ? pg[p] : own;
       own_lim = p == w ? lim[p] : own_lim;
     }
     if (own_lim <= 0) return 0;
