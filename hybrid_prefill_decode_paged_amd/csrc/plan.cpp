@@ -189,9 +189,13 @@ pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus
   if (c.decode_split_tokens > 0) {
     st_target = c.decode_split_tokens;
   } else {
-    long target_items = (long)num_cus * wgs_per_cu * kWaves * 4;   // ~4 items per decode wave
+    // About two items per decode wave: fewer, longer items cost fewer partials, tickets and
+    // combine work, while two per wave still lets the waves that start late (their workgroups
+    // begin on prefill tiles) finish with the rest (measured on the four bf16 workloads: one
+    // per wave left a tail, four per wave lost 1-5%).
+    long target_items = (long)num_cus * wgs_per_cu * kWaves * 2;
     long st = (total_tok + target_items - 1) / std::max(1L, target_items);
-    st = std::max(512L, std::min(4096L, st));
+    st = std::max(512L, std::min(32768L, st));
     st_target = round_up_int((int)st, 128);
   }
   p.decode_split_tokens = st_target;
