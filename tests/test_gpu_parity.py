@@ -131,6 +131,46 @@ def test_gather_is_bit_exact(dtype, D):
                 np.testing.assert_array_equal(got[:, g].to(torch.float64).numpy(), want)
 
 
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("fp32", 128)])
+@pytest.mark.parametrize("mode", MODES)
+def test_forced_splits_other_shapes(dtype, D, mode):
+    spec = gen.custom_spec(dtype, Hq=8, Hkv=4, D=D, prefill=[(90, 1300), (16, 40)],
+                           decode=[2, 400, 1900], seed=8)
+    b = gen.make_batch(spec, "cuda")
+    _, h, _, _ = _full_check(b, mode, f"splits-{dtype}-{D}", decode_split_tokens=128, prefill_split_cap=16)
+    assert h.stats()["decode_max_splits"] > 1
+
+
+@pytest.mark.parametrize("mode", ["fused", "separate"])
+def test_decode_at_the_split_limit(mode):
+    """A 64K-token decode with 512-token splits needs the largest split count (128), the size
+    the combine tables are laid out for."""
+    spec = gen.custom_spec("bf16", Hq=4, Hkv=2, D=128, prefill=[(32, 700)], decode=[65536, 300], seed=9)
+    b = gen.make_batch(spec, "cuda")
+    _, h, _, _ = _full_check(b, mode, "max-splits", decode_split_tokens=512)
+    assert h.stats()["decode_max_splits"] == 128
+
+
+@pytest.mark.parametrize("direction", ["rising", "falling"])
+@pytest.mark.parametrize("mode", ["fused", "separate"])
+def test_running_max_moves_by_large_steps(direction, mode):
+    """K rows scaled by 2^(t/64) along every sequence (rising), or by its mirror (falling): the
+    running maximum of the online softmax jumps by far more than 2^8 over and over (rising) or
+    is set by the first keys and never moves (falling).  Both must match the oracle."""
+    spec = gen.custom_spec("bf16", Hq=8, Hkv=2, D=128, prefill=[(200, 900), (64, 64)],
+                           decode=[700, 1000, 33], seed=31)
+    b = gen.make_batch(spec, "cuda")
+    kr = gen.k_rows_view(b.k_pool)                 # [page, head, slot, D/x, x]
+    for si, ctx in enumerate(spec.seq_ctx()):
+        row = b.block_tables_host[si]
+        for t0 in range(0, ctx, 16):
+            page, n = int(row[t0 // 16]), min(16, ctx - t0)
+            t = torch.arange(t0, t0 + n, device="cuda", dtype=torch.float32)
+            f = torch.exp2(t / 64) if direction == "rising" else torch.exp2((ctx - 1 - t) / 64)
+            kr[page, :, :n] = (kr[page, :, :n].float() * f.view(1, n, 1, 1)).to(kr.dtype)
+    _full_check(b, mode, f"rescale-{direction}")
+
+
 @pytest.mark.parametrize("mode", MODES)
 def test_every_item_claimed_exactly_once(mode):
     spec = gen.custom_spec("bf16", Hq=8, Hkv=2, D=128, prefill=[(300, 2000), (50, 60)],
