@@ -5,7 +5,7 @@ CPU-baseline leg; never by the library.  Every function is pinned by the ``-m "n
 tests in tests/test_oracle_*.py (no function here is "parity unpinned").
 """
 from .attention import (  # noqa: F401
-    PAGE, HybridProblem, attend, attend_blockwise, attend_online, bf16_bits_to_f64,
-    combine_partials, gather_kv, gather_kv_token, masked_scores, softmax_rows,
-    split_partials, to_f64,
+    PAGE, HybridProblem, append_tokens, attend, attend_blockwise, attend_online,
+    bf16_bits_to_f64, combine_partials, gather_kv, gather_kv_token, masked_scores,
+    row_positions, softmax_rows, split_partials, to_f64,
 )

@@ -98,6 +98,41 @@ def gather_kv(k_pool, v_pool, table_row, ctx: int, kv_head: int, dtype: str):
 
 
 # ----------------------------------------------------------------------------------------
+# KV append: the step before attention in every iteration
+# ----------------------------------------------------------------------------------------
+def row_positions(prefill_q_start, prefill_ctx_len, decode_ctx_len) -> List[Tuple[int, int]]:
+    """(sequence, absolute position) of every query row, in row order.  Prefill chunk i's L rows
+    sit at positions ctx_i-L .. ctx_i-1; decode i is the sequence after the prefill sequences,
+    its one row at position ctx_i-1 ([W6] "한 스텝에 여러 종류의 request 섞기": a decode is an
+    extend of one token)."""
+    out = []
+    n_pf = len(prefill_ctx_len)
+    for i in range(n_pf):
+        L = int(prefill_q_start[i + 1]) - int(prefill_q_start[i])
+        ctx = int(prefill_ctx_len[i])
+        out += [(i, ctx - L + j) for j in range(L)]
+    out += [(n_pf + i, int(c) - 1) for i, c in enumerate(decode_ctx_len)]
+    return out
+
+
+def append_tokens(k_pool, v_pool, block_tables, rows, k_new, v_new) -> None:
+    """Write every row's new K and V (raw elements, [rows][Hkv][D]) into the slot its position
+    falls in, in place: page = table[seq][pos // 16], slot = pos % 16 ([W6] "PagedAttention":
+    a logical block maps to a physical page; [W6] "KV Cache": the cache grows by appending the
+    new tokens' keys and values).  k_pool is [page, head, d//x, slot, d%x], v_pool
+    [page, head, d, slot].  Plain loops."""
+    Hkv, D = k_new.shape[1], k_new.shape[2]
+    x = k_pool.shape[-1]
+    for r, (s, pos) in enumerate(rows):
+        page = int(block_tables[s][pos // PAGE])
+        slot = pos % PAGE
+        for g in range(Hkv):
+            for d in range(D):
+                k_pool[page, g, d // x, slot, d % x] = k_new[r, g, d]
+                v_pool[page, g, d, slot] = v_new[r, g, d]
+
+
+# ----------------------------------------------------------------------------------------
 # attention, direct form
 # ----------------------------------------------------------------------------------------
 def masked_scores(qs: np.ndarray, pos: np.ndarray, K: np.ndarray, scale: float) -> np.ndarray:

@@ -257,6 +257,55 @@ def test_paged_equals_contiguous_bitwise():
     np.testing.assert_array_equal(outs[0], outs[1])
 
 
+# ------------------------------------------------------------------ KV append
+def test_row_positions_follow_the_mixed_batch_rows():
+    """Chunks (L=3, ctx=10), (L=0, ctx=4), (L=2, ctx=2) and decodes at ctx 5 and 1: rows are the
+    chunks' last L positions in order, then one row per decode at ctx-1."""
+    rows = orc.row_positions([0, 3, 3, 5], [10, 4, 2], [5, 1])
+    assert rows == [(0, 7), (0, 8), (0, 9), (2, 0), (2, 1), (3, 4), (4, 0)]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_append_writes_exactly_the_new_rows(dtype):
+    """The cache holds every sequence's tokens before this step's rows; appending the rows'
+    new K/V gives, bitwise, the pools that the test-side scatter (written from the header's
+    layout text) produces for the whole sequences, including the untouched NaN slots, and the
+    gather at each row's position returns that row's new K/V."""
+    spec = gen.custom_spec("fp32", Hq=4, Hkv=2, D=16, prefill=((5, 21), (3, 3), (0, 7)),
+                           decode=(1, 16, 17, 33), seed=15, pool_slack=6)
+    rng = np.random.default_rng(15)
+    ctx = spec.seq_ctx()
+    bt = gen.block_tables_for(spec)
+    K_seq = [rng.standard_normal((2, c, 16)).astype(np.float32) for c in ctx]
+    V_seq = [rng.standard_normal((2, c, 16)).astype(np.float32) for c in ctx]
+    q_start = np.concatenate([[0], np.cumsum(spec.prefill_q_len)]).astype(np.int32)
+    rows = orc.row_positions(q_start, spec.prefill_ctx_len, spec.decode_ctx_len)
+    new_pos = {(s, pos) for s, pos in rows}
+    old_K = [K.copy() for K in K_seq]
+    old_V = [V.copy() for V in V_seq]
+    for s, c in enumerate(ctx):                  # the cache before the step: new positions absent
+        for t in range(c):
+            if (s, t) in new_pos:
+                old_K[s][:, t] = np.nan
+                old_V[s][:, t] = np.nan
+    want_k, want_v = _scatter_contiguous(spec, K_seq, V_seq, bt)
+    kp, vp = _scatter_contiguous(spec, old_K, old_V, bt)
+    k_new = np.stack([K_seq[s][:, pos] for s, pos in rows])
+    v_new = np.stack([V_seq[s][:, pos] for s, pos in rows])
+    if dtype == "bf16":                          # raw 16-bit patterns: the append moves bits
+        to16 = lambda a: (a.view(np.uint32) >> 16).astype(np.uint16)
+        want_k, want_v, kp, vp = map(to16, (want_k, want_v, kp, vp))
+        k_new, v_new = to16(k_new), to16(v_new)
+    orc.append_tokens(kp, vp, bt, rows, k_new, v_new)
+    np.testing.assert_array_equal(kp, want_k)
+    np.testing.assert_array_equal(vp, want_v)
+    for r, (s, pos) in enumerate(rows):
+        for g in range(2):
+            kt, vt = orc.gather_kv_token(kp, vp, bt[s], pos, g, dtype)
+            np.testing.assert_array_equal(kt, orc.to_f64(k_new[r, g], dtype))
+            np.testing.assert_array_equal(vt, orc.to_f64(v_new[r, g], dtype))
+
+
 def test_bf16_decoding_matches_torch():
     x = torch.randn(4096, dtype=torch.float32).to(torch.bfloat16)
     x[:4] = torch.tensor([0.0, -0.0, float("inf"), 1e-40]).to(torch.bfloat16)
