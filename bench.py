@@ -4,7 +4,9 @@ fraction of the max(MFMA, HBM) roofline.
     python bench.py [--steps K] [--warmup W] [--workload N] [--mode fused]
 
 One step = one pod_attn_run over the whole hybrid batch (prefill tiles + decode split-KV +
-combine), inputs resident in HBM.  Prints ONE JSON line.  The default workload is the
+combine), inputs resident in HBM.  Prints ONE JSON line.  Beside it, "kv_append" times the
+same step preceded by the KV append of every row's new K/V (pod_attn_run_append) in the fused
+and separate modes.  The default workload is the
 Llama-2-7B-shaped layer (32 query / 32 KV heads, head_dim 128, bf16, 16-token pages): one
 1024-token prefill chunk at offset 3072 plus 64 decodes at context 4096, over a randomly
 permuted 40960-page pool.  The other workloads are parity-test cases; --workload selects them
@@ -57,12 +59,20 @@ def workload_desc(spec):
             "dtype": spec.dtype}
 
 
-def time_mode(torch, h, b, meta, out, ws, steps, warmup):
+def time_mode(torch, h, b, meta, out, ws, steps, warmup, new=None):
     """Wall time of `steps` runs (events on the launch stream around the loop) and the mean
-    duration of the kernels of one run (one-shot events armed before each run)."""
+    duration of the kernels of one run (one-shot events armed before each run).  With
+    new = (k_new, v_new) every run first appends those tokens (pod_attn_run_append)."""
     stream = torch.cuda.current_stream()
+
+    def one():
+        if new is None:
+            h.run(b.q, b.k_pool, b.v_pool, b.block_tables, meta, out, ws)
+        else:
+            h.run_append(b.q, new[0], new[1], b.k_pool, b.v_pool, b.block_tables, meta, out, ws)
+
     for _ in range(warmup):
-        h.run(b.q, b.k_pool, b.v_pool, b.block_tables, meta, out, ws)
+        one()
     torch.cuda.synchronize()
     ks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for a, z in ks:             # torch creates the HIP events on first record; the library re-records them
@@ -73,7 +83,7 @@ def time_mode(torch, h, b, meta, out, ws, steps, warmup):
     t0.record(stream)
     for i in range(steps):
         h.set_kernel_events(*ks[i])
-        h.run(b.q, b.k_pool, b.v_pool, b.block_tables, meta, out, ws)
+        one()
     t1.record(stream)
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
@@ -172,6 +182,7 @@ def main():
     ap.add_argument("--mode", default="fused", choices=["fused", "separate", "streams"])
     ap.add_argument("--no-compare", action="store_true", help="skip timing the other two modes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-append", action="store_true", help="skip timing the KV-append variant")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (counter calibration)")
@@ -224,6 +235,27 @@ def main():
         del ws, out
         h.close()
 
+    append = None
+    if not args.no_append:
+        # The same step preceded by the KV append of every query row's new K/V (the tokens
+        # drawn once; rewriting them each step moves the same bytes).
+        k_new, v_new = gen.new_tokens(spec, spec.seed + 7, "cuda")
+        append = {"append_bytes": 2 * 2 * spec.total_q * spec.num_kv_heads * spec.head_dim * spec.elem_bytes}
+        for mode in ("fused", "separate"):
+            h = binding.PodAttention(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.dtype, mode,
+                                     scale=spec.softmax_scale)
+            ws = torch.empty(h.workspace_size(meta), dtype=torch.uint8, device="cuda")
+            out = torch.empty_like(b.q)
+            steps = max(5, args.steps // 2)
+            print(f"[bench] timing mode={mode} with KV append steps={steps}", file=sys.stderr, flush=True)
+            ms, kern_ms, _ = time_mode(torch, h, b, meta, out, ws, steps, args.warmup, new=(k_new, v_new))
+            append[mode] = {"us_per_iter": round(ms * 1e3, 2), "kernel_us_mean": round(kern_ms * 1e3, 2),
+                            "extra_us_vs_no_append": round(ms * 1e3 - results[mode]["us_per_iter"], 2)
+                            if mode in results else None,
+                            "units": h.stats()["num_append_units"]}
+            del ws, out
+            h.close()
+
     main_ms = results[args.mode]["us_per_iter"] / 1e3
     kern_s = results[args.mode]["kernel_us_mean"] / 1e6
     if bound == "hbm":
@@ -256,6 +288,7 @@ def main():
         "modes": results,
         "fused_vs_separate": (round(results["separate"]["us_per_iter"] / results["fused"]["us_per_iter"], 4)
                               if "separate" in results and "fused" in results else None),
+        "kv_append": append,
         "plan": {k: st[k] for k in ("num_prefill_items", "num_decode_items", "num_combine_groups",
                                     "decode_split_tokens", "prefill_max_splits", "grid_wgs", "wgs_per_cu",
                                     "num_cus", "vgprs_per_lane", "lds_bytes_per_wg", "mode_used", "prefill_wg_budget",

@@ -53,7 +53,8 @@ class Stats(C.Structure):
         "num_combine_groups", "prefill_tile_cols", "prefill_tile_queries", "prefill_kv_tile",
         "prefill_max_splits", "decode_split_tokens", "decode_max_splits", "grid_wgs", "wgs_per_cu",
         "num_cus", "lds_bytes_per_wg", "vgprs_per_lane")] + [
-        ("workspace_bytes", C.c_size_t), ("host_plan_us", C.c_double), ("prefill_wg_budget", C.c_int)]
+        ("workspace_bytes", C.c_size_t), ("host_plan_us", C.c_double), ("prefill_wg_budget", C.c_int),
+        ("num_append_units", C.c_int)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -74,6 +75,7 @@ def load(path: str = LIB_PATH):
     lib.pod_attn_create.argtypes = [P(Config), P(VP)]
     lib.pod_attn_workspace_size.argtypes = [VP, P(Batch), P(C.c_size_t)]
     lib.pod_attn_run.argtypes = [VP, VP, VP, VP, VP, P(Batch), VP, VP, C.c_size_t, VP]
+    lib.pod_attn_run_append.argtypes = [VP, VP, VP, VP, VP, VP, VP, P(Batch), VP, VP, C.c_size_t, VP]
     lib.pod_attn_get_stats.argtypes = [VP, P(Stats)]
     lib.pod_attn_gather_kv.argtypes = [VP, VP, I, VP, I, I, P(Batch), VP, VP]
     lib.pod_attn_read_device_status.argtypes = [VP, VP, VP, P(C.c_int32), P(C.c_int32), I, P(I),
@@ -84,7 +86,7 @@ def load(path: str = LIB_PATH):
     lib.pod_attn_last_error.restype = C.c_char_p
     lib.pod_attn_destroy.argtypes = [VP]
     lib.pod_attn_destroy.restype = None
-    for name in ("pod_attn_create", "pod_attn_workspace_size", "pod_attn_run", "pod_attn_get_stats",
+    for name in ("pod_attn_create", "pod_attn_workspace_size", "pod_attn_run", "pod_attn_run_append", "pod_attn_get_stats",
                  "pod_attn_gather_kv", "pod_attn_read_device_status", "pod_attn_plan_inspect", "pod_attn_read_trace",
                  "pod_attn_set_kernel_events"):
         getattr(lib, name).restype = C.c_int
@@ -214,6 +216,24 @@ class PodAttention:
                                      C.byref(meta.c), _ptr(out), _ptr(workspace),
                                      0 if workspace is None else workspace.numel() * workspace.element_size(),
                                      _stream_handle(stream)))
+        return out
+
+    def run_append(self, q, k_new, v_new, k_cache, v_cache, block_tables, meta: BatchMeta, out, workspace,
+                   stream=None):
+        """pod_attn_run_append on device tensors: writes row r's k_new/v_new [total_q, Hkv, D] into the
+        cache at the row's position, then computes attention over the updated cache."""
+        if meta.total_q:
+            self.check_buffers(q, k_cache, v_cache, block_tables, meta, out)
+            c = self.cfg
+            want = meta.total_q * c.num_kv_heads * c.head_dim
+            for name, t in (("k_new", k_new), ("v_new", v_new)):
+                if t.element_size() != k_cache.element_size() or t.numel() < want or not t.is_contiguous():
+                    raise PodAttnError(-1, f"{name}: need a contiguous tensor of >= {want} elements of the "
+                                           f"cache's type, got {tuple(t.shape)} {t.dtype}")
+        _check(self.lib.pod_attn_run_append(self.h, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                            _ptr(block_tables), C.byref(meta.c), _ptr(out), _ptr(workspace),
+                                            0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                            _stream_handle(stream)))
         return out
 
     def set_kernel_events(self, ev_start, ev_end):

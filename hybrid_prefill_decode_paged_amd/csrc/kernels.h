@@ -9,7 +9,8 @@ struct KernelSet {
   const void* decode = nullptr;    // one workgroup per decode item (KernelParams)
   const void* combine = nullptr;   // one workgroup per combine group (KernelParams)
   const void* gather = nullptr;    // debug gather (cache, which, bt_row, ctx, hkv, num_pages, out, status)
-  const void* stage = nullptr;     // plan upload (src_host, dst, n_zero16, n_copy16)
+  const void* stage = nullptr;     // plan upload, with the KV append in fused mode (StageArgs)
+  const void* append = nullptr;    // KV append alone, one wave per unit (KernelParams)
   int fused_lds = 0;               // static LDS bytes of the fused kernel
   int prefill_kv_tile = 0;         // keys per prefill inner iteration
 };

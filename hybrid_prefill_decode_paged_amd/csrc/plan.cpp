@@ -107,6 +107,31 @@ pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus
   p.prefill_rows = (int)prefill_rows;
   p.total_q = (int)prefill_rows + b->num_decode;
 
+  // ---------------- KV append units
+  // Every query row's new token goes to its position's page slot before attention reads it
+  // (a prefill chunk's L rows at ctx-L .. ctx-1, a decode row at ctx-1).  A sequence's new
+  // tokens are cut at page boundaries into runs of consecutive slots, and each run into units
+  // of about append_token_heads (token, KV head) pairs.
+  auto add_units = [&](int seq, int row0, int pos0, int n) {
+    for (int a = 0; a < n;) {
+      const int pos = pos0 + a;
+      const int ntok = std::min(n - a, kPage - pos % kPage);
+      const int hg = std::max(1, std::min(c.hkv, c.append_token_heads / ntok));
+      for (int h0 = 0; h0 < c.hkv; h0 += hg) {
+        const int32_t u[kAUnitInts] = {seq, row0 + a, pos, ntok, h0, std::min(hg, c.hkv - h0), 0, 0};
+        p.aunits.insert(p.aunits.end(), u, u + kAUnitInts);
+      }
+      a += ntok;
+    }
+  };
+  for (int i = 0; i < b->num_decode; ++i)
+    add_units(b->num_prefill + i, (int)prefill_rows + i, b->decode_ctx_len[i] - 1, 1);
+  for (int i = 0; i < b->num_prefill; ++i) {
+    const int L = b->prefill_q_start[i + 1] - b->prefill_q_start[i];
+    if (L > 0) add_units(i, b->prefill_q_start[i], b->prefill_ctx_len[i] - L, L);
+  }
+  p.n_aunits = (int)(p.aunits.size() / kAUnitInts);
+
   // ---------------- prefill tiles
   // Tiles of one chunk share their split boundaries (one split length per chunk), so that the
   // tiles reading the same key range of the same KV head form a group.  Groups are dealt whole
@@ -237,6 +262,7 @@ pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus
   m.pdesc = off; off = align_up(off + sizeof(int32_t) * std::max<size_t>(1, p.pdesc.size()), 256);
   m.pitems = off; off = align_up(off + sizeof(int32_t) * p.pitems.size(), 256);
   m.ddesc = off; off = align_up(off + sizeof(int32_t) * std::max<size_t>(1, p.ddesc.size()), 256);
+  m.aunits = off; off = align_up(off + sizeof(int32_t) * std::max<size_t>(1, p.aunits.size()), 256);
   m.copy_bytes = off;
   m.part_o = off; off = align_up(off + sizeof(float) * (size_t)p.n_slots * c.d, 256);
   m.part_lse = off; off = align_up(off + sizeof(float) * (size_t)std::max(1, p.n_slots), 256);
@@ -249,12 +275,13 @@ pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus
   return POD_ATTN_OK;
 }
 
-void stage_plan(const Plan& p, const Config& c, uint8_t* dst) {
+void stage_plan(const Plan& p, const Config& c, uint8_t* dst, bool with_units) {
   const size_t base = p.map.pdesc;             // [0, pdesc) is zero-filled on the device
-  std::memset(dst, 0, p.map.copy_bytes - base);
+  std::memset(dst, 0, (with_units ? p.map.copy_bytes : p.map.aunits) - base);
   if (!p.pdesc.empty()) std::memcpy(dst + p.map.pdesc - base, p.pdesc.data(), p.pdesc.size() * 4);
   std::memcpy(dst + p.map.pitems - base, p.pitems.data(), p.pitems.size() * 4);
   if (!p.ddesc.empty()) std::memcpy(dst + p.map.ddesc - base, p.ddesc.data(), p.ddesc.size() * 4);
+  if (with_units && !p.aunits.empty()) std::memcpy(dst + p.map.aunits - base, p.aunits.data(), p.aunits.size() * 4);
   (void)c;
 }
 

@@ -13,6 +13,7 @@ struct Config {
   int hq = 0, hkv = 0, d = 0, page = 16, dtype = 0, mode = 0;
   float scale = 0.f;
   int decode_split_tokens = 0, prefill_split_cap = 0, wgs_per_cu = 0, flags = 0;
+  int append_token_heads = kAppendTokenHeads;   // (token, KV head) pairs per KV append unit
   int group() const { return hq / hkv; }
   int elem_bytes() const { return dtype == POD_ATTN_BF16 ? 2 : 4; }
 };
@@ -20,7 +21,8 @@ struct Config {
 struct Plan {
   std::vector<int32_t> pdesc, ddesc;   // kDescInts each
   std::vector<int32_t> pitems;         // prefill item table: kPItemHeader ints, then (desc, split << 16 | head)
-  int n_pdesc = 0, n_ddesc = 0;
+  std::vector<int32_t> aunits;         // KV append units, kAUnitInts each
+  int n_pdesc = 0, n_ddesc = 0, n_aunits = 0;
   int n_pf_items = 0, n_dc_items = 0;
   int n_pf_groups = 0, n_groups = 0, n_slots = 0;
   int tile_queries = 0, tile_cols = 0;
@@ -36,8 +38,9 @@ pod_attn_status validate_config(const pod_attn_config* c, Config* out, std::stri
 pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus, int wgs_per_cu,
                            Plan* out, std::string* err);
 // Write the host-staged part of the workspace, [map.pdesc, map.copy_bytes), into dst (from dst[0]);
-// [0, map.pdesc) (counters, tickets, claim counts) is zero-filled on the device.
-void stage_plan(const Plan& p, const Config& c, uint8_t* dst);
+// [0, map.pdesc) (counters, tickets, claim counts) is zero-filled on the device.  Without
+// with_units the staged part ends at map.aunits (no KV append this run).
+void stage_plan(const Plan& p, const Config& c, uint8_t* dst, bool with_units);
 // Expand descriptor-encoded items to the 16-int form of pod_attn_plan_inspect.
 void expand_items(const Plan& p, const Config& c, std::vector<int32_t>* items);
 

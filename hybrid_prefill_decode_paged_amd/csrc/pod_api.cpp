@@ -67,7 +67,6 @@ struct pod_attn_handle {
   Plan last_plan;
   int mode_env = -1;
   hipEvent_t prof_start = nullptr, prof_end = nullptr;   // one-shot profiling events
-  int decode_block_claim = 1;
   int prefill_wgs_override = 0;     // POD_ATTN_PREFILL_WGS
   int prefill_per_cu_override = 0;  // POD_ATTN_PREFILL_PER_CU
   int prefill_cus_override = 0;     // POD_ATTN_PREFILL_CUS (-1: per-CU cap policy)
@@ -109,7 +108,7 @@ pod_attn_status pod_attn_create(const pod_attn_config* cfg, pod_attn_handle** ou
   h->wgs_per_cu = std::max(1, std::min(w, std::max(1, occ)));
   if (c.decode_split_tokens == 0) h->cfg.decode_split_tokens = env_int("POD_ATTN_DECODE_SPLIT_TOKENS", 0) / 128 * 128;
   if (c.prefill_split_cap == 0) h->cfg.prefill_split_cap = std::max(0, env_int("POD_ATTN_PREFILL_SPLIT_CAP", 0));
-  h->decode_block_claim = env_int("POD_ATTN_DECODE_BLOCK_CLAIM", 1);
+  h->cfg.append_token_heads = std::max(1, env_int("POD_ATTN_APPEND_TOKEN_HEADS", kAppendTokenHeads));
   h->prefill_wgs_override = env_int("POD_ATTN_PREFILL_WGS", 0);
   h->prefill_per_cu_override = env_int("POD_ATTN_PREFILL_PER_CU", 0);
   h->prefill_cus_override = env_int("POD_ATTN_PREFILL_CUS", 0);
@@ -207,10 +206,14 @@ static hipError_t launch_combine(pod_attn_handle* h, const KernelParams& base, i
   return launch(h->ks.combine, (g1 - g0) * c.combine_col_blocks, c, s);
 }
 
-pod_attn_status pod_attn_run(pod_attn_handle* h, const void* q, const void* k_cache, const void* v_cache,
-                             const int32_t* block_tables, const pod_attn_batch* b, void* out,
-                             void* workspace, size_t workspace_bytes, void* stream_) {
+// One run: plan, stage the plan, then (with k_new / v_new) the KV append and the attention
+// launches of the chosen mode.
+static pod_attn_status run_impl(pod_attn_handle* h, const void* q, const void* k_new, const void* v_new,
+                                const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                                const pod_attn_batch* b, void* out, void* workspace, size_t workspace_bytes,
+                                void* stream_) {
   if (!h) return fail(POD_ATTN_ERR_INVALID_ARG, "null handle");
+  const bool append = k_new != nullptr;
   hipStream_t stream = (hipStream_t)stream_;
   const auto t0 = std::chrono::steady_clock::now();
   Plan p;
@@ -225,7 +228,8 @@ pod_attn_status pod_attn_run(pod_attn_handle* h, const void* q, const void* k_ca
   if (workspace_bytes < p.map.total)
     return fail(POD_ATTN_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) + " bytes, needs " +
                                             std::to_string(p.map.total));
-  if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out | (uintptr_t)workspace) & 15)
+  if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out | (uintptr_t)workspace |
+       (uintptr_t)k_new | (uintptr_t)v_new) & 15)
     return fail(POD_ATTN_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
 
   // mode
@@ -251,7 +255,7 @@ pod_attn_status pod_attn_run(pod_attn_handle* h, const void* q, const void* k_ca
     POD_HIP(hipEventSynchronize(slot.done));
     slot.pending = false;
   }
-  const size_t staged = p.map.copy_bytes - p.map.pdesc;
+  const size_t staged = (append ? p.map.copy_bytes : p.map.aunits) - p.map.pdesc;   // units only when appending
   if (slot.cap < staged) {
     if (slot.host) POD_HIP(hipHostFree(slot.host));
     slot.host = slot.dev = nullptr;
@@ -261,17 +265,6 @@ pod_attn_status pod_attn_run(pod_attn_handle* h, const void* q, const void* k_ca
     POD_HIP(hipHostGetDevicePointer(&slot.dev, slot.host, 0));
     slot.cap = cap;
   }
-  stage_plan(p, h->cfg, (uint8_t*)slot.host);
-  {
-    const void* src = slot.dev;
-    void* dst = workspace;
-    int nz = (int)(p.map.pdesc / 16), nc = (int)(staged / 16);
-    void* args[] = {(void*)&src, &dst, &nz, &nc};
-    POD_HIP(hipLaunchKernel(h->ks.stage, dim3((nz + nc + kThreads - 1) / kThreads), dim3(kThreads), args, 0, stream));
-  }
-  POD_HIP(hipEventRecord(slot.done, stream));
-  slot.pending = true;
-
   uint8_t* ws = (uint8_t*)workspace;
   KernelParams kp{};
   kp.q = q; kp.k = k_cache; kp.v = v_cache; kp.bt = block_tables; kp.out = out;
@@ -284,6 +277,9 @@ pod_attn_status pod_attn_run(pod_attn_handle* h, const void* q, const void* k_ca
   kp.ddesc = (const int32_t*)(ws + p.map.ddesc);
   kp.part_o = (float*)(ws + p.map.part_o);
   kp.part_lse = (float*)(ws + p.map.part_lse);
+  kp.k_new = k_new; kp.v_new = v_new;
+  kp.aunits = (const int32_t*)(ws + p.map.aunits);
+  kp.n_aunits = append ? p.n_aunits : 0;
   kp.n_pdesc = p.n_pdesc; kp.n_ddesc = p.n_ddesc;
   kp.n_pf_items = p.n_pf_items; kp.n_dc_items = p.n_dc_items;
   kp.n_pf_groups = p.n_pf_groups; kp.n_groups = p.n_groups;
@@ -293,7 +289,26 @@ pod_attn_status pod_attn_run(pod_attn_handle* h, const void* q, const void* k_ca
   kp.prefill_cap_per_cu = prefill_per_cu(h);
   kp.prefill_wg_budget = prefill_budget(h, p);
   kp.prefill_cus = prefill_cus(h, p);
-  kp.decode_block_claim = h->decode_block_claim;
+
+  // Plan upload (and, in fused mode, the KV append in the same launch).
+  stage_plan(p, h->cfg, (uint8_t*)slot.host, append);
+  {
+    StageArgs a{};
+    a.p = kp;
+    a.src = slot.dev;
+    a.dst = workspace;
+    a.n_zero16 = (int)(p.map.pdesc / 16);
+    a.n_copy16 = (int)(staged / 16);
+    a.copy_wgs = (a.n_zero16 + a.n_copy16 + kThreads - 1) / kThreads;
+    const bool fused_append = kp.n_aunits > 0 && mode == POD_ATTN_MODE_FUSED;
+    if (!fused_append) a.p.n_aunits = 0;
+    a.units_host = fused_append ? (const int32_t*)((const uint8_t*)slot.dev + (p.map.aunits - p.map.pdesc)) : nullptr;
+    const int grid = a.copy_wgs + (a.p.n_aunits + kWaves - 1) / kWaves;
+    void* args[] = {&a};
+    POD_HIP(hipLaunchKernel(h->ks.stage, dim3(grid), dim3(kThreads), args, 0, stream));
+  }
+  POD_HIP(hipEventRecord(slot.done, stream));
+  slot.pending = true;
 
   hipEvent_t prof_start = h->prof_start, prof_end = h->prof_end;
   h->prof_start = h->prof_end = nullptr;
@@ -305,12 +320,14 @@ pod_attn_status pod_attn_run(pod_attn_handle* h, const void* q, const void* k_ca
     POD_HIP(launch(h->ks.fused, grid, kp, stream));
   } else if (mode == POD_ATTN_MODE_SEPARATE) {
     kp.inline_combine = 0;
+    if (kp.n_aunits) POD_HIP(launch(h->ks.append, (kp.n_aunits + kWaves - 1) / kWaves, kp, stream));
     if (p.n_pf_items) POD_HIP(launch(h->ks.prefill, p.n_pf_items, kp, stream));
     if (p.n_dc_items) POD_HIP(launch(h->ks.decode, (p.n_dc_items + kWaves - 1) / kWaves, kp, stream));
     if (p.n_pf_groups) POD_HIP(launch_combine(h, kp, 0, p.n_pf_groups, p.tile_cols, stream));
     if (p.n_groups > p.n_pf_groups) POD_HIP(launch_combine(h, kp, p.n_pf_groups, p.n_groups, h->cfg.group(), stream));
   } else {
     kp.inline_combine = 0;
+    if (kp.n_aunits) POD_HIP(launch(h->ks.append, (kp.n_aunits + kWaves - 1) / kWaves, kp, stream));
     POD_HIP(hipEventRecord(h->evStart, stream));
     POD_HIP(hipStreamWaitEvent(h->sA, h->evStart, 0));
     POD_HIP(hipStreamWaitEvent(h->sB, h->evStart, 0));
@@ -341,11 +358,26 @@ pod_attn_status pod_attn_run(pod_attn_handle* h, const void* q, const void* k_ca
   s.prefill_wg_budget = mode == POD_ATTN_MODE_FUSED ? kp.prefill_wg_budget : 0;
   s.workspace_bytes = p.map.total;
   s.host_plan_us = plan_us;
+  s.num_append_units = kp.n_aunits;
   if (log_on())
     std::fprintf(stderr, "[pod_attn] run: mode=%d reason=%d pf_items=%d dc_items=%d groups=%d split=%d grid=%d plan=%.1fus\n",
                  mode, reason, p.n_pf_items, p.n_dc_items, p.n_groups, p.decode_split_tokens, grid, plan_us);
   h->last_plan = std::move(p);
   return POD_ATTN_OK;
+}
+
+pod_attn_status pod_attn_run(pod_attn_handle* h, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, const pod_attn_batch* b, void* out,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return run_impl(h, q, nullptr, nullptr, k_cache, v_cache, block_tables, b, out, workspace, workspace_bytes, stream);
+}
+
+pod_attn_status pod_attn_run_append(pod_attn_handle* h, const void* q, const void* k_new, const void* v_new,
+                                    void* k_cache, void* v_cache, const int32_t* block_tables,
+                                    const pod_attn_batch* b, void* out, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  if (!k_new || !v_new) return fail(POD_ATTN_ERR_INVALID_ARG, "null k_new or v_new");
+  return run_impl(h, q, k_new, v_new, k_cache, v_cache, block_tables, b, out, workspace, workspace_bytes, stream);
 }
 
 pod_attn_status pod_attn_set_kernel_events(pod_attn_handle* h, void* ev_start, void* ev_end) {

@@ -37,6 +37,19 @@ enum DescField {
   kDescInts = 16
 };
 
+// KV append unit: the new tokens of one sequence that fall in one page (a run of consecutive
+// slots), for a range of KV heads; one wave writes one unit before the attention launches.
+enum AUnitField {
+  kASeq = 0,        // block-table row
+  kARow,            // q/k_new/v_new row of the first token
+  kAPos,            // absolute position of the first token
+  kANtok,           // tokens (1..16, one page)
+  kAHead,           // first KV head
+  kANh,             // KV heads
+  kAUnitInts = 8
+};
+constexpr int kAppendTokenHeads = 16;   // token-heads per append unit (at most)
+
 // Control block (int32 words at the start of the workspace), zeroed by every run.
 enum CtrlWord {
   kCQueuePrefill = 0,
@@ -67,6 +80,10 @@ struct KernelParams {
   const int32_t* pdesc;      // prefill descriptors
   const int32_t* pitems;     // prefill item table (header, then (desc, split << 16 | head) per item)
   const int32_t* ddesc;      // decode descriptors
+  const void* k_new;         // [total_q][Hkv][D] keys of the new tokens (append), or null
+  const void* v_new;         // [total_q][Hkv][D] values of the new tokens
+  const int32_t* aunits;     // [n_aunits][kAUnitInts] append units (workspace copy)
+  int n_aunits;
   float* part_o;             // [slots][D]
   float* part_lse;           // [slots], log2-domain log-sum-exp
   int n_pdesc, n_ddesc;
@@ -80,12 +97,21 @@ struct KernelParams {
   int inline_combine;        // 1: the last-arriving decode split merges its group in-kernel (fused)
   int group_begin, group_end;// combine kernel range
   int combine_col_blocks;     // combine kernel: workgroups per group (16 columns each)
-  int decode_block_claim;     // fused: a decode-role workgroup claims 4 consecutive items at once
+};
+
+// Arguments of the plan-upload launch (which also writes the KV append in fused mode).
+struct StageArgs {
+  KernelParams p;            // append fields: k, v, bt, k_new, v_new, hkv, bt_stride, num_pages, n_aunits
+  const void* src;           // pinned host staging buffer (its device-visible address)
+  void* dst;                 // workspace
+  int n_zero16, n_copy16;    // 16-byte words zero-filled, then copied from src
+  int copy_wgs;              // workgroups [0, copy_wgs) upload the plan; the rest write append units
+  const int32_t* units_host; // append units inside the staging buffer, or null
 };
 
 // Workspace map (byte offsets), computed by the planner.
 struct WorkspaceMap {
-  size_t ctrl, tickets, claims, pdesc, pitems, ddesc, copy_bytes;  // [0, pdesc) zeroed, [pdesc, copy_bytes) staged from the host
+  size_t ctrl, tickets, claims, pdesc, pitems, ddesc, aunits, copy_bytes;  // [0, pdesc) zeroed, [pdesc, copy_bytes) staged from the host
   size_t part_o, part_lse, trace, total;
 };
 

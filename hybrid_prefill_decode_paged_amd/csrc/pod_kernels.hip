@@ -281,6 +281,117 @@ __device__ __forceinline__ int arrive_last(int32_t* ticket, int ns) {
   return __builtin_amdgcn_readfirstlane(last);
 }
 
+// ------------------------------------------------------------------ KV append
+// The step's new tokens are written into their pages before attention reads them ([W6] "KV
+// Cache": each step adds the new tokens' keys and values to the cache; [W6] "PagedAttention":
+// position p of a sequence lives in slot p % 16 of the physical page that the sequence's
+// block-table row names for logical page p / 16).  One wave writes one unit: a run of
+// consecutive slots of one page for a range of KV heads, through a buffer resource over all
+// KV-head slabs of that page with streaming stores (the attention kernels that read the pages
+// start after this launch has completed).
+// K: lane-consecutive stores are consecutive slots of one 16-byte chunk, i.e. contiguous bytes.
+// V: where the run covers a whole 16-byte part of a dim (8 bf16 or 4 fp32 slots), a lane gathers
+// the part's slots from the rows and stores the part, lanes covering consecutive parts; the
+// run's remaining slots are written one element at a time, lanes covering consecutive dims.  A
+// block-table entry outside the pool is not written through; the attention kernels, which read
+// every page of the context, report it.
+constexpr int kCachePolicyStream = 2;   // nt
+template <typename T, int D>
+__device__ void append_unit(const KernelParams& P, int seq, int row0, int pos0, int ntok, int h0, int nh) {
+  using Gm = Geo<T, D>;
+  constexpr int E = Gm::kBytes;
+  const int lane = threadIdx.x & 63;
+  const int slot0 = pos0 & (kPage - 1);
+  const int pg = ((CPTR(int32_t))P.bt)[(size_t)seq * P.bt_stride + (pos0 >> 4)];
+  if ((unsigned)pg < (unsigned)P.num_pages) {
+    const int bytes = P.hkv * Gm::kSlab;
+    const BufRsrc rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(slab_ptr<T, D>(P.k, pg, P.hkv, 0)), (short)0, bytes, 0x00020000);
+    const BufRsrc rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(slab_ptr<T, D>(P.v, pg, P.hkv, 0)), (short)0, bytes, 0x00020000);
+    const size_t row_bytes = (size_t)P.hkv * D * E;                 // one row of k_new / v_new
+    const char* kn = (const char*)P.k_new + (size_t)row0 * row_bytes + (size_t)h0 * D * E;
+    const char* vn = (const char*)P.v_new + (size_t)row0 * row_bytes + (size_t)h0 * D * E;
+    // Batches carry no branches: a lane past the end reloads the last item and its stores get an
+    // offset past the resource, which the hardware drops; so every load of a batch is in flight
+    // before the first store waits.
+    constexpr int kDrop = 1 << 30;
+    constexpr int kV = Gm::kEpc;                   // elements per 16 bytes = slots per V part
+    const int hd = D * E;                          // bytes of one head's row
+    // K: items (head, chunk, token), token fastest; 4 per lane in flight.
+    const int nk = nh * Gm::kNch * ntok;
+    for (int i0 = 0; i0 < nk; i0 += 64 * 4) {
+      u32x4 v[4];
+      int off[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = i0 + 64 * j + lane, ic = min(i, nk - 1);
+        const int t = ic % ntok, r = ic / ntok;
+        const int c = r % Gm::kNch, hh = r / Gm::kNch;
+        v[j] = ld16(kn + t * row_bytes + hh * hd + c * 16);
+        off[j] = i < nk ? (h0 + hh) * Gm::kSlab + k_chunk_off(c, slot0 + t) : kDrop;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) __builtin_amdgcn_raw_buffer_store_b128(v[j], rk, off[j], 0, kCachePolicyStream);
+    }
+    // V, whole 16-byte parts (kV consecutive slots of one dim): parts [pf_lo, pf_hi) lie inside
+    // the run.  Item (head, dim, part), part fastest, so that a store instruction's lanes write
+    // whole consecutive lines; each item gathers its kV slots from kV rows (consecutive lanes read
+    // consecutive dims of a row); 4 items per lane in flight.
+    const int pf_lo = (slot0 + kV - 1) / kV, pf_hi = (slot0 + ntok) / kV;
+    const int nfull = max(0, pf_hi - pf_lo);
+    const int nvf = nh * D * nfull;
+    for (int i0 = 0; i0 < nvf; i0 += 64 * 4) {
+      u32x4 w[4];
+      int off[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = i0 + 64 * j + lane, ic = min(i, nvf - 1);
+        const int pp = pf_lo + ic % nfull, r = ic / nfull;
+        const int d = r % D, hh = r / D;
+        const char* src = vn + (size_t)(pp * kV - slot0) * row_bytes + hh * hd + d * E;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          if constexpr (E == 2) {
+            const uint32_t lo = *(const uint16_t*)(src + (2 * m) * row_bytes);
+            const uint32_t hi = *(const uint16_t*)(src + (2 * m + 1) * row_bytes);
+            w[j][m] = lo | (hi << 16);
+          } else {
+            w[j][m] = *(const uint32_t*)(src + m * row_bytes);
+          }
+        }
+        off[j] = i < nvf ? (h0 + hh) * Gm::kSlab + v_elem_off<T>(d, pp * kV) : kDrop;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) __builtin_amdgcn_raw_buffer_store_b128(w[j], rv, off[j], 0, kCachePolicyStream);
+    }
+    // V, the run's other slots (before the first whole part and after the last), one element
+    // each.  Item (head, slot, dim), dim fastest: a load instruction reads consecutive dims of a
+    // row and a store instruction fills 4 elements of each line it touches; 16 per lane in flight.
+    const int head_len = nfull > 0 ? pf_lo * kV - slot0 : ntok;
+    const int npart = ntok - nfull * kV;
+    const int nvp = nh * D * npart;
+    for (int i0 = 0; i0 < nvp; i0 += 64 * 16) {
+      uint32_t x[16];
+      int off[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int i = i0 + 64 * j + lane, ic = min(i, nvp - 1);
+        const int d = ic % D, r = ic / D;
+        const int kk = r % npart, hh = r / npart;
+        const int slot = kk < head_len ? slot0 + kk : pf_hi * kV + (kk - head_len);
+        const char* src = vn + (size_t)(slot - slot0) * row_bytes + hh * hd + d * E;
+        if constexpr (E == 2) x[j] = *(const uint16_t*)src;
+        else x[j] = *(const uint32_t*)src;
+        off[j] = i < nvp ? (h0 + hh) * Gm::kSlab + v_elem_off<T>(d, slot) : kDrop;
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if constexpr (E == 2) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)x[j], rv, off[j], 0, kCachePolicyStream);
+        else __builtin_amdgcn_raw_buffer_store_b32(x[j], rv, off[j], 0, kCachePolicyStream);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ log-sum-exp combine
 // out = sum_s w_s o_s / sum_s w_s with w_s = 2^(lse_s - max lse); empty splits weigh zero.
 // In-kernel form, run by one wave for up to 16 columns of a group: the splits' lse values go to
@@ -1146,26 +1257,6 @@ __device__ __forceinline__ int claim_prefill(const KernelParams& P, int xcc) {
   return P.n_pf_items;
 }
 
-// Decode stream of one wave: claim items one at a time from the decode counter (the next
-// claim is issued before the current item is processed) until the counter passes the end.
-template <typename T, int D>
-__device__ void decode_wave_stream(const KernelParams& P, int cu, float* sw) {
-  const int lane = threadIdx.x & 63;
-  int* counter = P.ctrl + kCQueueDecode;
-  for (;;) {
-    // Claim after the previous item is done: items run for tens of microseconds, so claiming
-    // ahead would reserve work that idle waves could otherwise take at the end.
-    int item = 0;
-    if (lane == 0) item = atomicAdd(counter, 1);
-    item = __builtin_amdgcn_readfirstlane(item);
-    if (item >= P.n_dc_items) break;
-    if (lane == 0) note_claim(P, 1, item, cu);
-    const uint32_t t0 = trace_start(P);
-    decode_wave_item<T, D>(P, item, sw);
-    if (lane == 0) trace_item(P, 1, item, t0, cu);
-  }
-}
-
 // ------------------------------------------------------------------ kernels
 // Fused persistent kernel: every workgroup loops, taking a role and claiming work of that kind.
 // While decode work remains, at most `prefill_cap_per_cu` workgroups per CU (one by default) and
@@ -1216,27 +1307,22 @@ __global__ __launch_bounds__(kThreads, 2) void pod_fused_kernel(KernelParams P) 
     __syncthreads();
     if (role < 0) break;
     if (role == 1) {
-      if (P.decode_block_claim) {
-        // The workgroup claims 4 consecutive items (adjacent KV heads of one key range) and each
-        // wave streams one of them; the next block is claimed once the current one is done.
-        float* sw = (float*)(lds + wave_index() * kCombineLdsPerWave);
-        for (;;) {
-          if (tid == 0) s_item = atomicAdd(P.ctrl + kCQueueDecode, kWaves);
-          __syncthreads();
-          const int base = s_item;
-          __syncthreads();
-          if (base >= P.n_dc_items) break;
-          const int item = base + wave_index();
-          if (item < P.n_dc_items) {
-            if ((tid & 63) == 0) note_claim(P, 1, item, cu);
-            const uint32_t t0 = trace_start(P);
-            decode_wave_item<T, D>(P, item, sw);
-            if ((tid & 63) == 0) trace_item(P, 1, item, t0, cu);
-          }
-        }
-      } else {
-        decode_wave_stream<T, D>(P, cu, (float*)(lds + wave_index() * kCombineLdsPerWave));
+      // The workgroup claims 4 consecutive items (adjacent KV heads of one key range) and each
+      // wave streams one of them; the next block is claimed once the current one is done.
+      float* sw = (float*)(lds + wave_index() * kCombineLdsPerWave);
+      for (;;) {
+        if (tid == 0) s_item = atomicAdd(P.ctrl + kCQueueDecode, kWaves);
         __syncthreads();
+        const int base = s_item;
+        __syncthreads();
+        if (base >= P.n_dc_items) break;
+        const int item = base + wave_index();
+        if (item < P.n_dc_items) {
+          if ((tid & 63) == 0) note_claim(P, 1, item, cu);
+          const uint32_t t0 = trace_start(P);
+          decode_wave_item<T, D>(P, item, sw);
+          if ((tid & 63) == 0) trace_item(P, 1, item, t0, cu);
+        }
       }
       dc_open = false;
       continue;
@@ -1370,15 +1456,41 @@ __global__ __launch_bounds__(kThreads) void pod_gather_kernel(const void* cache,
   ((T*)out)[idx] = val;
 }
 
-// Plan upload, launched before the attention kernels on the same stream: the workspace's counter
-// region [0, 16 n_zero16) is zero-filled and the descriptor region after it is copied from the
-// pinned host staging buffer (read over the host link), one 16-byte word per thread.  A kernel
-// starts sooner after the previous kernel than a DMA copy's completion can release it.
-__global__ __launch_bounds__(kThreads) void pod_stage_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
-                                                             int n_zero16, int n_copy16) {
-  const int i = (int)blockIdx.x * kThreads + (int)threadIdx.x;
-  if (i < n_zero16) dst[i] = u32x4{0u, 0u, 0u, 0u};
-  else if (i < n_zero16 + n_copy16) dst[i] = src[i - n_zero16];
+// Separate-mode KV append, launched after the plan upload and before the attention kernels:
+// wave w of workgroup b writes unit 4b + w.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void pod_append_kernel(KernelParams P) {
+  const int u = (int)blockIdx.x * kWaves + wave_index();
+  if (u >= P.n_aunits) return;
+  CPTR(int32_t) a = (CPTR(int32_t))P.aunits + (size_t)u * kAUnitInts;
+  append_unit<T, D>(P, a[kASeq], a[kARow], a[kAPos], a[kANtok], a[kAHead], a[kANh]);
+}
+
+// Plan upload, launched before the attention kernels on the same stream: workgroups
+// [0, copy_wgs) zero-fill the workspace's counter region [0, 16 n_zero16) and copy the
+// descriptor region after it from the pinned host staging buffer (read over the host link), one
+// 16-byte word per thread.  A kernel starts sooner after the previous kernel than a DMA copy's
+// completion can release it.  In fused mode the KV append rides in the same launch: wave w of
+// workgroup copy_wgs + b writes unit 4b + w, its fields read from the staging buffer (the
+// workspace copy is being written by this launch), so the persistent kernel that follows reads
+// an updated cache and has nothing to wait for.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void pod_stage_kernel(StageArgs A) {
+  const int b = (int)blockIdx.x;
+  if (b < A.copy_wgs) {
+    const int i = b * kThreads + (int)threadIdx.x;
+    u32x4* dst = (u32x4*)A.dst;
+    if (i < A.n_zero16) dst[i] = u32x4{0u, 0u, 0u, 0u};
+    else if (i < A.n_zero16 + A.n_copy16) dst[i] = ((const u32x4*)A.src)[i - A.n_zero16];
+    return;
+  }
+  const int u = (b - A.copy_wgs) * kWaves + wave_index();
+  if (u >= A.p.n_aunits) return;
+  const u32x4* f = (const u32x4*)(A.units_host + (size_t)u * kAUnitInts);
+  const u32x4 f0 = f[0], f1 = f[1];          // every lane reads the same 32 bytes
+  append_unit<T, D>(A.p, __builtin_amdgcn_readfirstlane(f0[kASeq]), __builtin_amdgcn_readfirstlane(f0[kARow]),
+                    __builtin_amdgcn_readfirstlane(f0[kAPos]), __builtin_amdgcn_readfirstlane(f0[kANtok]),
+                    __builtin_amdgcn_readfirstlane(f1[kAHead - 4]), __builtin_amdgcn_readfirstlane(f1[kANh - 4]));
 }
 
 template <typename T, int D>
@@ -1389,7 +1501,8 @@ KernelSet make_set() {
   s.decode = (const void*)&pod_decode_kernel<T, D>;
   s.combine = (const void*)&pod_combine_kernel<T, D>;
   s.gather = (const void*)&pod_gather_kernel<T, D>;
-  s.stage = (const void*)&pod_stage_kernel;
+  s.stage = (const void*)&pod_stage_kernel<T, D>;
+  s.append = (const void*)&pod_append_kernel<T, D>;
   s.fused_lds = Geo<T, D>::kFusedLds;
   s.prefill_kv_tile = Geo<T, D>::kTileKeys;
   return s;

@@ -279,3 +279,18 @@ def custom_spec(dtype="bf16", Hq=4, Hkv=2, D=128, prefill=((16, 40),), decode=(3
     return BatchSpec(f"custom-{dtype}-{Hq}-{Hkv}-{D}", dtype, Hq, Hkv, D, pq, pc, dec,
                      num_pages=max(1, live + pool_slack), seed=seed,
                      value_scale=kw.pop("value_scale", 1.0 if dtype == "fp32" else 0.5), **kw)
+
+
+def new_tokens(spec: BatchSpec, seed: int, device="cpu"):
+    """The step's new keys and values, k_new and v_new [total_q, Hkv, D] in the batch's dtype
+    (rows in query-row order), drawn N(0,1) * value_scale from a torch generator seeded with
+    ``seed`` (k_new first, then v_new)."""
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    shape = (spec.total_q, spec.num_kv_heads, spec.head_dim)
+    k_new = torch.empty(shape, dtype=spec.torch_dtype, device=device)
+    v_new = torch.empty(shape, dtype=spec.torch_dtype, device=device)
+    _fill_normal(k_new, gen, spec.value_scale, 1 << 28)
+    _fill_normal(v_new, gen, spec.value_scale, 1 << 28)
+    return k_new, v_new

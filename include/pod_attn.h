@@ -145,6 +145,7 @@ typedef struct pod_attn_stats {
   size_t workspace_bytes;       /* workspace needed by this batch                             */
   double host_plan_us;          /* host planning time of the last run                         */
   int prefill_wg_budget;        /* FUSED: prefill-role workgroups allowed while decode remains */
+  int num_append_units;         /* KV append units of the last run (0 for pod_attn_run)      */
 } pod_attn_stats;
 
 /* Create a handle for one attention configuration on the current HIP device.  Validates the
@@ -166,6 +167,27 @@ pod_attn_status pod_attn_run(pod_attn_handle* h, const void* q, const void* k_ca
                              const void* v_cache, const int32_t* block_tables,
                              const pod_attn_batch* batch, void* out, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/* KV append, then the hybrid batch: the step's new tokens are first written into the cache and
+ * attention then reads them ([W6] "KV Cache": each step adds the new tokens' keys and values to
+ * the cache before attending; [W6] "PagedAttention": position p of sequence s is slot p % 16 of
+ * page block_tables[s][p / 16]).  k_new and v_new are device buffers [total_q][Hkv][D] of the
+ * cache's element type, rows in q's row order; row r's token is written at its query position
+ * (a prefill chunk's L rows at ctx-L .. ctx-1, a decode row at ctx-1) into k_cache / v_cache,
+ * then the result is exactly that of pod_attn_run on the updated cache.  Only the slots of the
+ * new positions are written; every other cache byte is left as it was.  FUSED: the append rides
+ * in the plan-upload launch that precedes the persistent attention kernel (no extra launch);
+ * SEPARATE and STREAMS: an append kernel of its own runs after the upload, before attention.
+ * Slots of the new positions must be distinct: two rows mapping to the same slot give an
+ * unspecified byte mix.  A block-table entry outside the pool is not written through and is
+ * reported as POD_ATTN_DEVICE_ERR_BAD_PAGE by the attention kernels, which read that page.  Null k_new or
+ * v_new, or buffers not 16-byte aligned, give POD_ATTN_ERR_INVALID_ARG; the workspace is sized
+ * by pod_attn_workspace_size as for pod_attn_run.  The caller owns every buffer. */
+pod_attn_status pod_attn_run_append(pod_attn_handle* h, const void* q, const void* k_new,
+                                    const void* v_new, void* k_cache, void* v_cache,
+                                    const int32_t* block_tables, const pod_attn_batch* batch,
+                                    void* out, void* workspace, size_t workspace_bytes,
+                                    void* stream);
 
 /* Copy the diagnostics of the last run into *st. */
 pod_attn_status pod_attn_get_stats(pod_attn_handle* h, pod_attn_stats* st);
@@ -212,10 +234,11 @@ pod_attn_status pod_attn_plan_inspect(const pod_attn_config* cfg, const pod_attn
                                       int items_cap, int* n_items, pod_attn_stats* stats);
 
 /* Profiling hook: when ev_start / ev_end (hipEvent_t, may be NULL) are set, the next
- * pod_attn_run records ev_start on the launch stream right after the plan copy, before the
- * first attention kernel, and ev_end after the last one (FUSED mode: the fused kernel alone;
- * SEPARATE mode: prefill, decode and combine kernels; STREAMS mode: after the join), so that
- * the attention kernels' own duration can be read with hipEventElapsedTime.
+ * pod_attn_run (or pod_attn_run_append) records ev_start on the launch stream right after the
+ * plan upload, before the first attention kernel, and ev_end after the last one (FUSED mode:
+ * the fused kernel alone; SEPARATE mode: the append kernel if any, then prefill, decode and
+ * combine kernels; STREAMS mode: from the append kernel if any to after the join), so that the
+ * kernels' own duration can be read with hipEventElapsedTime.
  * The hook is consumed by that run (one-shot); the events stay owned by the caller. */
 pod_attn_status pod_attn_set_kernel_events(pod_attn_handle* h, void* ev_start, void* ev_end);
 
