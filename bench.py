@@ -6,7 +6,8 @@ fraction of the max(MFMA, HBM) roofline.
 One step = one pod_attn_run over the whole hybrid batch (prefill tiles + decode split-KV +
 combine), inputs resident in HBM.  Prints ONE JSON line.  Beside it, "kv_append" times the
 same step preceded by the KV append of every row's new K/V (pod_attn_run_append) in the fused
-and separate modes.  The default workload is the
+and separate modes, and "small_q_extend" times a speculative-verification step (4-token
+extends) with the extends on the decode path and on the prefill-tile path.  The default workload is the
 Llama-2-7B-shaped layer (32 query / 32 KV heads, head_dim 128, bf16, 16-token pages): one
 1024-token prefill chunk at offset 3072 plus 64 decodes at context 4096, over a randomly
 permuted 40960-page pool.  The other workloads are parity-test cases; --workload selects them
@@ -49,10 +50,20 @@ def algorithmic_work(spec):
             "pairs_prefill": Hq * pairs_pf, "pairs_decode": Hq * pairs_dc}
 
 
+def _ctx_desc(ctx):
+    return f"{ctx[0]}" if len(set(ctx)) == 1 else f"{min(ctx)}..{max(ctx)}, mean {sum(ctx) / len(ctx):.0f}"
+
+
 def workload_desc(spec):
-    pre = ", ".join(f"{L}@{c - L}" for L, c in zip(spec.prefill_q_len, spec.prefill_ctx_len))
+    if len(spec.prefill_q_len) <= 4:
+        pre = ", ".join(f"{L}@{c - L}" for L, c in zip(spec.prefill_q_len, spec.prefill_ctx_len))
+    else:                                   # many chunks: one entry per chunk length
+        by_len = {}
+        for L, c in zip(spec.prefill_q_len, spec.prefill_ctx_len):
+            by_len.setdefault(L, []).append(c)
+        pre = ", ".join(f"{len(v)}x{L} (ctx {_ctx_desc(v)})" for L, v in sorted(by_len.items(), reverse=True))
     dc = spec.decode_ctx_len
-    dec = f"{len(dc)}x{dc[0]}" if len(set(dc)) == 1 else f"{len(dc)} (ctx {min(dc)}..{max(dc)}, mean {sum(dc) / len(dc):.0f})"
+    dec = f"{len(dc)} (ctx {_ctx_desc(dc)})" if dc else "0"
     return {"workload": f"{spec.name}: hybrid batch, prefill chunks [{pre}] + {dec} decodes",
             "heads_q_kv_dim": [spec.num_q_heads, spec.num_kv_heads, spec.head_dim],
             "page_tokens": 16, "pool_pages": spec.num_pages, "pages": "random permutation",
@@ -183,6 +194,7 @@ def main():
     ap.add_argument("--no-compare", action="store_true", help="skip timing the other two modes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-append", action="store_true", help="skip timing the KV-append variant")
+    ap.add_argument("--no-extend", action="store_true", help="skip timing the small-q extend workload")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (counter calibration)")
@@ -256,6 +268,33 @@ def main():
             del ws, out
             h.close()
 
+    extend = None
+    if not args.no_extend:
+        # Small-q extends: a speculative-verification step shaped like the Llama-3-8B workload
+        # (128 sequences extending by 4 tokens each, plus its 2048-token chunk), fused mode,
+        # with the extends on the decode path (default) and on the prefill-tile path.
+        xs = gen.spec_verify_spec(4)
+        print(f"[bench] generating {xs.name}: {xs.num_pages} pages", file=sys.stderr, flush=True)
+        xb = gen.make_batch(xs, "cuda")
+        xmeta = binding.BatchMeta.from_batch(xb)
+        xw = algorithmic_work(xs)
+        x_roof = max(xw["flops"] / PEAK_MFMA[xs.dtype], xw["bytes"] / PEAK_HBM)
+        extend = {"workload": workload_desc(xs)["workload"], "t_roof_us": round(x_roof * 1e6, 2)}
+        for name, emax in (("decode_path", 0), ("tile_path", -1)):
+            h = binding.PodAttention(xs.num_q_heads, xs.num_kv_heads, xs.head_dim, xs.dtype, "fused",
+                                     scale=xs.softmax_scale, extend_max_q=emax)
+            ws = torch.empty(h.workspace_size(xmeta), dtype=torch.uint8, device="cuda")
+            out = torch.empty_like(xb.q)
+            steps = max(5, args.steps // 2)
+            print(f"[bench] timing small-q extends on the {name} steps={steps}", file=sys.stderr, flush=True)
+            ms, kern_ms, _ = time_mode(torch, h, xb, xmeta, out, ws, steps, args.warmup)
+            extend[name] = {"us_per_iter": round(ms * 1e3, 2), "kernel_us_mean": round(kern_ms * 1e3, 2),
+                            "frac": round(x_roof / (kern_ms / 1e3), 4),
+                            "small_extends": h.stats()["num_small_extends"]}
+            del ws, out
+            h.close()
+        del xb
+
     main_ms = results[args.mode]["us_per_iter"] / 1e3
     kern_s = results[args.mode]["kernel_us_mean"] / 1e6
     if bound == "hbm":
@@ -289,6 +328,7 @@ def main():
         "fused_vs_separate": (round(results["separate"]["us_per_iter"] / results["fused"]["us_per_iter"], 4)
                               if "separate" in results and "fused" in results else None),
         "kv_append": append,
+        "small_q_extend": extend,
         "plan": {k: st[k] for k in ("num_prefill_items", "num_decode_items", "num_combine_groups",
                                     "decode_split_tokens", "prefill_max_splits", "grid_wgs", "wgs_per_cu",
                                     "num_cus", "vgprs_per_lane", "lds_bytes_per_wg", "mode_used", "prefill_wg_budget",

@@ -37,7 +37,7 @@ class Config(C.Structure):
     _fields_ = [("num_q_heads", C.c_int), ("num_kv_heads", C.c_int), ("head_dim", C.c_int),
                 ("page_size", C.c_int), ("dtype", C.c_int), ("mode", C.c_int), ("scale", C.c_float),
                 ("decode_split_tokens", C.c_int), ("prefill_split_cap", C.c_int),
-                ("wgs_per_cu", C.c_int), ("flags", C.c_int)]
+                ("wgs_per_cu", C.c_int), ("flags", C.c_int), ("extend_max_q", C.c_int)]
 
 
 class Batch(C.Structure):
@@ -54,7 +54,7 @@ class Stats(C.Structure):
         "prefill_max_splits", "decode_split_tokens", "decode_max_splits", "grid_wgs", "wgs_per_cu",
         "num_cus", "lds_bytes_per_wg", "vgprs_per_lane")] + [
         ("workspace_bytes", C.c_size_t), ("host_plan_us", C.c_double), ("prefill_wg_budget", C.c_int),
-        ("num_append_units", C.c_int)]
+        ("num_append_units", C.c_int), ("num_small_extends", C.c_int)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -108,10 +108,11 @@ def _check(status: int):
 
 
 def make_config(num_q_heads, num_kv_heads, head_dim, dtype="bf16", mode="fused", scale=0.0,
-                decode_split_tokens=0, prefill_split_cap=0, wgs_per_cu=0, flags=0) -> Config:
+                decode_split_tokens=0, prefill_split_cap=0, wgs_per_cu=0, flags=0, extend_max_q=0) -> Config:
     return Config(num_q_heads, num_kv_heads, head_dim, 16, BF16 if dtype == "bf16" else FP32,
                   MODES[mode] if isinstance(mode, str) else int(mode), float(scale),
-                  int(decode_split_tokens), int(prefill_split_cap), int(wgs_per_cu), int(flags))
+                  int(decode_split_tokens), int(prefill_split_cap), int(wgs_per_cu), int(flags),
+                  int(extend_max_q))
 
 
 class BatchMeta:
@@ -167,10 +168,10 @@ class PodAttention:
     """One library handle (one head configuration) on the current HIP device."""
 
     def __init__(self, num_q_heads, num_kv_heads, head_dim, dtype="bf16", mode="fused", scale=0.0,
-                 decode_split_tokens=0, prefill_split_cap=0, wgs_per_cu=0, flags=0):
+                 decode_split_tokens=0, prefill_split_cap=0, wgs_per_cu=0, flags=0, extend_max_q=0):
         self.lib = load()
         self.cfg = make_config(num_q_heads, num_kv_heads, head_dim, dtype, mode, scale,
-                               decode_split_tokens, prefill_split_cap, wgs_per_cu, flags)
+                               decode_split_tokens, prefill_split_cap, wgs_per_cu, flags, extend_max_q)
         h = C.c_void_p()
         _check(self.lib.pod_attn_create(C.byref(self.cfg), C.byref(h)))
         self.h = h

@@ -58,12 +58,15 @@ pod_attn_status validate_config(const pod_attn_config* c, Config* out, std::stri
   if (c->prefill_split_cap < 0 || c->prefill_split_cap > kMaxCombineSplits || c->wgs_per_cu < 0 || c->wgs_per_cu > 8) {
     *err = "prefill_split_cap must be in [0, 128] and wgs_per_cu in [0, 8]"; return POD_ATTN_ERR_INVALID_ARG;
   }
+  if (c->extend_max_q < -1 || c->extend_max_q > 256) {
+    *err = "extend_max_q must be -1, 0 or in [1, 256]"; return POD_ATTN_ERR_INVALID_ARG;
+  }
   Config k;
   k.hq = c->num_q_heads; k.hkv = c->num_kv_heads; k.d = c->head_dim; k.page = c->page_size;
   k.dtype = c->dtype; k.mode = c->mode;
   k.scale = c->scale > 0.f ? c->scale : 1.0f / std::sqrt((float)c->head_dim);
   k.decode_split_tokens = c->decode_split_tokens; k.prefill_split_cap = c->prefill_split_cap;
-  k.wgs_per_cu = c->wgs_per_cu; k.flags = c->flags;
+  k.wgs_per_cu = c->wgs_per_cu; k.flags = c->flags; k.extend_max_q = c->extend_max_q;
   *out = k;
   return POD_ATTN_OK;
 }
@@ -143,10 +146,17 @@ pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus
   p.prefill_max_splits = 0;
   struct PGroup { double work; std::vector<int32_t> items; };   // items: (desc, split << 16 | head)
   std::vector<PGroup> pgroups;
+  // Small-q extends: a chunk of at most extend_max_q rows reads its whole prefix for a few
+  // queries, which is a decode-shaped (bandwidth-bound) job; it runs on the decode path, cut
+  // into pieces of at most 16 (query, head) columns ([W6] "한 스텝에 여러 종류의 request 섞기":
+  // a decode is an extend of one token).
+  const int emax = c.extend_max_q < 0 ? 0 : (c.extend_max_q == 0 ? kExtendMaxQ : c.extend_max_q);
+  std::vector<int> small_chunks;
   for (int i = 0; i < b->num_prefill; ++i) {
     const int L = b->prefill_q_start[i + 1] - b->prefill_q_start[i];
     const int ctx = b->prefill_ctx_len[i];
     if (L == 0) continue;
+    if (L <= emax) { small_chunks.push_back(i); continue; }
     int ns_c = std::max(1, std::min(std::min(cap, kMaxCombineSplits), ceil_div(ctx, 4096)));
     const int st = round_up_int(ceil_div(ctx, ns_c), kPrefillKvTile);
     ns_c = ceil_div(ctx, st);
@@ -207,9 +217,23 @@ pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus
   p.pitems[kXcds] = p.n_pf_items;
   p.n_pf_groups = group;
 
-  // ---------------- decode sequences
+  // ---------------- decode sequences and small-q extend pieces
+  struct DPiece { int seq, q_row, n_q, q_pos, kv_len; };
+  std::vector<DPiece> pieces;
+  for (int i = 0; i < b->num_decode; ++i)
+    pieces.push_back({b->num_prefill + i, (int)prefill_rows + i, 1, b->decode_ctx_len[i] - 1, b->decode_ctx_len[i]});
+  const int qpp = std::max(1, kMaxGroup / G);   // queries per piece: 16 columns
+  for (int i : small_chunks) {
+    const int L = b->prefill_q_start[i + 1] - b->prefill_q_start[i];
+    const int ctx = b->prefill_ctx_len[i];
+    for (int t = 0; t < L; t += qpp) {
+      const int nq = std::min(qpp, L - t);
+      pieces.push_back({i, b->prefill_q_start[i] + t, nq, ctx - L + t, ctx - L + t + nq});
+    }
+  }
+  p.num_small_extends = (int)small_chunks.size();
   long total_tok = 0;
-  for (int i = 0; i < b->num_decode; ++i) total_tok += (long)b->decode_ctx_len[i] * c.hkv;
+  for (const DPiece& pc : pieces) total_tok += (long)pc.kv_len * c.hkv;
   int st_target;
   if (c.decode_split_tokens > 0) {
     st_target = c.decode_split_tokens;
@@ -224,29 +248,30 @@ pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus
     st_target = round_up_int((int)st, 128);
   }
   p.decode_split_tokens = st_target;
-  std::vector<int> order(b->num_decode);
+  std::vector<int> order(pieces.size());
   std::iota(order.begin(), order.end(), 0);
-  std::stable_sort(order.begin(), order.end(), [&](int x, int y) {
-    return b->decode_ctx_len[x] > b->decode_ctx_len[y];
-  });
+  std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return pieces[x].kv_len > pieces[y].kv_len; });
   int ditem = 0;
   p.decode_max_splits = 0;
+  p.decode_max_cols = G;
   for (int i : order) {
-    int ctx = b->decode_ctx_len[i];
-    int ns = std::min(kMaxCombineSplits, ceil_div(ctx, st_target));
-    int st = round_up_int(ceil_div(ctx, ns), 128);
-    ns = ceil_div(ctx, st);
+    const DPiece& pc = pieces[i];
+    const int kv = pc.kv_len, ncols = pc.n_q * G;
+    int ns = std::min(kMaxCombineSplits, ceil_div(kv, st_target));
+    int st = round_up_int(ceil_div(kv, ns), 128);
+    ns = ceil_div(kv, st);
     std::vector<int32_t> d(kDescInts, 0);
-    d[kDSeq] = b->num_prefill + i; d[kDQRow] = (int)prefill_rows + i; d[kDNq] = 1;
-    d[kDQPos] = ctx - 1; d[kDKvLen] = ctx; d[kDNSplit] = ns; d[kDSplitTok] = st;
-    d[kDItemBegin] = ditem; d[kDGroupBegin] = group; d[kDPartBase] = slot; d[kDNcols] = G;
+    d[kDSeq] = pc.seq; d[kDQRow] = pc.q_row; d[kDNq] = pc.n_q;
+    d[kDQPos] = pc.q_pos; d[kDKvLen] = kv; d[kDNSplit] = ns; d[kDSplitTok] = st;
+    d[kDItemBegin] = ditem; d[kDGroupBegin] = group; d[kDPartBase] = slot; d[kDNcols] = ncols;
     ditem += c.hkv * ns;
-    if (ns > 1) { group += c.hkv; slot += c.hkv * ns * G; }
+    if (ns > 1) { group += c.hkv; slot += c.hkv * ns * ncols; }
     p.decode_max_splits = std::max(p.decode_max_splits, ns);
-    p.decode_bytes += 2.0 * ctx * c.hkv * c.d * c.elem_bytes();
+    p.decode_max_cols = std::max(p.decode_max_cols, ncols);
+    p.decode_bytes += 2.0 * kv * c.hkv * c.d * c.elem_bytes();
     p.ddesc.insert(p.ddesc.end(), d.begin(), d.end());
   }
-  p.n_ddesc = b->num_decode;
+  p.n_ddesc = (int)pieces.size();
   p.n_dc_items = ditem;
   p.n_groups = group;
   p.n_slots = slot;

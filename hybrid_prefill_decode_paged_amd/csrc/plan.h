@@ -14,6 +14,7 @@ struct Config {
   float scale = 0.f;
   int decode_split_tokens = 0, prefill_split_cap = 0, wgs_per_cu = 0, flags = 0;
   int append_token_heads = kAppendTokenHeads;   // (token, KV head) pairs per KV append unit
+  int extend_max_q = 0;         // chunks of at most this many rows run on the decode path (0: kExtendMaxQ, <0: never)
   int group() const { return hq / hkv; }
   int elem_bytes() const { return dtype == POD_ATTN_BF16 ? 2 : 4; }
 };
@@ -27,6 +28,8 @@ struct Plan {
   int n_pf_groups = 0, n_groups = 0, n_slots = 0;
   int tile_queries = 0, tile_cols = 0;
   int prefill_max_splits = 0, decode_split_tokens = 0, decode_max_splits = 0;
+  int decode_max_cols = 0;      // widest decode-path descriptor: G, or n_q*G for small-q extends
+  int num_small_extends = 0;    // prefill chunks planned on the decode path
   int total_q = 0, prefill_rows = 0;
   double prefill_flops = 0.0;   // 4*D per visible (query head, key) pair of the prefill share
   double decode_bytes = 0.0;    // K+V bytes of the decode share

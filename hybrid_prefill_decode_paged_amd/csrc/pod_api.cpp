@@ -324,7 +324,7 @@ static pod_attn_status run_impl(pod_attn_handle* h, const void* q, const void* k
     if (p.n_pf_items) POD_HIP(launch(h->ks.prefill, p.n_pf_items, kp, stream));
     if (p.n_dc_items) POD_HIP(launch(h->ks.decode, (p.n_dc_items + kWaves - 1) / kWaves, kp, stream));
     if (p.n_pf_groups) POD_HIP(launch_combine(h, kp, 0, p.n_pf_groups, p.tile_cols, stream));
-    if (p.n_groups > p.n_pf_groups) POD_HIP(launch_combine(h, kp, p.n_pf_groups, p.n_groups, h->cfg.group(), stream));
+    if (p.n_groups > p.n_pf_groups) POD_HIP(launch_combine(h, kp, p.n_pf_groups, p.n_groups, p.decode_max_cols, stream));
   } else {
     kp.inline_combine = 0;
     if (kp.n_aunits) POD_HIP(launch(h->ks.append, (kp.n_aunits + kWaves - 1) / kWaves, kp, stream));
@@ -334,7 +334,7 @@ static pod_attn_status run_impl(pod_attn_handle* h, const void* q, const void* k
     if (p.n_pf_items) POD_HIP(launch(h->ks.prefill, p.n_pf_items, kp, h->sA));
     if (p.n_pf_groups) POD_HIP(launch_combine(h, kp, 0, p.n_pf_groups, p.tile_cols, h->sA));
     if (p.n_dc_items) POD_HIP(launch(h->ks.decode, (p.n_dc_items + kWaves - 1) / kWaves, kp, h->sB));
-    if (p.n_groups > p.n_pf_groups) POD_HIP(launch_combine(h, kp, p.n_pf_groups, p.n_groups, h->cfg.group(), h->sB));
+    if (p.n_groups > p.n_pf_groups) POD_HIP(launch_combine(h, kp, p.n_pf_groups, p.n_groups, p.decode_max_cols, h->sB));
     POD_HIP(hipEventRecord(h->evA, h->sA));
     POD_HIP(hipEventRecord(h->evB, h->sB));
     POD_HIP(hipStreamWaitEvent(stream, h->evA, 0));
@@ -359,6 +359,7 @@ static pod_attn_status run_impl(pod_attn_handle* h, const void* q, const void* k
   s.workspace_bytes = p.map.total;
   s.host_plan_us = plan_us;
   s.num_append_units = kp.n_aunits;
+  s.num_small_extends = p.num_small_extends;
   if (log_on())
     std::fprintf(stderr, "[pod_attn] run: mode=%d reason=%d pf_items=%d dc_items=%d groups=%d split=%d grid=%d plan=%.1fus\n",
                  mode, reason, p.n_pf_items, p.n_dc_items, p.n_groups, p.decode_split_tokens, grid, plan_us);
@@ -468,6 +469,7 @@ pod_attn_status pod_attn_plan_inspect(const pod_attn_config* cfg, const pod_attn
     s.decode_max_splits = p.decode_max_splits;
     s.num_cus = num_cus;
     s.wgs_per_cu = wgs_per_cu;
+    s.num_small_extends = p.num_small_extends;
     s.workspace_bytes = p.map.total;
     *stats = s;
   }

@@ -10,7 +10,8 @@ constexpr int kPage = 16;            // tokens per KV page
 constexpr int kWaves = 4;            // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTileCols = 128;       // (query, head) columns of one prefill tile: 4 waves x 32
-constexpr int kMaxGroup = 16;        // decode columns = group size, one 16-wide MFMA block
+constexpr int kMaxGroup = 16;        // decode-path columns: one 16-wide MFMA block
+constexpr int kExtendMaxQ = 16;      // default: prefill chunks of at most this many rows run on the decode path
 constexpr int kPrefillKvTile = 64;   // keys per prefill inner iteration (4 pages)
 constexpr int kDecodeStep = 32;      // keys per decode wave step (2 pages)
 constexpr int kCuSlots = 1024;       // hashed (XCC, SE, CU) slots for per-CU scheduler state

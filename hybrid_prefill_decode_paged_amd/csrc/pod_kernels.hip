@@ -456,7 +456,10 @@ __device__ void combine_block_wave(const KernelParams& P, CPTR(int32_t) dsc, int
 // One (decode sequence, KV head, key split) streamed by a single wave: the G query heads of
 // the KV head are the columns of one 16-wide MFMA block; 32 keys (two pages) per step, with
 // the next step's K/V loads in flight while the current step is computed.  Waves run their
-// decode items independently (no workgroup barrier, no LDS).
+// decode items independently (no workgroup barrier, no LDS).  A small-q extend piece (n_q
+// query rows at positions q_pos .. q_pos+n_q-1, n_q*G <= 16) takes the same path: column n is
+// query row n / G, head n % G, and on the steps that reach past q_pos each column sees the keys
+// up to its own position ([W6] "Non-Causal vs. Causal Attention").
 template <typename T, int D>
 __device__ void decode_wave_item(const KernelParams& P, int item, float* sw) {
   using Gm = Geo<T, D>;
@@ -471,6 +474,7 @@ __device__ void decode_wave_item(const KernelParams& P, int item, float* sw) {
   const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
   const int G = P.group;
   const int seq = dsc[kDSeq], q_row = dsc[kDQRow], kv_len = dsc[kDKvLen];
+  const int n_q = dsc[kDNq], ncols = dsc[kDNcols], q_pos = dsc[kDQPos];
   const int st = dsc[kDSplitTok];
   const int kv_begin = split * st;
   const int kv_end = min(kv_len, kv_begin + st);
@@ -478,15 +482,16 @@ __device__ void decode_wave_item(const KernelParams& P, int item, float* sw) {
   CPTR(int32_t) btr = (CPTR(int32_t))P.bt + (size_t)seq * P.bt_stride;
   const float sl2 = P.scale_log2;
 
-  // Q^T operand: column n is query head head*G+n (zero when n >= G).
+  // Q^T operand: column n is query row q_row + n/G, head head*G + n%G (zero when n >= ncols).
+  const int qi = n < ncols ? n / G : 0, hh = n < ncols ? n - qi * G : 0;
+  const int cmax = q_pos + qi;                 // the last key column n sees
   u32x4 qop[Gm::kNs];
   {
-    const int hcol = head * G + (n < G ? n : 0);
-    const char* qp = (const char*)P.q + ((size_t)q_row * P.hq + hcol) * (D * Gm::kBytes);
+    const char* qp = (const char*)P.q + ((size_t)(q_row + qi) * P.hq + head * G + hh) * (D * Gm::kBytes);
 #pragma unroll
     for (int s = 0; s < Gm::kNs; ++s) {
       u32x4 v = ld16(qp + (4 * s + q) * 16);
-      qop[s] = n < G ? v : u32x4{0u, 0u, 0u, 0u};
+      qop[s] = n < ncols ? v : u32x4{0u, 0u, 0u, 0u};
     }
   }
 
@@ -516,7 +521,7 @@ __device__ void decode_wave_item(const KernelParams& P, int item, float* sw) {
     }
   };
 
-  auto compute_step = [&](u32x4 (&kr)[2][Gm::kNs], VT (&vr)[2][Gm::kDb], const int (&lim)[2]) {
+  auto compute_step = [&](u32x4 (&kr)[2][Gm::kNs], VT (&vr)[2][Gm::kDb], const int (&lim)[2], int tok0) {
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < Gm::kNs; ++s) {
@@ -528,6 +533,13 @@ __device__ void decode_wave_item(const KernelParams& P, int item, float* sw) {
     for (int i = 0; i < 4; ++i) {
       x[i] = (4 * q + i < lim[0]) ? s0[i] : kNegInf;
       x[4 + i] = (4 * q + i < lim[1]) ? s1[i] : kNegInf;
+    }
+    if (n_q > 1 && tok0 + kDecodeStep - 1 > q_pos) {   // extend rows: causal limit per column
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (tok0 + 4 * q + i > cmax) x[i] = kNegInf;
+        if (tok0 + kPage + 4 * q + i > cmax) x[4 + i] = kNegInf;
+      }
     }
     rescale(o, softmax_update<8>(x, sl2, m_run, l_run));
     if (lim[0] < kPage || lim[1] < kPage) {
@@ -559,12 +571,12 @@ __device__ void decode_wave_item(const KernelParams& P, int item, float* sw) {
   for (;;) {
     int nxt = step + 1;
     load_step(nxt < n_steps ? nxt : step, kB, vB, limB);
-    compute_step(kA, vA, limA);
+    compute_step(kA, vA, limA, kv_begin + step * kDecodeStep);
     if (nxt >= n_steps) break;
     step = nxt;
     nxt = step + 1;
     load_step(nxt < n_steps ? nxt : step, kA, vA, limA);
-    compute_step(kB, vB, limB);
+    compute_step(kB, vB, limB, kv_begin + step * kDecodeStep);
     if (nxt >= n_steps) break;
     step = nxt;
   }
@@ -572,16 +584,16 @@ __device__ void decode_wave_item(const KernelParams& P, int item, float* sw) {
   // ---- epilogue: lane (n, q) holds O^T[16b + 4q + i][n]
   const float l_tot = sum_over_groups(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (n < G) {
+  if (n < ncols) {
     if (ns == 1) {
-      T* dst = (T*)P.out + ((size_t)q_row * P.hq + head * G + n) * D + 4 * q;
+      T* dst = (T*)P.out + ((size_t)(q_row + qi) * P.hq + head * G + hh) * D + 4 * q;
 #pragma unroll
       for (int b = 0; b < Gm::kDb; ++b) store4<T>(dst + 16 * b, o[b] * inv);
     } else {
-      const size_t run = (size_t)dsc[kDPartBase] + ((size_t)head * ns + split) * G;   // this split's G slots
+      const size_t run = (size_t)dsc[kDPartBase] + ((size_t)head * ns + split) * ncols;   // this split's slots
       const bool coh = P.inline_combine != 0;
       if (coh) {
-        const BufRsrc r = part_rsrc(P.part_o + run * D, G * D * 4);
+        const BufRsrc r = part_rsrc(P.part_o + run * D, ncols * D * 4);
 #pragma unroll
         for (int b = 0; b < Gm::kDb; ++b) store_coherent4(r, (n * D + 4 * q + 16 * b) * 4, o[b] * inv);
       } else {

@@ -117,6 +117,18 @@ def config_spec(idx: int) -> BatchSpec:
     raise ValueError(f"no workload {idx}")
 
 
+def spec_verify_spec(n_extend: int = 4) -> BatchSpec:
+    """A speculative-verification step on the Llama-3-8B-shaped workload: its 2048-token chunk at
+    offset 14336, and each of its 128 decode sequences extending by ``n_extend`` tokens instead of
+    one (the sequence's context as drawn for that workload, the extend's rows at its end)."""
+    base = config_spec(3)
+    dec = [int(c) for c in base.decode_ctx_len]
+    pq = [2048] + [n_extend] * len(dec)
+    pc = [16384] + dec
+    return BatchSpec(f"llama3-8b-specverify{n_extend}", "bf16", 32, 8, 128, pq, pc, [],
+                     num_pages=_live_plus_quarter(pc), seed=6, value_scale=0.5)
+
+
 def reduced_spec(idx: int, n_decode: int, ctx_div: int, seed: Optional[int] = None) -> BatchSpec:
     """A smaller batch with the same heads, dims, dtype and value law as workload ``idx``:
     the first ``n_decode`` decodes, every context (and prefill offset) divided by ``ctx_div``."""

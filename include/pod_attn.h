@@ -107,6 +107,9 @@ typedef struct pod_attn_config {
   int prefill_split_cap;    /* 0: automatic; else max KV splits of one prefill tile (>= 1)     */
   int wgs_per_cu;           /* 0: automatic; else persistent workgroups per CU in FUSED mode  */
   int flags;                /* POD_ATTN_FLAG_*                                                */
+  int extend_max_q;         /* prefill (extend) chunks of at most this many query rows run on
+                               the decode path as small-q extends, cut into pieces of
+                               floor(16 / group) rows: 0 = automatic (16), -1 = never, else 1..256 */
 } pod_attn_config;
 
 /* Batch metadata: host arrays ([W6] "vLLM 내부 구조": padding-free packing with offsets). */
@@ -146,6 +149,7 @@ typedef struct pod_attn_stats {
   double host_plan_us;          /* host planning time of the last run                         */
   int prefill_wg_budget;        /* FUSED: prefill-role workgroups allowed while decode remains */
   int num_append_units;         /* KV append units of the last run (0 for pod_attn_run)      */
+  int num_small_extends;        /* prefill chunks run on the decode path as small-q extends   */
 } pod_attn_stats;
 
 /* Create a handle for one attention configuration on the current HIP device.  Validates the

@@ -62,12 +62,15 @@ def _check_coverage(spec, items, G):
         else:
             assert len({p[5] for p in parts}) == 1 and parts[0][5] >= 0
         covered[q_row:q_row + n_q, g] += 1
-        if kind == 0:
+        if q_row < P:                         # a prefill chunk's rows: tile (kind 0) or small-q extend piece (kind 1)
             i = int(np.searchsorted(qs, q_row, side="right") - 1)
-            assert seq == i
+            assert seq == i and q_row + n_q <= qs[i + 1]
             L, ctx = spec.prefill_q_len[i], spec.prefill_ctx_len[i]
             assert q_pos == ctx - L + (q_row - qs[i])
+            if kind == 1:
+                assert n_q * G <= 16 or n_q == 1
         else:
+            assert kind == 1
             i = q_row - P
             assert seq == spec.num_prefill + i and n_q == 1
             assert kv_len == spec.decode_ctx_len[i]
@@ -107,6 +110,29 @@ def test_plan_ragged_batches(G, D, split, cap):
         assert st["prefill_max_splits"] <= cap
     if split:
         assert st["decode_split_tokens"] == split
+
+
+@pytest.mark.parametrize("G", [1, 3, 4, 8, 16])
+def test_small_chunks_take_the_decode_path(G):
+    """Chunks of at most 16 rows (the default) become decode-path pieces of floor(16/G) rows;
+    longer chunks stay prefill tiles; extend_max_q = -1 keeps every chunk on the tile path."""
+    pre = [(1, 9), (2, 300), (5, 40), (16, 16), (17, 900), (3, 3)]
+    spec = gen.custom_spec("bf16", Hq=2 * G, Hkv=2, D=128, prefill=pre, decode=[7, 4000])
+    items, st = B.plan_inspect(B.make_config(2 * G, 2, 128), _meta(spec), 80, 2)
+    _check_coverage(spec, items, G)
+    assert st["num_small_extends"] == 5
+    qs = np.concatenate([[0], np.cumsum(spec.prefill_q_len)])
+    qpp = max(1, 16 // G)
+    for i, (L, _) in enumerate(pre):
+        rows = items[(items[:, 1] >= qs[i]) & (items[:, 1] < qs[i + 1])]
+        kinds = set(rows[:, 10].tolist())
+        assert kinds == ({1} if L <= 16 else {0})
+        if L <= 16:
+            assert max(rows[:, 2]) == min(qpp, L)
+    items, st = B.plan_inspect(B.make_config(2 * G, 2, 128, extend_max_q=-1), _meta(spec), 80, 2)
+    _check_coverage(spec, items, G)
+    assert st["num_small_extends"] == 0
+    assert set(items[items[:, 1] < qs[-1]][:, 10].tolist()) == {0}
 
 
 def test_longest_first_order():
