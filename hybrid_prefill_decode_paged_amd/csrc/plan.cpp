@@ -146,17 +146,19 @@ pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus
   p.prefill_max_splits = 0;
   struct PGroup { double work; std::vector<int32_t> items; };   // items: (desc, split << 16 | head)
   std::vector<PGroup> pgroups;
-  // Small-q extends: a chunk of at most extend_max_q rows reads its whole prefix for a few
-  // queries, which is a decode-shaped (bandwidth-bound) job; it runs on the decode path, cut
-  // into pieces of at most 16 (query, head) columns ([W6] "한 스텝에 여러 종류의 request 섞기":
-  // a decode is an extend of one token).
+  // Small-q extends: a chunk whose rows x G fit one 16-column block (and of at most extend_max_q
+  // rows) reads its whole prefix for a few queries, a decode-shaped, bandwidth-bound job; it runs
+  // on the decode path ([W6] "한 스텝에 여러 종류의 request 섞기": a decode is an extend of one
+  // token).  Longer chunks stay prefill tiles, which read the prefix once for 128 columns
+  // (measured on 4-token to 16-token verification steps at G = 4: one block 1.3x faster than
+  // a tile, two or more blocks that each re-read the prefix 1.3-2.2x slower).
   const int emax = c.extend_max_q < 0 ? 0 : (c.extend_max_q == 0 ? kExtendMaxQ : c.extend_max_q);
   std::vector<int> small_chunks;
   for (int i = 0; i < b->num_prefill; ++i) {
     const int L = b->prefill_q_start[i + 1] - b->prefill_q_start[i];
     const int ctx = b->prefill_ctx_len[i];
     if (L == 0) continue;
-    if (L <= emax) { small_chunks.push_back(i); continue; }
+    if (L <= emax && L * G <= kMaxGroup) { small_chunks.push_back(i); continue; }
     int ns_c = std::max(1, std::min(std::min(cap, kMaxCombineSplits), ceil_div(ctx, 4096)));
     const int st = round_up_int(ceil_div(ctx, ns_c), kPrefillKvTile);
     ns_c = ceil_div(ctx, st);
@@ -218,18 +220,14 @@ pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus
   p.n_pf_groups = group;
 
   // ---------------- decode sequences and small-q extend pieces
-  struct DPiece { int seq, q_row, n_q, q_pos, kv_len; };
+  struct DPiece { int seq, q_row, n_q, q_pos, kv_len; };   // a decode, or a small-q extend chunk
   std::vector<DPiece> pieces;
   for (int i = 0; i < b->num_decode; ++i)
     pieces.push_back({b->num_prefill + i, (int)prefill_rows + i, 1, b->decode_ctx_len[i] - 1, b->decode_ctx_len[i]});
-  const int qpp = std::max(1, kMaxGroup / G);   // queries per piece: 16 columns
   for (int i : small_chunks) {
     const int L = b->prefill_q_start[i + 1] - b->prefill_q_start[i];
     const int ctx = b->prefill_ctx_len[i];
-    for (int t = 0; t < L; t += qpp) {
-      const int nq = std::min(qpp, L - t);
-      pieces.push_back({i, b->prefill_q_start[i] + t, nq, ctx - L + t, ctx - L + t + nq});
-    }
+    pieces.push_back({i, b->prefill_q_start[i], L, ctx - L, ctx});
   }
   p.num_small_extends = (int)small_chunks.size();
   long total_tok = 0;

@@ -107,9 +107,9 @@ typedef struct pod_attn_config {
   int prefill_split_cap;    /* 0: automatic; else max KV splits of one prefill tile (>= 1)     */
   int wgs_per_cu;           /* 0: automatic; else persistent workgroups per CU in FUSED mode  */
   int flags;                /* POD_ATTN_FLAG_*                                                */
-  int extend_max_q;         /* prefill (extend) chunks of at most this many query rows run on
-                               the decode path as small-q extends, cut into pieces of
-                               floor(16 / group) rows: 0 = automatic (16), -1 = never, else 1..256 */
+  int extend_max_q;         /* prefill (extend) chunks of at most this many query rows, whose
+                               rows x group <= 16, run on the decode path as small-q extends:
+                               0 = automatic (16), -1 = never, else 1..256                     */
 } pod_attn_config;
 
 /* Batch metadata: host arrays ([W6] "vLLM 내부 구조": padding-free packing with offsets). */

@@ -62,13 +62,13 @@ def _check_coverage(spec, items, G):
         else:
             assert len({p[5] for p in parts}) == 1 and parts[0][5] >= 0
         covered[q_row:q_row + n_q, g] += 1
-        if q_row < P:                         # a prefill chunk's rows: tile (kind 0) or small-q extend piece (kind 1)
+        if q_row < P:                         # a prefill chunk's rows: tile (kind 0) or small-q extend (kind 1)
             i = int(np.searchsorted(qs, q_row, side="right") - 1)
             assert seq == i and q_row + n_q <= qs[i + 1]
             L, ctx = spec.prefill_q_len[i], spec.prefill_ctx_len[i]
             assert q_pos == ctx - L + (q_row - qs[i])
             if kind == 1:
-                assert n_q * G <= 16 or n_q == 1
+                assert n_q == L and n_q * G <= 16
         else:
             assert kind == 1
             i = q_row - P
@@ -114,21 +114,22 @@ def test_plan_ragged_batches(G, D, split, cap):
 
 @pytest.mark.parametrize("G", [1, 3, 4, 8, 16])
 def test_small_chunks_take_the_decode_path(G):
-    """Chunks of at most 16 rows (the default) become decode-path pieces of floor(16/G) rows;
-    longer chunks stay prefill tiles; extend_max_q = -1 keeps every chunk on the tile path."""
+    """Chunks whose rows x G fit one 16-column block (at most 16 rows, the default) become one
+    decode-path item group each; longer chunks stay prefill tiles; extend_max_q = -1 keeps every
+    chunk on the tile path and extend_max_q = 2 caps the rows."""
     pre = [(1, 9), (2, 300), (5, 40), (16, 16), (17, 900), (3, 3)]
     spec = gen.custom_spec("bf16", Hq=2 * G, Hkv=2, D=128, prefill=pre, decode=[7, 4000])
-    items, st = B.plan_inspect(B.make_config(2 * G, 2, 128), _meta(spec), 80, 2)
-    _check_coverage(spec, items, G)
-    assert st["num_small_extends"] == 5
     qs = np.concatenate([[0], np.cumsum(spec.prefill_q_len)])
-    qpp = max(1, 16 // G)
-    for i, (L, _) in enumerate(pre):
-        rows = items[(items[:, 1] >= qs[i]) & (items[:, 1] < qs[i + 1])]
-        kinds = set(rows[:, 10].tolist())
-        assert kinds == ({1} if L <= 16 else {0})
-        if L <= 16:
-            assert max(rows[:, 2]) == min(qpp, L)
+    for emax, cap in ((0, 16), (2, 2)):
+        items, st = B.plan_inspect(B.make_config(2 * G, 2, 128, extend_max_q=emax), _meta(spec), 80, 2)
+        _check_coverage(spec, items, G)
+        small = [L <= cap and L * G <= 16 for L, _ in pre]
+        assert st["num_small_extends"] == sum(small)
+        for i, (L, _) in enumerate(pre):
+            rows = items[(items[:, 1] >= qs[i]) & (items[:, 1] < qs[i + 1])]
+            assert set(rows[:, 10].tolist()) == ({1} if small[i] else {0})
+            if small[i]:
+                assert set(rows[:, 2].tolist()) == {L} and set(rows[:, 1].tolist()) == {qs[i]}
     items, st = B.plan_inspect(B.make_config(2 * G, 2, 128, extend_max_q=-1), _meta(spec), 80, 2)
     _check_coverage(spec, items, G)
     assert st["num_small_extends"] == 0

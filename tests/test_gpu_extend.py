@@ -1,7 +1,7 @@
-"""GPU parity of small-q extends: prefill chunks of at most 16 rows run on the decode path (a
-decode is an extend of one token), pieces of floor(16/G) query rows with a causal limit per
-column; compared element by element with the oracle in every mode, with and without KV splits,
-and against the same batch planned on the prefill-tile path."""
+"""GPU parity of small-q extends: prefill chunks whose rows x G fit one 16-column block run on
+the decode path (a decode is an extend of one token) with a causal limit per column; compared
+element by element with the oracle in every mode, with and without KV splits, and against the
+same batch planned on the prefill-tile path."""
 import sys
 
 import numpy as np
@@ -31,13 +31,13 @@ def _need_gpu():
 
 EXTEND_CASES = [
     # (dtype, Hq, Hkv, D, prefill (q_len, ctx) pairs, decode ctx list)
-    ("bf16", 8, 2, 128, [(4, 300), (2, 2), (3, 17), (16, 700)], [33, 1000]),        # G=4: pieces of 4
-    ("bf16", 4, 4, 128, [(16, 16), (9, 4100), (2, 35)], [1, 64]),                   # G=1: pieces of 16
-    ("bf16", 16, 2, 64, [(5, 129), (2, 2000), (1, 1)], [700]),                      # G=8: pieces of 2
-    ("bf16", 16, 1, 128, [(3, 50), (16, 300)], [17, 2]),                            # G=16: one row a piece
-    ("fp32", 6, 2, 128, [(7, 97), (4, 4)], [300]),                                  # G=3: pieces of 5
-    ("fp32", 4, 1, 64, [(12, 600), (100, 400)], [77]),                              # one chunk stays a tile
-    ("bf16", 32, 8, 128, [(4, 8192), (4, 5000), (4, 31)], []),                      # extends only
+    ("bf16", 8, 2, 128, [(4, 300), (2, 2), (3, 17), (16, 700)], [33, 1000]),        # G=4: up to 4 rows
+    ("bf16", 4, 4, 128, [(16, 16), (9, 4100), (2, 35)], [1, 64]),                   # G=1: up to 16 rows
+    ("bf16", 16, 2, 64, [(5, 129), (2, 2000), (1, 1)], [700]),                      # G=8: up to 2 rows
+    ("bf16", 16, 1, 128, [(3, 50), (1, 300)], [17, 2]),                             # G=16: one row
+    ("fp32", 6, 2, 128, [(5, 97), (4, 4), (6, 80)], [300]),                         # G=3: up to 5 rows
+    ("fp32", 4, 1, 64, [(4, 600), (100, 400)], [77]),                               # one chunk stays a tile
+    ("bf16", 32, 8, 128, [(2, 8192), (2, 5000), (1, 31)], []),                      # extends only
 ]
 
 
@@ -50,7 +50,7 @@ def test_small_q_extends_match_the_oracle(case, mode):
     _say(f"extend case={case} mode={mode}")
     out, h, _ = run_library(b, mode=mode)
     st = h.stats()
-    assert st["num_small_extends"] == sum(1 for L, _ in pre if 0 < L <= 16)
+    assert st["num_small_extends"] == sum(1 for L, _ in pre if 0 < L and L * (hq // hkv) <= 16)
     check_close(to_f64(out), problem(b).full_output(), dt, f"extend{case}/{mode}")
 
 
@@ -69,7 +69,7 @@ def test_small_q_extends_with_splits(mode):
 
 
 def test_decode_path_and_tile_path_agree():
-    spec = gen.custom_spec("bf16", Hq=32, Hkv=8, D=128, prefill=[(4, 3000), (2, 900), (16, 64)],
+    spec = gen.custom_spec("bf16", Hq=16, Hkv=4, D=128, prefill=[(4, 3000), (2, 900), (3, 64)],
                            decode=[500], seed=411)
     b = gen.make_batch(spec, "cuda")
     _say("extend vs tile path")
@@ -84,7 +84,8 @@ def test_decode_path_and_tile_path_agree():
 
 def test_speculative_verify_batch_full_size():
     """A Llama-3-8B-shaped verification step at full size: 128 sequences each extending by 4
-    tokens at contexts of 4K-32K, plus one 2048-token chunk; sampled rows against the oracle."""
+    tokens (4 x G = 16 columns) at contexts of 4K-32K, plus one 2048-token chunk; sampled rows
+    against the oracle."""
     spec = gen.spec_verify_spec(4)
     b = gen.make_batch(spec, "cuda")
     _say("speculative verify full size")
