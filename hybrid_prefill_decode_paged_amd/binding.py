@@ -60,6 +60,17 @@ class Stats(C.Structure):
         return {n: getattr(self, n) for n, _ in self._fields_}
 
 
+class Signals(C.Structure):
+    _fields_ = [(n, C.c_int) for n in (
+        "prefill_items", "decode_items", "combine_groups", "small_extends", "grid_wgs",
+        "lds_bytes_per_wg", "fallback_reason")] + [("workspace_bytes", C.c_size_t)] + [
+        (n, C.c_double) for n in ("prefill_flops", "decode_flops", "prefill_bytes", "decode_bytes",
+                                  "intensity", "roofline_us")]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
 _lib = None
 
 
@@ -83,12 +94,13 @@ def load(path: str = LIB_PATH):
     lib.pod_attn_plan_inspect.argtypes = [P(Config), P(Batch), I, I, P(C.c_int32), I, P(I), P(Stats)]
     lib.pod_attn_read_trace.argtypes = [VP, VP, VP, P(C.c_uint32), I, P(I)]
     lib.pod_attn_set_kernel_events.argtypes = [VP, VP, VP]
+    lib.pod_attn_batch_signals.argtypes = [P(Config), P(Batch), I, I, C.c_double, C.c_double, P(Signals)]
     lib.pod_attn_last_error.restype = C.c_char_p
     lib.pod_attn_destroy.argtypes = [VP]
     lib.pod_attn_destroy.restype = None
     for name in ("pod_attn_create", "pod_attn_workspace_size", "pod_attn_run", "pod_attn_run_append", "pod_attn_get_stats",
                  "pod_attn_gather_kv", "pod_attn_read_device_status", "pod_attn_plan_inspect", "pod_attn_read_trace",
-                 "pod_attn_set_kernel_events"):
+                 "pod_attn_set_kernel_events", "pod_attn_batch_signals"):
         getattr(lib, name).restype = C.c_int
     _lib = lib
     return lib
@@ -151,6 +163,16 @@ def plan_inspect(cfg: Config, meta: BatchMeta, num_cus: int, wgs_per_cu: int):
                                      items.ctypes.data_as(C.POINTER(C.c_int32)), n.value,
                                      C.byref(n), None))
     return items[: n.value], st.as_dict()
+
+
+def batch_signals(cfg: Config, meta: BatchMeta, num_cus: int, wgs_per_cu: int, peak_gbps: float = 0.0,
+                  peak_tflops: float = 0.0) -> dict:
+    """Host-only scheduler signals of a batch (pod_attn_batch_signals): work items, LDS, per-share
+    FLOPs and bytes, intensity and the roofline time at the given peaks (0: MI355X's)."""
+    out = Signals()
+    _check(load().pod_attn_batch_signals(C.byref(cfg), C.byref(meta.c), int(num_cus), int(wgs_per_cu),
+                                         float(peak_gbps), float(peak_tflops), C.byref(out)))
+    return out.as_dict()
 
 
 def _ptr(t) -> int:

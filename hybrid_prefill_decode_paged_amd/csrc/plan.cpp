@@ -153,12 +153,15 @@ pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus
   // (measured on 4-token to 16-token verification steps at G = 4: one block 1.3x faster than
   // a tile, two or more blocks that each re-read the prefix 1.3-2.2x slower).
   const int emax = c.extend_max_q < 0 ? 0 : (c.extend_max_q == 0 ? kExtendMaxQ : c.extend_max_q);
+  const double kv_tok_bytes = 2.0 * c.hkv * c.d * c.elem_bytes();   // K and V of one token
+  const double qo_row_bytes = 2.0 * c.hq * c.d * c.elem_bytes();    // q in and out of one row
   std::vector<int> small_chunks;
   for (int i = 0; i < b->num_prefill; ++i) {
     const int L = b->prefill_q_start[i + 1] - b->prefill_q_start[i];
     const int ctx = b->prefill_ctx_len[i];
     if (L == 0) continue;
     if (L <= emax && L * G <= kMaxGroup) { small_chunks.push_back(i); continue; }
+    p.prefill_bytes += (double)ctx * kv_tok_bytes + (double)L * qo_row_bytes + 4.0 * ceil_div(ctx, kPage);
     int ns_c = std::max(1, std::min(std::min(cap, kMaxCombineSplits), ceil_div(ctx, 4096)));
     const int st = round_up_int(ceil_div(ctx, ns_c), kPrefillKvTile);
     ns_c = ceil_div(ctx, st);
@@ -229,6 +232,8 @@ pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus
     const int ctx = b->prefill_ctx_len[i];
     pieces.push_back({i, b->prefill_q_start[i], L, ctx - L, ctx});
   }
+  for (const DPiece& pc : pieces)   // every piece is a whole sequence's rows: its context once
+    p.decode_bytes += (double)pc.kv_len * kv_tok_bytes + (double)pc.n_q * qo_row_bytes + 4.0 * ceil_div(pc.kv_len, kPage);
   p.num_small_extends = (int)small_chunks.size();
   long total_tok = 0;
   for (const DPiece& pc : pieces) total_tok += (long)pc.kv_len * c.hkv;
@@ -266,7 +271,7 @@ pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus
     if (ns > 1) { group += c.hkv; slot += c.hkv * ns * ncols; }
     p.decode_max_splits = std::max(p.decode_max_splits, ns);
     p.decode_max_cols = std::max(p.decode_max_cols, ncols);
-    p.decode_bytes += 2.0 * kv * c.hkv * c.d * c.elem_bytes();
+    p.decode_flops += 4.0 * c.d * c.hq * ((double)pc.n_q * pc.q_pos + (double)pc.n_q * (pc.n_q + 1) / 2.0);
     p.ddesc.insert(p.ddesc.end(), d.begin(), d.end());
   }
   p.n_ddesc = (int)pieces.size();

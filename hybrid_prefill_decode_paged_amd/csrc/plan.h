@@ -31,8 +31,11 @@ struct Plan {
   int decode_max_cols = 0;      // widest decode-path descriptor: G, or n_q*G for small-q extends
   int num_small_extends = 0;    // prefill chunks planned on the decode path
   int total_q = 0, prefill_rows = 0;
-  double prefill_flops = 0.0;   // 4*D per visible (query head, key) pair of the prefill share
-  double decode_bytes = 0.0;    // K+V bytes of the decode share
+  // Algorithmic work per share (prefill tiles / decode path): 4*D FLOPs per visible (query head,
+  // key) pair; bytes = K and V once per KV head per context token, q and out once per row, one
+  // int32 block-table entry per page.
+  double prefill_flops = 0.0, decode_flops = 0.0;
+  double prefill_bytes = 0.0, decode_bytes = 0.0;
   WorkspaceMap map{};
 };
 

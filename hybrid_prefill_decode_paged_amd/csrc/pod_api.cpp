@@ -476,4 +476,37 @@ pod_attn_status pod_attn_plan_inspect(const pod_attn_config* cfg, const pod_attn
   return POD_ATTN_OK;
 }
 
+pod_attn_status pod_attn_batch_signals(const pod_attn_config* cfg, const pod_attn_batch* b, int num_cus, int wgs_per_cu,
+                                       double peak_gbps, double peak_tflops, pod_attn_signals* out) {
+  if (!out) return fail(POD_ATTN_ERR_INVALID_ARG, "null output");
+  Config c;
+  std::string err;
+  pod_attn_status st = validate_config(cfg, &c, &err);
+  if (st != POD_ATTN_OK) return fail(st, err);
+  Plan p;
+  st = plan_batch(c, b, num_cus, wgs_per_cu, &p, &err);
+  if (st != POD_ATTN_OK) return fail(st, err);
+  if (peak_gbps <= 0.0) peak_gbps = 8000.0;
+  if (peak_tflops <= 0.0) peak_tflops = c.dtype == POD_ATTN_BF16 ? 2500.0 : 157.3;
+  pod_attn_signals s{};
+  s.prefill_items = p.n_pf_items;
+  s.decode_items = p.n_dc_items;
+  s.combine_groups = p.n_groups;
+  s.small_extends = p.num_small_extends;
+  s.grid_wgs = num_cus * wgs_per_cu;
+  s.lds_bytes_per_wg = fused_lds_bytes(c.elem_bytes(), c.d);
+  s.fallback_reason = p.n_pf_items == 0 ? POD_ATTN_FALLBACK_NO_PREFILL
+                      : p.n_dc_items == 0 ? POD_ATTN_FALLBACK_NO_DECODE : POD_ATTN_FALLBACK_NONE;
+  s.workspace_bytes = p.map.total;
+  s.prefill_flops = p.prefill_flops;
+  s.decode_flops = p.decode_flops;
+  s.prefill_bytes = p.prefill_bytes;
+  s.decode_bytes = p.decode_bytes;
+  const double flops = p.prefill_flops + p.decode_flops, bytes = p.prefill_bytes + p.decode_bytes;
+  s.intensity = bytes > 0.0 ? flops / bytes : 0.0;
+  s.roofline_us = std::max(flops / (peak_tflops * 1e12), bytes / (peak_gbps * 1e9)) * 1e6;
+  *out = s;
+  return POD_ATTN_OK;
+}
+
 }  // extern "C"

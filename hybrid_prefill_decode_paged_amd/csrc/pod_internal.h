@@ -110,6 +110,16 @@ struct StageArgs {
   const int32_t* units_host; // append units inside the staging buffer, or null
 };
 
+// LDS of one fused workgroup: the prefill tile's double-buffered K and V pages (4 pages per
+// buffer when a (page, head) slab is at most 4 KiB, else 2) or the combine tables, whichever is
+// larger.  The kernels' geometry uses the same formula.
+constexpr int fused_lds_bytes(int elem_bytes, int d) {
+  const int slab = kPage * d * elem_bytes;
+  const int prefill = 2 * 2 * (slab <= 4096 ? 4 : 2) * slab;
+  const int combine = kWaves * kCombineLdsPerWave;
+  return prefill > combine ? prefill : combine;
+}
+
 // Workspace map (byte offsets), computed by the planner.
 struct WorkspaceMap {
   size_t ctrl, tickets, claims, pdesc, pitems, ddesc, aunits, copy_bytes;  // [0, pdesc) zeroed, [pdesc, copy_bytes) staged from the host

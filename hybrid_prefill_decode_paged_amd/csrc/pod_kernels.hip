@@ -70,6 +70,7 @@ template <typename T, int D> struct Geo {
   static constexpr int kPrefillLds = 2 * 2 * kTp * kSlab;              // 2 buffers x (K, V)
   static constexpr int kCombineLds = kWaves * kCombineLdsPerWave;    // in-kernel split combine tables
   static constexpr int kFusedLds = kPrefillLds > kCombineLds ? kPrefillLds : kCombineLds;
+  static_assert(kFusedLds == fused_lds_bytes(kBytes, D), "host-side LDS figure matches the kernels");
   static_assert(kStageChunks % kThreads == 0, "tile must split evenly over the workgroup");
   static_assert(kTp % 2 == 0, "bf16 PV pairs pages");
 };

@@ -237,6 +237,33 @@ pod_attn_status pod_attn_plan_inspect(const pod_attn_config* cfg, const pod_attn
                                       int num_cus, int wgs_per_cu, int32_t* items,
                                       int items_cap, int* n_items, pod_attn_stats* stats);
 
+/* Scheduler signals for one batch, host-only (no GPU): what an outer scheduler needs to bucket
+ * prefill chunks and decode groups by their resource use ([POD] "Resource characteristics as
+ * scheduling inputs": work units, shared memory, arithmetic intensity and bytes read), as this library would
+ * plan the batch on a device of num_cus CUs with wgs_per_cu persistent workgroups each.  The
+ * "prefill share" is the chunks planned as tiles; the "decode share" is the decodes plus the
+ * small-q extends.  FLOPs count 4*D per visible (query head, key) pair; bytes count K and V once
+ * per KV head per context token of the share's sequences plus q read and out written once.
+ * roofline_us = max(total FLOPs / peak_tflops, total bytes / peak_gbps) for the given peaks
+ * (<= 0 selects MI355X's: 8000 GB/s; 2500 TFLOP/s bf16, 157.3 fp32). */
+typedef struct pod_attn_signals {
+  int prefill_items;          /* prefill work items (tile x KV head x split)                    */
+  int decode_items;           /* decode-path work items (sequence or extend x KV head x split)  */
+  int combine_groups;         /* split groups merged by log-sum-exp                             */
+  int small_extends;          /* prefill chunks planned on the decode path                      */
+  int grid_wgs;               /* persistent workgroups of the fused launch                      */
+  int lds_bytes_per_wg;       /* LDS each fused workgroup holds                                 */
+  int fallback_reason;        /* what a FUSED run reports: NONE, NO_PREFILL or NO_DECODE         */
+  size_t workspace_bytes;
+  double prefill_flops, decode_flops;
+  double prefill_bytes, decode_bytes;
+  double intensity;           /* total FLOPs / total bytes                                      */
+  double roofline_us;
+} pod_attn_signals;
+pod_attn_status pod_attn_batch_signals(const pod_attn_config* cfg, const pod_attn_batch* batch,
+                                       int num_cus, int wgs_per_cu, double peak_gbps,
+                                       double peak_tflops, pod_attn_signals* out);
+
 /* Profiling hook: when ev_start / ev_end (hipEvent_t, may be NULL) are set, the next
  * pod_attn_run (or pod_attn_run_append) records ev_start on the launch stream right after the
  * plan upload, before the first attention kernel, and ev_end after the last one (FUSED mode:

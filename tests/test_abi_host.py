@@ -281,3 +281,54 @@ def test_prefill_queues_hold_whole_key_range_groups(idx):
         if len(st) > 1:
             assert len({y - x for x, y in zip(st[:-1], st[1:])}) == 1, "tiles of a chunk share split boundaries"
     assert work.max() <= 1.35 * work.mean(), work
+
+
+# ------------------------------------------------------------------ scheduler signals, cost table
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+def test_batch_signals_match_the_algorithmic_work(idx):
+    """pod_attn_batch_signals' per-share FLOPs and bytes add up to the whole-batch algorithmic work
+    computed independently in bench.py, and its roofline time is that work at MI355X's peaks."""
+    import bench
+    spec = gen.config_spec(idx)
+    sig = B.batch_signals(B.make_config(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.dtype),
+                          _meta(spec), 256, 2)
+    w = bench.algorithmic_work(spec)
+    assert sig["prefill_bytes"] + sig["decode_bytes"] == w["bytes"]
+    assert sig["prefill_flops"] + sig["decode_flops"] == w["flops"]
+    peak = bench.PEAK_MFMA[spec.dtype]
+    roof = max(w["flops"] / peak, w["bytes"] / bench.PEAK_HBM) * 1e6
+    assert abs(sig["roofline_us"] - roof) <= 1e-9 * roof
+    assert sig["lds_bytes_per_wg"] == 65536 and sig["grid_wgs"] == 512
+    assert sig["fallback_reason"] == 0
+
+
+def test_batch_signals_put_small_extends_in_the_decode_share():
+    spec = gen.custom_spec("bf16", Hq=8, Hkv=2, D=128, prefill=[(4, 1000), (300, 300)], decode=[])
+    cfg = B.make_config(8, 2, 128)
+    sig = B.batch_signals(cfg, _meta(spec), 256, 2)
+    assert sig["small_extends"] == 1 and sig["decode_items"] > 0 and sig["prefill_items"] > 0
+    elem, kv_tok, qo_row = 2, 2 * 2 * 128 * 2, 2 * 8 * 128 * 2
+    assert sig["decode_bytes"] == 1000 * kv_tok + 4 * qo_row + 4 * 63
+    assert sig["prefill_bytes"] == 300 * kv_tok + 300 * qo_row + 4 * 19
+    assert sig["decode_flops"] == 4 * 128 * 8 * (4 * 996 + 10)
+    sig2 = B.batch_signals(B.make_config(8, 2, 128, extend_max_q=-1), _meta(spec), 256, 2)
+    assert sig2["small_extends"] == 0 and sig2["fallback_reason"] == 2     # prefill only
+    assert sig2["prefill_flops"] == sig["prefill_flops"] + sig["decode_flops"]
+
+
+def test_cost_table_lookup_rounds_up_to_a_validated_bucket():
+    from hybrid_prefill_decode_paged_amd.cost_table import CostTable, Entry
+    mk = lambda L, C, n, Dc, us, ok=True: Entry(L, C, n, Dc, us, us, us, us, ok)
+    grid = [(L, C, n, Dc) for L in (0, 512, 1024) for C in ((0,) if L == 0 else (4096, 16384))
+            for n in (0, 64, 128) for Dc in ((0,) if n == 0 else (4096, 16384)) if L or n]
+    us = lambda L, C, n, Dc: 1.0 + L * C / 1e4 + n * Dc / 1e3
+    t = CostTable([32, 8, 128], "bf16", [mk(*g, us(*g), ok=(g != (1024, 4096, 64, 4096))) for g in grid])
+    assert t.lookup(100, 2000, 10, 3000).key() == (512, 4096, 64, 4096)
+    assert t.lookup(512, 4096, 64, 5000).key() == (512, 4096, 64, 16384)
+    assert t.lookup(0, 0, 30, 4000).key() == (0, 0, 64, 4096)       # decode-only bucket
+    assert t.lookup(600, 9000, 0, 0).key() == (1024, 16384, 0, 0)    # prefill-only bucket
+    assert t.lookup(700, 4096, 64, 4096) is None                     # that bucket failed validation
+    assert t.lookup(2048, 4096, 1, 1) is None                        # outside the table: admission says no
+    assert t.lookup(512, 20000, 0, 0) is None
+    t2 = CostTable.from_json(t.to_json())
+    assert [e.key() for e in t2.entries] == [e.key() for e in t.entries]

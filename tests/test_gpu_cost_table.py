@@ -1,0 +1,40 @@
+"""GPU check of the measured cost table: every bucket of a small grid runs on the fused path with
+no device error and a finite output, its timings are positive and ordered (max >= median), its
+signals are the host's for that bucket, and lookups round batches up to the right bucket."""
+import sys
+
+import pytest
+import torch
+
+from hybrid_prefill_decode_paged_amd import binding as B
+from hybrid_prefill_decode_paged_amd.cost_table import CostTable, bucket_batch, calibrate
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.load()
+
+
+def test_small_grid_calibrates_and_looks_up():
+    print("[gpu-test] cost table 8/2/128 bf16, 2x1x2x2 grid", flush=True)
+    sys.stdout.flush()
+    t = calibrate(8, 2, 128, "bf16", [0, 64], [1024], [0, 8], [512, 2048], steps=3)
+    keys = [e.key() for e in t.entries]
+    assert keys == sorted(keys) and len(keys) == 5        # (0,0,8,512) ... (64,1024,8,2048)
+    for e in t.entries:
+        assert e.validated, e
+        assert 0 < e.kernel_us_p50 <= e.kernel_us_max and 0 < e.step_us_p50 <= e.step_us_max
+        q_start, p_ctx, d_ctx = bucket_batch(*e.key())
+        meta = B.BatchMeta(q_start, p_ctx, d_ctx, 128, 1 << 16)
+        sig = B.batch_signals(B.make_config(8, 2, 128), meta, 256, 2)
+        assert sig["roofline_us"] == e.signals["roofline_us"] or abs(sig["roofline_us"] - e.signals["roofline_us"]) < 1e-9
+    hit = t.lookup(30, 900, 5, 600)
+    assert hit is not None and hit.key() == (64, 1024, 8, 2048)
+    assert t.lookup(0, 0, 8, 400).key() == (0, 0, 8, 512)
+    assert t.lookup(65, 100, 0, 0) is None
+    assert t.lookup(10, 100, 0, 0).key() == (64, 1024, 0, 0)
+    assert CostTable.from_json(t.to_json()).lookup(30, 900, 5, 600).key() == (64, 1024, 8, 2048)
