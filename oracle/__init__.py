@@ -6,6 +6,6 @@ tests in tests/test_oracle_*.py (no function here is "parity unpinned").
 """
 from .attention import (  # noqa: F401
     PAGE, HybridProblem, append_tokens, attend, attend_blockwise, attend_online,
-    bf16_bits_to_f64, combine_partials, gather_kv, gather_kv_token, masked_scores,
+    bf16_bits_to_f64, combine_partials, e4m3_to_f64, gather_kv, gather_kv_token, masked_scores,
     row_positions, softmax_rows, split_partials, to_f64,
 )

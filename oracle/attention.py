@@ -36,6 +36,12 @@ Variants used only to check invariants (they must equal the direct form):
 
 Buffer formats follow the C ABI header: K pool [P][Hkv][D/x][16][x] (x = 16 bytes / element
 size), V pool [P][Hkv][D][16]; bf16 arrays arrive as raw 16-bit patterns.
+
+FP8 cache ([W6] "KV Cache": the cache can be kept in a low-precision format such as FP8 to cut
+its size and the bytes every decode step reads; [W4] "1-3. 모델 압축": the scale granularity is
+an implementation choice to check).  Reading taken: OCP FP8 E4M3 codes (sign, 4 exponent bits
+with bias 7, 3 mantissa bits; no infinities, S.1111.111 is NaN) and one float32 scale per
+(page, KV head) for K and one for V; a cache element's value is decode(code) * scale.
 """
 from __future__ import annotations
 
@@ -56,11 +62,25 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return u.view(np.float32).astype(np.float64)
 
 
+def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    """OCP FP8 E4M3: exponent field e (bias 7) and mantissa m; e = 0 is subnormal (m/8 * 2^-6);
+    e = 15 with m = 7 is NaN (the format has no infinities)."""
+    c = np.asarray(codes).astype(np.uint8).astype(np.int64)
+    sign = (c >> 7) & 1
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    mag = np.where((e == 15) & ((c & 7) == 7), np.nan, mag)
+    return np.where(sign == 1, -mag, mag)
+
+
 def to_f64(raw: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return bf16_bits_to_f64(raw)
     if dtype == "fp32":
         return np.asarray(raw, dtype=np.float32).astype(np.float64)
+    if dtype == "fp8":
+        return e4m3_to_f64(raw)
     raise ValueError(dtype)
 
 
@@ -84,9 +104,10 @@ def gather_kv_token(k_pool, v_pool, table_row, t: int, kv_head: int, dtype: str)
     return k, v
 
 
-def gather_kv(k_pool, v_pool, table_row, ctx: int, kv_head: int, dtype: str):
+def gather_kv(k_pool, v_pool, table_row, ctx: int, kv_head: int, dtype: str, k_scale=None, v_scale=None):
     """K, V in [ctx, D] float64 for one sequence and KV head (whole pages fetched, then the
-    slots past ctx dropped).  Same result as gather_kv_token for every t < ctx."""
+    slots past ctx dropped).  Same result as gather_kv_token for every t < ctx.  With scales
+    ([page][KV head] arrays, FP8 cache) every row is multiplied by its page's scale."""
     n_pages = -(-ctx // PAGE)
     pages = np.asarray(table_row[:n_pages], dtype=np.int64)
     kp = np.asarray(k_pool[pages])[:, kv_head]          # [n, D/x, 16, x]
@@ -94,6 +115,9 @@ def gather_kv(k_pool, v_pool, table_row, ctx: int, kv_head: int, dtype: str):
     n, nchunk, _, x = kp.shape
     K = to_f64(kp, dtype).transpose(0, 2, 1, 3).reshape(n * PAGE, nchunk * x)
     V = to_f64(vp, dtype).transpose(0, 2, 1).reshape(n * PAGE, nchunk * x)
+    if k_scale is not None:
+        K = K * np.repeat(np.asarray(k_scale, dtype=np.float64)[pages, kv_head], PAGE)[:, None]
+        V = V * np.repeat(np.asarray(v_scale, dtype=np.float64)[pages, kv_head], PAGE)[:, None]
     return K[:ctx], V[:ctx]
 
 
@@ -239,8 +263,11 @@ class HybridProblem:
     """
 
     def __init__(self, q, k_pool, v_pool, block_tables, prefill_q_start, prefill_ctx_len,
-                 decode_ctx_len, num_q_heads, num_kv_heads, dtype, scale=None):
+                 decode_ctx_len, num_q_heads, num_kv_heads, dtype, scale=None, kv_dtype=None,
+                 k_scale=None, v_scale=None):
         self.q = q
+        self.kv_dtype = kv_dtype or dtype                  # "fp8": q is bf16, the cache FP8 with scales
+        self.k_scale, self.v_scale = k_scale, v_scale
         self.k_pool, self.v_pool = k_pool, v_pool
         self.bt = np.asarray(block_tables)
         self.q_start = np.asarray(prefill_q_start, dtype=np.int64)
@@ -276,7 +303,7 @@ class HybridProblem:
         return to_f64(np.asarray(self.q)[rows, h], self.dtype)
 
     def kv(self, s: int, g: int, ctx: int):
-        return gather_kv(self.k_pool, self.v_pool, self.bt[s], ctx, g, self.dtype)
+        return gather_kv(self.k_pool, self.v_pool, self.bt[s], ctx, g, self.kv_dtype, self.k_scale, self.v_scale)
 
     def sequence_output(self, s: int, heads: Iterable[int] | None = None) -> np.ndarray:
         """Reference output for every row of sequence s: [rows, len(heads), D]."""

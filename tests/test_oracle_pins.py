@@ -392,3 +392,78 @@ def test_gqa_mapping_is_contiguous_groups():
     out = _problem(b).full_output()
     np.testing.assert_allclose(out[:, 2:], 0.25, rtol=0, atol=1e-15)
     assert np.abs(out[:, :2] - 0.25).max() > 0.1
+
+
+# ------------------------------------------------------------------ FP8 (E4M3) cache
+def test_e4m3_decodes_every_code():
+    """All 256 codes against torch's float8_e4m3fn widening (a library routine for the same OCP
+    format), plus values fixed by the format: 1.0, the largest finite value 448, the smallest
+    normal 2^-6 and subnormal 2^-9, signed zero, and NaN at S.1111.111."""
+    codes = np.arange(256, dtype=np.uint8)
+    got = orc.e4m3_to_f64(codes)
+    want = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    np.testing.assert_array_equal(got[ok], want[ok])
+    assert np.isnan(got).sum() == 2 and np.isnan(got[0x7F]) and np.isnan(got[0xFF])
+    assert got[0x38] == 1.0 and got[0xB8] == -1.0 and got[0x7E] == 448.0
+    assert got[0x08] == 2.0 ** -6 and got[0x01] == 2.0 ** -9 and got[0x07] == 7 * 2.0 ** -9
+    assert got[0x00] == 0.0 and np.signbit(got[0x80]) and got[0x3C] == 1.5
+
+
+def _fp8_paged(rng, Hkv, D, ctx, n_pages, perm):
+    """Random E4M3 codes for one sequence's K and V ([Hkv, ctx, D], codes 0..0x7E and their
+    negatives, no NaN) scattered by the header's layout (x = 16), and per-(page, head) scales."""
+    mag = rng.integers(0, 0x7F, size=(2, Hkv, ctx, D)).astype(np.uint8)
+    sgn = (rng.integers(0, 2, size=mag.shape) << 7).astype(np.uint8)
+    codes = mag | sgn
+    kp = np.zeros((n_pages, Hkv, D // 16, 16, 16), np.uint8)
+    vp = np.zeros((n_pages, Hkv, D, 16), np.uint8)
+    for g in range(Hkv):
+        for t in range(ctx):
+            page, slot = perm[t // 16], t % 16
+            for d in range(D):
+                kp[page, g, d // 16, slot, d % 16] = codes[0, g, t, d]
+                vp[page, g, d, slot] = codes[1, g, t, d]
+    ks = np.exp2(rng.integers(-4, 3, size=(n_pages, Hkv))).astype(np.float32)
+    vs = np.exp2(rng.integers(-4, 3, size=(n_pages, Hkv))).astype(np.float32) * 0.75
+    return codes, kp, vp, ks, vs
+
+
+def test_fp8_scaled_gather_equals_decoded_rows_times_page_scale():
+    rng = np.random.default_rng(31)
+    Hkv, D, ctx, P = 2, 32, 45, 7
+    perm = rng.permutation(P)
+    codes, kp, vp, ks, vs = _fp8_paged(rng, Hkv, D, ctx, P, perm)
+    for g in range(Hkv):
+        K, V = orc.gather_kv(kp, vp, perm, ctx, g, "fp8", ks, vs)
+        for t in range(ctx):
+            page = perm[t // 16]
+            np.testing.assert_array_equal(K[t], orc.e4m3_to_f64(codes[0, g, t]) * float(ks[page, g]))
+            np.testing.assert_array_equal(V[t], orc.e4m3_to_f64(codes[1, g, t]) * float(vs[page, g]))
+        k1, v1 = orc.gather_kv_token(kp, vp, perm, ctx - 1, g, "fp8")     # unscaled brute force
+        np.testing.assert_array_equal(k1, orc.e4m3_to_f64(codes[0, g, ctx - 1]))
+        np.testing.assert_array_equal(v1, orc.e4m3_to_f64(codes[1, g, ctx - 1]))
+
+
+def test_fp8_scales_act_on_scores_and_on_values():
+    """A K scale c applied to every page is the softmax scale times c; a V scale c applied to
+    every page multiplies the output by c."""
+    rng = np.random.default_rng(32)
+    Hkv, D, ctx, P = 1, 32, 40, 3
+    perm = np.arange(P)
+    codes, kp, vp, _, _ = _fp8_paged(rng, Hkv, D, ctx, P, perm)
+    q = rng.standard_normal((2, 2, D)).astype(np.float32)
+    one = np.ones((P, Hkv), np.float32)
+    mk = lambda ks, vs, sc: orc.HybridProblem(q, kp, vp, perm[None, :], [0, 2], [ctx], [], 2, 1, "fp32",
+                                              sc, kv_dtype="fp8", k_scale=ks, v_scale=vs).full_output()
+    base = mk(one, one, 0.125)
+    np.testing.assert_allclose(mk(one * 4.0, one, 0.125), mk(one, one, 0.5), rtol=1e-12, atol=0)
+    np.testing.assert_allclose(mk(one, one * 0.375, 0.125), base * 0.375, rtol=1e-12, atol=0)
+    # and a mixed-scale cache equals attention over the decoded, scaled rows
+    ks = np.array([[0.5], [2.0], [0.25]], np.float32)
+    vs = np.array([[4.0], [1.0], [0.125]], np.float32)
+    K = orc.e4m3_to_f64(codes[0, 0]) * np.repeat(ks[:, 0], 16)[:ctx, None]
+    V = orc.e4m3_to_f64(codes[1, 0]) * np.repeat(vs[:, 0], 16)[:ctx, None]
+    want = orc.attend(q[:, 0].astype(np.float64), np.array([ctx - 2, ctx - 1]), K, V, 0.125)
+    np.testing.assert_allclose(mk(ks, vs, 0.125)[:, 0], want, rtol=1e-12, atol=1e-15)
