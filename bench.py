@@ -6,8 +6,9 @@ fraction of the max(MFMA, HBM) roofline.
 One step = one pod_attn_run over the whole hybrid batch (prefill tiles + decode split-KV +
 combine), inputs resident in HBM.  Prints ONE JSON line.  Beside it, "kv_append" times the
 same step preceded by the KV append of every row's new K/V (pod_attn_run_append) in the fused
-and separate modes, and "small_q_extend" times a speculative-verification step (4-token
-extends) with the extends on the decode path and on the prefill-tile path.  The default workload is the
+and separate modes, "small_q_extend" times a speculative-verification step (4-token
+extends) with the extends on the decode path and on the prefill-tile path, and "fp8_kv" the
+same workload with an FP8 E4M3 cache (per-(page, KV head) scales), fused and separate.  The default workload is the
 Llama-2-7B-shaped layer (32 query / 32 KV heads, head_dim 128, bf16, 16-token pages): one
 1024-token prefill chunk at offset 3072 plus 64 decodes at context 4096, over a randomly
 permuted 40960-page pool.  The other workloads are parity-test cases; --workload selects them
@@ -33,13 +34,14 @@ PEAK_MFMA = {"bf16": 2.5e15, "fp32": 157.3e12}   # dense FLOP/s, MI355X
 def algorithmic_work(spec):
     """Bytes and FLOPs the method must move / do (not what a kernel happens to do):
     K and V read once per KV head per live context token, q read and out written once, one
-    int32 block-table entry per live page; 4*D FLOPs per visible (query head, key) pair."""
+    int32 block-table entry per live page (and, for an FP8 cache, its two float scales per KV
+    head); 4*D FLOPs per visible (query head, key) pair."""
     eb = spec.elem_bytes
     D, Hq, Hkv = spec.head_dim, spec.num_q_heads, spec.num_kv_heads
     ctx = spec.seq_ctx()
     kv = sum(ctx) * Hkv * D * eb * 2
-    qo = spec.total_q * Hq * D * eb * 2
-    bt = sum(-(-c // 16) for c in ctx) * 4
+    qo = spec.total_q * Hq * D * spec.q_elem_bytes * 2
+    bt = sum(-(-c // 16) for c in ctx) * (4 + (8 * Hkv if spec.dtype == "fp8" else 0))
     pairs_pf = 0
     for L, c in zip(spec.prefill_q_len, spec.prefill_ctx_len):
         o = c - L
@@ -70,14 +72,17 @@ def workload_desc(spec):
             "dtype": spec.dtype}
 
 
-def time_mode(torch, h, b, meta, out, ws, steps, warmup, new=None):
+def time_mode(torch, h, b, meta, out, ws, steps, warmup, new=None, scaled=False):
     """Wall time of `steps` runs (events on the launch stream around the loop) and the mean
     duration of the kernels of one run (one-shot events armed before each run).  With
-    new = (k_new, v_new) every run first appends those tokens (pod_attn_run_append)."""
+    new = (k_new, v_new) every run first appends those tokens (pod_attn_run_append); scaled runs
+    an FP8 cache with its scales (pod_attn_run_scaled)."""
     stream = torch.cuda.current_stream()
 
     def one():
-        if new is None:
+        if scaled:
+            h.run_scaled(b.q, b.k_pool, b.v_pool, b.k_scale, b.v_scale, b.block_tables, meta, out, ws)
+        elif new is None:
             h.run(b.q, b.k_pool, b.v_pool, b.block_tables, meta, out, ws)
         else:
             h.run_append(b.q, new[0], new[1], b.k_pool, b.v_pool, b.block_tables, meta, out, ws)
@@ -195,6 +200,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-append", action="store_true", help="skip timing the KV-append variant")
     ap.add_argument("--no-extend", action="store_true", help="skip timing the small-q extend workload")
+    ap.add_argument("--no-fp8", action="store_true", help="skip timing the FP8-cache variant")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (counter calibration)")
@@ -295,6 +301,32 @@ def main():
             h.close()
         del xb
 
+    fp8 = None
+    if not args.no_fp8 and spec.dtype == "bf16":
+        # The same workload with its cache in FP8 E4M3 (per-(page, KV head) scales, bf16 q/out),
+        # fused and separate: half the K/V bytes of the decode stream.
+        fs = gen.fp8_spec(args.workload)
+        print(f"[bench] generating {fs.name}: {fs.num_pages} pages", file=sys.stderr, flush=True)
+        fb = gen.make_batch(fs, "cuda")
+        fmeta = binding.BatchMeta.from_batch(fb)
+        fw = algorithmic_work(fs)
+        f_roof = max(fw["flops"] / PEAK_MFMA["bf16"], fw["bytes"] / PEAK_HBM)
+        fp8 = {"workload": workload_desc(fs)["workload"], "algorithmic_bytes": fw["bytes"],
+               "t_roof_us": round(f_roof * 1e6, 2)}
+        for mode in ("fused", "separate"):
+            h = binding.PodAttention(fs.num_q_heads, fs.num_kv_heads, fs.head_dim, "fp8", mode,
+                                     scale=fs.softmax_scale)
+            ws = torch.empty(h.workspace_size(fmeta), dtype=torch.uint8, device="cuda")
+            out = torch.empty_like(fb.q)
+            steps = max(5, args.steps // 2)
+            print(f"[bench] timing the FP8 cache, mode={mode} steps={steps}", file=sys.stderr, flush=True)
+            ms, kern_ms, _ = time_mode(torch, h, fb, fmeta, out, ws, steps, args.warmup, scaled=True)
+            fp8[mode] = {"us_per_iter": round(ms * 1e3, 2), "kernel_us_mean": round(kern_ms * 1e3, 2),
+                         "frac": round(f_roof / (kern_ms / 1e3), 4)}
+            del ws, out
+            h.close()
+        del fb
+
     main_ms = results[args.mode]["us_per_iter"] / 1e3
     kern_s = results[args.mode]["kernel_us_mean"] / 1e6
     if bound == "hbm":
@@ -329,6 +361,7 @@ def main():
                               if "separate" in results and "fused" in results else None),
         "kv_append": append,
         "small_q_extend": extend,
+        "fp8_kv": fp8,
         "plan": {k: st[k] for k in ("num_prefill_items", "num_decode_items", "num_combine_groups",
                                     "decode_split_tokens", "prefill_max_splits", "grid_wgs", "wgs_per_cu",
                                     "num_cus", "vgprs_per_lane", "lds_bytes_per_wg", "mode_used", "prefill_wg_budget",

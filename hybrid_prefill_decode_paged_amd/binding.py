@@ -16,7 +16,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libpod_attn.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "pod_attn.h")
 
-BF16, FP32 = 0, 1
+BF16, FP32, FP8_E4M3 = 0, 1, 2
+DTYPES = {"bf16": BF16, "fp32": FP32, "fp8": FP8_E4M3}
 MODE_FUSED, MODE_SEPARATE, MODE_STREAMS = 0, 1, 2
 MODES = {"fused": MODE_FUSED, "separate": MODE_SEPARATE, "streams": MODE_STREAMS}
 FLAG_DEBUG_CLAIMS = 1
@@ -87,6 +88,7 @@ def load(path: str = LIB_PATH):
     lib.pod_attn_workspace_size.argtypes = [VP, P(Batch), P(C.c_size_t)]
     lib.pod_attn_run.argtypes = [VP, VP, VP, VP, VP, P(Batch), VP, VP, C.c_size_t, VP]
     lib.pod_attn_run_append.argtypes = [VP, VP, VP, VP, VP, VP, VP, P(Batch), VP, VP, C.c_size_t, VP]
+    lib.pod_attn_run_scaled.argtypes = [VP, VP, VP, VP, VP, VP, VP, P(Batch), VP, VP, C.c_size_t, VP]
     lib.pod_attn_get_stats.argtypes = [VP, P(Stats)]
     lib.pod_attn_gather_kv.argtypes = [VP, VP, I, VP, I, I, P(Batch), VP, VP]
     lib.pod_attn_read_device_status.argtypes = [VP, VP, VP, P(C.c_int32), P(C.c_int32), I, P(I),
@@ -98,7 +100,8 @@ def load(path: str = LIB_PATH):
     lib.pod_attn_last_error.restype = C.c_char_p
     lib.pod_attn_destroy.argtypes = [VP]
     lib.pod_attn_destroy.restype = None
-    for name in ("pod_attn_create", "pod_attn_workspace_size", "pod_attn_run", "pod_attn_run_append", "pod_attn_get_stats",
+    for name in ("pod_attn_create", "pod_attn_workspace_size", "pod_attn_run", "pod_attn_run_append",
+                 "pod_attn_run_scaled", "pod_attn_get_stats",
                  "pod_attn_gather_kv", "pod_attn_read_device_status", "pod_attn_plan_inspect", "pod_attn_read_trace",
                  "pod_attn_set_kernel_events", "pod_attn_batch_signals"):
         getattr(lib, name).restype = C.c_int
@@ -121,7 +124,7 @@ def _check(status: int):
 
 def make_config(num_q_heads, num_kv_heads, head_dim, dtype="bf16", mode="fused", scale=0.0,
                 decode_split_tokens=0, prefill_split_cap=0, wgs_per_cu=0, flags=0, extend_max_q=0) -> Config:
-    return Config(num_q_heads, num_kv_heads, head_dim, 16, BF16 if dtype == "bf16" else FP32,
+    return Config(num_q_heads, num_kv_heads, head_dim, 16, DTYPES[dtype] if isinstance(dtype, str) else int(dtype),
                   MODES[mode] if isinstance(mode, str) else int(mode), float(scale),
                   int(decode_split_tokens), int(prefill_split_cap), int(wgs_per_cu), int(flags),
                   int(extend_max_q))
@@ -218,12 +221,13 @@ class PodAttention:
     def check_buffers(self, q, k_cache, v_cache, block_tables, meta: BatchMeta, out):
         """Host-side shape checks of the caller's tensors against what the kernels will read."""
         c = self.cfg
-        elem = 2 if c.dtype == BF16 else 4
+        q_elem = 4 if c.dtype == FP32 else 2
+        kv_elem = {BF16: 2, FP32: 4, FP8_E4M3: 1}[c.dtype]
         want_q = meta.total_q * c.num_q_heads * c.head_dim
         pool = meta.c.num_pages_in_pool * c.num_kv_heads * 16 * c.head_dim
         n_seq = len(meta.p_ctx) + len(meta.d_ctx)
-        for name, t, n in (("q", q, want_q), ("out", out, want_q), ("k_cache", k_cache, pool),
-                           ("v_cache", v_cache, pool)):
+        for name, t, n, elem in (("q", q, want_q, q_elem), ("out", out, want_q, q_elem),
+                                 ("k_cache", k_cache, pool, kv_elem), ("v_cache", v_cache, pool, kv_elem)):
             if t.element_size() != elem or t.numel() < n or not t.is_contiguous():
                 raise PodAttnError(-1, f"{name}: need a contiguous tensor of >= {n} {elem}-byte elements, "
                                        f"got {tuple(t.shape)} {t.dtype}")
@@ -239,6 +243,22 @@ class PodAttention:
                                      C.byref(meta.c), _ptr(out), _ptr(workspace),
                                      0 if workspace is None else workspace.numel() * workspace.element_size(),
                                      _stream_handle(stream)))
+        return out
+
+    def run_scaled(self, q, k_cache, v_cache, k_scale, v_scale, block_tables, meta: BatchMeta, out, workspace,
+                   stream=None):
+        """pod_attn_run_scaled (FP8_E4M3 handles): k_scale / v_scale are float32 [pages, Hkv]."""
+        if meta.total_q:
+            self.check_buffers(q, k_cache, v_cache, block_tables, meta, out)
+            want = meta.c.num_pages_in_pool * self.cfg.num_kv_heads
+            for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+                if t.element_size() != 4 or t.numel() < want or not t.is_contiguous():
+                    raise PodAttnError(-1, f"{name}: need a contiguous float32 tensor of >= {want} elements")
+        _check(self.lib.pod_attn_run_scaled(self.h, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                            _ptr(v_scale), _ptr(block_tables), C.byref(meta.c), _ptr(out),
+                                            _ptr(workspace),
+                                            0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                            _stream_handle(stream)))
         return out
 
     def run_append(self, q, k_new, v_new, k_cache, v_cache, block_tables, meta: BatchMeta, out, workspace,

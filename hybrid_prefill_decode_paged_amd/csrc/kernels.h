@@ -15,7 +15,7 @@ struct KernelSet {
   int prefill_kv_tile = 0;         // keys per prefill inner iteration
 };
 
-// dtype: 0 bf16, 1 fp32; head_dim: 64 or 128.
+// dtype: 0 bf16, 1 fp32, 2 FP8 E4M3 cache with bf16 q/out; head_dim: 64 or 128.
 KernelSet kernel_set(int dtype, int head_dim);
 
 }  // namespace pod

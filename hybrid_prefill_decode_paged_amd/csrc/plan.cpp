@@ -43,8 +43,8 @@ pod_attn_status validate_config(const pod_attn_config* c, Config* out, std::stri
   if (c->head_dim != 64 && c->head_dim != 128) {
     *err = "head_dim must be 64 or 128"; return POD_ATTN_ERR_UNSUPPORTED;
   }
-  if (c->dtype != POD_ATTN_BF16 && c->dtype != POD_ATTN_FP32) {
-    *err = "dtype must be POD_ATTN_BF16 or POD_ATTN_FP32"; return POD_ATTN_ERR_INVALID_ARG;
+  if (c->dtype != POD_ATTN_BF16 && c->dtype != POD_ATTN_FP32 && c->dtype != POD_ATTN_FP8_E4M3) {
+    *err = "dtype must be POD_ATTN_BF16, POD_ATTN_FP32 or POD_ATTN_FP8_E4M3"; return POD_ATTN_ERR_INVALID_ARG;
   }
   if (c->mode < POD_ATTN_MODE_FUSED || c->mode > POD_ATTN_MODE_STREAMS) {
     *err = "unknown mode"; return POD_ATTN_ERR_INVALID_ARG;
@@ -154,14 +154,15 @@ pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus
   // a tile, two or more blocks that each re-read the prefix 1.3-2.2x slower).
   const int emax = c.extend_max_q < 0 ? 0 : (c.extend_max_q == 0 ? kExtendMaxQ : c.extend_max_q);
   const double kv_tok_bytes = 2.0 * c.hkv * c.d * c.elem_bytes();   // K and V of one token
-  const double qo_row_bytes = 2.0 * c.hq * c.d * c.elem_bytes();    // q in and out of one row
+  const double qo_row_bytes = 2.0 * c.hq * c.d * c.q_elem_bytes();  // q in and out of one row
+  const double page_bytes = 4.0 + (c.dtype == POD_ATTN_FP8_E4M3 ? 8.0 * c.hkv : 0.0);   // table entry (+ FP8 scales)
   std::vector<int> small_chunks;
   for (int i = 0; i < b->num_prefill; ++i) {
     const int L = b->prefill_q_start[i + 1] - b->prefill_q_start[i];
     const int ctx = b->prefill_ctx_len[i];
     if (L == 0) continue;
     if (L <= emax && L * G <= kMaxGroup) { small_chunks.push_back(i); continue; }
-    p.prefill_bytes += (double)ctx * kv_tok_bytes + (double)L * qo_row_bytes + 4.0 * ceil_div(ctx, kPage);
+    p.prefill_bytes += (double)ctx * kv_tok_bytes + (double)L * qo_row_bytes + page_bytes * ceil_div(ctx, kPage);
     int ns_c = std::max(1, std::min(std::min(cap, kMaxCombineSplits), ceil_div(ctx, 4096)));
     const int st = round_up_int(ceil_div(ctx, ns_c), kPrefillKvTile);
     ns_c = ceil_div(ctx, st);
@@ -233,7 +234,7 @@ pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus
     pieces.push_back({i, b->prefill_q_start[i], L, ctx - L, ctx});
   }
   for (const DPiece& pc : pieces)   // every piece is a whole sequence's rows: its context once
-    p.decode_bytes += (double)pc.kv_len * kv_tok_bytes + (double)pc.n_q * qo_row_bytes + 4.0 * ceil_div(pc.kv_len, kPage);
+    p.decode_bytes += (double)pc.kv_len * kv_tok_bytes + (double)pc.n_q * qo_row_bytes + page_bytes * ceil_div(pc.kv_len, kPage);
   p.num_small_extends = (int)small_chunks.size();
   long total_tok = 0;
   for (const DPiece& pc : pieces) total_tok += (long)pc.kv_len * c.hkv;

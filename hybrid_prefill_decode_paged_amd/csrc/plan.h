@@ -16,7 +16,8 @@ struct Config {
   int append_token_heads = kAppendTokenHeads;   // (token, KV head) pairs per KV append unit
   int extend_max_q = 0;         // chunks of at most this many rows run on the decode path (0: kExtendMaxQ, <0: never)
   int group() const { return hq / hkv; }
-  int elem_bytes() const { return dtype == POD_ATTN_BF16 ? 2 : 4; }
+  int elem_bytes() const { return dtype == POD_ATTN_FP32 ? 4 : dtype == POD_ATTN_BF16 ? 2 : 1; }   // cache element
+  int q_elem_bytes() const { return dtype == POD_ATTN_FP32 ? 4 : 2; }                           // q and out
 };
 
 struct Plan {

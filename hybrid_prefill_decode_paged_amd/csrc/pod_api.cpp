@@ -209,11 +209,17 @@ static hipError_t launch_combine(pod_attn_handle* h, const KernelParams& base, i
 // One run: plan, stage the plan, then (with k_new / v_new) the KV append and the attention
 // launches of the chosen mode.
 static pod_attn_status run_impl(pod_attn_handle* h, const void* q, const void* k_new, const void* v_new,
-                                const void* k_cache, const void* v_cache, const int32_t* block_tables,
-                                const pod_attn_batch* b, void* out, void* workspace, size_t workspace_bytes,
-                                void* stream_) {
+                                const void* k_cache, const void* v_cache, const float* k_scale,
+                                const float* v_scale, const int32_t* block_tables, const pod_attn_batch* b,
+                                void* out, void* workspace, size_t workspace_bytes, void* stream_) {
   if (!h) return fail(POD_ATTN_ERR_INVALID_ARG, "null handle");
   const bool append = k_new != nullptr;
+  const bool fp8 = h->cfg.dtype == POD_ATTN_FP8_E4M3;
+  if (fp8 && append) return fail(POD_ATTN_ERR_UNSUPPORTED, "the KV append does not write an FP8 cache");
+  if (fp8 != (k_scale != nullptr) || fp8 != (v_scale != nullptr))
+    return fail(POD_ATTN_ERR_INVALID_ARG, fp8 ? "an FP8_E4M3 cache needs k_scale and v_scale (pod_attn_run_scaled)"
+                                              : "scales are only taken by FP8_E4M3 handles");
+  if (((uintptr_t)k_scale | (uintptr_t)v_scale) & 3) return fail(POD_ATTN_ERR_INVALID_ARG, "scales must be 4-byte aligned");
   hipStream_t stream = (hipStream_t)stream_;
   const auto t0 = std::chrono::steady_clock::now();
   Plan p;
@@ -278,6 +284,7 @@ static pod_attn_status run_impl(pod_attn_handle* h, const void* q, const void* k
   kp.part_o = (float*)(ws + p.map.part_o);
   kp.part_lse = (float*)(ws + p.map.part_lse);
   kp.k_new = k_new; kp.v_new = v_new;
+  kp.k_scale = k_scale; kp.v_scale = v_scale;
   kp.aunits = (const int32_t*)(ws + p.map.aunits);
   kp.n_aunits = append ? p.n_aunits : 0;
   kp.n_pdesc = p.n_pdesc; kp.n_ddesc = p.n_ddesc;
@@ -370,7 +377,17 @@ static pod_attn_status run_impl(pod_attn_handle* h, const void* q, const void* k
 pod_attn_status pod_attn_run(pod_attn_handle* h, const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* block_tables, const pod_attn_batch* b, void* out,
                              void* workspace, size_t workspace_bytes, void* stream) {
-  return run_impl(h, q, nullptr, nullptr, k_cache, v_cache, block_tables, b, out, workspace, workspace_bytes, stream);
+  return run_impl(h, q, nullptr, nullptr, k_cache, v_cache, nullptr, nullptr, block_tables, b, out, workspace,
+                  workspace_bytes, stream);
+}
+
+pod_attn_status pod_attn_run_scaled(pod_attn_handle* h, const void* q, const void* k_cache, const void* v_cache,
+                                    const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                                    const pod_attn_batch* b, void* out, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  if (!k_scale || !v_scale) return fail(POD_ATTN_ERR_INVALID_ARG, "null k_scale or v_scale");
+  return run_impl(h, q, nullptr, nullptr, k_cache, v_cache, k_scale, v_scale, block_tables, b, out, workspace,
+                  workspace_bytes, stream);
 }
 
 pod_attn_status pod_attn_run_append(pod_attn_handle* h, const void* q, const void* k_new, const void* v_new,
@@ -378,7 +395,8 @@ pod_attn_status pod_attn_run_append(pod_attn_handle* h, const void* q, const voi
                                     const pod_attn_batch* b, void* out, void* workspace, size_t workspace_bytes,
                                     void* stream) {
   if (!k_new || !v_new) return fail(POD_ATTN_ERR_INVALID_ARG, "null k_new or v_new");
-  return run_impl(h, q, k_new, v_new, k_cache, v_cache, block_tables, b, out, workspace, workspace_bytes, stream);
+  return run_impl(h, q, k_new, v_new, k_cache, v_cache, nullptr, nullptr, block_tables, b, out, workspace,
+                  workspace_bytes, stream);
 }
 
 pod_attn_status pod_attn_set_kernel_events(pod_attn_handle* h, void* ev_start, void* ev_end) {
@@ -397,7 +415,9 @@ pod_attn_status pod_attn_get_stats(pod_attn_handle* h, pod_attn_stats* st) {
 pod_attn_status pod_attn_gather_kv(pod_attn_handle* h, const void* cache, int which, const int32_t* block_tables,
                                    int seq, int ctx, const pod_attn_batch* b, void* out_contig, void* stream) {
   if (!h || !cache || !block_tables || !b || !out_contig) return fail(POD_ATTN_ERR_INVALID_ARG, "null argument");
-  if (which != 0 && which != 1) return fail(POD_ATTN_ERR_INVALID_ARG, "which must be 0 (K) or 1 (V)");
+  const bool fp8 = h->cfg.dtype == POD_ATTN_FP8_E4M3;
+  if (!(which == 0 || which == 1 || (fp8 && (which == 2 || which == 3))))
+    return fail(POD_ATTN_ERR_INVALID_ARG, "which must be 0 (K) or 1 (V), or 2 / 3 (decoded, FP8_E4M3 handles)");
   if (seq < 0 || seq >= b->num_prefill + b->num_decode) return fail(POD_ATTN_ERR_INVALID_ARG, "seq out of range");
   if (ctx < 1 || (long)ctx > (long)b->block_table_stride * kPage) return fail(POD_ATTN_ERR_INVALID_ARG, "ctx out of range");
   const size_t total = (size_t)ctx * h->cfg.hkv * h->cfg.d;
@@ -487,7 +507,7 @@ pod_attn_status pod_attn_batch_signals(const pod_attn_config* cfg, const pod_att
   st = plan_batch(c, b, num_cus, wgs_per_cu, &p, &err);
   if (st != POD_ATTN_OK) return fail(st, err);
   if (peak_gbps <= 0.0) peak_gbps = 8000.0;
-  if (peak_tflops <= 0.0) peak_tflops = c.dtype == POD_ATTN_BF16 ? 2500.0 : 157.3;
+  if (peak_tflops <= 0.0) peak_tflops = c.dtype == POD_ATTN_FP32 ? 157.3 : 2500.0;   // FP8 cache: bf16 products
   pod_attn_signals s{};
   s.prefill_items = p.n_pf_items;
   s.decode_items = p.n_dc_items;

@@ -81,6 +81,8 @@ struct KernelParams {
   const int32_t* pdesc;      // prefill descriptors
   const int32_t* pitems;     // prefill item table (header, then (desc, split << 16 | head) per item)
   const int32_t* ddesc;      // decode descriptors
+  const float* k_scale;      // FP8 cache: [num_pages][Hkv] scale of each K slab, else null
+  const float* v_scale;      // FP8 cache: [num_pages][Hkv] scale of each V slab, else null
   const void* k_new;         // [total_q][Hkv][D] keys of the new tokens (append), or null
   const void* v_new;         // [total_q][Hkv][D] values of the new tokens
   const int32_t* aunits;     // [n_aunits][kAUnitInts] append units (workspace copy)

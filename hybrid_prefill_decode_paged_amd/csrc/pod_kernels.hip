@@ -33,6 +33,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kernels.h"
 #include "pod_internal.h"
 
@@ -50,16 +52,27 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
+// Cache element types: bf16, fp32, or Fp8 -- OCP FP8 E4M3 codes with one float scale per
+// (page, KV head) for K and one for V, q and out then being bf16.
+struct Fp8 {};
 template <typename T> struct ElemTraits;
 template <> struct ElemTraits<__bf16> { static constexpr int kBytes = 2; };
 template <> struct ElemTraits<float> { static constexpr int kBytes = 4; };
+template <> struct ElemTraits<Fp8> { static constexpr int kBytes = 1; };
+template <typename T> struct QOf { typedef T type; };       // q / out element type
+template <> struct QOf<Fp8> { typedef __bf16 type; };
+template <typename T> constexpr bool kIsFp8 = false;
+template <> constexpr bool kIsFp8<Fp8> = true;
 
 // Compile-time geometry of one (dtype, head_dim) instantiation.
 template <typename T, int D> struct Geo {
   static constexpr int kBytes = ElemTraits<T>::kBytes;
   static constexpr int kEpc = 16 / kBytes;              // elements per 16-byte chunk
   static constexpr int kNch = D / kEpc;                 // 16-byte chunks per K row
-  static constexpr int kNs = kNch / 4;                  // QK steps: one chunk per lane group
+  static constexpr int kNs = kIsFp8<T> ? D / 32 : kNch / 4;   // QK MFMA steps (bf16 MFMAs for Fp8)
+  typedef typename QOf<T>::type QT;                     // q / out element
+  static constexpr int kQBytes = sizeof(QT);
+  typedef typename std::conditional<kIsFp8<T>, u32x2, u32x4>::type KReg;   // K operand as loaded, per step
   static constexpr int kSlab = kPage * D * kBytes;      // bytes of one (page, KV head) slab
   static constexpr int kCps = kSlab / 16;               // 16-byte chunks per slab
   static constexpr int kTp = kSlab <= 4096 ? 4 : 2;     // pages per prefill KV tile
@@ -149,10 +162,32 @@ __device__ __forceinline__ f32x4 mfma_chunk(u32x4 a, u32x4 b, f32x4 c, float) {
   return c;
 }
 
+__device__ __forceinline__ f32x4 mfma_chunk(u32x4 a, u32x4 b, f32x4 c, Fp8) {   // operands already bf16
+  return mfma_chunk(a, b, c, __bf16());
+}
+
+// E4M3 -> bf16 for the Fp8 cache: the hardware converts two codes of a 16-bit half to fp32
+// (OCP E4M3 on gfx950), and every E4M3 value is exact in bf16, so keeping the upper half of
+// each fp32 loses nothing (NaN codes stay NaN).  Codes come lowest byte first.
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16(uint32_t v) {
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(v, false);
+  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(v, true);
+  return u32x2{(__float_as_uint(a.x) >> 16) | (__float_as_uint(a.y) & 0xFFFF0000u),
+               (__float_as_uint(b.x) >> 16) | (__float_as_uint(b.y) & 0xFFFF0000u)};
+}
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16(u32x2 v) {
+  const u32x2 lo = e4m3x4_to_bf16(v.x), hi = e4m3x4_to_bf16(v.y);
+  return u32x4{lo.x, lo.y, hi.x, hi.y};
+}
+// The K operand of one MFMA step as the matrix unit takes it.
+__device__ __forceinline__ u32x4 k_operand(u32x4 k) { return k; }
+__device__ __forceinline__ u32x4 k_operand(u32x2 k) { return e4m3x8_to_bf16(k); }
+
 // V^T operand of one page for one lane: 4 tokens (4q .. 4q+3) of dim d.
 template <typename T> struct VOp;
 template <> struct VOp<__bf16> { typedef u32x2 type; };
 template <> struct VOp<float> { typedef u32x4 type; };
+template <> struct VOp<Fp8> { typedef uint32_t type; };
 
 // Zero the V^T elements of slots >= lim (tokens 4q .. 4q+3), so that 0 * (NaN in an unused
 // slot) never enters the sum: masking selects, it does not multiply.
@@ -448,8 +483,9 @@ __device__ void combine_block_wave(const KernelParams& P, CPTR(int32_t) dsc, int
     }
     for (; sp < ns; ++sp) acc += wc[sp] * load_coherent4(grp, src + sp * sstride);
     const int cc = c0 + c, qi = cc / G, hh = cc - qi * G;
-    T* dst = (T*)P.out + ((size_t)(q_row + qi) * P.hq + head * G + hh) * D + 4 * d4;
-    store4<T>(dst, acc);
+    typedef typename QOf<T>::type QT;
+    QT* dst = (QT*)P.out + ((size_t)(q_row + qi) * P.hq + head * G + hh) * D + 4 * d4;
+    store4<QT>(dst, acc);
   }
 }
 
@@ -488,7 +524,7 @@ __device__ void decode_wave_item(const KernelParams& P, int item, float* sw) {
   const int cmax = q_pos + qi;                 // the last key column n sees
   u32x4 qop[Gm::kNs];
   {
-    const char* qp = (const char*)P.q + ((size_t)(q_row + qi) * P.hq + head * G + hh) * (D * Gm::kBytes);
+    const char* qp = (const char*)P.q + ((size_t)(q_row + qi) * P.hq + head * G + hh) * (D * Gm::kQBytes);
 #pragma unroll
     for (int s = 0; s < Gm::kNs; ++s) {
       u32x4 v = ld16(qp + (4 * s + q) * 16);
@@ -501,11 +537,13 @@ __device__ void decode_wave_item(const KernelParams& P, int item, float* sw) {
   for (int b = 0; b < Gm::kDb; ++b) o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegInf, l_run = 0.f;
 
-  u32x4 kA[2][Gm::kNs], kB[2][Gm::kNs];
+  typedef typename Gm::KReg KR;
+  KR kA[2][Gm::kNs], kB[2][Gm::kNs];
   VT vA[2][Gm::kDb], vB[2][Gm::kDb];
   int limA[2], limB[2];
+  float scA[4], scB[4];                        // Fp8: K scales of the step's two pages, then V scales
 
-  auto load_step = [&](int step, u32x4 (&kr)[2][Gm::kNs], VT (&vr)[2][Gm::kDb], int (&lim)[2]) {
+  auto load_step = [&](int step, KR (&kr)[2][Gm::kNs], VT (&vr)[2][Gm::kDb], int (&lim)[2], float (&sc)[4]) {
     const int tok0 = kv_begin + step * kDecodeStep;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
@@ -515,19 +553,31 @@ __device__ void decode_wave_item(const KernelParams& P, int item, float* sw) {
       lim[p] = __builtin_amdgcn_readfirstlane(l);
       const char* kp = slab_ptr<T, D>(P.k, pg, P.hkv, head);
       const char* vp = slab_ptr<T, D>(P.v, pg, P.hkv, head);
+      if constexpr (kIsFp8<T>) {
+        // 8 codes per lane and step: dims 32s+8q .. +7 sit in 16-code chunk 2s + q/2, half q%2
 #pragma unroll
-      for (int s = 0; s < Gm::kNs; ++s) kr[p][s] = ld_stream<u32x4>(kp + k_chunk_off(4 * s + q, n));
+        for (int s = 0; s < Gm::kNs; ++s) kr[p][s] = ld_stream<u32x2>(kp + k_chunk_off(2 * s + (q >> 1), n) + 8 * (q & 1));
+        sc[p] = ((CPTR(float))P.k_scale)[(size_t)pg * P.hkv + head];
+        sc[2 + p] = ((CPTR(float))P.v_scale)[(size_t)pg * P.hkv + head];
+      } else {
+#pragma unroll
+        for (int s = 0; s < Gm::kNs; ++s) kr[p][s] = ld_stream<u32x4>(kp + k_chunk_off(4 * s + q, n));
+      }
 #pragma unroll
       for (int b = 0; b < Gm::kDb; ++b) vr[p][b] = ld_stream<VT>(vp + v_elem_off<T>(16 * b + n, 4 * q));
     }
   };
 
-  auto compute_step = [&](u32x4 (&kr)[2][Gm::kNs], VT (&vr)[2][Gm::kDb], const int (&lim)[2], int tok0) {
+  auto compute_step = [&](KR (&kr)[2][Gm::kNs], VT (&vr)[2][Gm::kDb], const int (&lim)[2], const float (&sc)[4], int tok0) {
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < Gm::kNs; ++s) {
-      s0 = mfma_chunk(kr[0][s], qop[s], s0, T());
-      s1 = mfma_chunk(kr[1][s], qop[s], s1, T());
+      s0 = mfma_chunk(k_operand(kr[0][s]), qop[s], s0, T());
+      s1 = mfma_chunk(k_operand(kr[1][s]), qop[s], s1, T());
+    }
+    if constexpr (kIsFp8<T>) {                 // the K scale of each page multiplies its scores
+      s0 *= sc[0];
+      s1 *= sc[1];
     }
     float x[8];
 #pragma unroll
@@ -543,24 +593,46 @@ __device__ void decode_wave_item(const KernelParams& P, int item, float* sw) {
       }
     }
     rescale(o, softmax_update<8>(x, sl2, m_run, l_run));
-    if (lim[0] < kPage || lim[1] < kPage) {
+    if constexpr (kIsFp8<T>) {
+      // V codes -> bf16; the V scale of each page multiplies its probabilities in the product
+      // only (the row sum already has them unscaled)
+      u32x2 v8[2][Gm::kDb];
 #pragma unroll
       for (int b = 0; b < Gm::kDb; ++b) {
-        vr[0][b] = mask_vop(vr[0][b], q, lim[0]);
-        vr[1][b] = mask_vop(vr[1][b], q, lim[1]);
+        v8[0][b] = e4m3x4_to_bf16(vr[0][b]);
+        v8[1][b] = e4m3x4_to_bf16(vr[1][b]);
       }
-    }
-    if constexpr (Gm::kBytes == 2) {
-      const u32x4 pb = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]),
-                        pack_bf16(x[6], x[7])};
+      if (lim[0] < kPage || lim[1] < kPage) {
 #pragma unroll
-      for (int b = 0; b < Gm::kDb; ++b) o[b] = pv_pair(vr[0][b], vr[1][b], pb, o[b]);
+        for (int b = 0; b < Gm::kDb; ++b) {
+          v8[0][b] = mask_vop(v8[0][b], q, lim[0]);
+          v8[1][b] = mask_vop(v8[1][b], q, lim[1]);
+        }
+      }
+      const u32x4 pb = {pack_bf16(x[0] * sc[2], x[1] * sc[2]), pack_bf16(x[2] * sc[2], x[3] * sc[2]),
+                        pack_bf16(x[4] * sc[3], x[5] * sc[3]), pack_bf16(x[6] * sc[3], x[7] * sc[3])};
+#pragma unroll
+      for (int b = 0; b < Gm::kDb; ++b) o[b] = pv_pair(v8[0][b], v8[1][b], pb, o[b]);
     } else {
-      const f32x4 p0 = {x[0], x[1], x[2], x[3]}, p1 = {x[4], x[5], x[6], x[7]};
+      if (lim[0] < kPage || lim[1] < kPage) {
 #pragma unroll
-      for (int b = 0; b < Gm::kDb; ++b) {
-        o[b] = pv_page_f32(vr[0][b], p0, o[b]);
-        o[b] = pv_page_f32(vr[1][b], p1, o[b]);
+        for (int b = 0; b < Gm::kDb; ++b) {
+          vr[0][b] = mask_vop(vr[0][b], q, lim[0]);
+          vr[1][b] = mask_vop(vr[1][b], q, lim[1]);
+        }
+      }
+      if constexpr (Gm::kBytes == 2) {
+        const u32x4 pb = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]),
+                          pack_bf16(x[6], x[7])};
+#pragma unroll
+        for (int b = 0; b < Gm::kDb; ++b) o[b] = pv_pair(vr[0][b], vr[1][b], pb, o[b]);
+      } else {
+        const f32x4 p0 = {x[0], x[1], x[2], x[3]}, p1 = {x[4], x[5], x[6], x[7]};
+#pragma unroll
+        for (int b = 0; b < Gm::kDb; ++b) {
+          o[b] = pv_page_f32(vr[0][b], p0, o[b]);
+          o[b] = pv_page_f32(vr[1][b], p1, o[b]);
+        }
       }
     }
   };
@@ -568,16 +640,16 @@ __device__ void decode_wave_item(const KernelParams& P, int item, float* sw) {
   // Two register sets; past the last step the prefetch re-reads the current step (cache hits,
   // results unused) so that every load is unconditional.
   int step = 0;
-  load_step(0, kA, vA, limA);
+  load_step(0, kA, vA, limA, scA);
   for (;;) {
     int nxt = step + 1;
-    load_step(nxt < n_steps ? nxt : step, kB, vB, limB);
-    compute_step(kA, vA, limA, kv_begin + step * kDecodeStep);
+    load_step(nxt < n_steps ? nxt : step, kB, vB, limB, scB);
+    compute_step(kA, vA, limA, scA, kv_begin + step * kDecodeStep);
     if (nxt >= n_steps) break;
     step = nxt;
     nxt = step + 1;
-    load_step(nxt < n_steps ? nxt : step, kA, vA, limA);
-    compute_step(kB, vB, limB, kv_begin + step * kDecodeStep);
+    load_step(nxt < n_steps ? nxt : step, kA, vA, limA, scA);
+    compute_step(kB, vB, limB, scB, kv_begin + step * kDecodeStep);
     if (nxt >= n_steps) break;
     step = nxt;
   }
@@ -587,9 +659,10 @@ __device__ void decode_wave_item(const KernelParams& P, int item, float* sw) {
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (n < ncols) {
     if (ns == 1) {
-      T* dst = (T*)P.out + ((size_t)(q_row + qi) * P.hq + head * G + hh) * D + 4 * q;
+      typedef typename Gm::QT QT;
+      QT* dst = (QT*)P.out + ((size_t)(q_row + qi) * P.hq + head * G + hh) * D + 4 * q;
 #pragma unroll
-      for (int b = 0; b < Gm::kDb; ++b) store4<T>(dst + 16 * b, o[b] * inv);
+      for (int b = 0; b < Gm::kDb; ++b) store4<QT>(dst + 16 * b, o[b] * inv);
     } else {
       const size_t run = (size_t)dsc[kDPartBase] + ((size_t)head * ns + split) * ncols;   // this split's slots
       const bool coh = P.inline_combine != 0;
@@ -641,7 +714,7 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
     const int cc = cval[nb] ? c : 0;
     const int qi = cc / G, hh = cc - qi * G;
     pos[nb] = q_pos + qi;
-    const char* qp = (const char*)P.q + ((size_t)(q_row + qi) * P.hq + head * G + hh) * (D * Gm::kBytes);
+    const char* qp = (const char*)P.q + ((size_t)(q_row + qi) * P.hq + head * G + hh) * (D * Gm::kQBytes);
 #pragma unroll
     for (int s = 0; s < Gm::kNs; ++s) {
       u32x4 v = ld16(qp + (4 * s + q) * 16);
@@ -664,7 +737,8 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
   // registers); instruction r of wave w moves linear chunks r*256 + 64w .. +63 of
   // [K pages][V pages], one 16-byte chunk per lane, into consecutive LDS.
   int lim_cur[Gm::kTp], lim_nxt[Gm::kTp];
-  auto tile_pages = [&](int j, int (&lim)[Gm::kTp], int (&pg)[Gm::kTp]) {
+  float sc_cur[2 * Gm::kTp], sc_nxt[2 * Gm::kTp];     // Fp8: K then V scale of each page of the tile
+  auto tile_pages = [&](int j, int (&lim)[Gm::kTp], int (&pg)[Gm::kTp], float (&sc)[2 * Gm::kTp]) {
     const int tb = kv_begin + j * Gm::kTileKeys;
 #pragma unroll
     for (int p = 0; p < Gm::kTp; ++p) {
@@ -672,6 +746,12 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
       int l = min(kPage, kv_end - pi * kPage);
       pg[p] = __builtin_amdgcn_readfirstlane(page_or_empty(btr, pi, l, P.num_pages, P.ctrl + kCStatus));
       lim[p] = __builtin_amdgcn_readfirstlane(l);
+      if constexpr (kIsFp8<T>) {
+        sc[p] = ((CPTR(float))P.k_scale)[(size_t)pg[p] * P.hkv + head];
+        sc[Gm::kTp + p] = ((CPTR(float))P.v_scale)[(size_t)pg[p] * P.hkv + head];
+      } else {
+        sc[p] = sc[Gm::kTp + p] = 1.f;
+      }
     }
   };
   auto kbuf = [&](int b) { return lds + b * (2 * Gm::kTp * Gm::kSlab); };
@@ -687,9 +767,9 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
       return c;
     }
   };
-  auto issue_tile = [&](int j, int b, int (&lim)[Gm::kTp]) {
+  auto issue_tile = [&](int j, int b, int (&lim)[Gm::kTp], float (&sc)[2 * Gm::kTp]) {
     int pg[Gm::kTp];
-    tile_pages(j, lim, pg);
+    tile_pages(j, lim, pg, sc);
 #pragma unroll
     for (int r = 0; r < Gm::kStageR; ++r) {
       const int L0 = r * kThreads + 64 * w;                 // wave-uniform first chunk
@@ -706,7 +786,7 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
     }
   };
 
-  auto compute_tile = [&](int b, int j, const int (&lim)[Gm::kTp]) {
+  auto compute_tile = [&](int b, int j, const int (&lim)[Gm::kTp], const float (&sc)[2 * Gm::kTp]) {
     const int tb = kv_begin + j * Gm::kTileKeys;
     if (!wave_active || tb > pmax) return;                    // every key after every query
     bool full = tb + Gm::kTileKeys - 1 <= pmin;
@@ -719,12 +799,18 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
     for (int mb = 0; mb < Gm::kTp; ++mb) {
       u32x4 kop[Gm::kNs];
 #pragma unroll
-      for (int s = 0; s < Gm::kNs; ++s) kop[s] = *(const u32x4*)(kb + mb * Gm::kSlab + k_chunk_off(4 * s + q, n));
+      for (int s = 0; s < Gm::kNs; ++s) {
+        if constexpr (kIsFp8<T>)   // dims 32s+8q .. +7: 16-code chunk 2s + q/2, half q%2
+          kop[s] = e4m3x8_to_bf16(*(const u32x2*)(kb + mb * Gm::kSlab + k_chunk_off(2 * s + (q >> 1), n) + 8 * (q & 1)));
+        else
+          kop[s] = *(const u32x4*)(kb + mb * Gm::kSlab + k_chunk_off(4 * s + q, n));
+      }
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < Gm::kNs; ++s) acc = mfma_chunk(kop[s], qop[nb][s], acc, T());
+        if constexpr (kIsFp8<T>) acc *= sc[mb];   // the page's K scale
         S[nb][mb] = acc;
       }
     }
@@ -754,7 +840,30 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
     bool vmask = false;
 #pragma unroll
     for (int p = 0; p < Gm::kTp; ++p) vmask = vmask || lim[p] < kPage;
-    if constexpr (Gm::kBytes == 2) {
+    if constexpr (kIsFp8<T>) {
+      // V codes of 4 slots -> bf16; each page's V scale multiplies its probabilities here only
+#pragma unroll
+      for (int pp = 0; pp < Gm::kTp / 2; ++pp) {
+        u32x4 pb[2];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const f32x4 a = S[nb][2 * pp] * sc[Gm::kTp + 2 * pp], c = S[nb][2 * pp + 1] * sc[Gm::kTp + 2 * pp + 1];
+          pb[nb] = u32x4{pack_bf16(a.x, a.y), pack_bf16(a.z, a.w), pack_bf16(c.x, c.y), pack_bf16(c.z, c.w)};
+        }
+#pragma unroll
+        for (int b2 = 0; b2 < Gm::kDb; ++b2) {
+          const int d = 16 * b2 + n;
+          u32x2 va = e4m3x4_to_bf16(*(const uint32_t*)(vb + (2 * pp) * Gm::kSlab + v_elem_off<T>(d, 4 * q)));
+          u32x2 vc = e4m3x4_to_bf16(*(const uint32_t*)(vb + (2 * pp + 1) * Gm::kSlab + v_elem_off<T>(d, 4 * q)));
+          if (vmask) {
+            va = mask_vop(va, q, lim[2 * pp]);
+            vc = mask_vop(vc, q, lim[2 * pp + 1]);
+          }
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) o[nb][b2] = pv_pair(va, vc, pb[nb], o[nb][b2]);
+        }
+      }
+    } else if constexpr (Gm::kBytes == 2) {
 #pragma unroll
       for (int pp = 0; pp < Gm::kTp / 2; ++pp) {
         u32x4 pb[2];
@@ -792,17 +901,19 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
   };
 
   if (n_tiles > 0) {
-    issue_tile(0, 0, lim_cur);
+    issue_tile(0, 0, lim_cur, sc_cur);
     __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): this wave's LDS loads landed
     __syncthreads();
     for (int j = 0; j < n_tiles; ++j) {
       const bool more = j + 1 < n_tiles;
-      if (more) issue_tile(j + 1, (j + 1) & 1, lim_nxt);
-      compute_tile(j & 1, j, lim_cur);
+      if (more) issue_tile(j + 1, (j + 1) & 1, lim_nxt, sc_nxt);
+      compute_tile(j & 1, j, lim_cur, sc_cur);
       __builtin_amdgcn_s_waitcnt(0x0F70);
       __syncthreads();
 #pragma unroll
       for (int p = 0; p < Gm::kTp; ++p) lim_cur[p] = lim_nxt[p];
+#pragma unroll
+      for (int p = 0; p < 2 * Gm::kTp; ++p) sc_cur[p] = sc_nxt[p];
     }
   }
 
@@ -815,15 +926,22 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
     const int qi = c / G, hh = c - qi * G;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (ns == 1) {
-      T* dst = (T*)P.out + ((size_t)(q_row + qi) * P.hq + head * G + hh) * D + 4 * q;
+      typedef typename Gm::QT QT;
+      QT* dst = (QT*)P.out + ((size_t)(q_row + qi) * P.hq + head * G + hh) * D + 4 * q;
 #pragma unroll
-      for (int b2 = 0; b2 < Gm::kDb; ++b2) store4<T>(dst + 16 * b2, o[nb][b2] * inv);
+      for (int b2 = 0; b2 < Gm::kDb; ++b2) store4<QT>(dst + 16 * b2, o[nb][b2] * inv);
     } else {
       const size_t slot = (size_t)dsc[kDPartBase] + ((size_t)head * ns + split) * ncols + c;
-      float* dst = P.part_o + slot * D + 4 * q;
+      if (P.inline_combine) {                 // merged in-kernel by the group's last split (other dies read it)
+        const BufRsrc r = part_rsrc(P.part_o + slot * D, D * 4);
 #pragma unroll
-      for (int b2 = 0; b2 < Gm::kDb; ++b2) store_part4(dst + 16 * b2, o[nb][b2] * inv);   // merged by the combine kernel
-      if (q == 0) P.part_lse[slot] = l_tot > 0.f ? m_run[nb] + __log2f(l_tot) : kNegInf;
+        for (int b2 = 0; b2 < Gm::kDb; ++b2) store_coherent4(r, (4 * q + 16 * b2) * 4, o[nb][b2] * inv);
+      } else {                                 // merged by the combine kernel
+        float* dst = P.part_o + slot * D + 4 * q;
+#pragma unroll
+        for (int b2 = 0; b2 < Gm::kDb; ++b2) store_part4(dst + 16 * b2, o[nb][b2] * inv);
+      }
+      if (q == 0) store_part1(P.part_lse + slot, l_tot > 0.f ? m_run[nb] + __log2f(l_tot) : kNegInf, P.inline_combine != 0);
     }
   }
 }
@@ -1438,8 +1556,9 @@ __global__ __launch_bounds__(kThreads) void pod_combine_kernel(KernelParams P) {
       if (wgt > 0.f) acc += wgt * *(const f32x4*)(P.part_o + (base + (size_t)sp * ncols + c0 + c) * D + 4 * d4);
     }
     const int cc = c0 + c, qi = cc / G, hh = cc - qi * G;
-    T* dst = (T*)P.out + ((size_t)(q_row + qi) * P.hq + head * G + hh) * D + 4 * d4;
-    store4<T>(dst, acc * s_inv[c]);
+    typedef typename QOf<T>::type QT;
+    QT* dst = (QT*)P.out + ((size_t)(q_row + qi) * P.hq + head * G + hh) * D + 4 * d4;
+    store4<QT>(dst, acc * s_inv[c]);
   }
 }
 
@@ -1456,17 +1575,27 @@ __global__ __launch_bounds__(kThreads) void pod_gather_kernel(const void* cache,
   const int g = (int)((idx / D) % hkv);
   const int t = (int)(idx / ((size_t)D * hkv));
   const int pg = bt_row[t >> 4];
-  T val = T(0);
+  // element storage type: the cache's (raw codes for Fp8)
+  typedef typename std::conditional<kIsFp8<T>, uint8_t, T>::type ST;
+  ST val = ST(0);
+  const char* p = nullptr;
   if ((unsigned)pg < (unsigned)num_pages) {
     const char* sp = slab_ptr<T, D>(cache, pg, hkv, g);
     const int slot = t & 15;
-    const char* p = which == 0 ? sp + k_chunk_off(d / Gm::kEpc, slot) + (d % Gm::kEpc) * Gm::kBytes
-                               : sp + v_elem_off<T>(d, slot);
-    val = *(const T*)p;
+    p = (which & 1) == 0 ? sp + k_chunk_off(d / Gm::kEpc, slot) + (d % Gm::kEpc) * Gm::kBytes
+                         : sp + v_elem_off<T>(d, slot);
+    val = *(const ST*)p;
   } else if (status) {
     atomicOr(status, (int)kStatusBadPage);
   }
-  ((T*)out)[idx] = val;
+  if constexpr (kIsFp8<T>) {
+    if (which & 2) {                 // decoded through the kernels' E4M3 -> bf16 conversion
+      const u32x2 w = e4m3x4_to_bf16((uint32_t)val);
+      ((uint16_t*)out)[idx] = (uint16_t)(w.x & 0xFFFFu);
+      return;
+    }
+  }
+  ((ST*)out)[idx] = val;
 }
 
 // Separate-mode KV append, launched after the plan upload and before the attention kernels:
@@ -1476,7 +1605,7 @@ __global__ __launch_bounds__(kThreads) void pod_append_kernel(KernelParams P) {
   const int u = (int)blockIdx.x * kWaves + wave_index();
   if (u >= P.n_aunits) return;
   CPTR(int32_t) a = (CPTR(int32_t))P.aunits + (size_t)u * kAUnitInts;
-  append_unit<T, D>(P, a[kASeq], a[kARow], a[kAPos], a[kANtok], a[kAHead], a[kANh]);
+  if constexpr (!kIsFp8<T>) append_unit<T, D>(P, a[kASeq], a[kARow], a[kAPos], a[kANtok], a[kAHead], a[kANh]);
 }
 
 // Plan upload, launched before the attention kernels on the same stream: workgroups
@@ -1501,7 +1630,7 @@ __global__ __launch_bounds__(kThreads) void pod_stage_kernel(StageArgs A) {
   if (u >= A.p.n_aunits) return;
   const u32x4* f = (const u32x4*)(A.units_host + (size_t)u * kAUnitInts);
   const u32x4 f0 = f[0], f1 = f[1];          // every lane reads the same 32 bytes
-  append_unit<T, D>(A.p, __builtin_amdgcn_readfirstlane(f0[kASeq]), __builtin_amdgcn_readfirstlane(f0[kARow]),
+  if constexpr (!kIsFp8<T>) append_unit<T, D>(A.p, __builtin_amdgcn_readfirstlane(f0[kASeq]), __builtin_amdgcn_readfirstlane(f0[kARow]),
                     __builtin_amdgcn_readfirstlane(f0[kAPos]), __builtin_amdgcn_readfirstlane(f0[kANtok]),
                     __builtin_amdgcn_readfirstlane(f1[kAHead - 4]), __builtin_amdgcn_readfirstlane(f1[kANh - 4]));
 }
@@ -1526,6 +1655,8 @@ KernelSet make_set() {
 KernelSet kernel_set(int dtype, int head_dim) {
   if (dtype == 0 && head_dim == 128) return make_set<__bf16, 128>();
   if (dtype == 0 && head_dim == 64) return make_set<__bf16, 64>();
+  if (dtype == 2 && head_dim == 128) return make_set<Fp8, 128>();
+  if (dtype == 2 && head_dim == 64) return make_set<Fp8, 64>();
   if (dtype == 1 && head_dim == 128) return make_set<float, 128>();
   return make_set<float, 64>();
 }

@@ -33,7 +33,7 @@ UNUSED_PAGE_ID = 0x3FFFFFF0
 @dataclass
 class BatchSpec:
     name: str
-    dtype: str                      # "bf16" or "fp32"
+    dtype: str                      # "bf16", "fp32", or "fp8" (E4M3 cache with per-(page, head) scales, bf16 q)
     num_q_heads: int
     num_kv_heads: int
     head_dim: int
@@ -55,7 +55,12 @@ class BatchSpec:
 
     @property
     def elem_bytes(self) -> int:
-        return 2 if self.dtype == "bf16" else 4
+        """Bytes of one cache element."""
+        return {"bf16": 2, "fp32": 4, "fp8": 1}[self.dtype]
+
+    @property
+    def q_elem_bytes(self) -> int:
+        return 4 if self.dtype == "fp32" else 2
 
     @property
     def chunk_elems(self) -> int:
@@ -63,7 +68,12 @@ class BatchSpec:
 
     @property
     def torch_dtype(self):
-        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        """Element type of q and out (and of the cache, except for "fp8")."""
+        return torch.float32 if self.dtype == "fp32" else torch.bfloat16
+
+    @property
+    def cache_torch_dtype(self):
+        return torch.uint8 if self.dtype == "fp8" else self.torch_dtype
 
     @property
     def num_prefill(self) -> int:
@@ -117,6 +127,15 @@ def config_spec(idx: int) -> BatchSpec:
     raise ValueError(f"no workload {idx}")
 
 
+def fp8_spec(idx: int) -> BatchSpec:
+    """Workload idx (2..5) with its cache in FP8 E4M3 with per-(page, KV head) scales and bf16 q;
+    the Yi-6B-shaped workload's K outlier rows are left out (the scales are per slab)."""
+    base = config_spec(idx)
+    if base.dtype != "bf16":
+        raise ValueError("the FP8 variants are of the bf16 workloads")
+    return replace(base, name=base.name + "-fp8", dtype="fp8", k_outlier_frac=0.0)
+
+
 def spec_verify_spec(n_extend: int = 4) -> BatchSpec:
     """A speculative-verification step on the Llama-3-8B-shaped workload: its 2048-token chunk at
     offset 14336, and each of its 128 decode sequences extending by ``n_extend`` tokens instead of
@@ -157,6 +176,8 @@ class HybridBatch:
     prefill_q_start: np.ndarray     # int32 [num_prefill + 1]
     prefill_ctx_len: np.ndarray     # int32 [num_prefill]
     decode_ctx_len: np.ndarray      # int32 [num_decode]
+    k_scale: Optional[torch.Tensor] = None   # fp8: float32 [P, Hkv], scale of each K slab
+    v_scale: Optional[torch.Tensor] = None   # fp8: float32 [P, Hkv], scale of each V slab
 
     @property
     def device(self):
@@ -212,14 +233,20 @@ def make_batch(spec: BatchSpec, device="cpu", chunk_elems: int = 1 << 28) -> Hyb
     gen = torch.Generator(device=device)
     gen.manual_seed(spec.seed)
     q = torch.empty(spec.total_q, H, D, dtype=spec.torch_dtype, device=device)
-    k_pool = torch.empty(spec.num_pages, Hk, D // x, PAGE_SIZE, x, dtype=spec.torch_dtype, device=device)
-    v_pool = torch.empty(spec.num_pages, Hk, D, PAGE_SIZE, dtype=spec.torch_dtype, device=device)
+    k_pool = torch.empty(spec.num_pages, Hk, D // x, PAGE_SIZE, x, dtype=spec.cache_torch_dtype, device=device)
+    v_pool = torch.empty(spec.num_pages, Hk, D, PAGE_SIZE, dtype=spec.cache_torch_dtype, device=device)
     _fill_normal(q, gen, spec.value_scale, chunk_elems)
-    _fill_normal(k_pool, gen, spec.value_scale, chunk_elems)
-    _fill_normal(v_pool, gen, spec.value_scale, chunk_elems)
+    k_scale = v_scale = None
+    if spec.dtype == "fp8":
+        k_scale, v_scale = _fill_fp8(spec, k_pool, v_pool, gen, chunk_elems)
+    else:
+        _fill_normal(k_pool, gen, spec.value_scale, chunk_elems)
+        _fill_normal(v_pool, gen, spec.value_scale, chunk_elems)
 
     bt = block_tables_for(spec)
     if spec.k_outlier_frac > 0:
+        if spec.dtype == "fp8":
+            raise ValueError("K outlier rows are drawn for bf16/fp32 caches only")
         _scale_k_outliers(spec, k_pool, bt)
 
     q_start = np.zeros(spec.num_prefill + 1, dtype=np.int32)
@@ -231,7 +258,30 @@ def make_batch(spec: BatchSpec, device="cpu", chunk_elems: int = 1 << 28) -> Hyb
         prefill_q_start=q_start,
         prefill_ctx_len=np.asarray(spec.prefill_ctx_len, dtype=np.int32),
         decode_ctx_len=np.asarray(spec.decode_ctx_len, dtype=np.int32),
+        k_scale=k_scale, v_scale=v_scale,
     )
+
+
+def _fill_fp8(spec: BatchSpec, k_pool: torch.Tensor, v_pool: torch.Tensor, gen: torch.Generator,
+              chunk_elems: int):
+    """FP8 cache: one scale per (page, KV head) slab for K and for V, powers of two 2^-3 .. 2^0
+    drawn by numpy PCG64(seed + 2); each slab holds N(0,1) * value_scale / its scale, converted to
+    OCP E4M3 codes by torch's float8_e4m3fn cast (round to nearest even), K pool then V pool."""
+    P, Hk = spec.num_pages, spec.num_kv_heads
+    rng = np.random.Generator(np.random.PCG64(spec.seed + 2))
+    dev = k_pool.device
+    k_scale = torch.from_numpy(np.exp2(rng.integers(-3, 1, size=(P, Hk))).astype(np.float32)).to(dev)
+    v_scale = torch.from_numpy(np.exp2(rng.integers(-3, 1, size=(P, Hk))).astype(np.float32)).to(dev)
+    slab = PAGE_SIZE * spec.head_dim
+    step = max(1, chunk_elems // (Hk * slab))
+    for pool, scale in ((k_pool, k_scale), (v_pool, v_scale)):
+        flat = pool.view(P, Hk, slab)
+        for a in range(0, P, step):
+            b = min(P, a + step)
+            x = torch.randn((b - a) * Hk * slab, generator=gen, device=dev, dtype=torch.float32)
+            x = x.view(b - a, Hk, slab) * spec.value_scale / scale[a:b, :, None]
+            flat[a:b].copy_(x.to(torch.float8_e4m3fn).view(torch.uint8))
+    return k_scale, v_scale
 
 
 def _scale_k_outliers(spec: BatchSpec, k_pool: torch.Tensor, bt: np.ndarray):
@@ -269,6 +319,8 @@ def poison_unused(batch: HybridBatch, value=float("nan")):
     used = np.zeros(spec.num_pages, dtype=bool)
     for s, c in enumerate(spec.seq_ctx()):
         used[bt[s, : -(-c // PAGE_SIZE)]] = True
+    if spec.dtype == "fp8":
+        value = 0x7F                        # an E4M3 NaN code
     unused = torch.from_numpy(np.nonzero(~used)[0]).to(batch.k_pool.device)
     if unused.numel():
         batch.k_pool[unused] = value

@@ -72,7 +72,12 @@ typedef enum {
   POD_ATTN_ERR_NO_DEVICE = -5      /* no usable gfx950 device for create()                     */
 } pod_attn_status;
 
-typedef enum { POD_ATTN_BF16 = 0, POD_ATTN_FP32 = 1 } pod_attn_dtype;
+/* Element types.  FP8_E4M3: q and out are bf16; k_cache and v_cache hold OCP FP8 E4M3 codes
+ * (1 byte, x = 16 in the K layout) and every (page, KV head) slab has one float scale for K and
+ * one for V: an element's value is decode(code) * scale ([W6] "KV Cache": a low-precision cache
+ * such as FP8 halves what each decode step reads).  Runs take the scales through
+ * pod_attn_run_scaled. */
+typedef enum { POD_ATTN_BF16 = 0, POD_ATTN_FP32 = 1, POD_ATTN_FP8_E4M3 = 2 } pod_attn_dtype;
 
 /* FUSED: one persistent launch, prefill and decode work claimed per compute unit.
  * SEPARATE: prefill kernel, then decode kernel, then the split combine, serially on `stream`.
@@ -172,6 +177,19 @@ pod_attn_status pod_attn_run(pod_attn_handle* h, const void* q, const void* k_ca
                              const pod_attn_batch* batch, void* out, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* pod_attn_run for an FP8_E4M3 handle: k_scale and v_scale are device float arrays
+ * [num_pages_in_pool][Hkv], the scale of each (page, KV head) slab of k_cache / v_cache.  The
+ * scores of a key are multiplied by its page's K scale before the softmax and its probability by
+ * its page's V scale in the output sum (the row sum takes it unscaled), which is attention over
+ * the decoded, scaled cache.  Other handles: POD_ATTN_ERR_INVALID_ARG.  Everything else as
+ * pod_attn_run; pod_attn_run on an FP8_E4M3 handle returns POD_ATTN_ERR_INVALID_ARG (the scales
+ * are required) and pod_attn_run_append POD_ATTN_ERR_UNSUPPORTED (writing FP8 needs a
+ * quantizer, which stays with the cache's producer). */
+pod_attn_status pod_attn_run_scaled(pod_attn_handle* h, const void* q, const void* k_cache,
+                                    const void* v_cache, const float* k_scale, const float* v_scale,
+                                    const int32_t* block_tables, const pod_attn_batch* batch,
+                                    void* out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* KV append, then the hybrid batch: the step's new tokens are first written into the cache and
  * attention then reads them ([W6] "KV Cache": each step adds the new tokens' keys and values to
  * the cache before attending; [W6] "PagedAttention": position p of sequence s is slot p % 16 of
@@ -198,7 +216,8 @@ pod_attn_status pod_attn_get_stats(pod_attn_handle* h, pod_attn_stats* st);
 
 /* Debug/test: gather one sequence's K (which = 0) or V (which = 1) for all KV heads into
  * out_contig [ctx][Hkv][D] (same element type), through the same page-address arithmetic the
- * attention kernels use.  Bit-exact copy; asynchronous on `stream`. */
+ * attention kernels use.  Bit-exact copy; asynchronous on `stream`.  FP8_E4M3 handles also take
+ * which = 2 (K) / 3 (V): each code decoded to bf16 (unscaled) by the kernels' conversion. */
 pod_attn_status pod_attn_gather_kv(pod_attn_handle* h, const void* cache, int which,
                                    const int32_t* block_tables, int seq, int ctx,
                                    const pod_attn_batch* batch, void* out_contig, void* stream);
@@ -243,7 +262,8 @@ pod_attn_status pod_attn_plan_inspect(const pod_attn_config* cfg, const pod_attn
  * plan the batch on a device of num_cus CUs with wgs_per_cu persistent workgroups each.  The
  * "prefill share" is the chunks planned as tiles; the "decode share" is the decodes plus the
  * small-q extends.  FLOPs count 4*D per visible (query head, key) pair; bytes count K and V once
- * per KV head per context token of the share's sequences plus q read and out written once.
+ * per KV head per context token of the share's sequences, q read and out written once, and per
+ * page its block-table entry (and, for an FP8 cache, its K and V scales of every KV head).
  * roofline_us = max(total FLOPs / peak_tflops, total bytes / peak_gbps) for the given peaks
  * (<= 0 selects MI355X's: 8000 GB/s; 2500 TFLOP/s bf16, 157.3 fp32). */
 typedef struct pod_attn_signals {

@@ -10,8 +10,9 @@ from hybrid_prefill_decode_paged_amd import inputs as gen
 from oracle import attention as orc
 
 # Tolerances: bf16 inputs with fp32 accumulation: max abs <= 2e-2 and mean abs <= 2e-3;
-# fp32 inputs: max abs <= 1e-5.
-TOL = {"bf16": (2e-2, 2e-3), "fp32": (1e-5, 1e-5)}
+# fp32 inputs: max abs <= 1e-5.  FP8 cache (bf16 q/out): the bf16 bar -- the oracle decodes the
+# same codes and scales, so the difference is the bf16 rounding of q, P*scale and out.
+TOL = {"bf16": (2e-2, 2e-3), "fp32": (1e-5, 1e-5), "fp8": (2e-2, 2e-3)}
 
 
 class DevicePages:
@@ -32,7 +33,12 @@ class DevicePages:
 def problem(b: gen.HybridBatch) -> orc.HybridProblem:
     s = b.spec
     q = b.q.cpu()
-    qraw = q.view(torch.int16).numpy() if s.dtype == "bf16" else q.numpy()
+    qraw = q.view(torch.int16).numpy() if q.dtype == torch.bfloat16 else q.numpy()
+    if s.dtype == "fp8":
+        return orc.HybridProblem(qraw, DevicePages(b.k_pool, "fp8"), DevicePages(b.v_pool, "fp8"),
+                                 b.block_tables_host, b.prefill_q_start, b.prefill_ctx_len, b.decode_ctx_len,
+                                 s.num_q_heads, s.num_kv_heads, "bf16", s.softmax_scale, kv_dtype="fp8",
+                                 k_scale=b.k_scale.cpu().numpy(), v_scale=b.v_scale.cpu().numpy())
     if b.k_pool.is_cuda:
         kp, vp = DevicePages(b.k_pool, s.dtype), DevicePages(b.v_pool, s.dtype)
     else:
@@ -52,7 +58,10 @@ def run_library(b: gen.HybridBatch, mode="fused", flags=0, handle=None, out=None
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=b.q.device)
     if out is None:
         out = torch.full_like(b.q, float("nan"))
-    h.run(b.q, b.k_pool, b.v_pool, b.block_tables, meta, out, workspace)
+    if s.dtype == "fp8":
+        h.run_scaled(b.q, b.k_pool, b.v_pool, b.k_scale, b.v_scale, b.block_tables, meta, out, workspace)
+    else:
+        h.run(b.q, b.k_pool, b.v_pool, b.block_tables, meta, out, workspace)
     torch.cuda.synchronize()
     return out, h, workspace
 

@@ -284,21 +284,22 @@ def test_prefill_queues_hold_whole_key_range_groups(idx):
 
 
 # ------------------------------------------------------------------ scheduler signals, cost table
-@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5, -2, -5])
 def test_batch_signals_match_the_algorithmic_work(idx):
     """pod_attn_batch_signals' per-share FLOPs and bytes add up to the whole-batch algorithmic work
-    computed independently in bench.py, and its roofline time is that work at MI355X's peaks."""
+    computed independently in bench.py, and its roofline time is that work at MI355X's peaks
+    (negative: the workload with an FP8 cache)."""
     import bench
-    spec = gen.config_spec(idx)
+    spec = gen.config_spec(idx) if idx > 0 else gen.fp8_spec(-idx)
     sig = B.batch_signals(B.make_config(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.dtype),
                           _meta(spec), 256, 2)
     w = bench.algorithmic_work(spec)
     assert sig["prefill_bytes"] + sig["decode_bytes"] == w["bytes"]
     assert sig["prefill_flops"] + sig["decode_flops"] == w["flops"]
-    peak = bench.PEAK_MFMA[spec.dtype]
+    peak = bench.PEAK_MFMA["fp32" if spec.dtype == "fp32" else "bf16"]
     roof = max(w["flops"] / peak, w["bytes"] / bench.PEAK_HBM) * 1e6
     assert abs(sig["roofline_us"] - roof) <= 1e-9 * roof
-    assert sig["lds_bytes_per_wg"] == 65536 and sig["grid_wgs"] == 512
+    assert sig["lds_bytes_per_wg"] == (32768 if spec.dtype == "fp8" else 65536) and sig["grid_wgs"] == 512
     assert sig["fallback_reason"] == 0
 
 
