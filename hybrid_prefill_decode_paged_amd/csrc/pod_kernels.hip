@@ -166,14 +166,14 @@ __device__ __forceinline__ f32x4 mfma_chunk(u32x4 a, u32x4 b, f32x4 c, Fp8) {   
   return mfma_chunk(a, b, c, __bf16());
 }
 
-// E4M3 -> bf16 for the Fp8 cache: the hardware converts two codes of a 16-bit half to fp32
-// (OCP E4M3 on gfx950), and every E4M3 value is exact in bf16, so keeping the upper half of
-// each fp32 loses nothing (NaN codes stay NaN).  Codes come lowest byte first.
+// E4M3 -> bf16 for the Fp8 cache: gfx950 converts the two codes of a 16-bit half straight to
+// a packed bf16 pair (OCP E4M3), here with a unit scale; every E4M3 value is exact in bf16, so
+// nothing is rounded (NaN codes stay NaN).  Codes come lowest byte first.
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32x2 e4m3x4_to_bf16(uint32_t v) {
-  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(v, false);
-  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(v, true);
-  return u32x2{(__float_as_uint(a.x) >> 16) | (__float_as_uint(a.y) & 0xFFFF0000u),
-               (__float_as_uint(b.x) >> 16) | (__float_as_uint(b.y) & 0xFFFF0000u)};
+  const bf16x2v a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, false);
+  const bf16x2v b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, true);
+  return u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
 }
 __device__ __forceinline__ u32x4 e4m3x8_to_bf16(u32x2 v) {
   const u32x2 lo = e4m3x4_to_bf16(v.x), hi = e4m3x4_to_bf16(v.y);
@@ -983,15 +983,38 @@ __device__ __forceinline__ u32x4 mask_v8(u32x4 v, int lt) {
   return r;
 }
 
-template <int D>
-__device__ void prefill_item_bf16(const KernelParams& P, CPTR(int32_t) dsc, int head, int split, char* lds) {
-  constexpr int kNs = D / 32;                  // QK steps of 32 dims = K units per page
-  constexpr int kVg = D / 32;                  // V units per page
+// Zero the E4M3 codes of token slots >= lt in one 16-byte V row chunk (one dim, 16 slots).
+__device__ __forceinline__ u32x4 mask_v16_codes(u32x4 v, int lt) {
+  u32x4 r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) m |= (4 * k + b < lt ? 0xFFu : 0u) << (8 * b);
+    r[k] = v[k] & m;
+  }
+  return r;
+}
+// FP8 K slots in LDS: page parity par swaps slot bit 2, so that the b64 operand reads of the two
+// pages of a pair (rows 0..7 and 8..15 of a block) fall on different LDS banks.
+__device__ __forceinline__ int kslot8(int par, int t) { return t ^ (par << 2); }
+
+// The same tile for the bf16 cache (T = __bf16) and the FP8 cache (T = Fp8: E4M3 codes staged
+// as they are, half the bytes; operands converted to bf16 as they are read from LDS, the page's K
+// scale applied to its scores and its V scale to its probabilities in the output product).
+// FP8 LDS units are 1 KB as well: a K unit holds 4 chunks of 16 dims (64 dims) for the page's 16
+// slots, a V unit 64 dims x 16 slots.
+template <typename T, int D>
+__device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int head, int split, char* lds) {
+  constexpr bool kF8 = kIsFp8<T>;
+  constexpr int kNs = D / 32;                  // QK steps of 32 dims
+  constexpr int kKu = kF8 ? D / 64 : D / 32;   // K units per page
+  constexpr int kVg = kF8 ? D / 64 : D / 32;   // V units per page
   constexpr int kDb = D / 16;                  // 16-dim blocks of O^T
   constexpr int kTp = 4, kTileKeys = kTp * kPage;
-  constexpr int kKBytes = kTp * kNs * 1024;
+  constexpr int kKBytes = kTp * kKu * 1024;
   constexpr int kBufBytes = kKBytes + kTp * kVg * 1024;
-  static_assert(kBufBytes * 2 == Geo<__bf16, D>::kPrefillLds, "two staged tiles fill the prefill LDS");
+  static_assert(kBufBytes * 2 == Geo<T, D>::kPrefillLds, "two staged tiles fill the prefill LDS");
   const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
   const int w = wave_index();
   const int G = P.group;
@@ -1028,6 +1051,7 @@ __device__ void prefill_item_bf16(const KernelParams& P, CPTR(int32_t) dsc, int 
   const int pmax = q_pos + (min(ncols, wc0 + 32) - 1) / G;
 
   f32x4 o[2][kDb], lsum[2];
+  float lrow[2] = {0.f, 0.f};                  // FP8: this lane's share of the row sums
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     lsum[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1039,11 +1063,18 @@ __device__ void prefill_item_bf16(const KernelParams& P, CPTR(int32_t) dsc, int 
   // lane-constant LDS offsets of the operand reads and of the staging sources
   const int par = n >> 3;
   const int t_a = 8 * ((n >> 2) & 1) + (n & 3);
-  const int koff_a = par * 1024 + (q * 16 + kslot(par, t_a)) * 16;
-  const int koff_b = par * 1024 + (q * 16 + kslot(par, t_a + 4)) * 16;
-  const int voff = (q >> 1) * 1024 + (2 * n + (q & 1)) * 16;
-  const int src_k = ((lane >> 4) * 16 + kslot(w & 1, lane & 15)) * 16;
+  // bf16: K read = chunk q of the unit, 16 bytes; FP8: chunk (2(s&1) + q/2) of unit s/2, the
+  // half q%2 (8 codes), the s-dependent part added at the read
+  const int koff_a = kF8 ? par * 1024 + ((q >> 1) * 16 + kslot8(par, t_a)) * 16 + 8 * (q & 1)
+                         : par * 1024 + (q * 16 + kslot(par, t_a)) * 16;
+  const int koff_b = kF8 ? par * 1024 + ((q >> 1) * 16 + kslot8(par, t_a + 4)) * 16 + 8 * (q & 1)
+                         : par * 1024 + (q * 16 + kslot(par, t_a + 4)) * 16;
+  const int voff = kF8 ? (q >> 1) * 1024 + n * 16 + 8 * (q & 1) : (q >> 1) * 1024 + (2 * n + (q & 1)) * 16;
+  const int src_k = kF8 ? ((lane >> 4) * 16 + kslot8(w & 1, lane & 15)) * 16
+                        : ((lane >> 4) * 16 + kslot(w & 1, lane & 15)) * 16;
   const int src_v = lane * 16;
+  // FP8: K and V scales of the pages of the tiles whose K / V buffer has parity b
+  float ksc[2][kTp], vsc[2][kTp];
 
   // LDS: K buffers [2][kKBytes], then V buffers [2][kVBytes].  K(t) (tile t) lives in K buffer
   // t&1 and is staged two tiles ahead of the QK product that reads it, V(t) in V buffer t&1 one
@@ -1081,11 +1112,15 @@ __device__ void prefill_item_bf16(const KernelParams& P, CPTR(int32_t) dsc, int 
       own = p == w ? pg[p] : own;
       own_lim = p == w ? lim[p] : own_lim;
     }
+    if constexpr (kF8) {
+#pragma unroll
+      for (int p = 0; p < kTp; ++p) ksc[t & 1][p] = ((CPTR(float))P.k_scale)[(size_t)pg[p] * P.hkv + head];
+    }
     if (own_lim <= 0) return;                  // absent page: nothing is read
-    const char* kp = slab_ptr<__bf16, D>(P.k, own, P.hkv, head) + src_k;
+    const char* kp = slab_ptr<T, D>(P.k, own, P.hkv, head) + src_k;
     char* dst = kbuf(t & 1) + w * 1024;
 #pragma unroll
-    for (int s = 0; s < kNs; ++s)
+    for (int s = 0; s < kKu; ++s)
       __builtin_amdgcn_global_load_lds((const void*)(kp + s * 1024),
                                        (__attribute__((address_space(3))) void*)(dst + s * 4096), 16, 0, 0);
   };
@@ -1099,8 +1134,12 @@ __device__ void prefill_item_bf16(const KernelParams& P, CPTR(int32_t) dsc, int 
       own = p == w ? pg[p] : own;
       own_lim = p == w ? lim[p] : own_lim;
     }
+    if constexpr (kF8) {
+#pragma unroll
+      for (int p = 0; p < kTp; ++p) vsc[t & 1][p] = ((CPTR(float))P.v_scale)[(size_t)pg[p] * P.hkv + head];
+    }
     if (own_lim <= 0) return 0;
-    const char* vp = slab_ptr<__bf16, D>(P.v, own, P.hkv, head) + src_v;
+    const char* vp = slab_ptr<T, D>(P.v, own, P.hkv, head) + src_v;
     char* dst = vbuf(t & 1) + w * 1024;
 #pragma unroll
     for (int g = 0; g < kVg; ++g)
@@ -1115,10 +1154,14 @@ __device__ void prefill_item_bf16(const KernelParams& P, CPTR(int32_t) dsc, int 
     char* vu = vbuf(t & 1) + w * 1024;
 #pragma unroll
     for (int g = 0; g < kVg; ++g) {
-      const int h = lane & 1;                  // the chunk holds tokens 8h .. 8h+7
       u32x4* cp = (u32x4*)(vu + g * 4096 + lane * 16);
       const u32x4 v = lim_own > 0 ? *cp : u32x4{0u, 0u, 0u, 0u};
-      *cp = mask_v8(v, lim_own - 8 * h);
+      if constexpr (kF8) {
+        *cp = mask_v16_codes(v, lim_own);      // the chunk holds the 16 slots of one dim
+      } else {
+        const int h = lane & 1;                // the chunk holds tokens 8h .. 8h+7
+        *cp = mask_v8(v, lim_own - 8 * h);
+      }
     }
   };
 
@@ -1126,12 +1169,16 @@ __device__ void prefill_item_bf16(const KernelParams& P, CPTR(int32_t) dsc, int 
   typedef f32x4 Scores[2][2][2];               // S^T blocks [nb][pp][blk]
 
   // QK of one staged tile; the K operands of step k+1 are read while step k multiplies.
-  auto qk = [&](const char* kb, Scores& S) {
+  auto qk = [&](const char* kb, Scores& S, const float (&ks)[kTp]) {
     auto kread = [&](int k, u32x4 (&kop)[kNs]) {
       const int pp = k >> 1, blk = k & 1;
 #pragma unroll
-      for (int s = 0; s < kNs; ++s)
-        kop[s] = *(const u32x4*)(kb + (s * 4 + 2 * pp) * 1024 + (blk ? koff_b : koff_a));
+      for (int s = 0; s < kNs; ++s) {
+        if constexpr (kF8)
+          kop[s] = e4m3x8_to_bf16(*(const u32x2*)(kb + ((s >> 1) * 4 + 2 * pp) * 1024 + (s & 1) * 512 + (blk ? koff_b : koff_a)));
+        else
+          kop[s] = *(const u32x4*)(kb + (s * 4 + 2 * pp) * 1024 + (blk ? koff_b : koff_a));
+      }
     };
     u32x4 kop0[kNs], kop1[kNs];
     kread(0, kop0);
@@ -1145,6 +1192,7 @@ __device__ void prefill_item_bf16(const KernelParams& P, CPTR(int32_t) dsc, int 
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < kNs; ++s) acc = mfma_chunk(cur[s], qop[nb][s], acc, __bf16());
+        if constexpr (kF8) acc *= (q >> 1) ? ks[2 * (k >> 1) + 1] : ks[2 * (k >> 1)];   // rows of page 2pp + q/2
         S[nb][k >> 1][k & 1] = acc;
       }
     }
@@ -1171,7 +1219,10 @@ __device__ void prefill_item_bf16(const KernelParams& P, CPTR(int32_t) dsc, int 
   // than 2^kRescaleLog2: any reference value gives the same softmax as long as numerator and
   // denominator share it, and the bound keeps every probability <= 2^kRescaleLog2.  Returns
   // (per lane) whether the running output must be rescaled by alpha before the PV product.
-  auto softmax = [&](Scores& S, u32x4 (&pb)[2][2], float (&alpha)[2]) -> bool {
+  // FP8: the product's operand carries the V scale of each key's page, so it cannot give the
+  // row sums; those are summed from the fp32 probabilities instead (xsum: this lane's keys).
+  auto softmax = [&](Scores& S, u32x4 (&pb)[2][2], const float (&vs)[kTp], float (&alpha)[2],
+                     float (&xsum)[2]) -> bool {
     bool grow_any = false;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
@@ -1188,18 +1239,34 @@ __device__ void prefill_item_bf16(const KernelParams& P, CPTR(int32_t) dsc, int 
 #pragma unroll
       for (int k = 0; k < 16; ++k) x[k] = exp2_fast(__builtin_fmaf(S[nb][k >> 3][(k >> 2) & 1][k & 3], sl2, -m_use));
 #pragma unroll
-      for (int pp = 0; pp < 2; ++pp)
-        pb[nb][pp] = u32x4{pack_bf16(x[8 * pp + 0], x[8 * pp + 1]), pack_bf16(x[8 * pp + 2], x[8 * pp + 3]),
-                           pack_bf16(x[8 * pp + 4], x[8 * pp + 5]), pack_bf16(x[8 * pp + 6], x[8 * pp + 7])};
+      for (int pp = 0; pp < 2; ++pp) {
+        if constexpr (kF8) {                   // keys 8q .. 8q+7 of the pair lie in page 2pp + q/2
+          const float c = (q >> 1) ? vs[2 * pp + 1] : vs[2 * pp];
+          pb[nb][pp] = u32x4{pack_bf16(x[8 * pp + 0] * c, x[8 * pp + 1] * c), pack_bf16(x[8 * pp + 2] * c, x[8 * pp + 3] * c),
+                             pack_bf16(x[8 * pp + 4] * c, x[8 * pp + 5] * c), pack_bf16(x[8 * pp + 6] * c, x[8 * pp + 7] * c)};
+        } else {
+          pb[nb][pp] = u32x4{pack_bf16(x[8 * pp + 0], x[8 * pp + 1]), pack_bf16(x[8 * pp + 2], x[8 * pp + 3]),
+                             pack_bf16(x[8 * pp + 4], x[8 * pp + 5]), pack_bf16(x[8 * pp + 6], x[8 * pp + 7])};
+        }
+      }
+      if constexpr (kF8) {
+        float t = 0.f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) t += x[k];
+        xsum[nb] = t;
+      }
     }
     return grow_any;
   };
-  // PV of one staged tile: V^T operands two blocks ahead of the products that use them; the
-  // row sums come from the same P^T against a ones operand.
+  // PV of one staged tile: V^T operands two blocks ahead of the products that use them; for the
+  // bf16 cache the row sums come from the same P^T against a ones operand.
   auto pv = [&](const char* vb, const u32x4 (&pb)[2][2]) {
     auto vread = [&](int k) {
       const int pp = k / kDb, b2 = k % kDb;
-      return *(const u32x4*)(vb + ((b2 >> 1) * 4 + 2 * pp) * 1024 + (b2 & 1) * 512 + voff);
+      if constexpr (kF8)                       // dims 16b2 .. +15: unit b2/4, rows 16(b2%4) ..
+        return e4m3x8_to_bf16(*(const u32x2*)(vb + ((b2 >> 2) * 4 + 2 * pp) * 1024 + (b2 & 3) * 256 + voff));
+      else
+        return *(const u32x4*)(vb + ((b2 >> 1) * 4 + 2 * pp) * 1024 + (b2 & 1) * 512 + voff);
     };
     constexpr int kPv = 2 * kDb;
     u32x4 vq[3];
@@ -1211,7 +1278,7 @@ __device__ void prefill_item_bf16(const KernelParams& P, CPTR(int32_t) dsc, int 
       if (k + 2 < kPv) vq[(k + 2) % 3] = vread(k + 2);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) o[nb][b2] = mfma_chunk(vq[k % 3], pb[nb][pp], o[nb][b2], __bf16());
-      if (b2 == kDb - 1) {
+      if (!kF8 && b2 == kDb - 1) {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) lsum[nb] = mfma_chunk(ones, pb[nb][pp], lsum[nb], __bf16());
       }
@@ -1232,16 +1299,21 @@ __device__ void prefill_item_bf16(const KernelParams& P, CPTR(int32_t) dsc, int 
       const bool full = (tb + kTileKeys - 1 <= pmin) & (lim_cur[0] == kPage) & (lim_cur[1] == kPage) &
                         (lim_cur[2] == kPage) & (lim_cur[3] == kPage);
       if (!full) apply_mask(Sc, tb, lim_cur);
-      qk(kbuf((j + 1) & 1), Sn);
+      qk(kbuf((j + 1) & 1), Sn, ksc[(j + 1) & 1]);
       u32x4 pb[2][2];
-      float alpha[2];
-      if (__any(softmax(Sc, pb, alpha))) {
+      float alpha[2], xsum[2];
+      if (__any(softmax(Sc, pb, vsc[j & 1], alpha, xsum))) {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
           for (int b = 0; b < kDb; ++b) o[nb][b] *= alpha[nb];
-          lsum[nb] *= alpha[nb];
+          if constexpr (kF8) lrow[nb] *= alpha[nb];
+          else lsum[nb] *= alpha[nb];
         }
+      }
+      if constexpr (kF8) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) lrow[nb] += xsum[nb];
       }
       pv(vbuf(j & 1), pb);
     }
@@ -1260,7 +1332,7 @@ __device__ void prefill_item_bf16(const KernelParams& P, CPTR(int32_t) dsc, int 
     __builtin_amdgcn_s_waitcnt(0x0F70);
     if (own0 < kPage) zero_v_tail(0, own0);
     __syncthreads();
-    if (wave_active && kv_begin <= pmax) qk(kbuf(0), SA);
+    if (wave_active && kv_begin <= pmax) qk(kbuf(0), SA, ksc[0]);
     __syncthreads();                           // K buffer 0 is restaged by the first iteration
     for (int j = 0; j < n_tiles; j += 2) {
       iteration(j, SA, SB);
@@ -1271,7 +1343,11 @@ __device__ void prefill_item_bf16(const KernelParams& P, CPTR(int32_t) dsc, int 
   // ---- epilogue: normalise and write the output, or the split partial (o, lse)
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    const float l_tot = lsum[nb][0];           // every row of the ones-product holds the column sum
+    float l_tot = lsum[nb][0];                 // every row of the ones-product holds the column sum
+    if constexpr (kF8) {                       // the four lanes of a column hold a quarter each
+      l_tot = lrow[nb] + __shfl_xor(lrow[nb], 16);
+      l_tot += __shfl_xor(l_tot, 32);
+    }
     if (!cval[nb]) continue;
     const int c = 32 * w + 16 * nb + n;
     const int qi = c / G, hh = c - qi * G;
@@ -1305,7 +1381,7 @@ __device__ void run_prefill_item(const KernelParams& P, int item, char* lds) {
   CPTR(int32_t) e = (CPTR(int32_t))P.pitems + kPItemHeader + 2 * (size_t)item;
   CPTR(int32_t) dsc = (CPTR(int32_t))P.pdesc + (size_t)e[0] * kDescInts;
   const int split = e[1] >> 16, head = e[1] & 0xFFFF;
-  if constexpr (sizeof(T) == 2) prefill_item_bf16<D>(P, dsc, head, split, lds);
+  if constexpr (sizeof(T) == 2 || kIsFp8<T>) prefill_item_tile<T, D>(P, dsc, head, split, lds);
   else prefill_item<T, D>(P, dsc, head, split, lds);
   const int ns = dsc[kDNSplit];
   if (ns > 1 && P.inline_combine) {

@@ -95,6 +95,23 @@ def test_fp8_with_splits(mode):
     check_close(to_f64(out), problem(b).full_output(), "fp8", f"fp8-splits/{mode}")
 
 
+@pytest.mark.parametrize("mode", MODES)
+def test_fp8_general_scales(mode):
+    """Scales that are not powers of two: each (page, KV head) scale multiplied by a factor drawn
+    from [0.6, 1.5], which keeps the values' law; the scaled scores and the scaled probabilities
+    are then rounded, and a scale applied to the wrong page, head or side of the product shows."""
+    spec = gen.custom_spec("fp8", Hq=8, Hkv=2, D=128, prefill=[(150, 1500), (40, 900), (3, 70)],
+                           decode=[1, 37, 900, 2500], seed=73)
+    b = gen.make_batch(spec, "cuda")
+    gen.poison_unused(b)
+    rng = np.random.Generator(np.random.PCG64(730))
+    for t in (b.k_scale, b.v_scale):
+        t.mul_(torch.from_numpy(rng.uniform(0.6, 1.5, size=tuple(t.shape)).astype(np.float32)).to(t.device))
+    _say(f"fp8 general scales mode={mode}")
+    out, _, _ = run_library(b, mode=mode, decode_split_tokens=256, prefill_split_cap=4)
+    check_close(to_f64(out), problem(b).full_output(), "fp8", f"fp8-scales/{mode}")
+
+
 def test_fp8_entry_points_reject_what_they_cannot_do():
     spec = gen.custom_spec("fp8", Hq=4, Hkv=2, D=128, prefill=[(8, 40)], decode=[9], seed=71)
     b = gen.make_batch(spec, "cuda")
