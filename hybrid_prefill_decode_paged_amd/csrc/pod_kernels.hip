@@ -1073,8 +1073,10 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
   const int src_k = kF8 ? ((lane >> 4) * 16 + kslot8(w & 1, lane & 15)) * 16
                         : ((lane >> 4) * 16 + kslot(w & 1, lane & 15)) * 16;
   const int src_v = lane * 16;
-  // FP8: K and V scales of the pages of the tiles whose K / V buffer has parity b
-  float ksc[2][kTp], vsc[2][kTp];
+  // FP8: K and V scales of the tiles' pages, [K, V][tile parity][page], each published by the
+  // page's owner (the wave that stages it) before the barrier that precedes their use
+  __shared__ float s_scale[2][2][kTp];
+  float ks_own = 1.f, vs_own = 1.f;            // this wave's page of the tile just staged
 
   // LDS: K buffers [2][kKBytes], then V buffers [2][kVBytes].  K(t) (tile t) lives in K buffer
   // t&1 and is staged two tiles ahead of the QK product that reads it, V(t) in V buffer t&1 one
@@ -1083,39 +1085,44 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
   auto kbuf = [&](int b) { return lds + b * kKBytes; };
   auto vbuf = [&](int b) { return lds + 2 * kKBytes + b * kVBytes; };
 
-  // Block-table entries of tile t: the four loads are issued together and checked afterwards
-  // (an entry outside the pool is reported and its page counts as absent); pages past kv_end
-  // are absent and read the tile's first entry, which exists.
-  auto tile_pages = [&](int t, int (&pg)[kTp], int (&lim)[kTp]) {
-    const int pi0 = (kv_begin + t * kTileKeys) >> 4;
-#pragma unroll
-    for (int p = 0; p < kTp; ++p) {
-      lim[p] = __builtin_amdgcn_readfirstlane(max(0, min(kPage, kv_end - (pi0 + p) * kPage)));
-      pg[p] = btr[lim[p] > 0 ? pi0 + p : pi0];
-    }
+  // Block-table entries, read one tile ahead: K and V each keep the entry of their own page of
+  // the next tile they stage, so no staging waits for a scalar load, and page key counts are
+  // arithmetic.  Absent pages past kv_end read the item's first entry, which exists.  Entries
+  // outside the pool: the item's range is scanned once (every wave scans all of it, so all
+  // agree); in an item that has one, such an entry becomes -1, is never dereferenced, its page
+  // counts as absent, and page owners publish their key counts in s_lims.
+  const int pfirst = kv_begin >> 4;
+  bool clean;
+  {
     bool bad = false;
-#pragma unroll
-    for (int p = 0; p < kTp; ++p) {
-      const bool b = lim[p] > 0 && (unsigned)pg[p] >= (unsigned)P.num_pages;
-      lim[p] = b ? 0 : lim[p];
-      bad = bad | b;
-    }
-    if (bad && (threadIdx.x & 63) == 0) atomicOr(P.ctrl + kCStatus, (int)kStatusBadPage);
+    for (int i = pfirst + lane; i < (kv_end + kPage - 1) >> 4; i += 64)
+      bad = bad | ((unsigned)btr[i] >= (unsigned)P.num_pages);
+    clean = !__any(bad);
+    if (!clean && threadIdx.x == 0) atomicOr(P.ctrl + kCStatus, (int)kStatusBadPage);
+  }
+  __shared__ int s_lims[2][kTp];
+  auto page_lim = [&](int t, int p) {          // keys of page p of tile t (0: absent)
+    return min(kPage, max(0, kv_end - (((kv_begin + t * kTileKeys) >> 4) + p) * kPage));
   };
+  auto fetch_id = [&](int t) {                 // this wave's entry of tile t
+    const int id = btr[page_lim(t, w) > 0 ? ((kv_begin + t * kTileKeys) >> 4) + w : pfirst];
+    return clean || (unsigned)id < (unsigned)P.num_pages ? id : -1;
+  };
+  int kpf, vpf;                                // entries of the next K / V tile to stage
+  // Item with an entry outside the pool: tile t's key counts as its page owners published them
+  // in stage_v (call after the barrier that follows).
+  auto lims_after_barrier = [&](int t, int (&lim)[kTp]) {
+    if (!clean) {
+#pragma unroll
+      for (int p = 0; p < kTp; ++p) lim[p] = s_lims[t & 1][p];
+    }
+  };
+
   // K(t): this wave stages page w of tile t.
   auto stage_k = [&](int t) {
-    int pg[kTp], lim[kTp];
-    tile_pages(t, pg, lim);
-    int own = pg[0], own_lim = lim[0];
-#pragma unroll
-    for (int p = 1; p < kTp; ++p) {
-      own = p == w ? pg[p] : own;
-      own_lim = p == w ? lim[p] : own_lim;
-    }
-    if constexpr (kF8) {
-#pragma unroll
-      for (int p = 0; p < kTp; ++p) ksc[t & 1][p] = ((CPTR(float))P.k_scale)[(size_t)pg[p] * P.hkv + head];
-    }
+    const int own = kpf, own_lim = own < 0 ? 0 : page_lim(t, w);
+    if constexpr (kF8) ks_own = own < 0 ? 1.f : ((CPTR(float))P.k_scale)[(size_t)own * P.hkv + head];
+    kpf = fetch_id(t + 1);
     if (own_lim <= 0) return;                  // absent page: nothing is read
     const char* kp = slab_ptr<T, D>(P.k, own, P.hkv, head) + src_k;
     char* dst = kbuf(t & 1) + w * 1024;
@@ -1124,20 +1131,16 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
       __builtin_amdgcn_global_load_lds((const void*)(kp + s * 1024),
                                        (__attribute__((address_space(3))) void*)(dst + s * 4096), 16, 0, 0);
   };
-  // V(t): key counts of the tile's pages into lim; this wave stages page w; returns its count.
+  // V(t): key counts of the tile's pages into lim (item with an entry outside the pool: complete
+  // only after the next barrier, see lims_after_barrier); this wave stages page w; returns its
+  // count.
   auto stage_v = [&](int t, int (&lim)[kTp]) -> int {
-    int pg[kTp];
-    tile_pages(t, pg, lim);
-    int own = pg[0], own_lim = lim[0];
+    const int own = vpf, own_lim = own < 0 ? 0 : page_lim(t, w);
 #pragma unroll
-    for (int p = 1; p < kTp; ++p) {
-      own = p == w ? pg[p] : own;
-      own_lim = p == w ? lim[p] : own_lim;
-    }
-    if constexpr (kF8) {
-#pragma unroll
-      for (int p = 0; p < kTp; ++p) vsc[t & 1][p] = ((CPTR(float))P.v_scale)[(size_t)pg[p] * P.hkv + head];
-    }
+    for (int p = 0; p < kTp; ++p) lim[p] = page_lim(t, p);
+    if (!clean && lane == 0) s_lims[t & 1][w] = own_lim;
+    if constexpr (kF8) vs_own = own < 0 ? 1.f : ((CPTR(float))P.v_scale)[(size_t)own * P.hkv + head];
+    vpf = fetch_id(t + 1);
     if (own_lim <= 0) return 0;
     const char* vp = slab_ptr<T, D>(P.v, own, P.hkv, head) + src_v;
     char* dst = vbuf(t & 1) + w * 1024;
@@ -1285,6 +1288,21 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
     }
   };
 
+  // FP8: publish this wave's page scales of the tiles it just staged (lane 0; read by every wave
+  // after the next barrier).  Deferred to the end of the iteration, when their loads are done.
+  auto publish_k = [&](int t) {
+    if constexpr (kF8) { if (lane == 0) s_scale[0][t & 1][w] = ks_own; }
+  };
+  auto publish_v = [&](int t) {
+    if constexpr (kF8) { if (lane == 0) s_scale[1][t & 1][w] = vs_own; }
+  };
+  auto read_scales = [&](int which, int t, float (&sc)[kTp]) {
+    if constexpr (kF8) {
+#pragma unroll
+      for (int p = 0; p < kTp; ++p) sc[p] = s_scale[which][t & 1][p];
+    }
+  };
+
   int lim_cur[kTp], lim_nxt[kTp];
   // Iteration j: stage K(j+2) and V(j+1); QK(j+1) beside softmax(j) (one basic block, so the
   // matrix and vector units overlap); PV(j).  The product for tile j+1 past the last tile reads
@@ -1299,10 +1317,13 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
       const bool full = (tb + kTileKeys - 1 <= pmin) & (lim_cur[0] == kPage) & (lim_cur[1] == kPage) &
                         (lim_cur[2] == kPage) & (lim_cur[3] == kPage);
       if (!full) apply_mask(Sc, tb, lim_cur);
-      qk(kbuf((j + 1) & 1), Sn, ksc[(j + 1) & 1]);
+      float ks[kTp], vs[kTp];
+      read_scales(0, j + 1, ks);
+      read_scales(1, j, vs);
+      qk(kbuf((j + 1) & 1), Sn, ks);
       u32x4 pb[2][2];
       float alpha[2], xsum[2];
-      if (__any(softmax(Sc, pb, vsc[j & 1], alpha, xsum))) {
+      if (__any(softmax(Sc, pb, vs, alpha, xsum))) {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
@@ -1317,22 +1338,34 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
       }
       pv(vbuf(j & 1), pb);
     }
+    if (j + 2 < n_tiles) publish_k(j + 2);
+    if (more1) publish_v(j + 1);
     __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): this wave's staging loads landed
     if (own_nv < kPage) zero_v_tail(j + 1, own_nv);
     __syncthreads();
 #pragma unroll
     for (int p = 0; p < kTp; ++p) lim_cur[p] = lim_nxt[p];
+    lims_after_barrier(j + 1, lim_cur);
   };
 
   if (n_tiles > 0) {
     Scores SA, SB;
+    kpf = vpf = fetch_id(0);
     stage_k(0);
-    if (n_tiles > 1) stage_k(1);
+    publish_k(0);
+    if (n_tiles > 1) {
+      stage_k(1);
+      publish_k(1);
+    }
     const int own0 = stage_v(0, lim_cur);
+    publish_v(0);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     if (own0 < kPage) zero_v_tail(0, own0);
     __syncthreads();
-    if (wave_active && kv_begin <= pmax) qk(kbuf(0), SA, ksc[0]);
+    lims_after_barrier(0, lim_cur);
+    float ks0[kTp];
+    read_scales(0, 0, ks0);
+    if (wave_active && kv_begin <= pmax) qk(kbuf(0), SA, ks0);
     __syncthreads();                           // K buffer 0 is restaged by the first iteration
     for (int j = 0; j < n_tiles; j += 2) {
       iteration(j, SA, SB);

@@ -254,6 +254,40 @@ def test_out_of_pool_page_id_is_reported_not_read():
         assert not torch.isnan(out[16:]).any()
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("split_cap", [0, 4])
+def test_out_of_pool_entry_inside_a_prefill_chunk(dtype, split_cap):
+    """A bad entry inside a prefill chunk's cached prefix: the chunk's rows equal attention with
+    that page's 16 keys left out (the oracle's scores with those columns at -inf), every other
+    sequence is unaffected, and the status word reports it."""
+    spec = gen.custom_spec(dtype, Hq=8, Hkv=2, D=128, prefill=[(150, 1500), (20, 300)],
+                           decode=[700], seed=12)
+    b = gen.make_batch(spec, "cuda")
+    prob = problem(b)                           # built from the clean table
+    bad_pg = 10                                 # tokens 160 .. 175 of sequence 0
+    bt = b.block_tables_host.copy()
+    bt[0, bad_pg] = spec.num_pages + 77
+    b.block_tables = torch.from_numpy(bt).cuda()
+    for mode in MODES:
+        _say(f"bad entry in a chunk dtype={dtype} split_cap={split_cap} mode={mode}")
+        kw = {"prefill_split_cap": split_cap} if split_cap else {}
+        out, h, ws = run_library(b, mode=mode, **kw)
+        status, _, _ = h.read_device_status(ws)
+        assert status & B.DEVICE_ERR_BAD_PAGE
+        rows = prob.seq_rows(0)
+        pos = np.array([prob.row_info(int(r))[1] for r in rows])
+        want = np.empty((len(rows), spec.num_q_heads, spec.head_dim))
+        for hh in range(spec.num_q_heads):
+            K, V = prob.kv(0, prob.kv_head_of(hh), 1500)
+            S = orc.masked_scores(prob.q_f64(rows, hh), pos, K, prob.scale)
+            S[:, 16 * bad_pg: 16 * bad_pg + 16] = -np.inf
+            want[:, hh] = orc.softmax_rows(S) @ V
+        check_close(to_f64(out[rows]), want, dtype, f"bad-chunk/{dtype}/{mode}")
+        for s in (1, 2):
+            r = prob.seq_rows(s)
+            check_close(to_f64(out[r]), prob.sequence_output(s), dtype, f"bad-chunk/clean seq {s}/{mode}")
+
+
 def test_empty_batch_is_a_no_op():
     h = B.PodAttention(4, 2, 128, "bf16")
     meta = B.BatchMeta([0], [], [], 1, 1)
