@@ -107,6 +107,36 @@ def time_mode(torch, h, b, meta, out, ws, steps, warmup, new=None, scaled=False)
     return total_ms / steps, sum(kern) / len(kern), min(kern)
 
 
+def measured_peaks(torch, B):
+    """This GPU's HBM read rate and dense bf16 MFMA rate, from the library's probes
+    (pod_attn_probe_hbm_read over a 2 GiB buffer, pod_attn_probe_mfma), timed with HIP events
+    on the launch stream after one untimed call each."""
+    stream = torch.cuda.current_stream()
+    nbytes = 2 << 30
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+    isink = torch.empty(B.PROBE_WGS, dtype=torch.int32, device="cuda")
+    fsink = torch.empty(4 * B.PROBE_WGS, dtype=torch.float32, device="cuda")
+    iters = 2048
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        z.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(z) / 1e3 / reps
+
+    t_hbm = timed(lambda: B.probe_hbm_read(buf, isink, stream), 10)
+    flops = B.probe_mfma(iters, fsink, stream)
+    t_mfma = timed(lambda: B.probe_mfma(iters, fsink, stream), 5)
+    del buf
+    return {"hbm_read_gbps": round(nbytes / t_hbm / 1e9, 1), "mfma_bf16_tflops": round(flops / t_mfma / 1e12, 1),
+            "how": "library probes: streaming read of 2 GiB in 16 KiB blocks; 4096x4 waves x 4 chains of bf16 32x32x16 MFMA"}
+
+
 def measured_traffic(kernel_name, workload_name):
     """HBM bytes per launch from the committed counter record (FETCH_SIZE + WRITE_SIZE, each
     calibrated on a plain copy), or None when absent or taken on different kernel sources."""
@@ -336,6 +366,9 @@ def main():
     st = stats[args.mode]
     kernel_name = "pod_fused_kernel" if args.mode == "fused" else f"{args.mode} kernels"
     traffic = measured_traffic(kernel_name, spec.name)
+    print("[bench] measuring this GPU's HBM read and MFMA peaks", file=sys.stderr, flush=True)
+    peaks = measured_peaks(torch, binding)
+    m_peak = peaks["hbm_read_gbps"] if bound == "hbm" else (peaks["mfma_bf16_tflops"] if spec.dtype == "bf16" else None)
     line = {
         "metric": METRIC,
         "value": results[args.mode]["us_per_iter"],
@@ -352,10 +385,12 @@ def main():
         "config": workload_desc(spec),
         "roofline": {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "frac_vs_measured_peak": round(achieved / m_peak, 4) if m_peak else None,
                      "kernel": kernel_name,
                      "algorithmic_bytes": work["bytes"], "algorithmic_flops": work["flops"],
                      "t_roof_us": round(t_roof_s * 1e6, 2),
                      "roof_fraction_of_step": round(t_roof_s / main_ms * 1e3, 4)},
+        "measured_peaks": peaks,
         "modes": results,
         "fused_vs_separate": (round(results["separate"]["us_per_iter"] / results["fused"]["us_per_iter"], 4)
                               if "separate" in results and "fused" in results else None),
@@ -365,7 +400,7 @@ def main():
         "plan": {k: st[k] for k in ("num_prefill_items", "num_decode_items", "num_combine_groups",
                                     "decode_split_tokens", "prefill_max_splits", "grid_wgs", "wgs_per_cu",
                                     "num_cus", "vgprs_per_lane", "lds_bytes_per_wg", "mode_used", "prefill_wg_budget",
-                                    "fallback_reason")},
+                                    "fallback_reason", "host_plan_us")},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)

@@ -97,13 +97,16 @@ def load(path: str = LIB_PATH):
     lib.pod_attn_read_trace.argtypes = [VP, VP, VP, P(C.c_uint32), I, P(I)]
     lib.pod_attn_set_kernel_events.argtypes = [VP, VP, VP]
     lib.pod_attn_batch_signals.argtypes = [P(Config), P(Batch), I, I, C.c_double, C.c_double, P(Signals)]
+    lib.pod_attn_probe_hbm_read.argtypes = [VP, C.c_size_t, VP, VP]
+    lib.pod_attn_probe_mfma.argtypes = [I, VP, P(C.c_double), VP]
     lib.pod_attn_last_error.restype = C.c_char_p
     lib.pod_attn_destroy.argtypes = [VP]
     lib.pod_attn_destroy.restype = None
     for name in ("pod_attn_create", "pod_attn_workspace_size", "pod_attn_run", "pod_attn_run_append",
                  "pod_attn_run_scaled", "pod_attn_get_stats",
                  "pod_attn_gather_kv", "pod_attn_read_device_status", "pod_attn_plan_inspect", "pod_attn_read_trace",
-                 "pod_attn_set_kernel_events", "pod_attn_batch_signals"):
+                 "pod_attn_set_kernel_events", "pod_attn_batch_signals", "pod_attn_probe_hbm_read",
+                 "pod_attn_probe_mfma"):
         getattr(lib, name).restype = C.c_int
     _lib = lib
     return lib
@@ -166,6 +169,24 @@ def plan_inspect(cfg: Config, meta: BatchMeta, num_cus: int, wgs_per_cu: int):
                                      items.ctypes.data_as(C.POINTER(C.c_int32)), n.value,
                                      C.byref(n), None))
     return items[: n.value], st.as_dict()
+
+
+PROBE_WGS = 4096          # workgroups of either probe (pod_attn_probe_*)
+
+
+def probe_hbm_read(buf, sink, stream=None) -> None:
+    """pod_attn_probe_hbm_read: one streaming read of the device tensor buf; sink is a device
+    uint32 (int32) tensor of PROBE_WGS elements receiving per-workgroup XORs of the words read."""
+    _check(load().pod_attn_probe_hbm_read(_ptr(buf), int(buf.numel() * buf.element_size()), _ptr(sink),
+                                          _stream_handle(stream)))
+
+
+def probe_mfma(iters: int, sink, stream=None) -> float:
+    """pod_attn_probe_mfma: dense bf16 MFMA work; sink is a device float tensor of 4*PROBE_WGS
+    elements (each receives 4*iters).  Returns the FLOPs performed."""
+    flops = C.c_double(0.0)
+    _check(load().pod_attn_probe_mfma(int(iters), _ptr(sink), C.byref(flops), _stream_handle(stream)))
+    return flops.value
 
 
 def batch_signals(cfg: Config, meta: BatchMeta, num_cus: int, wgs_per_cu: int, peak_gbps: float = 0.0,

@@ -18,4 +18,13 @@ struct KernelSet {
 // dtype: 0 bf16, 1 fp32, 2 FP8 E4M3 cache with bf16 q/out; head_dim: 64 or 128.
 KernelSet kernel_set(int dtype, int head_dim);
 
+// Measurement probes (peaks on the machine at hand).
+constexpr int kProbeWgs = 4096;    // workgroups of either probe
+constexpr int kProbeChains = 4;    // independent 32x32x16 MFMA chains per wave
+struct ProbeKernels {
+  const void* hbm_read = nullptr;  // (const u32x4* buf, size_t n16, uint32_t* sink)
+  const void* mfma = nullptr;      // (int iters, float* sink)
+};
+ProbeKernels probe_kernels();
+
 }  // namespace pod

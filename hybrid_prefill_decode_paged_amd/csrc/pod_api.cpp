@@ -406,6 +406,27 @@ pod_attn_status pod_attn_set_kernel_events(pod_attn_handle* h, void* ev_start, v
   return POD_ATTN_OK;
 }
 
+pod_attn_status pod_attn_probe_hbm_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink) return fail(POD_ATTN_ERR_INVALID_ARG, "null buffer or sink");
+  if (bytes == 0 || bytes % 16 != 0 || ((uintptr_t)buf & 15) != 0)
+    return fail(POD_ATTN_ERR_INVALID_ARG, "bytes must be a positive multiple of 16 and buf 16-byte aligned");
+  const ProbeKernels pk = probe_kernels();
+  size_t n16 = bytes / 16;
+  void* args[] = {(void*)&buf, &n16, (void*)&sink};
+  POD_HIP(hipLaunchKernel(pk.hbm_read, dim3(kProbeWgs), dim3(kThreads), args, 0, (hipStream_t)stream));
+  return POD_ATTN_OK;
+}
+
+pod_attn_status pod_attn_probe_mfma(int iters, float* sink, double* flops, void* stream) {
+  if (!sink) return fail(POD_ATTN_ERR_INVALID_ARG, "null sink");
+  if (iters < 1 || iters > (1 << 20)) return fail(POD_ATTN_ERR_INVALID_ARG, "iters must be in [1, 2^20]");
+  const ProbeKernels pk = probe_kernels();
+  void* args[] = {&iters, (void*)&sink};
+  POD_HIP(hipLaunchKernel(pk.mfma, dim3(kProbeWgs), dim3(kThreads), args, 0, (hipStream_t)stream));
+  if (flops) *flops = (double)kProbeWgs * kWaves * kProbeChains * (double)iters * (2.0 * 32 * 32 * 16);
+  return POD_ATTN_OK;
+}
+
 pod_attn_status pod_attn_get_stats(pod_attn_handle* h, pod_attn_stats* st) {
   if (!h || !st) return fail(POD_ATTN_ERR_INVALID_ARG, "null handle or stats");
   *st = h->stats;

@@ -1759,7 +1759,70 @@ KernelSet make_set() {
   return s;
 }
 
+// ------------------------------------------------------------------ measurement probes
+// Streaming read of n16 16-byte chunks in 16 KiB blocks: wave v of the grid reads blocks v,
+// v + waves, ..., all 16 loads of a block in flight (16 per lane, consecutive lanes on consecutive
+// chunks); each workgroup writes the XOR of its words to sink[wg] (so the read cannot be dropped,
+// and a test can check that every byte was read).
+__global__ __launch_bounds__(kThreads) void pod_probe_hbm_read_kernel(const u32x4* buf, size_t n16, uint32_t* sink) {
+  constexpr int kPer = 16;                     // loads per lane per block
+  constexpr size_t kBlock = 64 * kPer;         // chunks per block (16 KiB)
+  const size_t nwaves = (size_t)gridDim.x * kWaves;
+  const size_t lane = threadIdx.x & 63;
+  uint32_t x = 0;
+  for (size_t blk = (size_t)blockIdx.x * kWaves + (threadIdx.x >> 6); blk * kBlock < n16; blk += nwaves) {
+    const size_t base = blk * kBlock + lane;
+    u32x4 v[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const size_t i = base + (size_t)j * 64;
+      v[j] = i < n16 ? __builtin_nontemporal_load(buf + i) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) x ^= v[j][0] ^ v[j][1] ^ v[j][2] ^ v[j][3];
+  }
+  for (int o = 32; o >= 1; o >>= 1) x ^= (uint32_t)__shfl_xor((int)x, o);
+  __shared__ uint32_t s_x[kWaves];
+  if ((threadIdx.x & 63) == 0) s_x[threadIdx.x >> 6] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = s_x[0] ^ s_x[1] ^ s_x[2] ^ s_x[3];
+}
+
+// Dense bf16 MFMA: every wave runs kProbeChains independent 32x32x16 accumulation chains for
+// `iters` rounds (the 32x32 form keeps the matrix unit busy with few chains; the 16x16x32 form
+// needs about 16).  A is all ones and B all 2^-4, so each product adds exactly 1.0 to every
+// accumulator element; lane 0 of each wave writes the sum of its chains' first elements
+// (kProbeChains * iters) to sink[4 * wg + wave].
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__global__ __launch_bounds__(kThreads) void pod_probe_mfma_kernel(int iters, float* sink) {
+  const uint32_t bv = iters > 0 ? 0x3D803D80u : 0u;    // bf16 2^-4 pairs, opaque to the compiler
+  const u32x4 a = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  const u32x4 b = {bv, bv, bv, bv};
+  const bf16x8_t A = __builtin_bit_cast(bf16x8_t, a), B = __builtin_bit_cast(bf16x8_t, b);
+  f32x16 c[kProbeChains];
+#pragma unroll
+  for (int k = 0; k < kProbeChains; ++k) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) c[k][e] = 0.f;
+  }
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < kProbeChains; ++k) c[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, c[k], 0, 0, 0);
+  }
+  float t = 0.f;
+#pragma unroll
+  for (int k = 0; k < kProbeChains; ++k) t += c[k][0];
+  if ((threadIdx.x & 63) == 0) sink[4 * blockIdx.x + (threadIdx.x >> 6)] = t;
+}
+
 }  // namespace
+
+ProbeKernels probe_kernels() {
+  ProbeKernels p;
+  p.hbm_read = (const void*)&pod_probe_hbm_read_kernel;
+  p.mfma = (const void*)&pod_probe_mfma_kernel;
+  return p;
+}
 
 KernelSet kernel_set(int dtype, int head_dim) {
   if (dtype == 0 && head_dim == 128) return make_set<__bf16, 128>();
