@@ -24,6 +24,12 @@
 namespace pod {
 
 namespace {
+// Sustained rates of the two shares on gfx950, used only to tell a prefill-heavy batch from a
+// decode-heavy one when sizing decode splits: the prefill tile at about a third of the bf16
+// matrix peak, the decode stream at about 6.5 TB/s (both measured with rocprofv3).
+constexpr double kPrefillFlopsPerSec = 0.85e15;
+constexpr double kDecodeBytesPerSec = 6.5e12;
+constexpr double kPrefillHeavyRatio = 0.75;   // prefill share >= 3/4 of the decode share
 int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 int round_up_int(int a, int m) { return ceil_div(a, m) * m; }
 }  // namespace
@@ -247,6 +253,15 @@ pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus
     // begin on prefill tiles) finish with the rest (measured on the four bf16 workloads: one
     // per wave left a tail, four per wave lost 1-5%).
     long target_items = (long)num_cus * wgs_per_cu * kWaves * 2;
+    // Fused handles, when the prefill share is about as long as the decode share: about one
+    // item per workgroup slot instead.  The decode-role workgroups that find the queue empty
+    // take prefill tiles, so the matrix work gets the CUs the stream does not need (measured on
+    // the Yi-6B-shaped batch: 601 -> 574 us; decode-dominant batches keep the rule above, where
+    // it was measured best).  Shares estimated at what the tile and the stream sustain.  The
+    // separate decode kernel keeps many items (one workgroup per four).
+    const double t_prefill = p.prefill_flops / kPrefillFlopsPerSec, t_decode = p.decode_bytes / kDecodeBytesPerSec;
+    if (c.mode == POD_ATTN_MODE_FUSED && t_prefill >= kPrefillHeavyRatio * t_decode)
+      target_items = (long)num_cus * wgs_per_cu;
     long st = (total_tok + target_items - 1) / std::max(1L, target_items);
     st = std::max(512L, std::min(32768L, st));
     st_target = round_up_int((int)st, 128);

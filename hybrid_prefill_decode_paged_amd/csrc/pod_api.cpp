@@ -70,6 +70,7 @@ struct pod_attn_handle {
   int prefill_wgs_override = 0;     // POD_ATTN_PREFILL_WGS
   int prefill_per_cu_override = 0;  // POD_ATTN_PREFILL_PER_CU
   int prefill_cus_override = 0;     // POD_ATTN_PREFILL_CUS (-1: per-CU cap policy)
+  int role_prio = 0;                // POD_ATTN_ROLE_PRIO (decode | prefill << 2)
 };
 
 extern "C" {
@@ -112,6 +113,7 @@ pod_attn_status pod_attn_create(const pod_attn_config* cfg, pod_attn_handle** ou
   h->prefill_wgs_override = env_int("POD_ATTN_PREFILL_WGS", 0);
   h->prefill_per_cu_override = env_int("POD_ATTN_PREFILL_PER_CU", 0);
   h->prefill_cus_override = env_int("POD_ATTN_PREFILL_CUS", 0);
+  h->role_prio = env_int("POD_ATTN_ROLE_PRIO", 0) & 15;
   if (const char* m = std::getenv("POD_ATTN_MODE")) {
     if (!std::strcmp(m, "fused")) h->mode_env = POD_ATTN_MODE_FUSED;
     else if (!std::strcmp(m, "separate")) h->mode_env = POD_ATTN_MODE_SEPARATE;
@@ -296,6 +298,7 @@ static pod_attn_status run_impl(pod_attn_handle* h, const void* q, const void* k
   kp.prefill_cap_per_cu = prefill_per_cu(h);
   kp.prefill_wg_budget = prefill_budget(h, p);
   kp.prefill_cus = prefill_cus(h, p);
+  kp.role_prio = h->role_prio;
 
   // Plan upload (and, in fused mode, the KV append in the same launch).
   stage_plan(p, h->cfg, (uint8_t*)slot.host, append);

@@ -98,6 +98,7 @@ struct KernelParams {
   int prefill_wg_budget;     // fused: prefill-role workgroups allowed device-wide while decode remains
   int prefill_cus;           // fused: > 0: CUs (spread over the dies) whose workgroups all take prefill while decode remains
   int inline_combine;        // 1: the last-arriving decode split merges its group in-kernel (fused)
+  int role_prio;             // fused: wave priority (0..3) of decode-role (low 2 bits) and prefill-role (next 2) waves
   int group_begin, group_end;// combine kernel range
   int combine_col_blocks;     // combine kernel: workgroups per group (16 columns each)
 };

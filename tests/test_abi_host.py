@@ -112,6 +112,31 @@ def test_plan_ragged_batches(G, D, split, cap):
         assert st["decode_split_tokens"] == split
 
 
+@pytest.mark.parametrize("idx", [2, 3, 4, 5])
+def test_decode_split_length_follows_the_share_balance(idx):
+    """Fused plans of a batch whose prefill share is about as long as its decode share (the
+    Yi-6B-shaped one) cut decode sequences into about one item per workgroup slot; decode-heavy
+    batches, and every separate-mode plan, keep about two items per decode wave."""
+    spec = gen.config_spec(idx)
+    meta = _meta(spec)
+    slots = 256 * 2
+    tok = sum(spec.decode_ctx_len) * spec.num_kv_heads
+    for mode in ("fused", "separate"):
+        cfg = B.make_config(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.dtype, mode)
+        _, st = B.plan_inspect(cfg, meta, 256, 2)
+        per_wave = -(-tok // (slots * 4 * 2))
+        expect = -(-min(32768, max(512, per_wave)) // 128) * 128
+        if mode == "fused" and idx == 4:
+            expect = -(-min(32768, max(512, -(-tok // slots))) // 128) * 128
+        assert st["decode_split_tokens"] == expect, (idx, mode)
+    cfg = B.make_config(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.dtype, "fused")
+    _, st = B.plan_inspect(cfg, meta, 256, 2)
+    if idx == 4:
+        assert st["num_decode_items"] <= 2 * slots
+    else:
+        assert st["num_decode_items"] >= 4 * slots
+
+
 @pytest.mark.parametrize("G", [1, 3, 4, 8, 16])
 def test_small_chunks_take_the_decode_path(G):
     """Chunks whose rows x G fit one 16-column block (at most 16 rows, the default) become one
