@@ -149,15 +149,29 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 template <typename V>
 __device__ __forceinline__ V ld_stream(const char* p) { return __builtin_nontemporal_load((const V*)p); }
 
+// Maxima of scores (finite, or -inf where masked) without the NaN-quieting the compiler puts
+// around fmaxf: it emits v_max_f32 x, x on every operand it cannot prove canonical, and scores
+// come straight from the matrix unit or a lane swap.  Plain VALU instructions, no memory.
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // Reductions over lanes l, l^16, l^32, l^48 with the gfx950 lane-swap instructions (VALU, no
 // LDS round trip): v_permlane16_swap applied to (v, v) hands every lane the values of lanes
 // l&~16 and l|16, i.e. its own and its partner's, in the same order on both partners, so the
 // results are bit-identical across the four lanes.
 __device__ __forceinline__ float max_over_groups(float v) {
   auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  v = max_raw(__uint_as_float(a[0]), __uint_as_float(a[1]));
   auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return max_raw(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float sum_over_groups(float v) {
   auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -1253,9 +1267,11 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
     bool grow_any = false;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      float m = S[nb][0][0][0];
+      auto sv = [&](int k) { return S[nb][k >> 3][(k >> 2) & 1][k & 3]; };
+      float m = max3_raw(sv(0), sv(1), sv(2));
 #pragma unroll
-      for (int k = 1; k < 16; ++k) m = fmaxf(m, S[nb][k >> 3][(k >> 2) & 1][k & 3]);
+      for (int k = 3; k + 1 < 16; k += 2) m = max3_raw(m, sv(k), sv(k + 1));
+      m = max_raw(m, sv(15));
       const float mx = max_over_groups(m) * sl2;
       const bool grow = mx > m_run[nb] + kRescaleLog2;
       alpha[nb] = grow ? exp2_fast(m_run[nb] - mx) : 1.f;
