@@ -83,31 +83,9 @@ template <typename T, int D> struct Geo {
   static constexpr int kPrefillLds = 2 * 2 * kTp * kSlab;              // 2 buffers x (K, V)
   static constexpr int kCombineLds = kWaves * kCombineLdsPerWave;    // in-kernel split combine tables
   static constexpr int kFusedLds = kPrefillLds > kCombineLds ? kPrefillLds : kCombineLds;
-  static constexpr int kStageBuf = kPrefillLds / 4;                    // one K or V staging buffer
-  static constexpr int kFusedBuf = kFusedLds / 4;                      // the same, fused kernel
   static_assert(kFusedLds == fused_lds_bytes(kBytes, D), "host-side LDS figure matches the kernels");
   static_assert(kStageChunks % kThreads == 0, "tile must split evenly over the workgroup");
   static_assert(kTp % 2 == 0, "bf16 PV pairs pages");
-  static_assert(kFusedBuf % kCombineLdsPerWave == 0 && kFusedBuf >= kStageBuf, "buffers hold the combine tables");
-};
-
-// LDS of a prefill workgroup: the K and V staging buffers, two of each, as four separate LDS
-// objects.  The compiler's wait-count pass tracks LDS-DMA loads per LDS object: with one object
-// it makes every LDS read wait for all staging loads in flight (vmcnt(0) before the first
-// operand read of each tile); with four, a read of one buffer does not wait for the loads into
-// another, and the next tile's staging overlaps this tile's products.  Index the buffers with
-// compile-time constants wherever that overlap matters.
-struct LdsBufs {
-  char* k[2];
-  char* v[2];
-  // per-wave split-combine tables (kCombineLdsPerWave bytes each) laid over the buffers
-  template <int kBuf>
-  __device__ float* combine_table(int w) const {
-    constexpr int kPer = kBuf / kCombineLdsPerWave;   // tables per buffer: 1 or 2
-    const int b = w / kPer;
-    char* base = b == 0 ? k[0] : b == 1 ? k[1] : b == 2 ? v[0] : v[1];
-    return (float*)(base + (w - b * kPer) * kCombineLdsPerWave);
-  }
 };
 
 // ------------------------------------------------------------------ page addressing
@@ -725,7 +703,7 @@ __device__ void decode_wave_item(const KernelParams& P, int item, float* sw) {
 // owns columns 32w .. 32w+31 (two 16-wide blocks).  Keys advance 64 (or 32) at a time,
 // staged in LDS by all 256 threads with the next tile's global loads in flight.
 template <typename T, int D>
-__device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head, int split, const LdsBufs& L) {
+__device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head, int split, char* lds) {
   using Gm = Geo<T, D>;
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, q = lane >> 4;
   const int w = wave_index();
@@ -790,8 +768,8 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
       }
     }
   };
-  auto kbuf = [&](int b) { return b ? L.k[1] : L.k[0]; };
-  auto vbuf = [&](int b) { return b ? L.v[1] : L.v[0]; };
+  auto kbuf = [&](int b) { return lds + b * (2 * Gm::kTp * Gm::kSlab); };
+  auto vbuf = [&](int b) { return lds + b * (2 * Gm::kTp * Gm::kSlab) + Gm::kTp * Gm::kSlab; };
   // bf16 V rows are 32 bytes (two 16-byte halves); rows 8..15 of each 16-row block swap their
   // halves so that a wave's 8-byte reads of 16 consecutive rows spread over all LDS banks.
   // The swap is its own inverse, so LDS chunk c is loaded from source chunk vswz(c).
@@ -1041,7 +1019,7 @@ __device__ __forceinline__ int kslot8(int par, int t) { return t ^ (par << 2); }
 // FP8 LDS units are 1 KB as well: a K unit holds 4 chunks of 16 dims (64 dims) for the page's 16
 // slots, a V unit 64 dims x 16 slots.
 template <typename T, int D>
-__device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int head, int split, const LdsBufs& L) {
+__device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int head, int split, char* lds) {
   constexpr bool kF8 = kIsFp8<T>;
   constexpr int kNs = D / 32;                  // QK steps of 32 dims
   constexpr int kKu = kF8 ? D / 64 : D / 32;   // K units per page
@@ -1051,9 +1029,6 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
   constexpr int kKBytes = kTp * kKu * 1024;
   constexpr int kBufBytes = kKBytes + kTp * kVg * 1024;
   static_assert(kBufBytes * 2 == Geo<T, D>::kPrefillLds, "two staged tiles fill the prefill LDS");
-  static_assert(kKBytes == Geo<T, D>::kStageBuf && kBufBytes == 2 * kKBytes, "one K or V tile per buffer");
-  typedef std::integral_constant<int, 0> Par0;
-  typedef std::integral_constant<int, 1> Par1;
   const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
   const int w = wave_index();
   const int G = P.group;
@@ -1117,11 +1092,12 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
   __shared__ float s_scale[2][2][kTp];
   float ks_own = 1.f, vs_own = 1.f;            // this wave's page of the tile just staged
 
-  // LDS: K(t) (tile t) lives in K buffer t&1 and is staged two tiles ahead of the QK product
-  // that reads it, V(t) in V buffer t&1 one tile ahead of its PV product, so that tile t's
-  // softmax can run beside tile t+1's QK.  The buffer parity is a compile-time constant (par).
-  auto kbuf = [&](auto par) { return L.k[decltype(par)::value]; };
-  auto vbuf = [&](auto par) { return L.v[decltype(par)::value]; };
+  // LDS: K buffers [2][kKBytes], then V buffers [2][kVBytes].  K(t) (tile t) lives in K buffer
+  // t&1 and is staged two tiles ahead of the QK product that reads it, V(t) in V buffer t&1 one
+  // tile ahead of its PV product, so that tile t's softmax can run beside tile t+1's QK.
+  constexpr int kVBytes = kTp * kVg * 1024;
+  auto kbuf = [&](int b) { return lds + b * kKBytes; };
+  auto vbuf = [&](int b) { return lds + 2 * kKBytes + b * kVBytes; };
 
   // Block-table entries, read one tile ahead: K and V each keep the entry of their own page of
   // the next tile they stage, so no staging waits for a scalar load, and page key counts are
@@ -1156,14 +1132,14 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
     }
   };
 
-  // K(t): this wave stages page w of tile t (par = t & 1).
-  auto stage_k = [&](auto par, int t) {
+  // K(t): this wave stages page w of tile t.
+  auto stage_k = [&](int t) {
     const int own = kpf, own_lim = own < 0 ? 0 : page_lim(t, w);
     if constexpr (kF8) ks_own = own < 0 ? 1.f : ((CPTR(float))P.k_scale)[(size_t)own * P.hkv + head];
     kpf = fetch_id(t + 1);
     if (own_lim <= 0) return;                  // absent page: nothing is read
     const char* kp = slab_ptr<T, D>(P.k, own, P.hkv, head) + src_k;
-    char* dst = kbuf(par) + w * 1024;
+    char* dst = kbuf(t & 1) + w * 1024;
 #pragma unroll
     for (int s = 0; s < kKu; ++s)
       __builtin_amdgcn_global_load_lds((const void*)(kp + s * 1024),
@@ -1172,7 +1148,7 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
   // V(t): key counts of the tile's pages into lim (item with an entry outside the pool: complete
   // only after the next barrier, see lims_after_barrier); this wave stages page w; returns its
   // count.
-  auto stage_v = [&](auto par, int t, int (&lim)[kTp]) -> int {
+  auto stage_v = [&](int t, int (&lim)[kTp]) -> int {
     const int own = vpf, own_lim = own < 0 ? 0 : page_lim(t, w);
 #pragma unroll
     for (int p = 0; p < kTp; ++p) lim[p] = page_lim(t, p);
@@ -1181,7 +1157,7 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
     vpf = fetch_id(t + 1);
     if (own_lim <= 0) return 0;
     const char* vp = slab_ptr<T, D>(P.v, own, P.hkv, head) + src_v;
-    char* dst = vbuf(par) + w * 1024;
+    char* dst = vbuf(t & 1) + w * 1024;
 #pragma unroll
     for (int g = 0; g < kVg; ++g)
       __builtin_amdgcn_global_load_lds((const void*)(vp + g * 1024),
@@ -1191,8 +1167,8 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
   // After this wave's staging loads have landed: zero the V slots of tokens >= lim of its page
   // (all of them for an absent page), so that a zero probability never meets a NaN or stale
   // value in the PV product.  Scores of those slots are masked by select.
-  auto zero_v_tail = [&](auto par, int lim_own) {
-    char* vu = vbuf(par) + w * 1024;
+  auto zero_v_tail = [&](int t, int lim_own) {
+    char* vu = vbuf(t & 1) + w * 1024;
 #pragma unroll
     for (int g = 0; g < kVg; ++g) {
       u32x4* cp = (u32x4*)(vu + g * 4096 + lane * 16);
@@ -1347,13 +1323,12 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
   // Iteration j: stage K(j+2) and V(j+1); QK(j+1) beside softmax(j) (one basic block, so the
   // matrix and vector units overlap); PV(j).  The product for tile j+1 past the last tile reads
   // a stale buffer and is discarded.
-  auto iteration = [&](auto par, int j, Scores& Sc, Scores& Sn) {
-    const std::integral_constant<int, 1 - decltype(par)::value> npar;   // parity of tile j+1
+  auto iteration = [&](int j, Scores& Sc, Scores& Sn) {
     const int tb = kv_begin + j * kTileKeys;
     const bool more1 = j + 1 < n_tiles;
-    if (j + 2 < n_tiles) stage_k(par, j + 2);
+    if (j + 2 < n_tiles) stage_k(j + 2);
     int own_nv = kPage;
-    if (more1) own_nv = stage_v(npar, j + 1, lim_nxt);
+    if (more1) own_nv = stage_v(j + 1, lim_nxt);
     if (wave_active && tb <= pmax) {          // else every key follows every query of the wave
       const bool full = (tb + kTileKeys - 1 <= pmin) & (lim_cur[0] == kPage) & (lim_cur[1] == kPage) &
                         (lim_cur[2] == kPage) & (lim_cur[3] == kPage);
@@ -1361,7 +1336,7 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
       float ks[kTp], vs[kTp];
       read_scales(0, j + 1, ks);
       read_scales(1, j, vs);
-      qk(kbuf(npar), Sn, ks);
+      qk(kbuf((j + 1) & 1), Sn, ks);
       u32x4 pb[2][2];
       float alpha[2], xsum[2];
       if (__any(softmax(Sc, pb, vs, alpha, xsum))) {
@@ -1377,12 +1352,12 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) lrow[nb] += xsum[nb];
       }
-      pv(vbuf(par), pb);
+      pv(vbuf(j & 1), pb);
     }
     if (j + 2 < n_tiles) publish_k(j + 2);
     if (more1) publish_v(j + 1);
     __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): this wave's staging loads landed
-    if (own_nv < kPage) zero_v_tail(npar, own_nv);
+    if (own_nv < kPage) zero_v_tail(j + 1, own_nv);
     __syncthreads();
 #pragma unroll
     for (int p = 0; p < kTp; ++p) lim_cur[p] = lim_nxt[p];
@@ -1392,25 +1367,25 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
   if (n_tiles > 0) {
     Scores SA, SB;
     kpf = vpf = fetch_id(0);
-    stage_k(Par0(), 0);
+    stage_k(0);
     publish_k(0);
     if (n_tiles > 1) {
-      stage_k(Par1(), 1);
+      stage_k(1);
       publish_k(1);
     }
-    const int own0 = stage_v(Par0(), 0, lim_cur);
+    const int own0 = stage_v(0, lim_cur);
     publish_v(0);
     __builtin_amdgcn_s_waitcnt(0x0F70);
-    if (own0 < kPage) zero_v_tail(Par0(), own0);
+    if (own0 < kPage) zero_v_tail(0, own0);
     __syncthreads();
     lims_after_barrier(0, lim_cur);
     float ks0[kTp];
     read_scales(0, 0, ks0);
-    if (wave_active && kv_begin <= pmax) qk(kbuf(Par0()), SA, ks0);
+    if (wave_active && kv_begin <= pmax) qk(kbuf(0), SA, ks0);
     __syncthreads();                           // K buffer 0 is restaged by the first iteration
     for (int j = 0; j < n_tiles; j += 2) {
-      iteration(Par0(), j, SA, SB);
-      if (j + 1 < n_tiles) iteration(Par1(), j + 1, SB, SA);
+      iteration(j, SA, SB);
+      if (j + 1 < n_tiles) iteration(j + 1, SB, SA);
     }
   }
 
@@ -1450,16 +1425,15 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
 // Prefill item: the whole workgroup.  Split partials (up to 128 columns x D floats per item) are
 // merged in-kernel by the last-arriving split when inline_combine is set (fused mode; partials
 // written through with 16-byte device-coherent stores), else by the combine kernel.
-template <typename T, int D, int kBuf>
-__device__ void run_prefill_item(const KernelParams& P, int item, const LdsBufs& L) {
+template <typename T, int D>
+__device__ void run_prefill_item(const KernelParams& P, int item, char* lds) {
   CPTR(int32_t) e = (CPTR(int32_t))P.pitems + kPItemHeader + 2 * (size_t)item;
   CPTR(int32_t) dsc = (CPTR(int32_t))P.pdesc + (size_t)e[0] * kDescInts;
   const int split = e[1] >> 16, head = e[1] & 0xFFFF;
-  if constexpr (sizeof(T) == 2 || kIsFp8<T>) prefill_item_tile<T, D>(P, dsc, head, split, L);
-  else prefill_item<T, D>(P, dsc, head, split, L);
+  if constexpr (sizeof(T) == 2 || kIsFp8<T>) prefill_item_tile<T, D>(P, dsc, head, split, lds);
+  else prefill_item<T, D>(P, dsc, head, split, lds);
   const int ns = dsc[kDNSplit];
-  // in-kernel merging is a fused-kernel feature (its buffers hold the combine tables)
-  if constexpr (kBuf >= kCombineLdsPerWave) if (ns > 1 && P.inline_combine) {
+  if (ns > 1 && P.inline_combine) {
     // Each wave's partial stores (write-through) complete before the barrier; thread 0 takes the
     // group's ticket; the workgroup holding the last split merges the group, each wave a block
     // of 16 columns at a time.  No workgroup waits for another.
@@ -1469,7 +1443,7 @@ __device__ void run_prefill_item(const KernelParams& P, int item, const LdsBufs&
     if (threadIdx.x == 0) s_last = atomicAdd(P.tickets + dsc[kDGroupBegin] + head, 1) == ns - 1;
     __syncthreads();
     if (s_last) {
-      float* sw = L.template combine_table<kBuf>(wave_index());
+      float* sw = (float*)(lds + wave_index() * kCombineLdsPerWave);
       for (int c0 = 16 * wave_index(); c0 < dsc[kDNcols]; c0 += 16 * kWaves) combine_block_wave<T, D>(P, dsc, head, c0, sw);
     }
   }
@@ -1560,10 +1534,7 @@ __device__ __forceinline__ int claim_prefill(const KernelParams& P, int xcc) {
 // ends when both are drained.
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 2) void pod_fused_kernel(KernelParams P) {
-  constexpr int kBuf = Geo<T, D>::kFusedBuf;
-  __shared__ __attribute__((aligned(16))) char lds_k0[kBuf], lds_k1[kBuf], lds_v0[kBuf], lds_v1[kBuf];
-  LdsBufs L;
-  L.k[0] = lds_k0, L.k[1] = lds_k1, L.v[0] = lds_v0, L.v[1] = lds_v1;
+  __shared__ __attribute__((aligned(16))) char lds[Geo<T, D>::kFusedLds];
   __shared__ int s_role, s_item;
   const int tid = threadIdx.x;
   const int cu = cu_slot();
@@ -1605,7 +1576,7 @@ __global__ __launch_bounds__(kThreads, 2) void pod_fused_kernel(KernelParams P) 
     if (role == 1) {
       // The workgroup claims 4 consecutive items (adjacent KV heads of one key range) and each
       // wave streams one of them; the next block is claimed once the current one is done.
-      float* sw = L.template combine_table<kBuf>(wave_index());
+      float* sw = (float*)(lds + wave_index() * kCombineLdsPerWave);
       for (;;) {
         if (tid == 0) s_item = atomicAdd(P.ctrl + kCQueueDecode, kWaves);
         __syncthreads();
@@ -1626,7 +1597,7 @@ __global__ __launch_bounds__(kThreads, 2) void pod_fused_kernel(KernelParams P) 
     while (item < P.n_pf_items) {
       if (tid == 0) note_claim(P, 0, item, cu);
       const uint32_t t0 = trace_start(P);
-      run_prefill_item<T, D, kBuf>(P, item, L);   // ends with a barrier
+      run_prefill_item<T, D>(P, item, lds);   // ends with a barrier
       if (tid == 0) trace_item(P, 0, item, t0, cu);
       if (tid == 0) s_item = claim_prefill(P, xcc);   // claim once idle
       __syncthreads();
@@ -1644,10 +1615,7 @@ __global__ __launch_bounds__(kThreads, 2) void pod_fused_kernel(KernelParams P) 
 
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 2) void pod_prefill_kernel(KernelParams P) {
-  constexpr int kBuf = Geo<T, D>::kStageBuf;
-  __shared__ __attribute__((aligned(16))) char lds_k0[kBuf], lds_k1[kBuf], lds_v0[kBuf], lds_v1[kBuf];
-  LdsBufs L;
-  L.k[0] = lds_k0, L.k[1] = lds_k1, L.v[0] = lds_v0, L.v[1] = lds_v1;
+  __shared__ __attribute__((aligned(16))) char lds[Geo<T, D>::kPrefillLds];
   __shared__ int s_item;
   // one item per workgroup (the grid has n_pf_items workgroups), taken from this die's queue
   const int cu = cu_slot();
@@ -1659,7 +1627,7 @@ __global__ __launch_bounds__(kThreads, 2) void pod_prefill_kernel(KernelParams P
   const int item = s_item;
   if (item >= P.n_pf_items) return;
   const uint32_t t0 = trace_start(P);
-  run_prefill_item<T, D, kBuf>(P, item, L);
+  run_prefill_item<T, D>(P, item, lds);
   if (threadIdx.x == 0) trace_item(P, 0, item, t0, cu);
 }
 
