@@ -316,12 +316,19 @@ def test_full_size_workloads_sampled(idx):
     prob = problem(b)
     pairs = sample_pairs(b, n_prefill=6, n_decode=6, seed=idx)
     want = prob.sampled_output(pairs)
+    outs = {}
     for mode in ("fused", "separate"):
         _say(f"cfg{idx} mode={mode}")
         out, h, ws = run_library(b, mode=mode)
         got = np.stack([to_f64(out[r, hh]) for r, hh in pairs])
         check_close(got, want, "bf16", f"cfg{idx}/{mode}")
         assert not torch.isnan(out).any()
-        del out, ws
-    del b, prob
+        outs[mode] = out
+        del ws
+    # Every output element, beyond the sampled rows: the two modes plan different key splits
+    # (fused cuts decode sequences by the share balance, separate by the wave count), so they
+    # agree only within rounding; both sit within the tolerance of the exact result.
+    diff = (outs["fused"].float() - outs["separate"].float()).abs()
+    assert diff.max().item() <= 2e-2 and diff.mean().item() <= 2e-3, (diff.max().item(), diff.mean().item())
+    del outs, diff, b, prob
     torch.cuda.empty_cache()
