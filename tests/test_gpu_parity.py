@@ -66,6 +66,20 @@ def test_small_batches_all_modes(case, mode):
     _full_check(b, mode, f"small{case}")
 
 
+def test_prefill_heavy_batch_with_long_decode_splits():
+    """A batch whose prefill share outweighs its decode share: fused handles plan longer decode
+    splits (about one item per workgroup slot) than separate ones; both match the oracle on
+    every output element."""
+    spec = gen.custom_spec("bf16", Hq=8, Hkv=2, D=128, prefill=[(1024, 8192)],
+                           decode=[20000, 15000, 9000, 30000, 12000, 25000, 4000, 33000], seed=31)
+    b = gen.make_batch(spec, "cuda")
+    splits = {}
+    for mode in ("fused", "separate"):
+        _, h, _, _ = _full_check(b, mode, "prefill-heavy")
+        splits[mode] = h.stats()["decode_split_tokens"]
+    assert splits["fused"] > splits["separate"], splits
+
+
 @pytest.mark.parametrize("mode", MODES)
 def test_forced_splits_use_the_combine(mode):
     """Short split lengths force multi-split prefill tiles and decode sequences, so the
