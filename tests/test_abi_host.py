@@ -137,6 +137,32 @@ def test_decode_split_length_follows_the_share_balance(idx):
         assert st["num_decode_items"] >= 4 * slots
 
 
+@pytest.mark.parametrize("idx,tapered", [(2, False), (3, True), (5, False)])
+def test_decode_tail_taper(idx, tapered):
+    """Decode items are claimed in queue order (longest sequences first).  When sequence lengths
+    vary, the pieces claimed last take a quarter of the split length, about two short items per
+    wave of the grid; batches of equal sequences keep one split length.  Either way every key of
+    every decode piece is covered once."""
+    spec = gen.config_spec(idx)
+    cfg = B.make_config(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.dtype, "fused")
+    items, st = B.plan_inspect(cfg, _meta(spec), 256, 2)
+    _check_coverage(spec, items, spec.num_q_heads // spec.num_kv_heads)
+    dec = items[items[:, 10] == 1]
+    lengths = dec[:, 6] - dec[:, 5]
+    target = st["decode_split_tokens"]
+    short = dec[(lengths <= target // 4) & (dec[:, 2] == 1)]
+    if not tapered:
+        assert np.all(lengths <= target) and len(short) == 0
+        return
+    tail = max(512, target // 4)
+    # the short items form the end of the queue, and they hold about two per wave of the grid
+    first_short = int(np.flatnonzero((lengths <= tail))[0])
+    assert np.all(lengths[first_short:] <= tail)
+    assert np.all(lengths[:first_short] > tail)
+    waves = 256 * 2 * 4
+    assert 1.5 * waves <= len(dec) - first_short <= 3 * waves
+
+
 @pytest.mark.parametrize("G", [1, 3, 4, 8, 16])
 def test_small_chunks_take_the_decode_path(G):
     """Chunks whose rows x G fit one 16-column block (at most 16 rows, the default) become one
