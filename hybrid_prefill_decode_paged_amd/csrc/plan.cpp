@@ -31,6 +31,7 @@ namespace {
 constexpr double kPrefillFlopsPerSec = 0.85e15;
 constexpr double kDecodeBytesPerSec = 6.5e12;
 constexpr double kPrefillHeavyRatio = 0.75;   // prefill share >= 3/4 of the decode share
+constexpr int kOneRoundMaxSplit = 8192;       // longest decode split of the prefill-heavy fused plan
 int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 int round_up_int(int a, int m) { return ceil_div(a, m) * m; }
 }  // namespace
@@ -267,6 +268,15 @@ pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus
       one_round = true;
     }
     long st = (total_tok + target_items - 1) / std::max(1L, target_items);
+    // Items are sized by what they stream: an FP8 token is half a bf16 token's bytes, so it
+    // takes twice the tokens for an item to last as long and to amortise the same fixed costs
+    // (q load, partial store, merge).  Measured on the Llama-2-7B-shaped FP8 batch: 2048-token
+    // items 496 us, 4096-token items 418 us; the bf16 batch is flat between the two.
+    if (!one_round) st = st * 2 / c.elem_bytes();
+    // The one-item-per-slot plan stops at 8192 tokens: longer items outlast the prefill share
+    // (FP8 cache, Llama-3-8B-shaped batch: 32768-token items 1503 us, 16384: 1347, 8192: 1302,
+    // 4096: 1320; the Yi-6B-shaped bf16 batch is best at 8192 too).
+    if (one_round) st = std::min(st, (long)kOneRoundMaxSplit);
     st = std::max(512L, std::min(32768L, st));
     st_target = round_up_int((int)st, 128);
   }

@@ -137,6 +137,26 @@ def test_decode_split_length_follows_the_share_balance(idx):
         assert st["num_decode_items"] >= 4 * slots
 
 
+def test_decode_items_sized_by_bytes():
+    """Decode items are sized by the bytes they stream: the FP8 cache's items hold twice the
+    tokens of the bf16 cache's on the same batch, and the prefill-heavy fused plan (here the
+    FP8 Llama-3-8B-shaped batch, whose halved decode bytes make it prefill-heavy) stops at
+    8192-token splits."""
+    for idx in (2, 5):
+        bf, f8 = gen.config_spec(idx), gen.fp8_spec(idx)
+        st = {}
+        for spec in (bf, f8):
+            cfg = B.make_config(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.dtype, "separate")
+            _, s_ = B.plan_inspect(cfg, _meta(spec), 256, 2)
+            st[spec.dtype] = s_["decode_split_tokens"]
+        assert st["fp8"] == min(32768, 2 * st["bf16"]), (idx, st)
+    spec = gen.fp8_spec(3)
+    cfg = B.make_config(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.dtype, "fused")
+    items, s_ = B.plan_inspect(cfg, _meta(spec), 256, 2)
+    assert s_["decode_split_tokens"] == 8192
+    _check_coverage(spec, items, spec.num_q_heads // spec.num_kv_heads)
+
+
 @pytest.mark.parametrize("idx,tapered", [(2, False), (3, True), (5, False)])
 def test_decode_tail_taper(idx, tapered):
     """Decode items are claimed in queue order (longest sequences first).  When sequence lengths
