@@ -251,11 +251,12 @@ pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus
   if (c.decode_split_tokens > 0) {
     st_target = c.decode_split_tokens;
   } else {
-    // About two items per decode wave: fewer, longer items cost fewer partials, tickets and
-    // combine work, while two per wave still lets the waves that start late (their workgroups
-    // begin on prefill tiles) finish with the rest (measured on the four bf16 workloads: one
-    // per wave left a tail, four per wave lost 1-5%).
-    long target_items = (long)num_cus * wgs_per_cu * kWaves * 2;
+    // About one item per decode wave of the grid: fewer, longer items cost fewer partials,
+    // tickets and combine work, and the tapered tail below keeps the end of the queue short.
+    // Measured, fused kernel us, one / two / three items per wave: Llama-2-7B-shaped 679 / 690 /
+    // 705, Llama-3-8B-shaped 1617 / 1616 / 1615, long-context 5040 / 5060 / 5094, speculative
+    // verification 1696 / 1701; separate mode on the first 740 / 757.
+    long target_items = (long)num_cus * wgs_per_cu * kWaves * std::max(1, c.decode_items_per_wave);
     // Fused handles, when the prefill share is about as long as the decode share: about one
     // item per workgroup slot instead.  The decode-role workgroups that find the queue empty
     // take prefill tiles, so the matrix work gets the CUs the stream does not need (measured on

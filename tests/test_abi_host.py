@@ -116,7 +116,7 @@ def test_plan_ragged_batches(G, D, split, cap):
 def test_decode_split_length_follows_the_share_balance(idx):
     """Fused plans of a batch whose prefill share is about as long as its decode share (the
     Yi-6B-shaped one) cut decode sequences into about one item per workgroup slot; decode-heavy
-    batches, and every separate-mode plan, keep about two items per decode wave."""
+    batches, and every separate-mode plan, plan about one item per decode wave."""
     spec = gen.config_spec(idx)
     meta = _meta(spec)
     slots = 256 * 2
@@ -124,7 +124,7 @@ def test_decode_split_length_follows_the_share_balance(idx):
     for mode in ("fused", "separate"):
         cfg = B.make_config(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.dtype, mode)
         _, st = B.plan_inspect(cfg, meta, 256, 2)
-        per_wave = -(-tok // (slots * 4 * 2))
+        per_wave = -(-tok // (slots * 4))
         expect = -(-min(32768, max(512, per_wave)) // 128) * 128
         if mode == "fused" and idx == 4:
             expect = -(-min(32768, max(512, -(-tok // slots))) // 128) * 128
