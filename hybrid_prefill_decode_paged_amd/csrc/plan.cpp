@@ -256,7 +256,12 @@ pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus
     // Measured, fused kernel us, one / two / three items per wave: Llama-2-7B-shaped 679 / 690 /
     // 705, Llama-3-8B-shaped 1617 / 1616 / 1615, long-context 5040 / 5060 / 5094, speculative
     // verification 1696 / 1701; separate mode on the first 740 / 757.
-    long target_items = (long)num_cus * wgs_per_cu * kWaves * std::max(1, c.decode_items_per_wave);
+    // Streams handles keep two per wave: their decode kernel shares the GPU with a concurrent
+    // prefill kernel, and one long item per wave left a tail there (long-context batch 5549 ->
+    // 6120 us, Llama-2-7B-shaped 730 -> 756 us).
+    const int per_wave = c.decode_items_per_wave > 0 ? c.decode_items_per_wave
+                                                     : (c.mode == POD_ATTN_MODE_STREAMS ? 2 : 1);
+    long target_items = (long)num_cus * wgs_per_cu * kWaves * per_wave;
     // Fused handles, when the prefill share is about as long as the decode share: about one
     // item per workgroup slot instead.  The decode-role workgroups that find the queue empty
     // take prefill tiles, so the matrix work gets the CUs the stream does not need (measured on

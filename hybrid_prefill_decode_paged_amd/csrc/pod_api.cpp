@@ -111,7 +111,7 @@ pod_attn_status pod_attn_create(const pod_attn_config* cfg, pod_attn_handle** ou
   if (c.prefill_split_cap == 0) h->cfg.prefill_split_cap = std::max(0, env_int("POD_ATTN_PREFILL_SPLIT_CAP", 0));
   h->cfg.append_token_heads = std::max(1, env_int("POD_ATTN_APPEND_TOKEN_HEADS", kAppendTokenHeads));
   h->cfg.decode_taper = env_int("POD_ATTN_DECODE_TAPER", h->cfg.decode_taper);
-  h->cfg.decode_items_per_wave = std::max(1, env_int("POD_ATTN_DECODE_ITEMS_PER_WAVE", h->cfg.decode_items_per_wave));
+  h->cfg.decode_items_per_wave = std::max(0, env_int("POD_ATTN_DECODE_ITEMS_PER_WAVE", h->cfg.decode_items_per_wave));
   h->prefill_wgs_override = env_int("POD_ATTN_PREFILL_WGS", 0);
   h->prefill_per_cu_override = env_int("POD_ATTN_PREFILL_PER_CU", 0);
   h->prefill_cus_override = env_int("POD_ATTN_PREFILL_CUS", 0);
