@@ -223,7 +223,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", type=int, default=2, help="1..5; 2 is the measured workload")
     ap.add_argument("--mode", default="fused", choices=["fused", "separate", "streams"])
     ap.add_argument("--no-compare", action="store_true", help="skip timing the other two modes")
