@@ -1,18 +1,24 @@
 """Benchmark: hybrid-batch attention microseconds per iteration on one MI355X, and the achieved
 fraction of the max(MFMA, HBM) roofline.
 
-    python bench.py [--steps K] [--warmup W] [--workload N] [--mode fused]
+    python bench.py [--steps K] [--warmup W] [--workload N] [--mode fused] [--legs 2,3,4]
 
-One step = one pod_attn_run over the whole hybrid batch (prefill tiles + decode split-KV +
-combine), inputs resident in HBM.  Prints ONE JSON line.  Beside it, "kv_append" times the
-same step preceded by the KV append of every row's new K/V (pod_attn_run_append) in the fused
-and separate modes, "small_q_extend" times a speculative-verification step (4-token
-extends) with the extends on the decode path and on the prefill-tile path, and "fp8_kv" the
-same workload with an FP8 E4M3 cache (per-(page, KV head) scales), fused and separate.  The default workload is the
-Llama-2-7B-shaped layer (32 query / 32 KV heads, head_dim 128, bf16, 16-token pages): one
-1024-token prefill chunk at offset 3072 plus 64 decodes at context 4096, over a randomly
-permuted 40960-page pool.  The other workloads are parity-test cases; --workload selects them
-for manual runs.
+One step = one pod_attn_run over the whole hybrid batch (host planning, plan upload, prefill
+tiles + decode split-KV + combine), inputs resident in HBM.  Prints ONE JSON line.
+
+The measured workload (``value``, ``roofline``) is the largest single-GPU one: Llama-3-8B heads
+(32 query / 8 KV heads, head_dim 128, bf16, 16-token pages), one 512-token prefill chunk at
+offset 32256 plus 256 decodes at context 32768, over a randomly permuted 2^20-page (64 GiB) pool.
+``value`` is the median per-step wall time of exactly K timed steps after a warm-up of W steps
+and at least 0.2 s of GPU work.  Beside it:
+  * modes: the same workload in the separate and two-stream modes;
+  * legs: the Llama-2-7B-, Llama-3-8B- and Yi-6B-shaped workloads, each in every mode, with at
+    least 0.1 s of timed steps per mode and the roofline fraction of the median kernel time;
+  * kv_append: the step preceded by the KV append of every row's new K/V (pod_attn_run_append);
+  * small_q_extend: a speculative-verification step (4-token extends) with the extends on the
+    decode path and on the prefill-tile path;
+  * fp8_kv: the measured and the Llama-2-7B-shaped workloads with an FP8 E4M3 cache;
+  * cpu_baseline: the fp64 oracle on a bounded sample of the measured workload, scaled.
 """
 from __future__ import annotations
 
@@ -20,6 +26,7 @@ import argparse
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -72,11 +79,19 @@ def workload_desc(spec):
             "dtype": spec.dtype}
 
 
-def time_mode(torch, h, b, meta, out, ws, steps, warmup, new=None, scaled=False):
-    """Wall time of `steps` runs (events on the launch stream around the loop) and the mean
-    duration of the kernels of one run (one-shot events armed before each run).  With
-    new = (k_new, v_new) every run first appends those tokens (pod_attn_run_append); scaled runs
-    an FP8 cache with its scales (pod_attn_run_scaled)."""
+WARM_FLOOR_S = 0.2           # untimed GPU work before any timed mode, whatever --warmup says
+MIN_TIMED_S = 0.1            # the comparison legs time at least this much GPU work per mode
+
+
+def time_mode(torch, h, b, meta, out, ws, steps, warmup, new=None, scaled=False, min_timed_s=0.0):
+    """Time one handle on one batch.  Untimed warm-up: ``warmup`` runs, then more until at least
+    WARM_FLOOR_S of GPU time has run (the first mode timed in a process otherwise meets a GPU
+    still coming up from host-side input generation).  Timed: ``steps`` runs (more when
+    ``min_timed_s`` asks for a longer window), each bracketed by wall events on the launch stream
+    and by the library's one-shot kernel events (pod_attn_set_kernel_events).  Returns the
+    per-step wall and kernel times (ms) and the warm-up count.  With new = (k_new, v_new) every
+    run first appends those tokens (pod_attn_run_append); scaled runs an FP8 cache with its scales
+    (pod_attn_run_scaled)."""
     stream = torch.cuda.current_stream()
 
     def one():
@@ -87,24 +102,57 @@ def time_mode(torch, h, b, meta, out, ws, steps, warmup, new=None, scaled=False)
         else:
             h.run_append(b.q, new[0], new[1], b.k_pool, b.v_pool, b.block_tables, meta, out, ws)
 
-    for _ in range(warmup):
-        one()
-    torch.cuda.synchronize()
+    def batch_ms(n):
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            one()
+        z.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(z)
+
+    warm, warm_ms = max(1, warmup), 0.0
+    warm_ms += batch_ms(warm)
+    while warm_ms < WARM_FLOOR_S * 1e3:
+        per = warm_ms / warm
+        n = max(1, math.ceil((WARM_FLOOR_S * 1e3 - warm_ms) / per))
+        warm_ms += batch_ms(n)
+        warm += n
+    per = warm_ms / warm
+    if min_timed_s > 0:
+        steps = max(steps, math.ceil(min_timed_s * 1e3 / per))
+    walls = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     ks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for a, z in ks:             # torch creates the HIP events on first record; the library re-records them
         a.record(stream)
         z.record(stream)
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for e in walls:
+        e.record(stream)
     torch.cuda.synchronize()
-    t0.record(stream)
+    walls[0].record(stream)
     for i in range(steps):
         h.set_kernel_events(*ks[i])
         one()
-    t1.record(stream)
+        walls[i + 1].record(stream)
     torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
+    wall = [walls[i].elapsed_time(walls[i + 1]) for i in range(steps)]
     kern = [a.elapsed_time(z) for a, z in ks]
-    return total_ms / steps, sum(kern) / len(kern), min(kern)
+    return {"steps": steps, "warmup_runs": warm, "total_ms": walls[0].elapsed_time(walls[-1]),
+            "wall_ms": wall, "kernel_ms": kern}
+
+
+def summarize(t, t_roof_s=None):
+    """Median / mean / min per-step wall and kernel microseconds of a time_mode result, and the
+    roofline fraction of the median kernel time when a bound is given."""
+    r = {"us_per_iter": round(statistics.median(t["wall_ms"]) * 1e3, 2),
+         "us_per_iter_mean": round(t["total_ms"] / t["steps"] * 1e3, 2),
+         "kernel_us": round(statistics.median(t["kernel_ms"]) * 1e3, 2),
+         "kernel_us_mean": round(statistics.mean(t["kernel_ms"]) * 1e3, 2),
+         "kernel_us_min": round(min(t["kernel_ms"]) * 1e3, 2),
+         "steps": t["steps"], "timed_ms": round(t["total_ms"], 1)}
+    if t_roof_s is not None:
+        r["frac"] = round(t_roof_s / (statistics.median(t["kernel_ms"]) / 1e3), 4)
+    return r
 
 
 def measured_peaks(torch, B):
@@ -219,18 +267,52 @@ def cpu_baseline(b, budget_s=12.0):
                        f"scaled by visible (head,key) pairs to the full batch")}
 
 
+def roofline_of(spec):
+    """Algorithmic work of a workload and its max(MFMA, HBM) bound (seconds, bound name)."""
+    work = algorithmic_work(spec)
+    peak_mfma = PEAK_MFMA["fp32" if spec.dtype == "fp32" else "bf16"]
+    t_math, t_mem = work["flops"] / peak_mfma, work["bytes"] / PEAK_HBM
+    return work, max(t_math, t_mem), ("hbm" if t_mem >= t_math else "mfma"), peak_mfma
+
+
+def run_modes(torch, binding, gen, spec, b, modes, steps, warmup, min_timed_s, t_roof_s, say):
+    """Time every mode of ``modes`` on one resident batch; returns ({mode: summary}, {mode: stats},
+    {mode: raw time_mode result})."""
+    meta = binding.BatchMeta.from_batch(b)
+    res, stats, raw = {}, {}, {}
+    for mode in modes:
+        h = binding.PodAttention(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.dtype, mode,
+                                 scale=spec.softmax_scale)
+        ws = torch.empty(h.workspace_size(meta), dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(b.q)
+        say(f"timing {spec.name} mode={mode}")
+        t = time_mode(torch, h, b, meta, out, ws, steps, warmup, scaled=spec.dtype == "fp8",
+                      min_timed_s=min_timed_s)
+        res[mode] = summarize(t, t_roof_s)
+        res[mode]["warmup_runs"] = t["warmup_runs"]
+        stats[mode] = h.stats()
+        raw[mode] = t
+        del ws, out
+        h.close()
+    return res, stats, raw
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", type=int, default=2, help="1..5; 2 is the measured workload")
+    ap.add_argument("--workload", type=int, default=5,
+                    help="1..5; 5 (Llama-3-8B heads, 512-token chunk + 256 decodes at 32K) is the measured workload")
     ap.add_argument("--mode", default="fused", choices=["fused", "separate", "streams"])
-    ap.add_argument("--no-compare", action="store_true", help="skip timing the other two modes")
+    ap.add_argument("--legs", default="2,3,4",
+                    help="other workloads timed in every mode beside the headline ('' for none)")
+    ap.add_argument("--no-compare", action="store_true", help="skip timing the other two modes of the headline workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-append", action="store_true", help="skip timing the KV-append variant")
     ap.add_argument("--no-extend", action="store_true", help="skip timing the small-q extend workload")
     ap.add_argument("--no-fp8", action="store_true", help="skip timing the FP8-cache variant")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the HBM / MFMA probes")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (counter calibration)")
@@ -254,55 +336,69 @@ def main():
     from hybrid_prefill_decode_paged_amd import binding
     from hybrid_prefill_decode_paged_amd import inputs as gen
 
+    def say(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
     binding.load()
     torch.cuda.set_device(0)
     spec = gen.config_spec(args.workload)
-    print(f"[bench] generating {spec.name}: {spec.num_pages} pages", file=sys.stderr, flush=True)
+    say(f"generating {spec.name}: {spec.num_pages} pages")
     b = gen.make_batch(spec, "cuda")
     torch.cuda.synchronize()
-    meta = binding.BatchMeta.from_batch(b)
-    work = algorithmic_work(spec)
-    peak_mfma = PEAK_MFMA[spec.dtype]
-    t_roof_s = max(work["flops"] / peak_mfma, work["bytes"] / PEAK_HBM)
-    bound = "hbm" if work["bytes"] / PEAK_HBM >= work["flops"] / peak_mfma else "mfma"
+    work, t_roof_s, bound, peak_mfma = roofline_of(spec)
 
-    results = {}
-    stats = {}
+    # ---- the headline: the asked mode on the measured workload, exactly --steps timed runs
     modes = [args.mode] + ([] if args.no_compare else [m for m in ("fused", "separate", "streams") if m != args.mode])
-    for mode in modes:
-        h = binding.PodAttention(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.dtype, mode,
-                                 scale=spec.softmax_scale)
-        ws = torch.empty(h.workspace_size(meta), dtype=torch.uint8, device="cuda")
-        out = torch.empty_like(b.q)
-        steps = args.steps if mode == args.mode else max(5, args.steps // 2)
-        print(f"[bench] timing mode={mode} steps={steps}", file=sys.stderr, flush=True)
-        ms, kern_ms, kern_min = time_mode(torch, h, b, meta, out, ws, steps, args.warmup)
-        results[mode] = {"us_per_iter": round(ms * 1e3, 2), "kernel_us_mean": round(kern_ms * 1e3, 2),
-                         "kernel_us_min": round(kern_min * 1e3, 2)}
-        stats[mode] = h.stats()
-        del ws, out
-        h.close()
+    results, stats, raw = {}, {}, {}
+    for i, mode in enumerate(modes):
+        r, st, rw = run_modes(torch, binding, gen, spec, b, [mode], args.steps, args.warmup,
+                              0.0 if i == 0 else MIN_TIMED_S, t_roof_s, say)
+        results.update(r)
+        stats.update(st)
+        raw.update(rw)
+    head = raw[args.mode]
+
+    # ---- the other workloads, each in every mode, >= MIN_TIMED_S of timed steps per mode
+    legs = {}
+    for idx in [int(x) for x in args.legs.split(",") if x.strip()]:
+        if idx == args.workload:
+            continue
+        ls = gen.config_spec(idx)
+        say(f"generating {ls.name}: {ls.num_pages} pages")
+        lb = gen.make_batch(ls, "cuda")
+        lw, lroof, lbound, _ = roofline_of(ls)
+        r, _, _ = run_modes(torch, binding, gen, ls, lb, ["fused", "separate", "streams"], args.steps,
+                            args.warmup, MIN_TIMED_S, lroof, say)
+        legs[ls.name] = {"workload": workload_desc(ls)["workload"], "t_roof_us": round(lroof * 1e6, 2),
+                         "bound": lbound, "algorithmic_bytes": lw["bytes"], "algorithmic_flops": lw["flops"],
+                         "modes": r,
+                         "fused_vs_separate": round(r["separate"]["us_per_iter"] / r["fused"]["us_per_iter"], 4)}
+        del lb
+        torch.cuda.empty_cache()
 
     append = None
     if not args.no_append:
         # The same step preceded by the KV append of every query row's new K/V (the tokens
         # drawn once; rewriting them each step moves the same bytes).
         k_new, v_new = gen.new_tokens(spec, spec.seed + 7, "cuda")
+        meta = binding.BatchMeta.from_batch(b)
         append = {"append_bytes": 2 * 2 * spec.total_q * spec.num_kv_heads * spec.head_dim * spec.elem_bytes}
         for mode in ("fused", "separate"):
             h = binding.PodAttention(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.dtype, mode,
                                      scale=spec.softmax_scale)
             ws = torch.empty(h.workspace_size(meta), dtype=torch.uint8, device="cuda")
             out = torch.empty_like(b.q)
-            steps = max(5, args.steps // 2)
-            print(f"[bench] timing mode={mode} with KV append steps={steps}", file=sys.stderr, flush=True)
-            ms, kern_ms, _ = time_mode(torch, h, b, meta, out, ws, steps, args.warmup, new=(k_new, v_new))
-            append[mode] = {"us_per_iter": round(ms * 1e3, 2), "kernel_us_mean": round(kern_ms * 1e3, 2),
-                            "extra_us_vs_no_append": round(ms * 1e3 - results[mode]["us_per_iter"], 2)
-                            if mode in results else None,
-                            "units": h.stats()["num_append_units"]}
+            say(f"timing mode={mode} with KV append")
+            t = time_mode(torch, h, b, meta, out, ws, args.steps, args.warmup, new=(k_new, v_new),
+                          min_timed_s=MIN_TIMED_S)
+            r = summarize(t, t_roof_s)
+            if mode in results:
+                r["extra_us_vs_no_append"] = round(r["us_per_iter"] - results[mode]["us_per_iter"], 2)
+            r["units"] = h.stats()["num_append_units"]
+            append[mode] = r
             del ws, out
             h.close()
+        del k_new, v_new
 
     extend = None
     if not args.no_extend:
@@ -310,55 +406,45 @@ def main():
         # (128 sequences extending by 4 tokens each, plus its 2048-token chunk), fused mode,
         # with the extends on the decode path (default) and on the prefill-tile path.
         xs = gen.spec_verify_spec(4)
-        print(f"[bench] generating {xs.name}: {xs.num_pages} pages", file=sys.stderr, flush=True)
+        say(f"generating {xs.name}: {xs.num_pages} pages")
         xb = gen.make_batch(xs, "cuda")
         xmeta = binding.BatchMeta.from_batch(xb)
-        xw = algorithmic_work(xs)
-        x_roof = max(xw["flops"] / PEAK_MFMA[xs.dtype], xw["bytes"] / PEAK_HBM)
+        _, x_roof, _, _ = roofline_of(xs)
         extend = {"workload": workload_desc(xs)["workload"], "t_roof_us": round(x_roof * 1e6, 2)}
         for name, emax in (("decode_path", 0), ("tile_path", -1)):
             h = binding.PodAttention(xs.num_q_heads, xs.num_kv_heads, xs.head_dim, xs.dtype, "fused",
                                      scale=xs.softmax_scale, extend_max_q=emax)
             ws = torch.empty(h.workspace_size(xmeta), dtype=torch.uint8, device="cuda")
             out = torch.empty_like(xb.q)
-            steps = max(5, args.steps // 2)
-            print(f"[bench] timing small-q extends on the {name} steps={steps}", file=sys.stderr, flush=True)
-            ms, kern_ms, _ = time_mode(torch, h, xb, xmeta, out, ws, steps, args.warmup)
-            extend[name] = {"us_per_iter": round(ms * 1e3, 2), "kernel_us_mean": round(kern_ms * 1e3, 2),
-                            "frac": round(x_roof / (kern_ms / 1e3), 4),
-                            "small_extends": h.stats()["num_small_extends"]}
+            say(f"timing small-q extends on the {name}")
+            t = time_mode(torch, h, xb, xmeta, out, ws, args.steps, args.warmup, min_timed_s=MIN_TIMED_S)
+            extend[name] = summarize(t, x_roof)
+            extend[name]["small_extends"] = h.stats()["num_small_extends"]
             del ws, out
             h.close()
         del xb
+        torch.cuda.empty_cache()
 
     fp8 = None
     if not args.no_fp8 and spec.dtype == "bf16":
-        # The same workload with its cache in FP8 E4M3 (per-(page, KV head) scales, bf16 q/out),
-        # fused and separate: half the K/V bytes of the decode stream.
-        fs = gen.fp8_spec(args.workload)
-        print(f"[bench] generating {fs.name}: {fs.num_pages} pages", file=sys.stderr, flush=True)
-        fb = gen.make_batch(fs, "cuda")
-        fmeta = binding.BatchMeta.from_batch(fb)
-        fw = algorithmic_work(fs)
-        f_roof = max(fw["flops"] / PEAK_MFMA["bf16"], fw["bytes"] / PEAK_HBM)
-        fp8 = {"workload": workload_desc(fs)["workload"], "algorithmic_bytes": fw["bytes"],
-               "t_roof_us": round(f_roof * 1e6, 2)}
-        for mode in ("fused", "separate"):
-            h = binding.PodAttention(fs.num_q_heads, fs.num_kv_heads, fs.head_dim, "fp8", mode,
-                                     scale=fs.softmax_scale)
-            ws = torch.empty(h.workspace_size(fmeta), dtype=torch.uint8, device="cuda")
-            out = torch.empty_like(fb.q)
-            steps = max(5, args.steps // 2)
-            print(f"[bench] timing the FP8 cache, mode={mode} steps={steps}", file=sys.stderr, flush=True)
-            ms, kern_ms, _ = time_mode(torch, h, fb, fmeta, out, ws, steps, args.warmup, scaled=True)
-            fp8[mode] = {"us_per_iter": round(ms * 1e3, 2), "kernel_us_mean": round(kern_ms * 1e3, 2),
-                         "frac": round(f_roof / (kern_ms / 1e3), 4)}
-            del ws, out
-            h.close()
-        del fb
+        # Workloads with their cache in FP8 E4M3 (per-(page, KV head) scales, bf16 q/out), fused
+        # and separate: half the K/V bytes of the decode stream.  The measured workload and the
+        # Llama-2-7B-shaped one.
+        fp8 = {}
+        for idx in sorted({args.workload, 2}):
+            fs = gen.fp8_spec(idx)
+            say(f"generating {fs.name}: {fs.num_pages} pages")
+            fb = gen.make_batch(fs, "cuda")
+            fw, f_roof, _, _ = roofline_of(fs)
+            r, _, _ = run_modes(torch, binding, gen, fs, fb, ["fused", "separate"], args.steps, args.warmup,
+                                MIN_TIMED_S, f_roof, say)
+            fp8[fs.name] = {"workload": workload_desc(fs)["workload"], "algorithmic_bytes": fw["bytes"],
+                            "t_roof_us": round(f_roof * 1e6, 2), "modes": r}
+            del fb
+            torch.cuda.empty_cache()
 
-    main_ms = results[args.mode]["us_per_iter"] / 1e3
-    kern_s = results[args.mode]["kernel_us_mean"] / 1e6
+    # ---- roofline of the dominant kernel: algorithmic work / its median launch duration
+    kern_s = statistics.median(head["kernel_ms"]) / 1e3
     if bound == "hbm":
         achieved, peak, unit = work["bytes"] / kern_s / 1e9, PEAK_HBM / 1e9, "GB/s"
     else:
@@ -366,44 +452,48 @@ def main():
     st = stats[args.mode]
     kernel_name = "pod_fused_kernel" if args.mode == "fused" else f"{args.mode} kernels"
     traffic = measured_traffic(kernel_name, spec.name)
-    print("[bench] measuring this GPU's HBM read and MFMA peaks", file=sys.stderr, flush=True)
-    peaks = measured_peaks(torch, binding)
-    m_peak = peaks["hbm_read_gbps"] if bound == "hbm" else (peaks["mfma_bf16_tflops"] if spec.dtype == "bf16" else None)
+    peaks = None
+    if not args.no_peaks:
+        say("measuring this GPU's HBM read and MFMA rates")
+        peaks = measured_peaks(torch, binding)
     line = {
         "metric": METRIC,
-        "value": results[args.mode]["us_per_iter"],
+        "value": round(statistics.median(head["wall_ms"]) * 1e3, 2),
         "unit": "us/iter",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(main_ms, 4),
+        "ms_per_step": round(head["total_ms"] / head["steps"], 4),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": spec.dtype,
         "data": "synthetic (seeded N(0,1)*0.5 values, seeded page permutation)",
         "config": workload_desc(spec),
+        "value_is": "median per-step wall time of the timed steps (events on the launch stream); "
+                    "ms_per_step is their mean",
+        "warmup_runs": head["warmup_runs"],
         "roofline": {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "frac_vs_measured_peak": round(achieved / m_peak, 4) if m_peak else None,
-                     "kernel": kernel_name,
+                     "kernel": kernel_name, "kernel_us_median": round(kern_s * 1e6, 2),
                      "algorithmic_bytes": work["bytes"], "algorithmic_flops": work["flops"],
                      "t_roof_us": round(t_roof_s * 1e6, 2),
-                     "roof_fraction_of_step": round(t_roof_s / main_ms * 1e3, 4)},
-        "measured_peaks": peaks,
+                     "roof_fraction_of_step": round(t_roof_s / (statistics.median(head["wall_ms"]) / 1e3), 4)},
         "modes": results,
         "fused_vs_separate": (round(results["separate"]["us_per_iter"] / results["fused"]["us_per_iter"], 4)
                               if "separate" in results and "fused" in results else None),
+        "legs": legs,
         "kv_append": append,
         "small_q_extend": extend,
         "fp8_kv": fp8,
+        "measured_rates": peaks,
         "plan": {k: st[k] for k in ("num_prefill_items", "num_decode_items", "num_combine_groups",
                                     "decode_split_tokens", "prefill_max_splits", "grid_wgs", "wgs_per_cu",
                                     "num_cus", "vgprs_per_lane", "lds_bytes_per_wg", "mode_used", "prefill_wg_budget",
                                     "fallback_reason", "host_plan_us")},
     }
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        say("timing the CPU oracle on a sample")
         line["cpu_baseline"] = cpu_baseline(b, args.cpu_budget)
     print(json.dumps(line), flush=True)
 

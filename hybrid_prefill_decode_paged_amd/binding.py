@@ -23,6 +23,7 @@ MODES = {"fused": MODE_FUSED, "separate": MODE_SEPARATE, "streams": MODE_STREAMS
 FLAG_DEBUG_CLAIMS = 1
 FLAG_TRACE = 2
 DEVICE_ERR_BAD_PAGE = 1
+FALLBACK = {"none": 0, "no_prefill": 1, "no_decode": 2, "occupancy": 3, "env": 4}
 
 STATUS = {0: "OK", -1: "ERR_INVALID_ARG", -2: "ERR_UNSUPPORTED", -3: "ERR_WORKSPACE",
           -4: "ERR_HIP", -5: "ERR_NO_DEVICE"}
@@ -55,7 +56,25 @@ class Stats(C.Structure):
         "prefill_max_splits", "decode_split_tokens", "decode_max_splits", "grid_wgs", "wgs_per_cu",
         "num_cus", "lds_bytes_per_wg", "vgprs_per_lane")] + [
         ("workspace_bytes", C.c_size_t), ("host_plan_us", C.c_double), ("prefill_wg_budget", C.c_int),
-        ("num_append_units", C.c_int), ("num_small_extends", C.c_int)]
+        ("num_append_units", C.c_int), ("num_small_extends", C.c_int),
+        ("runs", C.c_uint64), ("runs_fused_path", C.c_uint64), ("fallback_runs", C.c_uint64 * 5),
+        ("algorithmic_bytes", C.c_double), ("algorithmic_flops", C.c_double), ("timed_run", C.c_uint64),
+        ("kernel_us", C.c_double), ("achieved_gbps", C.c_double), ("achieved_tflops", C.c_double)]
+
+    def as_dict(self):
+        d = {n: getattr(self, n) for n, _ in self._fields_}
+        d["fallback_runs"] = list(self.fallback_runs)
+        return d
+
+
+class RunDiag(C.Structure):
+    _fields_ = [(n, C.c_int) for n in (
+        "status_word", "planned_prefill_items", "planned_decode_items", "prefill_items", "decode_items",
+        "cus_any", "cus_prefill", "cus_decode", "cus_both", "max_prefill_per_cu", "max_decode_per_cu")] + [
+        (n, C.c_double) for n in ("prefill_decode_ratio", "mean_prefill_share", "min_prefill_share",
+                                  "max_prefill_share")] + [
+        ("run", C.c_uint64), ("timed_run", C.c_uint64)] + [
+        (n, C.c_double) for n in ("kernel_us", "achieved_gbps", "achieved_tflops")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -90,7 +109,8 @@ def load(path: str = LIB_PATH):
     lib.pod_attn_run_append.argtypes = [VP, VP, VP, VP, VP, VP, VP, P(Batch), VP, VP, C.c_size_t, VP]
     lib.pod_attn_run_scaled.argtypes = [VP, VP, VP, VP, VP, VP, VP, P(Batch), VP, VP, C.c_size_t, VP]
     lib.pod_attn_get_stats.argtypes = [VP, P(Stats)]
-    lib.pod_attn_gather_kv.argtypes = [VP, VP, I, VP, I, I, P(Batch), VP, VP]
+    lib.pod_attn_gather_kv.argtypes = [VP, VP, I, VP, I, I, P(Batch), VP, VP, VP]
+    lib.pod_attn_read_run_diagnostics.argtypes = [VP, VP, VP, P(RunDiag)]
     lib.pod_attn_read_device_status.argtypes = [VP, VP, VP, P(C.c_int32), P(C.c_int32), I, P(I),
                                                 P(C.c_int32), P(C.c_int32), I]
     lib.pod_attn_plan_inspect.argtypes = [P(Config), P(Batch), I, I, P(C.c_int32), I, P(I), P(Stats)]
@@ -106,7 +126,7 @@ def load(path: str = LIB_PATH):
                  "pod_attn_run_scaled", "pod_attn_get_stats",
                  "pod_attn_gather_kv", "pod_attn_read_device_status", "pod_attn_plan_inspect", "pod_attn_read_trace",
                  "pod_attn_set_kernel_events", "pod_attn_batch_signals", "pod_attn_probe_hbm_read",
-                 "pod_attn_probe_mfma"):
+                 "pod_attn_probe_mfma", "pod_attn_read_run_diagnostics"):
         getattr(lib, name).restype = C.c_int
     _lib = lib
     return lib
@@ -310,10 +330,20 @@ class PodAttention:
         _check(self.lib.pod_attn_get_stats(self.h, C.byref(st)))
         return st.as_dict()
 
-    def gather_kv(self, cache, which: int, block_tables, seq: int, ctx: int, meta: BatchMeta, out, stream=None):
+    def gather_kv(self, cache, which: int, block_tables, seq: int, ctx: int, meta: BatchMeta, out, stream=None,
+                  device_status=None):
+        """pod_attn_gather_kv; device_status (a device int32 tensor, optional) receives the bad-page bit."""
         _check(self.lib.pod_attn_gather_kv(self.h, _ptr(cache), int(which), _ptr(block_tables), int(seq),
-                                           int(ctx), C.byref(meta.c), _ptr(out), _stream_handle(stream)))
+                                           int(ctx), C.byref(meta.c), _ptr(out), _ptr(device_status),
+                                           _stream_handle(stream)))
         return out
+
+    def run_diagnostics(self, workspace, stream=None) -> dict:
+        """pod_attn_read_run_diagnostics: synchronises and reads the last run's per-CU claim balance,
+        status word and kernel time."""
+        d = RunDiag()
+        _check(self.lib.pod_attn_read_run_diagnostics(self.h, _ptr(workspace), _stream_handle(stream), C.byref(d)))
+        return d.as_dict()
 
     def read_trace(self, workspace, stream=None) -> np.ndarray:
         """Per-item timeline of the last run (handle created with FLAG_TRACE): uint32 [n, 4] rows

@@ -12,8 +12,12 @@ control.
 context is ``chunk_ctx``, plus ``n_decode`` decodes at context ``decode_ctx`` -- on synthetic
 data in this library's buffer formats, ``steps`` times, and records the step's wall time (median
 and maximum), the fused kernel's own time, and the batch's signals (``pod_attn_batch_signals``).
-A bucket is validated when its runs took the fused path, reported no device error and wrote a
-finite output.  ``CostTable.lookup`` rounds each axis of a batch up to the table's next grid
+A bucket is validated when its runs took the fused path, reported no device error, wrote a
+finite output, and its output matched an independent reference within the library's stated
+tolerance (bf16: max abs 2e-2, mean abs 2e-3; fp32: 1e-5) on the sampled rows of
+``checked_rows`` (every head of the first and last prefill row and of the first and last decode
+row).  The reference is the caller's (``calibrate(reference=...)``): this module computes no
+attention itself, and a table calibrated without one publishes no validated bucket.  ``CostTable.lookup`` rounds each axis of a batch up to the table's next grid
 value (as a static-shape backend pads a batch to its bucket, [W6] "Batching의 비용은 bucket
 크기로 정해진다") and returns None outside the table or for a bucket that failed validation.
 """
@@ -22,7 +26,7 @@ from __future__ import annotations
 import json
 import statistics
 from dataclasses import asdict, dataclass, field
-from typing import Dict, List, Optional, Sequence
+from typing import Callable, Dict, List, Optional, Sequence
 
 import numpy as np
 
@@ -43,6 +47,8 @@ class Entry:
     kernel_us_max: float
     validated: bool
     signals: Dict[str, float] = field(default_factory=dict)
+    max_abs_err: Optional[float] = None     # against the reference, over the sampled rows
+    mean_abs_err: Optional[float] = None
 
     def key(self):
         return (self.chunk_len, self.chunk_ctx, self.n_decode, self.decode_ctx)
@@ -93,10 +99,43 @@ def bucket_batch(chunk_len: int, chunk_ctx: int, n_decode: int, decode_ctx: int)
     return np.asarray(q_start, np.int32), np.asarray(p_ctx, np.int32), np.full(n_decode, decode_ctx, np.int32)
 
 
+TOLERANCE = {"bf16": (2e-2, 2e-3), "fp32": (1e-5, 1e-5)}   # (max abs, mean abs) of a validated bucket
+
+
+@dataclass
+class BucketRun:
+    """What a reference checker gets for one bucket: the inputs in the C ABI's formats (device
+    tensors and host metadata), the library's output, and the q rows to compare (all heads)."""
+    q: object
+    k_pool: object
+    v_pool: object
+    block_tables_host: np.ndarray
+    prefill_q_start: np.ndarray
+    prefill_ctx_len: np.ndarray
+    decode_ctx_len: np.ndarray
+    num_q_heads: int
+    num_kv_heads: int
+    dtype: str
+    scale: float
+    out: object
+    rows: List[int]
+
+
+def checked_rows(chunk_len: int, n_decode: int) -> List[int]:
+    """q rows a bucket is validated on: the first and last prefill row, the first and last decode."""
+    rows = sorted({0, chunk_len - 1}) if chunk_len > 0 else []
+    if n_decode:
+        rows += sorted({chunk_len, chunk_len + n_decode - 1})
+    return rows
+
+
 def calibrate(num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: str,
               chunk_lens: Sequence[int], chunk_ctxs: Sequence[int], decode_counts: Sequence[int],
-              decode_ctxs: Sequence[int], steps: int = 5, warmup: int = 1, seed: int = 0) -> CostTable:
-    """Measure every bucket of the grid in fused mode on the current GPU (see the module text)."""
+              decode_ctxs: Sequence[int], steps: int = 5, warmup: int = 1, seed: int = 0,
+              reference: Optional[Callable[[BucketRun], "tuple[float, float]"]] = None) -> CostTable:
+    """Measure every bucket of the grid in fused mode on the current GPU (see the module text).
+    ``reference(run)`` returns the (max, mean) absolute error of ``run.out`` on ``run.rows``
+    against an independent reference; without it no bucket is validated."""
     import torch
 
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
@@ -152,11 +191,20 @@ def calibrate(num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: str,
         st = h.stats()
         status, _, _ = h.read_device_status(ws)
         ok = st["mode_used"] == binding.MODES["fused"] and status == 0 and bool(torch.isfinite(out).all())
+        max_err = mean_err = None
+        if reference is not None:
+            max_err, mean_err = reference(BucketRun(qv, k_pool, v_pool, bt, q_start, p_ctx, d_ctx, num_q_heads,
+                                                    num_kv_heads, dtype, h.cfg.scale if h.cfg.scale > 0
+                                                    else 1.0 / head_dim ** 0.5, out, checked_rows(L, n)))
+            max_err, mean_err = float(max_err), float(mean_err)
+        tol = TOLERANCE[dtype]
+        ok = ok and max_err is not None and max_err <= tol[0] and mean_err <= tol[1]
         sig = binding.batch_signals(h.cfg, meta, st["num_cus"], st["wgs_per_cu"])
         entries.append(Entry(L, C, n, Dc, round(statistics.median(walls), 2), round(max(walls), 2),
                              round(statistics.median(kerns), 2), round(max(kerns), 2), ok,
                              {k: sig[k] for k in ("prefill_items", "decode_items", "lds_bytes_per_wg",
-                                                  "prefill_flops", "decode_bytes", "intensity", "roofline_us")}))
+                                                  "prefill_flops", "decode_bytes", "intensity", "roofline_us")},
+                             max_err, mean_err))
         del ws, out, bt_dev
     h.close()
     return CostTable([num_q_heads, num_kv_heads, head_dim], dtype, entries)
@@ -166,7 +214,8 @@ if __name__ == "__main__":
     import argparse
     import sys
 
-    ap = argparse.ArgumentParser(description="measure a cost table on the current GPU and print it as JSON")
+    ap = argparse.ArgumentParser(description="measure a cost table on the current GPU and print it as JSON "
+                                             "(timings only: without a reference no bucket is validated)")
     ap.add_argument("--heads", default="32,8,128", help="Hq,Hkv,D")
     ap.add_argument("--dtype", default="bf16")
     ap.add_argument("--chunk-lens", default="0,512,1024,2048")

@@ -49,6 +49,14 @@ struct StagingSlot {
   bool pending = false;
 };
 constexpr int kRing = 4;
+
+// Kernel-time record of one run: events around its attention kernels and its algorithmic work.
+struct TimingSlot {
+  hipEvent_t start = nullptr, end = nullptr;
+  bool armed = false;
+  uint64_t run = 0;
+  double bytes = 0.0, flops = 0.0;
+};
 }  // namespace
 
 struct pod_attn_handle {
@@ -67,9 +75,8 @@ struct pod_attn_handle {
   Plan last_plan;
   int mode_env = -1;
   hipEvent_t prof_start = nullptr, prof_end = nullptr;   // one-shot profiling events
-  int prefill_wgs_override = 0;     // POD_ATTN_PREFILL_WGS
-  int prefill_per_cu_override = 0;  // POD_ATTN_PREFILL_PER_CU
-  int prefill_cus_override = 0;     // POD_ATTN_PREFILL_CUS (-1: per-CU cap policy)
+  TimingSlot timing[kRing];         // kernel time of the last runs (one slot per run, round robin)
+  int timing_next = 0;
   int role_prio = 0;                // POD_ATTN_ROLE_PRIO (decode | prefill << 2)
 };
 
@@ -112,9 +119,6 @@ pod_attn_status pod_attn_create(const pod_attn_config* cfg, pod_attn_handle** ou
   h->cfg.append_token_heads = std::max(1, env_int("POD_ATTN_APPEND_TOKEN_HEADS", kAppendTokenHeads));
   h->cfg.decode_taper = env_int("POD_ATTN_DECODE_TAPER", h->cfg.decode_taper);
   h->cfg.decode_items_per_wave = std::max(0, env_int("POD_ATTN_DECODE_ITEMS_PER_WAVE", h->cfg.decode_items_per_wave));
-  h->prefill_wgs_override = env_int("POD_ATTN_PREFILL_WGS", 0);
-  h->prefill_per_cu_override = env_int("POD_ATTN_PREFILL_PER_CU", 0);
-  h->prefill_cus_override = env_int("POD_ATTN_PREFILL_CUS", 0);
   h->role_prio = env_int("POD_ATTN_ROLE_PRIO", 0) & 15;
   if (const char* m = std::getenv("POD_ATTN_MODE")) {
     if (!std::strcmp(m, "fused")) h->mode_env = POD_ATTN_MODE_FUSED;
@@ -129,6 +133,10 @@ pod_attn_status pod_attn_create(const pod_attn_config* cfg, pod_attn_handle** ou
   if (e == hipSuccess) e = hipEventCreateWithFlags(&h->evA, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&h->evB, hipEventDisableTiming);
   for (int i = 0; i < kRing && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&h->ring[i].done, hipEventDisableTiming);
+  for (int i = 0; i < kRing && e == hipSuccess; ++i) {
+    e = hipEventCreate(&h->timing[i].start);
+    if (e == hipSuccess) e = hipEventCreate(&h->timing[i].end);
+  }
   if (e != hipSuccess) {
     pod_attn_destroy(h);
     return fail(POD_ATTN_ERR_HIP, std::string("stream/event creation: ") + hipGetErrorString(e));
@@ -154,6 +162,10 @@ void pod_attn_destroy(pod_attn_handle* h) {
     }
     if (h->ring[i].host) (void)hipHostFree(h->ring[i].host);
   }
+  for (int i = 0; i < kRing; ++i) {
+    if (h->timing[i].start) (void)hipEventDestroy(h->timing[i].start);
+    if (h->timing[i].end) (void)hipEventDestroy(h->timing[i].end);
+  }
   if (h->evStart) (void)hipEventDestroy(h->evStart);
   if (h->evA) (void)hipEventDestroy(h->evA);
   if (h->evB) (void)hipEventDestroy(h->evB);
@@ -175,28 +187,6 @@ pod_attn_status pod_attn_workspace_size(pod_attn_handle* h, const pod_attn_batch
 static hipError_t launch(const void* fn, int grid, KernelParams& p, hipStream_t s) {
   void* args[] = {&p};
   return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
-}
-
-// Prefill-role workgroups allowed while decode work remains (fused mode).  The binding limit is
-// the per-CU cap (one prefill workgroup per CU, so every CU keeps a decode workgroup streaming
-// beside its matrix work); the device-wide budget is the whole grid unless overridden.  Measured
-// on the four bf16 workloads (interleaved A/B runs): one per CU beat three quarters of the grid
-// with two per CU by 1-8%, and adding a device-wide budget of one per CU on top only lost (its
-// counter rejects transiently).
-static int prefill_budget(const pod_attn_handle* h, const Plan& p) {
-  const int total = h->num_cus * h->wgs_per_cu;
-  if (h->prefill_wgs_override > 0) return std::min(h->prefill_wgs_override, total);
-  (void)p;
-  return total;
-}
-static int prefill_cus(const pod_attn_handle* h, const Plan& p) {
-  if (h->prefill_cus_override != 0) return std::max(0, std::min(h->prefill_cus_override, h->num_cus));
-  (void)p;
-  return 0;
-}
-static int prefill_per_cu(const pod_attn_handle* h) {
-  if (h->prefill_per_cu_override > 0) return std::min(h->prefill_per_cu_override, h->wgs_per_cu);
-  return 1;
 }
 
 // Combine groups [g0, g1), whose groups have at most max_cols columns: one workgroup per
@@ -297,9 +287,6 @@ static pod_attn_status run_impl(pod_attn_handle* h, const void* q, const void* k
   kp.hq = h->cfg.hq; kp.hkv = h->cfg.hkv; kp.group = h->cfg.group();
   kp.bt_stride = b->block_table_stride; kp.num_pages = b->num_pages_in_pool;
   kp.scale_log2 = h->cfg.scale * 1.4426950408889634f;
-  kp.prefill_cap_per_cu = prefill_per_cu(h);
-  kp.prefill_wg_budget = prefill_budget(h, p);
-  kp.prefill_cus = prefill_cus(h, p);
   kp.role_prio = h->role_prio;
 
   // Plan upload (and, in fused mode, the KV append in the same launch).
@@ -325,6 +312,12 @@ static pod_attn_status run_impl(pod_attn_handle* h, const void* q, const void* k
   hipEvent_t prof_start = h->prof_start, prof_end = h->prof_end;
   h->prof_start = h->prof_end = nullptr;
   if (prof_start) POD_HIP(hipEventRecord(prof_start, stream));
+  // Kernel time of this run, for the diagnostics: events around the attention kernels (the same
+  // span the profiling hook brackets), kept with the run's algorithmic work.
+  TimingSlot& tslot = h->timing[h->timing_next];
+  h->timing_next = (h->timing_next + 1) % kRing;
+  tslot.armed = false;
+  POD_HIP(hipEventRecord(tslot.start, stream));
   int grid = 0;
   if (mode == POD_ATTN_MODE_FUSED) {
     kp.inline_combine = 1;                    // split groups merge in-kernel (last arriver)
@@ -353,8 +346,18 @@ static pod_attn_status run_impl(pod_attn_handle* h, const void* q, const void* k
     POD_HIP(hipStreamWaitEvent(stream, h->evB, 0));
   }
   if (prof_end) POD_HIP(hipEventRecord(prof_end, stream));
+  POD_HIP(hipEventRecord(tslot.end, stream));
 
   pod_attn_stats& s = h->stats;
+  s.runs += 1;
+  if (mode == POD_ATTN_MODE_FUSED && reason == POD_ATTN_FALLBACK_NONE) s.runs_fused_path += 1;
+  if (reason >= 0 && reason < POD_ATTN_NUM_FALLBACK_REASONS) s.fallback_runs[reason] += 1;
+  s.algorithmic_bytes = p.prefill_bytes + p.decode_bytes;
+  s.algorithmic_flops = p.prefill_flops + p.decode_flops;
+  tslot.armed = true;
+  tslot.run = s.runs;
+  tslot.bytes = s.algorithmic_bytes;
+  tslot.flops = s.algorithmic_flops;
   s.mode_requested = requested;
   s.mode_used = mode;
   s.fallback_reason = reason;
@@ -367,7 +370,7 @@ static pod_attn_status run_impl(pod_attn_handle* h, const void* q, const void* k
   s.decode_split_tokens = p.decode_split_tokens;
   s.decode_max_splits = p.decode_max_splits;
   s.grid_wgs = grid;
-  s.prefill_wg_budget = mode == POD_ATTN_MODE_FUSED ? kp.prefill_wg_budget : 0;
+  s.prefill_wg_budget = mode == POD_ATTN_MODE_FUSED ? h->num_cus * kPrefillPerCu : 0;
   s.workspace_bytes = p.map.total;
   s.host_plan_us = plan_us;
   s.num_append_units = kp.n_aunits;
@@ -432,14 +435,35 @@ pod_attn_status pod_attn_probe_mfma(int iters, float* sink, double* flops, void*
   return POD_ATTN_OK;
 }
 
+// Kernel time of the newest run whose attention kernels have completed (non-blocking).
+static void fill_timing(pod_attn_handle* h, pod_attn_stats* st) {
+  st->timed_run = 0;
+  st->kernel_us = -1.0;
+  st->achieved_gbps = st->achieved_tflops = -1.0;
+  const TimingSlot* best = nullptr;
+  for (const TimingSlot& t : h->timing) {
+    if (!t.armed || (best && t.run <= best->run)) continue;
+    if (hipEventQuery(t.end) != hipSuccess) continue;
+    best = &t;
+  }
+  float ms = 0.f;
+  if (!best || hipEventElapsedTime(&ms, best->start, best->end) != hipSuccess || ms <= 0.f) return;
+  st->timed_run = best->run;
+  st->kernel_us = ms * 1e3;
+  st->achieved_gbps = best->bytes / (ms * 1e-3) / 1e9;
+  st->achieved_tflops = best->flops / (ms * 1e-3) / 1e12;
+}
+
 pod_attn_status pod_attn_get_stats(pod_attn_handle* h, pod_attn_stats* st) {
   if (!h || !st) return fail(POD_ATTN_ERR_INVALID_ARG, "null handle or stats");
   *st = h->stats;
+  fill_timing(h, st);
   return POD_ATTN_OK;
 }
 
 pod_attn_status pod_attn_gather_kv(pod_attn_handle* h, const void* cache, int which, const int32_t* block_tables,
-                                   int seq, int ctx, const pod_attn_batch* b, void* out_contig, void* stream) {
+                                   int seq, int ctx, const pod_attn_batch* b, void* out_contig,
+                                   int32_t* device_status, void* stream) {
   if (!h || !cache || !block_tables || !b || !out_contig) return fail(POD_ATTN_ERR_INVALID_ARG, "null argument");
   const bool fp8 = h->cfg.dtype == POD_ATTN_FP8_E4M3;
   if (!(which == 0 || which == 1 || (fp8 && (which == 2 || which == 3))))
@@ -450,7 +474,8 @@ pod_attn_status pod_attn_gather_kv(pod_attn_handle* h, const void* cache, int wh
   const int grid = (int)((total + kThreads - 1) / kThreads);
   const int32_t* row = block_tables + (size_t)seq * b->block_table_stride;
   int hkv = h->cfg.hkv, np = b->num_pages_in_pool;
-  int32_t* status = nullptr;
+  int32_t* status = device_status;
+  if (((uintptr_t)status & 3) != 0) return fail(POD_ATTN_ERR_INVALID_ARG, "device_status must be 4-byte aligned");
   void* args[] = {(void*)&cache, &which, (void*)&row, &ctx, &hkv, &np, &out_contig, (void*)&status};
   POD_HIP(hipLaunchKernel(h->ks.gather, dim3(grid), dim3(kThreads), args, 0, (hipStream_t)stream));
   return POD_ATTN_OK;
@@ -471,6 +496,56 @@ pod_attn_status pod_attn_read_device_status(pod_attn_handle* h, const void* work
   const int m = std::min(cu_cap, (int)kCuSlots);
   if (pf_cu && m > 0) POD_HIP(hipMemcpy(pf_cu, ws + p.map.ctrl + 4 * kCClaimsPrefillCu, 4 * (size_t)m, hipMemcpyDeviceToHost));
   if (dc_cu && m > 0) POD_HIP(hipMemcpy(dc_cu, ws + p.map.ctrl + 4 * kCClaimsDecodeCu, 4 * (size_t)m, hipMemcpyDeviceToHost));
+  return POD_ATTN_OK;
+}
+
+pod_attn_status pod_attn_read_run_diagnostics(pod_attn_handle* h, const void* workspace, void* stream,
+                                              pod_attn_run_diag* d) {
+  if (!h || !workspace || !d) return fail(POD_ATTN_ERR_INVALID_ARG, "null handle, workspace or output");
+  POD_HIP(hipStreamSynchronize((hipStream_t)stream));
+  const uint8_t* ws = (const uint8_t*)workspace;
+  const Plan& p = h->last_plan;
+  std::vector<int32_t> pf(kCuSlots), dc(kCuSlots);
+  int32_t status = 0;
+  POD_HIP(hipMemcpy(&status, ws + p.map.ctrl + 4 * kCStatus, 4, hipMemcpyDeviceToHost));
+  POD_HIP(hipMemcpy(pf.data(), ws + p.map.ctrl + 4 * kCClaimsPrefillCu, 4 * (size_t)kCuSlots, hipMemcpyDeviceToHost));
+  POD_HIP(hipMemcpy(dc.data(), ws + p.map.ctrl + 4 * kCClaimsDecodeCu, 4 * (size_t)kCuSlots, hipMemcpyDeviceToHost));
+  pod_attn_run_diag r{};
+  r.status_word = status;
+  r.planned_prefill_items = p.n_pf_items;
+  r.planned_decode_items = p.n_dc_items;
+  r.min_prefill_share = 1.0;
+  double share_sum = 0.0;
+  int cus_any = 0;
+  for (int i = 0; i < kCuSlots; ++i) {
+    const int a = pf[i], b = dc[i];
+    r.prefill_items += a;
+    r.decode_items += b;
+    r.cus_prefill += a > 0;
+    r.cus_decode += b > 0;
+    r.cus_both += a > 0 && b > 0;
+    r.max_prefill_per_cu = std::max(r.max_prefill_per_cu, a);
+    r.max_decode_per_cu = std::max(r.max_decode_per_cu, b);
+    if (a + b > 0) {
+      const double sh = (double)a / (a + b);
+      share_sum += sh;
+      r.min_prefill_share = std::min(r.min_prefill_share, sh);
+      r.max_prefill_share = std::max(r.max_prefill_share, sh);
+      ++cus_any;
+    }
+  }
+  r.cus_any = cus_any;
+  r.mean_prefill_share = cus_any ? share_sum / cus_any : 0.0;
+  if (!cus_any) r.min_prefill_share = 0.0;
+  r.prefill_decode_ratio = r.decode_items > 0 ? (double)r.prefill_items / r.decode_items : 0.0;
+  pod_attn_stats st = h->stats;
+  fill_timing(h, &st);
+  r.run = st.runs;
+  r.timed_run = st.timed_run;
+  r.kernel_us = st.kernel_us;
+  r.achieved_gbps = st.achieved_gbps;
+  r.achieved_tflops = st.achieved_tflops;
+  *d = r;
   return POD_ATTN_OK;
 }
 

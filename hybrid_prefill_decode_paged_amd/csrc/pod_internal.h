@@ -56,15 +56,15 @@ enum CtrlWord {
   kCQueuePrefill = 0,
   kCQueueDecode = 64,
   kCStatus = 128,
-  kCActivePrefillAll = 192,                 // prefill-role workgroups now active, device-wide
   kCActivePrefill = 256,                    // [kCuSlots] prefill-role WGs now on each CU
-  kCClaimsPrefillCu = 256 + kCuSlots,       // [kCuSlots] prefill items claimed per CU
-  kCClaimsDecodeCu = 256 + 2 * kCuSlots,    // [kCuSlots] decode items claimed per CU
+  kCClaimsPrefillCu = 256 + kCuSlots,       // [kCuSlots] prefill items claimed per CU (every run)
+  kCClaimsDecodeCu = 256 + 2 * kCuSlots,    // [kCuSlots] decode items claimed per CU (every run)
   kCQueuePrefillXcd = 256 + 3 * kCuSlots,   // [kXcds] prefill queues, one 128-byte line each
-  kCCuRole = 256 + 3 * kCuSlots + kXcds * 32,   // [kCuSlots] fused CU-partition role: 0 open, 1 prefill, 2 decode, 3 deciding
-  kCXcdPrefillCus = kCCuRole + kCuSlots,        // [kXcds] prefill CUs chosen on each die, one line each
-  kCtrlInts = kCXcdPrefillCus + kXcds * 32
+  kCtrlInts = kCQueuePrefillXcd + kXcds * 32
 };
+// Fused kernel: prefill-role workgroups allowed on one CU while decode work remains.  One, so
+// that every CU keeps a decode workgroup streaming beside its matrix work.
+constexpr int kPrefillPerCu = 1;
 
 enum StatusBits { kStatusBadPage = 1 };
 
@@ -94,9 +94,6 @@ struct KernelParams {
   int n_pf_groups, n_groups; // groups [0, n_pf_groups) are prefill, the rest decode
   int hq, hkv, group, bt_stride, num_pages;
   float scale_log2;          // softmax scale * log2(e)
-  int prefill_cap_per_cu;    // fused: prefill-role workgroups allowed per CU while decode remains
-  int prefill_wg_budget;     // fused: prefill-role workgroups allowed device-wide while decode remains
-  int prefill_cus;           // fused: > 0: CUs (spread over the dies) whose workgroups all take prefill while decode remains
   int inline_combine;        // 1: the last-arriving decode split merges its group in-kernel (fused)
   int role_prio;             // fused: wave priority (0..3) of decode-role (low 2 bits) and prefill-role (next 2) waves
   int group_begin, group_end;// combine kernel range

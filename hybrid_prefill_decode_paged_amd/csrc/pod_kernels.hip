@@ -1467,11 +1467,12 @@ __device__ __forceinline__ int cu_slot() {
   return (int)(((xcc & 7u) << 7) | (se << 5) | (sh << 4) | cu);
 }
 
+// Claim accounting: every run counts the items of each kind each CU claimed (the per-CU
+// balance of the two kinds, read back as a run diagnostic); with POD_ATTN_FLAG_DEBUG_CLAIMS
+// every item also counts its own claims.
 __device__ __forceinline__ void note_claim(const KernelParams& P, int kind, int item, int cu) {
-  if (P.claims) {
-    atomicAdd(P.claims + (kind == 0 ? 0 : P.n_pf_items) + item, 1);
-    atomicAdd(P.ctrl + (kind == 0 ? kCClaimsPrefillCu : kCClaimsDecodeCu) + cu, 1);
-  }
+  if (P.claims) atomicAdd(P.claims + (kind == 0 ? 0 : P.n_pf_items) + item, 1);
+  atomicAdd(P.ctrl + (kind == 0 ? kCClaimsPrefillCu : kCClaimsDecodeCu) + cu, 1);
 }
 
 // Timeline record of one work item (POD_ATTN_FLAG_TRACE): low 32 bits of the 100 MHz constant
@@ -1483,28 +1484,6 @@ __device__ __forceinline__ void trace_item(const KernelParams& P, int kind, int 
     const uint32_t t1 = clock100();
     *(u32x4*)(P.trace + 4 * ((size_t)(kind == 0 ? 0 : P.n_pf_items) + item)) = u32x4{t0, t1, (uint32_t)cu, (uint32_t)kind};
   }
-}
-
-// CU-partition role (fused kernel, prefill_cus > 0), called by thread 0: the first workgroup to
-// ask on a CU decides for the whole CU, taking one of its die's prefill-CU places while any is
-// left (prefill_cus spread evenly over the dies, so that every die's prefill queue keeps its
-// own CUs).  Returns 1 for a prefill CU, 2 for a decode CU.  A workgroup that finds its CU's
-// decision in progress (a few atomics by the other workgroup) polls with a bounded wait and
-// takes decode if it never settles.
-__device__ __forceinline__ int cu_role(const KernelParams& P, int cu, int xcc) {
-  int* slot = P.ctrl + kCCuRole + cu;
-  int prev = atomicCAS(slot, 0, 3);
-  if (prev == 0) {
-    const int quota = P.prefill_cus / kXcds + (xcc < P.prefill_cus % kXcds ? 1 : 0);
-    const int r = atomicAdd(P.ctrl + kCXcdPrefillCus + 32 * xcc, 1) < quota ? 1 : 2;
-    atomicExch(slot, r);
-    return r;
-  }
-  for (int i = 0; prev == 3 && i < 4096; ++i) {
-    __builtin_amdgcn_s_sleep(2);
-    prev = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  return prev == 1 ? 1 : 2;
 }
 
 // Prefill claim for a workgroup on XCC `xcc`: queue x is the item range [hdr[x], hdr[x+1]) of
@@ -1525,9 +1504,8 @@ __device__ __forceinline__ int claim_prefill(const KernelParams& P, int xcc) {
 
 // ------------------------------------------------------------------ kernels
 // Fused persistent kernel: every workgroup loops, taking a role and claiming work of that kind.
-// While decode work remains, at most `prefill_cap_per_cu` workgroups per CU (one by default) and
-// `prefill_wg_budget` device-wide hold the prefill role, so every CU keeps decode loads in
-// flight beside its matrix work ([POD], "Virtual CTAs and per-SM balance": the scheduler places
+// While decode work remains, at most kPrefillPerCu workgroups per CU hold the prefill role, so
+// every CU keeps decode loads in flight beside its matrix work ([POD], "Virtual CTAs and per-SM balance": the scheduler places
 // complementary work per SM).  A prefill-role workgroup works on one tile at a time with all
 // four waves, taking tiles from its die's queue; a decode-role workgroup's four waves stream four
 // adjacent decode items.  A workgroup whose kind is drained takes the other kind; the kernel
@@ -1540,23 +1518,18 @@ __global__ __launch_bounds__(kThreads, 2) void pod_fused_kernel(KernelParams P) 
   const int cu = cu_slot();
   const int xcc = cu >> 7;
   int* active = P.ctrl + kCActivePrefill + cu;
-  int* active_all = P.ctrl + kCActivePrefillAll;
   bool pf_open = P.n_pf_items > 0, dc_open = P.n_dc_items > 0;
-  bool counted = false;                       // thread 0: holds a prefill slot
+  bool counted = false;                       // thread 0: holds its CU's prefill slot
   for (;;) {
     if (tid == 0) {
       int role = -1;
-      if (pf_open && dc_open && P.prefill_cus > 0) {
-        role = cu_role(P, cu, xcc) == 1 ? 0 : 1;
-      } else if (pf_open && dc_open) {
+      if (pf_open && dc_open) {
         const int a = atomicAdd(active, 1);
-        const int g = atomicAdd(active_all, 1);
-        if (a < P.prefill_cap_per_cu && g < P.prefill_wg_budget) {
+        if (a < kPrefillPerCu) {
           role = 0;
           counted = true;
         } else {
           atomicSub(active, 1);
-          atomicSub(active_all, 1);
           role = 1;
         }
       } else if (dc_open) {
@@ -1607,7 +1580,6 @@ __global__ __launch_bounds__(kThreads, 2) void pod_fused_kernel(KernelParams P) 
     pf_open = false;
     if (tid == 0 && counted) {
       atomicSub(active, 1);
-      atomicSub(active_all, 1);
       counted = false;
     }
   }

@@ -93,7 +93,8 @@ typedef enum {
   POD_ATTN_FALLBACK_NO_PREFILL = 1,    /* nothing to overlap: fused kernel runs decode only    */
   POD_ATTN_FALLBACK_NO_DECODE = 2,     /* nothing to overlap: fused kernel runs prefill only   */
   POD_ATTN_FALLBACK_OCCUPANCY = 3,     /* fused kernel cannot keep 2 workgroups per CU; ran SEPARATE */
-  POD_ATTN_FALLBACK_ENV = 4            /* mode overridden by POD_ATTN_MODE                      */
+  POD_ATTN_FALLBACK_ENV = 4,           /* mode overridden by POD_ATTN_MODE                      */
+  POD_ATTN_NUM_FALLBACK_REASONS = 5
 } pod_attn_fallback;
 
 /* Flags */
@@ -130,8 +131,13 @@ typedef struct pod_attn_batch {
 
 typedef struct pod_attn_handle pod_attn_handle;   /* opaque, host-side */
 
-/* Diagnostics of the last pod_attn_run on a handle ([POD], "Predictable latency and
- * diagnostics": virtual-CTA ratio, tile choice, occupancy, fallback reason). */
+/* Diagnostics of a handle's runs ([POD], "Predictable latency and diagnostics": virtual-CTA
+ * ratio, tile choice, occupancy, memory throughput, fallback reason; [POD], "Reproduction and
+ * hardware evaluation": the share of iterations that took the fused path and every fallback
+ * cause).  The fields up to num_small_extends describe the last run; runs, runs_fused_path and
+ * fallback_runs count over the handle's life; kernel_us and the achieved rates are those of the
+ * newest run whose attention kernels have completed when pod_attn_get_stats is called (timed_run
+ * names it; pod_attn_get_stats never waits for the GPU). */
 typedef struct pod_attn_stats {
   int mode_requested;
   int mode_used;
@@ -155,6 +161,16 @@ typedef struct pod_attn_stats {
   int prefill_wg_budget;        /* FUSED: prefill-role workgroups allowed while decode remains */
   int num_append_units;         /* KV append units of the last run (0 for pod_attn_run)      */
   int num_small_extends;        /* prefill chunks run on the decode path as small-q extends   */
+  uint64_t runs;                /* runs (pod_attn_run*) that launched work on this handle      */
+  uint64_t runs_fused_path;     /* of them, runs on the fused kernel with both kinds of work  */
+  uint64_t fallback_runs[POD_ATTN_NUM_FALLBACK_REASONS];   /* runs per fallback_reason value  */
+  double algorithmic_bytes;     /* last run: K and V once per KV head per context token, q in,
+                                   out, one block-table entry per page (+ FP8 scales)         */
+  double algorithmic_flops;     /* last run: 4*D per visible (query head, key) pair           */
+  uint64_t timed_run;           /* run number (1-based) the kernel time below belongs to; 0: none */
+  double kernel_us;             /* that run's attention kernels, first start to last end (< 0: none) */
+  double achieved_gbps;         /* that run's algorithmic bytes / kernel_us                    */
+  double achieved_tflops;       /* that run's algorithmic FLOPs / kernel_us                    */
 } pod_attn_stats;
 
 /* Create a handle for one attention configuration on the current HIP device.  Validates the
@@ -166,8 +182,13 @@ pod_attn_status pod_attn_create(const pod_attn_config* cfg, pod_attn_handle** ou
  * partials).  Validates the batch metadata. */
 pod_attn_status pod_attn_workspace_size(pod_attn_handle* h, const pod_attn_batch* batch, size_t* bytes);
 
-/* Compute the hybrid batch.  q, k_cache, v_cache, block_tables, out and workspace are device
- * pointers in the formats above; `stream` is a hipStream_t (NULL = null stream).  Plans the
+/* Compute the hybrid batch: for every query row, exact causal attention over its sequence's
+ * cached keys and values ([W6] "Attention에 적용하기": softmax(Q K^T / sqrt(d_k)) V; [W6]
+ * "Non-Causal vs. Causal Attention": a token sees itself and earlier tokens; [W6] "한 스텝에
+ * 여러 종류의 request 섞기": extend and decode rows in one batch), read through the block tables
+ * ([W6] "PagedAttention"), long key ranges split and merged by their maxima and sums ([W4]
+ * "FlashDecoding -- decode 단계의 병렬성 확보").  q, k_cache, v_cache, block_tables, out and
+ * workspace are device pointers in the formats above; `stream` is a hipStream_t (NULL = null stream).  Plans the
  * work on the host, copies the plan into `workspace` and launches on `stream` (FUSED: one
  * kernel; SEPARATE: up to three; STREAMS: as SEPARATE on two internal streams joined by
  * events).  Returns before the GPU finishes.  `out` rows are each written exactly once; no
@@ -216,23 +237,56 @@ pod_attn_status pod_attn_get_stats(pod_attn_handle* h, pod_attn_stats* st);
 
 /* Debug/test: gather one sequence's K (which = 0) or V (which = 1) for all KV heads into
  * out_contig [ctx][Hkv][D] (same element type), through the same page-address arithmetic the
- * attention kernels use.  Bit-exact copy; asynchronous on `stream`.  FP8_E4M3 handles also take
- * which = 2 (K) / 3 (V): each code decoded to bf16 (unscaled) by the kernels' conversion. */
+ * attention kernels use: logical token t is slot t % 16 of the physical page that row `seq` of
+ * block_tables names for logical page t / 16 ([W6] "PagedAttention"; [W4] "PagedAttention --
+ * 메모리 단편화를 없애는 커널": the kernel follows the block table to the scattered pages).
+ * Bit-exact copy; asynchronous on `stream`.  FP8_E4M3 handles also take which = 2 (K) / 3 (V):
+ * each code decoded to bf16 (unscaled) by the kernels' conversion.  A block-table entry outside
+ * [0, num_pages_in_pool) is not read: its tokens come out as zeros and, when device_status (a
+ * device int32, may be NULL) is given, POD_ATTN_DEVICE_ERR_BAD_PAGE is OR-ed into it.  Errors:
+ * POD_ATTN_ERR_INVALID_ARG for null buffers, a bad `which`, `seq` or `ctx`, or a misaligned
+ * device_status. */
 pod_attn_status pod_attn_gather_kv(pod_attn_handle* h, const void* cache, int which,
                                    const int32_t* block_tables, int seq, int ctx,
-                                   const pod_attn_batch* batch, void* out_contig, void* stream);
+                                   const pod_attn_batch* batch, void* out_contig,
+                                   int32_t* device_status, void* stream);
 
 /* Debug/test: synchronise `stream` and read the workspace status word written by the last run
- * (bit POD_ATTN_DEVICE_ERR_BAD_PAGE) and, if the handle has POD_ATTN_FLAG_DEBUG_CLAIMS, the
- * per-item claim counts (claims[i] for prefill items first, then decode items; up to
- * claims_cap entries) and per-CU claim totals of each kind (up to cu_cap entries each; may be
- * NULL).  Returns the number of items in *n_items. */
+ * (bit POD_ATTN_DEVICE_ERR_BAD_PAGE), the per-CU claim totals of each kind (every run counts
+ * them; up to cu_cap entries each, indexed by the cu_slot of pod_attn_read_trace; may be NULL)
+ * and, if the handle has POD_ATTN_FLAG_DEBUG_CLAIMS, the per-item claim counts (claims[i] for
+ * prefill items first, then decode items; up to claims_cap entries).  Returns the number of
+ * items in *n_items. */
 #define POD_ATTN_DEVICE_ERR_BAD_PAGE 1
 pod_attn_status pod_attn_read_device_status(pod_attn_handle* h, const void* workspace,
                                             void* stream, int32_t* status_word,
                                             int32_t* claims, int claims_cap, int* n_items,
                                             int32_t* prefill_claims_per_cu,
                                             int32_t* decode_claims_per_cu, int cu_cap);
+
+/* Run diagnostics ([POD] "Predictable latency and diagnostics": the runtime should expose the
+ * virtual-CTA ratio, occupancy and memory throughput of the fused kernel).  Synchronises
+ * `stream`, then reads what the last run on this handle left in `workspace` (which must be the
+ * workspace of that run): every run counts, per compute unit, the work items of each kind the
+ * CU's workgroups claimed, so the balance of the two kinds on each CU is known without a debug
+ * flag.  Shares are prefill items / all items of a CU, over the CUs that ran any item.  The
+ * kernel time and achieved rates are those of the last run (the same figures pod_attn_get_stats
+ * gives once the run has completed). */
+typedef struct pod_attn_run_diag {
+  int status_word;              /* device status bits of the run (POD_ATTN_DEVICE_ERR_*)       */
+  int planned_prefill_items, planned_decode_items;
+  int prefill_items, decode_items;   /* items claimed, summed over the CUs (equal to the planned counts) */
+  int cus_any;                  /* CUs that ran any item                                      */
+  int cus_prefill, cus_decode;  /* CUs that ran at least one item of the kind                 */
+  int cus_both;                 /* CUs that ran both kinds in this run                        */
+  int max_prefill_per_cu, max_decode_per_cu;
+  double prefill_decode_ratio;  /* prefill items / decode items (0 when there is no decode)  */
+  double mean_prefill_share, min_prefill_share, max_prefill_share;
+  uint64_t run, timed_run;      /* the last run's number and the run the timing belongs to    */
+  double kernel_us, achieved_gbps, achieved_tflops;
+} pod_attn_run_diag;
+pod_attn_status pod_attn_read_run_diagnostics(pod_attn_handle* h, const void* workspace,
+                                              void* stream, pod_attn_run_diag* out);
 
 /* Debug/profiling: synchronise `stream` and copy the per-item timeline of the last run, for a
  * handle created with POD_ATTN_FLAG_TRACE (else POD_ATTN_ERR_INVALID_ARG).  One record of 4

@@ -20,6 +20,38 @@ def test_library_exports_every_declared_function():
         assert hasattr(lib, n), f"{n} declared in include/pod_attn.h but not exported"
 
 
+def test_binding_structures_match_the_header_layout(tmp_path):
+    """Every ctypes structure of the binding has the size and field offsets that a C compiler
+    gives the header's structure (gcc on include/pod_attn.h)."""
+    import ctypes
+    import os
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no gcc")
+    structs = {"pod_attn_config": B.Config, "pod_attn_batch": B.Batch, "pod_attn_stats": B.Stats,
+               "pod_attn_signals": B.Signals, "pod_attn_run_diag": B.RunDiag}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "pod_attn.h"', "int main(void) {"]
+    for cname, cls in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in cls._fields_:
+            lines.append(f'  printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(B.HEADER))
+    subprocess.run(["gcc", "-I", inc, str(src), "-o", str(exe)], check=True)
+    got = {}
+    for line in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.splitlines():
+        parts = line.split()
+        got[tuple(parts[:-1])] = int(parts[-1])
+    for cname, cls in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(cls), cname
+        for f, _ in cls._fields_:
+            assert got[(cname, f)] == getattr(cls, f).offset, (cname, f)
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
 def test_create_without_device_reports_no_device():
     with pytest.raises(B.PodAttnError) as e:

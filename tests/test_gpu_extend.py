@@ -11,7 +11,7 @@ import torch
 from hybrid_prefill_decode_paged_amd import binding as B
 from hybrid_prefill_decode_paged_amd import inputs as gen
 
-from helpers import check_close, problem, run_library, sample_pairs, to_f64
+from helpers import check_close, check_rows, checked_rows, problem, reference_rows, run_library, to_f64
 
 pytestmark = pytest.mark.gpu
 MODES = ["fused", "separate", "streams"]
@@ -82,16 +82,20 @@ def test_decode_path_and_tile_path_agree():
     assert np.abs(to_f64(o1) - to_f64(o2)).max() <= 2e-2
 
 
-def test_speculative_verify_batch_full_size():
-    """A Llama-3-8B-shaped verification step at full size: 128 sequences each extending by 4
-    tokens (4 x G = 16 columns) at contexts of 4K-32K, plus one 2048-token chunk; sampled rows
-    against the oracle."""
+@pytest.mark.parametrize("mode", MODES)
+def test_speculative_verify_batch_full_size(mode):
+    """A Llama-3-8B-shaped verification step at full size in every mode: 128 sequences each
+    extending by 4 tokens (4 x G = 16 columns) at contexts of 4K-32K, plus one 2048-token chunk.
+    Against the oracle: the first and last row of every tile of the chunk and all 4 rows of every
+    4th extend, all heads; every output row written."""
     spec = gen.spec_verify_spec(4)
     b = gen.make_batch(spec, "cuda")
-    _say("speculative verify full size")
-    out, h, _ = run_library(b, mode="fused")
-    assert h.stats()["num_small_extends"] == 128
-    pairs = sample_pairs(b, 2, 0, seed=5)
-    got = np.stack([to_f64(out[r, hh]) for r, hh in pairs])
-    check_close(got, problem(b).sampled_output(pairs), "bf16", "spec-verify")
-    assert not torch.isnan(out).any()
+    _say(f"speculative verify full size mode={mode}")
+    out, h, _ = run_library(b, mode=mode)
+    st = h.stats()
+    assert st["num_small_extends"] == 128
+    per_seq = checked_rows(b, st["prefill_tile_queries"])
+    chunk, extends = per_seq[0], per_seq[1:129]
+    per_seq = [chunk] + [(s, list(range(r[0], r[-1] + 1))) for s, r in extends[::4]]
+    rows, want = reference_rows(b, per_seq)
+    check_rows(out, rows, want, "bf16", f"spec-verify/{mode}")
