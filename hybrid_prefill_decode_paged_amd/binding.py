@@ -108,6 +108,7 @@ def load(path: str = LIB_PATH):
     lib.pod_attn_run.argtypes = [VP, VP, VP, VP, VP, P(Batch), VP, VP, C.c_size_t, VP]
     lib.pod_attn_run_append.argtypes = [VP, VP, VP, VP, VP, VP, VP, P(Batch), VP, VP, C.c_size_t, VP]
     lib.pod_attn_run_scaled.argtypes = [VP, VP, VP, VP, VP, VP, VP, P(Batch), VP, VP, C.c_size_t, VP]
+    lib.pod_attn_run_noalloc.argtypes = [VP, VP, VP, VP, VP, P(Batch), VP, VP]
     lib.pod_attn_get_stats.argtypes = [VP, P(Stats)]
     lib.pod_attn_gather_kv.argtypes = [VP, VP, I, VP, I, I, P(Batch), VP, VP, VP]
     lib.pod_attn_read_run_diagnostics.argtypes = [VP, VP, VP, P(RunDiag)]
@@ -126,7 +127,7 @@ def load(path: str = LIB_PATH):
                  "pod_attn_run_scaled", "pod_attn_get_stats",
                  "pod_attn_gather_kv", "pod_attn_read_device_status", "pod_attn_plan_inspect", "pod_attn_read_trace",
                  "pod_attn_set_kernel_events", "pod_attn_batch_signals", "pod_attn_probe_hbm_read",
-                 "pod_attn_probe_mfma", "pod_attn_read_run_diagnostics"):
+                 "pod_attn_probe_mfma", "pod_attn_read_run_diagnostics", "pod_attn_run_noalloc"):
         getattr(lib, name).restype = C.c_int
     _lib = lib
     return lib
@@ -192,6 +193,7 @@ def plan_inspect(cfg: Config, meta: BatchMeta, num_cus: int, wgs_per_cu: int):
 
 
 PROBE_WGS = 4096          # workgroups of either probe (pod_attn_probe_*)
+NOALLOC_SCRATCH_BYTES = 256 << 20   # pod_attn_run_noalloc's per-GPU scratch
 
 
 def probe_hbm_read(buf, sink, stream=None) -> None:
@@ -284,6 +286,14 @@ class PodAttention:
                                      C.byref(meta.c), _ptr(out), _ptr(workspace),
                                      0 if workspace is None else workspace.numel() * workspace.element_size(),
                                      _stream_handle(stream)))
+        return out
+
+    def run_noalloc(self, q, k_cache, v_cache, block_tables, meta: BatchMeta, out, stream=None):
+        """pod_attn_run_noalloc: pod_attn_run with the library's fixed per-GPU scratch as the workspace."""
+        if meta.total_q:
+            self.check_buffers(q, k_cache, v_cache, block_tables, meta, out)
+        _check(self.lib.pod_attn_run_noalloc(self.h, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                             C.byref(meta.c), _ptr(out), _stream_handle(stream)))
         return out
 
     def run_scaled(self, q, k_cache, v_cache, k_scale, v_scale, block_tables, meta: BatchMeta, out, workspace,

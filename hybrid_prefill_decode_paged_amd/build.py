@@ -28,6 +28,7 @@ DEVICE = ["-x", "hip", f"--offload-arch={ARCH}", "-Xclang", "-target-feature",
 
 SOURCES = [
     ("pod_kernels.hip", True),
+    ("pod_scratch.hip", True),
     ("pod_api.cpp", False),
     ("plan.cpp", False),
 ]

@@ -1,5 +1,7 @@
 // Kernel entry points of one (dtype, head_dim) instantiation, as launchable function handles.
 #pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
 
 namespace pod {
 
@@ -26,5 +28,10 @@ struct ProbeKernels {
   const void* mfma = nullptr;      // (int iters, float* sink)
 };
 ProbeKernels probe_kernels();
+
+// pod_attn_run_noalloc's device scratch: bytes per GPU, and its device address on `device`
+// (which must be current), looked up on the first call per device and kept.
+constexpr size_t kNoAllocScratchBytes = (size_t)256 << 20;
+hipError_t noalloc_scratch(int device, void** ptr);
 
 }  // namespace pod

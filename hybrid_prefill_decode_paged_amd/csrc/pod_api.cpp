@@ -49,6 +49,10 @@ struct StagingSlot {
   bool pending = false;
 };
 constexpr int kRing = 4;
+// Pinned staging bytes each ring slot gets at handle creation: plans of the measured workloads
+// stage a few to ~70 KiB.  pod_attn_run grows a slot for a larger plan; pod_attn_run_noalloc,
+// which allocates nothing, rejects such a plan instead.
+constexpr size_t kStagingPrealloc = (size_t)256 << 10;
 
 // Kernel-time record of one run: events around its attention kernels and its algorithmic work.
 struct TimingSlot {
@@ -78,6 +82,7 @@ struct pod_attn_handle {
   TimingSlot timing[kRing];         // kernel time of the last runs (one slot per run, round robin)
   int timing_next = 0;
   int role_prio = 0;                // POD_ATTN_ROLE_PRIO (decode | prefill << 2)
+  void* scratch = nullptr;          // pod_attn_run_noalloc's device scratch on this handle's device
 };
 
 extern "C" {
@@ -137,9 +142,15 @@ pod_attn_status pod_attn_create(const pod_attn_config* cfg, pod_attn_handle** ou
     e = hipEventCreate(&h->timing[i].start);
     if (e == hipSuccess) e = hipEventCreate(&h->timing[i].end);
   }
+  for (int i = 0; i < kRing && e == hipSuccess; ++i) {
+    e = hipHostMalloc(&h->ring[i].host, kStagingPrealloc, hipHostMallocCoherent | hipHostMallocMapped);
+    if (e == hipSuccess) e = hipHostGetDevicePointer(&h->ring[i].dev, h->ring[i].host, 0);
+    if (e == hipSuccess) h->ring[i].cap = kStagingPrealloc;
+  }
+  if (e == hipSuccess) e = noalloc_scratch(dev, &h->scratch);
   if (e != hipSuccess) {
     pod_attn_destroy(h);
-    return fail(POD_ATTN_ERR_HIP, std::string("stream/event creation: ") + hipGetErrorString(e));
+    return fail(POD_ATTN_ERR_HIP, std::string("stream/event/staging/scratch set-up: ") + hipGetErrorString(e));
   }
   h->stats.num_cus = h->num_cus;
   h->stats.wgs_per_cu = h->wgs_per_cu;
@@ -205,8 +216,13 @@ static hipError_t launch_combine(pod_attn_handle* h, const KernelParams& base, i
 static pod_attn_status run_impl(pod_attn_handle* h, const void* q, const void* k_new, const void* v_new,
                                 const void* k_cache, const void* v_cache, const float* k_scale,
                                 const float* v_scale, const int32_t* block_tables, const pod_attn_batch* b,
-                                void* out, void* workspace, size_t workspace_bytes, void* stream_) {
+                                void* out, void* workspace, size_t workspace_bytes, void* stream_,
+                                bool noalloc = false) {
   if (!h) return fail(POD_ATTN_ERR_INVALID_ARG, "null handle");
+  if (noalloc) {
+    workspace = h->scratch;
+    workspace_bytes = kNoAllocScratchBytes;
+  }
   const bool append = k_new != nullptr;
   const bool fp8 = h->cfg.dtype == POD_ATTN_FP8_E4M3;
   if (fp8 && append) return fail(POD_ATTN_ERR_UNSUPPORTED, "the KV append does not write an FP8 cache");
@@ -226,8 +242,11 @@ static pod_attn_status run_impl(pod_attn_handle* h, const void* q, const void* k
     return fail(POD_ATTN_ERR_INVALID_ARG, "null device buffer (q, k_cache, v_cache, block_tables or out)");
   if (!workspace) return fail(POD_ATTN_ERR_WORKSPACE, "null workspace");
   if (workspace_bytes < p.map.total)
-    return fail(POD_ATTN_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) + " bytes, needs " +
-                                            std::to_string(p.map.total));
+    return fail(POD_ATTN_ERR_WORKSPACE, noalloc ? "the batch needs " + std::to_string(p.map.total) +
+                                                      " workspace bytes; pod_attn_run_noalloc's scratch holds " +
+                                                      std::to_string(kNoAllocScratchBytes)
+                                                : "workspace has " + std::to_string(workspace_bytes) +
+                                                      " bytes, needs " + std::to_string(p.map.total));
   if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out | (uintptr_t)workspace |
        (uintptr_t)k_new | (uintptr_t)v_new) & 15)
     return fail(POD_ATTN_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
@@ -256,6 +275,9 @@ static pod_attn_status run_impl(pod_attn_handle* h, const void* q, const void* k
     slot.pending = false;
   }
   const size_t staged = (append ? p.map.copy_bytes : p.map.aunits) - p.map.pdesc;   // units only when appending
+  if (noalloc && slot.cap < staged)
+    return fail(POD_ATTN_ERR_WORKSPACE, "the plan stages " + std::to_string(staged) +
+                                            " bytes; pod_attn_run_noalloc's staging slots hold " + std::to_string(slot.cap));
   if (slot.cap < staged) {
     if (slot.host) POD_HIP(hipHostFree(slot.host));
     slot.host = slot.dev = nullptr;
@@ -387,6 +409,12 @@ pod_attn_status pod_attn_run(pod_attn_handle* h, const void* q, const void* k_ca
                              void* workspace, size_t workspace_bytes, void* stream) {
   return run_impl(h, q, nullptr, nullptr, k_cache, v_cache, nullptr, nullptr, block_tables, b, out, workspace,
                   workspace_bytes, stream);
+}
+
+pod_attn_status pod_attn_run_noalloc(pod_attn_handle* h, const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* block_tables, const pod_attn_batch* b, void* out, void* stream) {
+  return run_impl(h, q, nullptr, nullptr, k_cache, v_cache, nullptr, nullptr, block_tables, b, out, nullptr, 0,
+                  stream, true);
 }
 
 pod_attn_status pod_attn_run_scaled(pod_attn_handle* h, const void* q, const void* k_cache, const void* v_cache,

@@ -42,8 +42,9 @@
  *            of a row are read; slots past ctx in the last page are never used in the result.
  *
  * Ownership: the caller owns every device buffer (q, caches, block tables, out, workspace) and
- * every host array.  The handle owns host state only (plus, in STREAMS mode, two HIP streams
- * and events, and a small pinned host staging ring).  No call allocates device memory.
+ * every host array.  The handle owns host state only (plus two HIP streams and events for STREAMS
+ * mode, timing events, and a small pinned host staging ring).  No call allocates device memory;
+ * the library itself holds one fixed scratch array per GPU for pod_attn_run_noalloc.
  *
  * Errors: every call returns a pod_attn_status; on a non-OK status pod_attn_last_error()
  * returns a message for the calling thread.  pod_attn_run is asynchronous on `stream`;
@@ -231,6 +232,25 @@ pod_attn_status pod_attn_run_append(pod_attn_handle* h, const void* q, const voi
                                     const int32_t* block_tables, const pod_attn_batch* batch,
                                     void* out, void* workspace, size_t workspace_bytes,
                                     void* stream);
+
+/* For callers that cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  pod_attn_run, with the workspace taken from a fixed
+ * device array that the library holds on every GPU it runs on (POD_ATTN_NOALLOC_SCRATCH_BYTES,
+ * 256 MiB, held from the first pod_attn_create on that GPU until the process ends) instead of a
+ * caller's buffer.  The caller still passes q, the caches, the block tables and out, in the formats
+ * above; the result is bitwise that of pod_attn_run with a workspace of its own (same plan, same
+ * kernels).  The call allocates nothing: no device or pinned memory (the handle's pinned staging
+ * slots were made by pod_attn_create).  Errors as pod_attn_run, plus POD_ATTN_ERR_WORKSPACE when
+ * the batch needs more workspace than the scratch holds (pod_attn_workspace_size tells) or a plan
+ * larger than the handle's staging slots (256 KiB each), both before anything is launched.  Every
+ * call on a GPU shares that GPU's scratch, which keeps the last call's contents (each run clears
+ * the counters it needs): calls that overlap on one GPU -- concurrent streams, or handles used
+ * from several threads -- race and must be serialised by the caller.  FP8_E4M3 handles need their
+ * scales: POD_ATTN_ERR_INVALID_ARG. */
+#define POD_ATTN_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+pod_attn_status pod_attn_run_noalloc(pod_attn_handle* h, const void* q, const void* k_cache,
+                                     const void* v_cache, const int32_t* block_tables,
+                                     const pod_attn_batch* batch, void* out, void* stream);
 
 /* Copy the diagnostics of the last run into *st. */
 pod_attn_status pod_attn_get_stats(pod_attn_handle* h, pod_attn_stats* st);
