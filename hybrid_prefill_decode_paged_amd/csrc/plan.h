@@ -16,7 +16,7 @@ struct Config {
   int append_token_heads = kAppendTokenHeads;   // (token, KV head) pairs per KV append unit
   int extend_max_q = 0;         // chunks of at most this many rows run on the decode path (0: kExtendMaxQ, <0: never)
   int decode_items_per_wave = 0; // decode items per decode wave of the grid (0: 1, streams handles 2)
-  int decode_taper = 4;         // the decode sequences claimed last take 1/decode_taper of the split length (< 2: off)
+  int decode_taper = 8;         // the decode sequences claimed last take 1/decode_taper of the split length (< 2: off)
   int group() const { return hq / hkv; }
   int elem_bytes() const { return dtype == POD_ATTN_FP32 ? 4 : dtype == POD_ATTN_BF16 ? 2 : 1; }   // cache element
   int q_elem_bytes() const { return dtype == POD_ATTN_FP32 ? 4 : 2; }                           // q and out

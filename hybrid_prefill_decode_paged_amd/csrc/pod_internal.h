@@ -110,14 +110,14 @@ struct StageArgs {
   const int32_t* units_host; // append units inside the staging buffer, or null
 };
 
-// LDS of one fused workgroup: the prefill tile's double-buffered K and V pages (4 pages per
-// buffer when a (page, head) slab is at most 4 KiB, else 2) or the combine tables, whichever is
-// larger.  The kernels' geometry uses the same formula.
+// LDS of one fused workgroup: four objects (K and V staging buffers 0 and 1 of the prefill tile,
+// each also one wave's combine table), each the larger of a staged half (4 pages per buffer when
+// a (page, head) slab is at most 4 KiB, else 2) and a combine table.  The kernels' geometry uses
+// the same formula.
 constexpr int fused_lds_bytes(int elem_bytes, int d) {
   const int slab = kPage * d * elem_bytes;
-  const int prefill = 2 * 2 * (slab <= 4096 ? 4 : 2) * slab;
-  const int combine = kWaves * kCombineLdsPerWave;
-  return prefill > combine ? prefill : combine;
+  const int half = (slab <= 4096 ? 4 : 2) * slab;
+  return 4 * (half > kCombineLdsPerWave ? half : kCombineLdsPerWave);
 }
 
 // Workspace map (byte offsets), computed by the planner.

@@ -81,8 +81,12 @@ template <typename T, int D> struct Geo {
   static constexpr int kStageChunks = 2 * kTp * kCps;   // K + V chunks of one prefill tile
   static constexpr int kStageR = kStageChunks / kThreads;
   static constexpr int kPrefillLds = 2 * 2 * kTp * kSlab;              // 2 buffers x (K, V)
-  static constexpr int kCombineLds = kWaves * kCombineLdsPerWave;    // in-kernel split combine tables
-  static constexpr int kFusedLds = kPrefillLds > kCombineLds ? kPrefillLds : kCombineLds;
+  // LDS is four separate objects: K and V staging buffers 0 and 1 of the prefill tile, each also
+  // one wave's combine table.  Separate objects let the compiler's wait-count pass tell a read of
+  // one buffer from the LDS-DMA loads in flight into another, so a tile's operand reads do not
+  // wait for the next tile's staging loads.
+  static constexpr int kObjBytes = kTp * kSlab > kCombineLdsPerWave ? kTp * kSlab : kCombineLdsPerWave;
+  static constexpr int kFusedLds = 4 * kObjBytes;
   static_assert(kFusedLds == fused_lds_bytes(kBytes, D), "host-side LDS figure matches the kernels");
   static_assert(kStageChunks % kThreads == 0, "tile must split evenly over the workgroup");
   static_assert(kTp % 2 == 0, "bf16 PV pairs pages");
@@ -127,29 +131,15 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 template <typename V>
 __device__ __forceinline__ V ld_stream(const char* p) { return __builtin_nontemporal_load((const V*)p); }
 
-// Maxima of scores (finite, or -inf where masked) without the NaN-quieting the compiler puts
-// around fmaxf: it emits v_max_f32 x, x on every operand it cannot prove canonical, and scores
-// come straight from the matrix unit or a lane swap.  Plain VALU instructions, no memory.
-__device__ __forceinline__ float max_raw(float a, float b) {
-  float r;
-  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
-__device__ __forceinline__ float max3_raw(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-
 // Reductions over lanes l, l^16, l^32, l^48 with the gfx950 lane-swap instructions (VALU, no
 // LDS round trip): v_permlane16_swap applied to (v, v) hands every lane the values of lanes
 // l&~16 and l|16, i.e. its own and its partner's, in the same order on both partners, so the
 // results are bit-identical across the four lanes.
 __device__ __forceinline__ float max_over_groups(float v) {
   auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = max_raw(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
   auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return max_raw(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float sum_over_groups(float v) {
   auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -252,6 +242,23 @@ __device__ __forceinline__ int find_desc(CPTR(int32_t) descs, int n, int field, 
 
 __device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+// The four LDS objects of a kernel (see Geo::kObjBytes): K and V staging buffers 0 and 1 of the
+// prefill tile, and, for the decode role and the split merge, one combine table per wave.  The
+// tile selects a buffer by a compile-time parity (its key loop is unrolled by two), so every
+// access names one object.
+struct Stage {
+  char* k0;
+  char* k1;
+  char* v0;
+  char* v1;
+  __device__ __forceinline__ float* table(int w) const {
+    return (float*)(w == 0 ? k0 : w == 1 ? k1 : w == 2 ? v0 : v1);
+  }
+};
+template <int PAR> __device__ __forceinline__ char* kbuf_of(const Stage& B) { return PAR ? B.k1 : B.k0; }
+template <int PAR> __device__ __forceinline__ char* vbuf_of(const Stage& B) { return PAR ? B.v1 : B.v0; }
+template <int V> using Par = std::integral_constant<int, V>;
+
 // ------------------------------------------------------------------ online-softmax update
 // Per query column (lane l holds column l%16): x = raw scores of this block, -inf where masked,
 // NV values per lane.  The running max m is kept in the log2 domain (scores times sl2 =
@@ -320,6 +327,22 @@ __device__ __forceinline__ void store_coherent4(BufRsrc r, int off, f32x4 v) {
 }
 __device__ __forceinline__ f32x4 load_coherent4(BufRsrc r, int off) {
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCachePolicyCoherent));
+}
+
+// Prefill staging: one 16-byte chunk per lane from a (page, KV head) slab straight into LDS (lane
+// i's chunk to dst + 16 i, dst wave-uniform), through a buffer resource over the slab (offsets
+// past the slab are dropped by the hardware).  The buffer form of the LDS-DMA load, not the
+// global one: the compiler's wait-count pass treats a global (flat) load that writes LDS as a
+// pending access to both memory and LDS, and then drains every LDS read in flight at each
+// operand wait of the tile.
+// The LDS address of a lane is dst + 16 * lane: the load's immediate offset would be added to the
+// LDS address as well as to the memory address, so a unit's position in the slab goes into the
+// resource's base (kUnit bytes past the slab's start) and the immediate stays 0.
+template <typename T, int D, int kUnit>
+__device__ __forceinline__ void stage_chunk(const void* pool, int page, int hkv, int head, int lane_off, char* dst) {
+  const BufRsrc r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(slab_ptr<T, D>(pool, page, hkv, head) + kUnit),
+                                                      (short)0, Geo<T, D>::kSlab - kUnit, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, lane_off, 0, 0, 0);
 }
 
 // Arrival of one split: every store of the calling wave has completed (vmcnt 0); one lane takes
@@ -703,7 +726,7 @@ __device__ void decode_wave_item(const KernelParams& P, int item, float* sw) {
 // owns columns 32w .. 32w+31 (two 16-wide blocks).  Keys advance 64 (or 32) at a time,
 // staged in LDS by all 256 threads with the next tile's global loads in flight.
 template <typename T, int D>
-__device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head, int split, char* lds) {
+__device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head, int split, const Stage& LB) {
   using Gm = Geo<T, D>;
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, q = lane >> 4;
   const int w = wave_index();
@@ -768,8 +791,8 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
       }
     }
   };
-  auto kbuf = [&](int b) { return lds + b * (2 * Gm::kTp * Gm::kSlab); };
-  auto vbuf = [&](int b) { return lds + b * (2 * Gm::kTp * Gm::kSlab) + Gm::kTp * Gm::kSlab; };
+  auto kbuf = [&](auto par) { return kbuf_of<decltype(par)::value>(LB); };
+  auto vbuf = [&](auto par) { return vbuf_of<decltype(par)::value>(LB); };
   // bf16 V rows are 32 bytes (two 16-byte halves); rows 8..15 of each 16-row block swap their
   // halves so that a wave's 8-byte reads of 16 consecutive rows spread over all LDS banks.
   // The swap is its own inverse, so LDS chunk c is loaded from source chunk vswz(c).
@@ -781,7 +804,7 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
       return c;
     }
   };
-  auto issue_tile = [&](int j, int b, int (&lim)[Gm::kTp], float (&sc)[2 * Gm::kTp]) {
+  auto issue_tile = [&](int j, auto b, int (&lim)[Gm::kTp], float (&sc)[2 * Gm::kTp]) {
     int pg[Gm::kTp];
     tile_pages(j, lim, pg, sc);
 #pragma unroll
@@ -794,13 +817,12 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
 #pragma unroll
       for (int pp = 1; pp < Gm::kTp; ++pp) page = p == pp ? pg[pp] : page;
       const int c = c0 + lane;
-      const char* src = slab_ptr<T, D>(half ? P.v : P.k, page, P.hkv, head) + (half ? vswz(c) : c) * 16;
       char* dst = (half ? vbuf(b) : kbuf(b)) + p * Gm::kSlab + c0 * 16;
-      __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+      stage_chunk<T, D, 0>(half ? P.v : P.k, page, P.hkv, head, (half ? vswz(c) : c) * 16, dst);
     }
   };
 
-  auto compute_tile = [&](int b, int j, const int (&lim)[Gm::kTp], const float (&sc)[2 * Gm::kTp]) {
+  auto compute_tile = [&](auto b, int j, const int (&lim)[Gm::kTp], const float (&sc)[2 * Gm::kTp]) {
     const int tb = kv_begin + j * Gm::kTileKeys;
     if (!wave_active || tb > pmax) return;                    // every key after every query
     bool full = tb + Gm::kTileKeys - 1 <= pmin;
@@ -914,20 +936,26 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
     }
   };
 
+  // Tile j is staged in buffer j & 1 while tile j - 1 is computed; the loop is unrolled by two so
+  // that each step names its buffers at compile time.
+  auto step = [&](auto par, int j) {
+    constexpr int PAR = decltype(par)::value;
+    if (j + 1 < n_tiles) issue_tile(j + 1, Par<1 - PAR>(), lim_nxt, sc_nxt);
+    compute_tile(par, j, lim_cur, sc_cur);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < Gm::kTp; ++p) lim_cur[p] = lim_nxt[p];
+#pragma unroll
+    for (int p = 0; p < 2 * Gm::kTp; ++p) sc_cur[p] = sc_nxt[p];
+  };
   if (n_tiles > 0) {
-    issue_tile(0, 0, lim_cur, sc_cur);
+    issue_tile(0, Par<0>(), lim_cur, sc_cur);
     __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): this wave's LDS loads landed
     __syncthreads();
-    for (int j = 0; j < n_tiles; ++j) {
-      const bool more = j + 1 < n_tiles;
-      if (more) issue_tile(j + 1, (j + 1) & 1, lim_nxt, sc_nxt);
-      compute_tile(j & 1, j, lim_cur, sc_cur);
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-      __syncthreads();
-#pragma unroll
-      for (int p = 0; p < Gm::kTp; ++p) lim_cur[p] = lim_nxt[p];
-#pragma unroll
-      for (int p = 0; p < 2 * Gm::kTp; ++p) sc_cur[p] = sc_nxt[p];
+    for (int j = 0; j < n_tiles; j += 2) {
+      step(Par<0>(), j);
+      if (j + 1 < n_tiles) step(Par<1>(), j + 1);
     }
   }
 
@@ -982,6 +1010,7 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
 // operand read is conflict-free unpermuted.  Wave w stages page w of every tile: contiguous
 // 1 KB HBM reads straight into LDS.
 constexpr float kRescaleLog2 = 8.f;   // keep a stale running max while scores exceed it by < 2^8
+constexpr float kRescaleBound = 256.f; // 2^kRescaleLog2: the largest probability the stale max allows
 
 __device__ __forceinline__ int kslot(int par, int t) { return t ^ ((((t >> 3) & 1) ^ par) << 2); }
 
@@ -1019,7 +1048,7 @@ __device__ __forceinline__ int kslot8(int par, int t) { return t ^ (par << 2); }
 // FP8 LDS units are 1 KB as well: a K unit holds 4 chunks of 16 dims (64 dims) for the page's 16
 // slots, a V unit 64 dims x 16 slots.
 template <typename T, int D>
-__device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int head, int split, char* lds) {
+__device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int head, int split, const Stage& LB) {
   constexpr bool kF8 = kIsFp8<T>;
   constexpr int kNs = D / 32;                  // QK steps of 32 dims
   constexpr int kKu = kF8 ? D / 64 : D / 32;   // K units per page
@@ -1029,6 +1058,7 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
   constexpr int kKBytes = kTp * kKu * 1024;
   constexpr int kBufBytes = kKBytes + kTp * kVg * 1024;
   static_assert(kBufBytes * 2 == Geo<T, D>::kPrefillLds, "two staged tiles fill the prefill LDS");
+  static_assert(kKBytes <= Geo<T, D>::kObjBytes && kTp * kVg * 1024 <= Geo<T, D>::kObjBytes, "a staged half fits its object");
   const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
   const int w = wave_index();
   const int G = P.group;
@@ -1092,12 +1122,12 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
   __shared__ float s_scale[2][2][kTp];
   float ks_own = 1.f, vs_own = 1.f;            // this wave's page of the tile just staged
 
-  // LDS: K buffers [2][kKBytes], then V buffers [2][kVBytes].  K(t) (tile t) lives in K buffer
-  // t&1 and is staged two tiles ahead of the QK product that reads it, V(t) in V buffer t&1 one
-  // tile ahead of its PV product, so that tile t's softmax can run beside tile t+1's QK.
-  constexpr int kVBytes = kTp * kVg * 1024;
-  auto kbuf = [&](int b) { return lds + b * kKBytes; };
-  auto vbuf = [&](int b) { return lds + 2 * kKBytes + b * kVBytes; };
+  // LDS: K buffers 0 and 1, V buffers 0 and 1, four separate objects.  K(t) (tile t) lives in K
+  // buffer t&1 and is staged two tiles ahead of the QK product that reads it, V(t) in V buffer
+  // t&1 one tile ahead of its PV product, so that tile t's softmax can run beside tile t+1's QK.
+  // Buffers are named by a compile-time parity (the loop below is unrolled by two).
+  auto kbuf = [&](auto par) { return kbuf_of<decltype(par)::value>(LB); };
+  auto vbuf = [&](auto par) { return vbuf_of<decltype(par)::value>(LB); };
 
   // Block-table entries, read one tile ahead: K and V each keep the entry of their own page of
   // the next tile they stage, so no staging waits for a scalar load, and page key counts are
@@ -1132,23 +1162,23 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
     }
   };
 
-  // K(t): this wave stages page w of tile t.
-  auto stage_k = [&](int t) {
+  // K(t): this wave stages page w of tile t into K buffer par = t & 1.
+  auto stage_k = [&](auto par, int t) {
     const int own = kpf, own_lim = own < 0 ? 0 : page_lim(t, w);
     if constexpr (kF8) ks_own = own < 0 ? 1.f : ((CPTR(float))P.k_scale)[(size_t)own * P.hkv + head];
     kpf = fetch_id(t + 1);
     if (own_lim <= 0) return;                  // absent page: nothing is read
-    const char* kp = slab_ptr<T, D>(P.k, own, P.hkv, head) + src_k;
-    char* dst = kbuf(t & 1) + w * 1024;
-#pragma unroll
-    for (int s = 0; s < kKu; ++s)
-      __builtin_amdgcn_global_load_lds((const void*)(kp + s * 1024),
-                                       (__attribute__((address_space(3))) void*)(dst + s * 4096), 16, 0, 0);
+    char* dst = kbuf(par) + w * 1024;
+    stage_chunk<T, D, 0>(P.k, own, P.hkv, head, src_k, dst);
+    if constexpr (kKu > 1) stage_chunk<T, D, 1024>(P.k, own, P.hkv, head, src_k, dst + 4096);
+    if constexpr (kKu > 2) stage_chunk<T, D, 2048>(P.k, own, P.hkv, head, src_k, dst + 8192);
+    if constexpr (kKu > 3) stage_chunk<T, D, 3072>(P.k, own, P.hkv, head, src_k, dst + 12288);
+    static_assert(kKu <= 4, "K units per page");
   };
   // V(t): key counts of the tile's pages into lim (item with an entry outside the pool: complete
   // only after the next barrier, see lims_after_barrier); this wave stages page w; returns its
   // count.
-  auto stage_v = [&](int t, int (&lim)[kTp]) -> int {
+  auto stage_v = [&](auto par, int t, int (&lim)[kTp]) -> int {
     const int own = vpf, own_lim = own < 0 ? 0 : page_lim(t, w);
 #pragma unroll
     for (int p = 0; p < kTp; ++p) lim[p] = page_lim(t, p);
@@ -1156,19 +1186,19 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
     if constexpr (kF8) vs_own = own < 0 ? 1.f : ((CPTR(float))P.v_scale)[(size_t)own * P.hkv + head];
     vpf = fetch_id(t + 1);
     if (own_lim <= 0) return 0;
-    const char* vp = slab_ptr<T, D>(P.v, own, P.hkv, head) + src_v;
-    char* dst = vbuf(t & 1) + w * 1024;
-#pragma unroll
-    for (int g = 0; g < kVg; ++g)
-      __builtin_amdgcn_global_load_lds((const void*)(vp + g * 1024),
-                                       (__attribute__((address_space(3))) void*)(dst + g * 4096), 16, 0, 0);
+    char* dst = vbuf(par) + w * 1024;
+    stage_chunk<T, D, 0>(P.v, own, P.hkv, head, src_v, dst);
+    if constexpr (kVg > 1) stage_chunk<T, D, 1024>(P.v, own, P.hkv, head, src_v, dst + 4096);
+    if constexpr (kVg > 2) stage_chunk<T, D, 2048>(P.v, own, P.hkv, head, src_v, dst + 8192);
+    if constexpr (kVg > 3) stage_chunk<T, D, 3072>(P.v, own, P.hkv, head, src_v, dst + 12288);
+    static_assert(kVg <= 4, "V units per page");
     return own_lim;
   };
   // After this wave's staging loads have landed: zero the V slots of tokens >= lim of its page
   // (all of them for an absent page), so that a zero probability never meets a NaN or stale
   // value in the PV product.  Scores of those slots are masked by select.
-  auto zero_v_tail = [&](int t, int lim_own) {
-    char* vu = vbuf(t & 1) + w * 1024;
+  auto zero_v_tail = [&](auto par, int lim_own) {
+    char* vu = vbuf(par) + w * 1024;
 #pragma unroll
     for (int g = 0; g < kVg; ++g) {
       u32x4* cp = (u32x4*)(vu + g * 4096 + lane * 16);
@@ -1232,50 +1262,77 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
       }
     }
   };
-  // Probabilities of a scored tile.  The running max only moves when a score exceeds it by more
-  // than 2^kRescaleLog2: any reference value gives the same softmax as long as numerator and
-  // denominator share it, and the bound keeps every probability <= 2^kRescaleLog2.  Returns
-  // (per lane) whether the running output must be rescaled by alpha before the PV product.
-  // FP8: the product's operand carries the V scale of each key's page, so it cannot give the
-  // row sums; those are summed from the fp32 probabilities instead (xsum: this lane's keys).
-  auto softmax = [&](Scores& S, u32x4 (&pb)[2][2], const float (&vs)[kTp], float (&alpha)[2],
-                     float (&xsum)[2]) -> bool {
-    bool grow_any = false;
+  // Probabilities of a scored tile.  The running max m_run is a reference value that only moves
+  // when a score exceeds it by more than 2^kRescaleLog2: any reference gives the same softmax as
+  // long as numerator and denominator share it, and the bound keeps every probability <=
+  // 2^kRescaleLog2.  So the common case takes the exponentials against the current reference
+  // with no reduction first, and they issue beside the next tile's QK products; `probs` returns,
+  // wave-uniformly, whether some column must move its reference (a probability above the bound,
+  // or a column with none yet), and then `settle` takes the tile's per-column maxima, moves the
+  // references that grew by more than the bound, rescales those columns' running output and sum by
+  // 2^(m_old - m_new), and recomputes the probabilities.
+  typedef float Probs[2][16];                  // [nb][key slot k = 8pp + 4blk + i]
+  auto sval = [&](const Scores& S, int nb, int k) { return S[nb][k >> 3][(k >> 2) & 1][k & 3]; };
+  auto exps = [&](const Scores& S, int nb, Probs& x) {
+    const float mu = m_run[nb] == kNegInf ? 0.f : m_run[nb];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) x[nb][k] = exp2_fast(__builtin_fmaf(sval(S, nb, k), sl2, -mu));
+  };
+  auto probs = [&](const Scores& S, Probs& x) -> bool {
+    bool slow = false;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      auto sv = [&](int k) { return S[nb][k >> 3][(k >> 2) & 1][k & 3]; };
-      float m = max3_raw(sv(0), sv(1), sv(2));
+      exps(S, nb, x);
+      float xm = fmaxf(x[nb][0], x[nb][1]);
 #pragma unroll
-      for (int k = 3; k + 1 < 16; k += 2) m = max3_raw(m, sv(k), sv(k + 1));
-      m = max_raw(m, sv(15));
+      for (int k = 2; k < 16; ++k) xm = fmaxf(xm, x[nb][k]);
+      slow = slow | (xm > kRescaleBound) | (m_run[nb] == kNegInf);
+    }
+    return __any(slow);
+  };
+  auto settle = [&](const Scores& S, Probs& x) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      float m = fmaxf(sval(S, nb, 0), sval(S, nb, 1));
+#pragma unroll
+      for (int k = 2; k < 16; ++k) m = fmaxf(m, sval(S, nb, k));
       const float mx = max_over_groups(m) * sl2;
       const bool grow = mx > m_run[nb] + kRescaleLog2;
-      alpha[nb] = grow ? exp2_fast(m_run[nb] - mx) : 1.f;
+      const float alpha = grow ? exp2_fast(m_run[nb] - mx) : 1.f;
       m_run[nb] = grow ? mx : m_run[nb];
-      grow_any = grow_any | grow;
-      const float m_use = m_run[nb] == kNegInf ? 0.f : m_run[nb];
-      float x[16];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) x[k] = exp2_fast(__builtin_fmaf(S[nb][k >> 3][(k >> 2) & 1][k & 3], sl2, -m_use));
+      for (int b = 0; b < kDb; ++b) o[nb][b] *= alpha;
+      if constexpr (kF8) lrow[nb] *= alpha;
+      else lsum[nb] *= alpha;
+      exps(S, nb, x);
+    }
+  };
+  // Product operands of the probabilities: bf16 pairs, keys 8q .. 8q+7 of a page pair per lane;
+  // with an FP8 cache each page's V scale multiplies its probabilities here, and the row sums are
+  // taken from the unscaled fp32 probabilities (xsum: this lane's keys).
+  auto pack = [&](const Probs& x, const float (&vs)[kTp], u32x4 (&pb)[2][2], float (&xsum)[2]) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp) {
         if constexpr (kF8) {                   // keys 8q .. 8q+7 of the pair lie in page 2pp + q/2
           const float c = (q >> 1) ? vs[2 * pp + 1] : vs[2 * pp];
-          pb[nb][pp] = u32x4{pack_bf16(x[8 * pp + 0] * c, x[8 * pp + 1] * c), pack_bf16(x[8 * pp + 2] * c, x[8 * pp + 3] * c),
-                             pack_bf16(x[8 * pp + 4] * c, x[8 * pp + 5] * c), pack_bf16(x[8 * pp + 6] * c, x[8 * pp + 7] * c)};
+          const float* xp = &x[nb][8 * pp];
+          pb[nb][pp] = u32x4{pack_bf16(xp[0] * c, xp[1] * c), pack_bf16(xp[2] * c, xp[3] * c),
+                             pack_bf16(xp[4] * c, xp[5] * c), pack_bf16(xp[6] * c, xp[7] * c)};
         } else {
-          pb[nb][pp] = u32x4{pack_bf16(x[8 * pp + 0], x[8 * pp + 1]), pack_bf16(x[8 * pp + 2], x[8 * pp + 3]),
-                             pack_bf16(x[8 * pp + 4], x[8 * pp + 5]), pack_bf16(x[8 * pp + 6], x[8 * pp + 7])};
+          const float* xp = &x[nb][8 * pp];
+          pb[nb][pp] = u32x4{pack_bf16(xp[0], xp[1]), pack_bf16(xp[2], xp[3]), pack_bf16(xp[4], xp[5]),
+                             pack_bf16(xp[6], xp[7])};
         }
       }
       if constexpr (kF8) {
         float t = 0.f;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) t += x[k];
+        for (int k = 0; k < 16; ++k) t += x[nb][k];
         xsum[nb] = t;
       }
     }
-    return grow_any;
   };
   // PV of one staged tile: V^T operands two blocks ahead of the products that use them; for the
   // bf16 cache the row sums come from the same P^T against a ones operand.
@@ -1323,12 +1380,13 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
   // Iteration j: stage K(j+2) and V(j+1); QK(j+1) beside softmax(j) (one basic block, so the
   // matrix and vector units overlap); PV(j).  The product for tile j+1 past the last tile reads
   // a stale buffer and is discarded.
-  auto iteration = [&](int j, Scores& Sc, Scores& Sn) {
+  auto iteration = [&](auto par, int j, Scores& Sc, Scores& Sn) {
+    constexpr int PAR = decltype(par)::value;     // j & 1
     const int tb = kv_begin + j * kTileKeys;
     const bool more1 = j + 1 < n_tiles;
-    if (j + 2 < n_tiles) stage_k(j + 2);
+    if (j + 2 < n_tiles) stage_k(par, j + 2);
     int own_nv = kPage;
-    if (more1) own_nv = stage_v(j + 1, lim_nxt);
+    if (more1) own_nv = stage_v(Par<1 - PAR>(), j + 1, lim_nxt);
     if (wave_active && tb <= pmax) {          // else every key follows every query of the wave
       const bool full = (tb + kTileKeys - 1 <= pmin) & (lim_cur[0] == kPage) & (lim_cur[1] == kPage) &
                         (lim_cur[2] == kPage) & (lim_cur[3] == kPage);
@@ -1336,28 +1394,22 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
       float ks[kTp], vs[kTp];
       read_scales(0, j + 1, ks);
       read_scales(1, j, vs);
-      qk(kbuf((j + 1) & 1), Sn, ks);
+      qk(kbuf(Par<1 - PAR>()), Sn, ks);
+      Probs x;
+      if (probs(Sc, x)) settle(Sc, x);
       u32x4 pb[2][2];
-      float alpha[2], xsum[2];
-      if (__any(softmax(Sc, pb, vs, alpha, xsum))) {
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-          for (int b = 0; b < kDb; ++b) o[nb][b] *= alpha[nb];
-          if constexpr (kF8) lrow[nb] *= alpha[nb];
-          else lsum[nb] *= alpha[nb];
-        }
-      }
+      float xsum[2];
+      pack(x, vs, pb, xsum);
       if constexpr (kF8) {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) lrow[nb] += xsum[nb];
       }
-      pv(vbuf(j & 1), pb);
+      pv(vbuf(par), pb);
     }
     if (j + 2 < n_tiles) publish_k(j + 2);
     if (more1) publish_v(j + 1);
     __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): this wave's staging loads landed
-    if (own_nv < kPage) zero_v_tail(j + 1, own_nv);
+    if (own_nv < kPage) zero_v_tail(Par<1 - PAR>(), own_nv);
     __syncthreads();
 #pragma unroll
     for (int p = 0; p < kTp; ++p) lim_cur[p] = lim_nxt[p];
@@ -1367,25 +1419,25 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
   if (n_tiles > 0) {
     Scores SA, SB;
     kpf = vpf = fetch_id(0);
-    stage_k(0);
+    stage_k(Par<0>(), 0);
     publish_k(0);
     if (n_tiles > 1) {
-      stage_k(1);
+      stage_k(Par<1>(), 1);
       publish_k(1);
     }
-    const int own0 = stage_v(0, lim_cur);
+    const int own0 = stage_v(Par<0>(), 0, lim_cur);
     publish_v(0);
     __builtin_amdgcn_s_waitcnt(0x0F70);
-    if (own0 < kPage) zero_v_tail(0, own0);
+    if (own0 < kPage) zero_v_tail(Par<0>(), own0);
     __syncthreads();
     lims_after_barrier(0, lim_cur);
     float ks0[kTp];
     read_scales(0, 0, ks0);
-    if (wave_active && kv_begin <= pmax) qk(kbuf(0), SA, ks0);
+    if (wave_active && kv_begin <= pmax) qk(kbuf(Par<0>()), SA, ks0);
     __syncthreads();                           // K buffer 0 is restaged by the first iteration
     for (int j = 0; j < n_tiles; j += 2) {
-      iteration(j, SA, SB);
-      if (j + 1 < n_tiles) iteration(j + 1, SB, SA);
+      iteration(Par<0>(), j, SA, SB);
+      if (j + 1 < n_tiles) iteration(Par<1>(), j + 1, SB, SA);
     }
   }
 
@@ -1426,12 +1478,12 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
 // merged in-kernel by the last-arriving split when inline_combine is set (fused mode; partials
 // written through with 16-byte device-coherent stores), else by the combine kernel.
 template <typename T, int D>
-__device__ void run_prefill_item(const KernelParams& P, int item, char* lds) {
+__device__ void run_prefill_item(const KernelParams& P, int item, const Stage& LB) {
   CPTR(int32_t) e = (CPTR(int32_t))P.pitems + kPItemHeader + 2 * (size_t)item;
   CPTR(int32_t) dsc = (CPTR(int32_t))P.pdesc + (size_t)e[0] * kDescInts;
   const int split = e[1] >> 16, head = e[1] & 0xFFFF;
-  if constexpr (sizeof(T) == 2 || kIsFp8<T>) prefill_item_tile<T, D>(P, dsc, head, split, lds);
-  else prefill_item<T, D>(P, dsc, head, split, lds);
+  if constexpr (sizeof(T) == 2 || kIsFp8<T>) prefill_item_tile<T, D>(P, dsc, head, split, LB);
+  else prefill_item<T, D>(P, dsc, head, split, LB);
   const int ns = dsc[kDNSplit];
   if (ns > 1 && P.inline_combine) {
     // Each wave's partial stores (write-through) complete before the barrier; thread 0 takes the
@@ -1443,7 +1495,7 @@ __device__ void run_prefill_item(const KernelParams& P, int item, char* lds) {
     if (threadIdx.x == 0) s_last = atomicAdd(P.tickets + dsc[kDGroupBegin] + head, 1) == ns - 1;
     __syncthreads();
     if (s_last) {
-      float* sw = (float*)(lds + wave_index() * kCombineLdsPerWave);
+      float* sw = LB.table(wave_index());
       for (int c0 = 16 * wave_index(); c0 < dsc[kDNcols]; c0 += 16 * kWaves) combine_block_wave<T, D>(P, dsc, head, c0, sw);
     }
   }
@@ -1512,7 +1564,11 @@ __device__ __forceinline__ int claim_prefill(const KernelParams& P, int xcc) {
 // ends when both are drained.
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 2) void pod_fused_kernel(KernelParams P) {
-  __shared__ __attribute__((aligned(16))) char lds[Geo<T, D>::kFusedLds];
+  __shared__ __attribute__((aligned(16))) char lds_k0[Geo<T, D>::kObjBytes];
+  __shared__ __attribute__((aligned(16))) char lds_k1[Geo<T, D>::kObjBytes];
+  __shared__ __attribute__((aligned(16))) char lds_v0[Geo<T, D>::kObjBytes];
+  __shared__ __attribute__((aligned(16))) char lds_v1[Geo<T, D>::kObjBytes];
+  const Stage LB{lds_k0, lds_k1, lds_v0, lds_v1};
   __shared__ int s_role, s_item;
   const int tid = threadIdx.x;
   const int cu = cu_slot();
@@ -1549,7 +1605,7 @@ __global__ __launch_bounds__(kThreads, 2) void pod_fused_kernel(KernelParams P) 
     if (role == 1) {
       // The workgroup claims 4 consecutive items (adjacent KV heads of one key range) and each
       // wave streams one of them; the next block is claimed once the current one is done.
-      float* sw = (float*)(lds + wave_index() * kCombineLdsPerWave);
+      float* sw = LB.table(wave_index());
       for (;;) {
         if (tid == 0) s_item = atomicAdd(P.ctrl + kCQueueDecode, kWaves);
         __syncthreads();
@@ -1570,7 +1626,7 @@ __global__ __launch_bounds__(kThreads, 2) void pod_fused_kernel(KernelParams P) 
     while (item < P.n_pf_items) {
       if (tid == 0) note_claim(P, 0, item, cu);
       const uint32_t t0 = trace_start(P);
-      run_prefill_item<T, D>(P, item, lds);   // ends with a barrier
+      run_prefill_item<T, D>(P, item, LB);   // ends with a barrier
       if (tid == 0) trace_item(P, 0, item, t0, cu);
       if (tid == 0) s_item = claim_prefill(P, xcc);   // claim once idle
       __syncthreads();
@@ -1587,7 +1643,11 @@ __global__ __launch_bounds__(kThreads, 2) void pod_fused_kernel(KernelParams P) 
 
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 2) void pod_prefill_kernel(KernelParams P) {
-  __shared__ __attribute__((aligned(16))) char lds[Geo<T, D>::kPrefillLds];
+  __shared__ __attribute__((aligned(16))) char lds_k0[Geo<T, D>::kObjBytes];
+  __shared__ __attribute__((aligned(16))) char lds_k1[Geo<T, D>::kObjBytes];
+  __shared__ __attribute__((aligned(16))) char lds_v0[Geo<T, D>::kObjBytes];
+  __shared__ __attribute__((aligned(16))) char lds_v1[Geo<T, D>::kObjBytes];
+  const Stage LB{lds_k0, lds_k1, lds_v0, lds_v1};
   __shared__ int s_item;
   // one item per workgroup (the grid has n_pf_items workgroups), taken from this die's queue
   const int cu = cu_slot();
@@ -1599,7 +1659,7 @@ __global__ __launch_bounds__(kThreads, 2) void pod_prefill_kernel(KernelParams P
   const int item = s_item;
   if (item >= P.n_pf_items) return;
   const uint32_t t0 = trace_start(P);
-  run_prefill_item<T, D>(P, item, lds);
+  run_prefill_item<T, D>(P, item, LB);
   if (threadIdx.x == 0) trace_item(P, 0, item, t0, cu);
 }
 

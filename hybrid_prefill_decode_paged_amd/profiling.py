@@ -38,7 +38,7 @@ def kernel_source_hash() -> str:
 
 
 def _counter_csv(d: str) -> str:
-    files = glob.glob(os.path.join(d, "*counter_collection.csv"))
+    files = sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True))
     if not files:
         raise FileNotFoundError(f"no counter_collection.csv under {d}")
     return files[0]
