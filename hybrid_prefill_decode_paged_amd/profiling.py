@@ -27,6 +27,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ("csrc/pod_kernels.hip", "csrc/pod_internal.h", "csrc/plan.cpp", "csrc/pod_api.cpp")
 COPY_BYTES = 1 << 30
+MI355X_XCDS = 8
+MI355X_SIMDS = 256 * 4
 
 
 def kernel_source_hash() -> str:
@@ -91,11 +93,21 @@ def pmc_summary(dirs, title: str, command: str) -> str:
                 continue
             rows.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     counters = sorted({c for v in rows.values() for c in v})
+    busy = "SQ_VALU_MFMA_BUSY_CYCLES" in counters and "GRBM_GUI_ACTIVE" in counters
+    extra = ["MFMA busy"] if busy else []
     out = [f"# {title}", "", f"Command: `{command}`", "",
-           "Per-dispatch mean of each counter (summed over the device by rocprofv3), dispatches in brackets.", "",
-           "| kernel | " + " | ".join(counters) + " |", "|---" * (len(counters) + 1) + "|"]
+           "Per-dispatch mean of each counter (summed over the device by rocprofv3), dispatches in brackets."]
+    if busy:
+        out += ["MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDs x SIMDs): the share of the "
+                f"kernel's span in which a SIMD's matrix core is busy, averaged over the {MI355X_SIMDS} SIMDs "
+                f"(GRBM_GUI_ACTIVE is summed over the {MI355X_XCDS} XCDs)."]
+    out += ["", "| kernel | " + " | ".join(counters + extra) + " |", "|---" * (len(counters) + len(extra) + 1) + "|"]
     for name, d in rows.items():
         cells = [f"{statistics.mean(d[c]):.4g} ({len(d[c])})" if c in d else "" for c in counters]
+        if busy:
+            span = statistics.mean(d["GRBM_GUI_ACTIVE"]) / MI355X_XCDS * MI355X_SIMDS if "GRBM_GUI_ACTIVE" in d else 0
+            mf = statistics.mean(d["SQ_VALU_MFMA_BUSY_CYCLES"]) if "SQ_VALU_MFMA_BUSY_CYCLES" in d else None
+            cells.append(f"{100 * mf / span:.1f}%" if span and mf is not None else "")
         out.append(f"| {name[:70]} | " + " | ".join(cells) + " |")
     return "\n".join(out) + "\n"
 
