@@ -336,13 +336,16 @@ __device__ __forceinline__ f32x4 load_coherent4(BufRsrc r, int off) {
 // pending access to both memory and LDS, and then drains every LDS read in flight at each
 // operand wait of the tile.
 // The LDS address of a lane is dst + 16 * lane: the load's immediate offset would be added to the
-// LDS address as well as to the memory address, so a unit's position in the slab goes into the
-// resource's base (kUnit bytes past the slab's start) and the immediate stays 0.
-template <typename T, int D, int kUnit>
-__device__ __forceinline__ void stage_chunk(const void* pool, int page, int hkv, int head, int lane_off, char* dst) {
-  const BufRsrc r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(slab_ptr<T, D>(pool, page, hkv, head) + kUnit),
-                                                      (short)0, Geo<T, D>::kSlab - kUnit, 0x00020000);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, lane_off, 0, 0, 0);
+// LDS address as well as to the memory address, so it stays 0; the scalar offset moves only the
+// memory address, and carries a unit's position in the slab, so that one resource serves every
+// unit of a slab.
+template <typename T, int D>
+__device__ __forceinline__ BufRsrc slab_rsrc(const void* pool, int page, int hkv, int head) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(slab_ptr<T, D>(pool, page, hkv, head)), (short)0,
+                                           Geo<T, D>::kSlab, 0x00020000);
+}
+__device__ __forceinline__ void stage_chunk(BufRsrc r, int unit_off, int lane_off, char* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, lane_off, unit_off, 0, 0);
 }
 
 // Arrival of one split: every store of the calling wave has completed (vmcnt 0); one lane takes
@@ -818,7 +821,7 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
       for (int pp = 1; pp < Gm::kTp; ++pp) page = p == pp ? pg[pp] : page;
       const int c = c0 + lane;
       char* dst = (half ? vbuf(b) : kbuf(b)) + p * Gm::kSlab + c0 * 16;
-      stage_chunk<T, D, 0>(half ? P.v : P.k, page, P.hkv, head, (half ? vswz(c) : c) * 16, dst);
+      stage_chunk(slab_rsrc<T, D>(half ? P.v : P.k, page, P.hkv, head), 0, (half ? vswz(c) : c) * 16, dst);
     }
   };
 
@@ -1148,10 +1151,12 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
   auto page_lim = [&](int t, int p) {          // keys of page p of tile t (0: absent)
     return min(kPage, max(0, kv_end - (((kv_begin + t * kTileKeys) >> 4) + p) * kPage));
   };
-  auto fetch_id = [&](int t) {                 // this wave's entry of tile t
-    const int id = btr[page_lim(t, w) > 0 ? ((kv_begin + t * kTileKeys) >> 4) + w : pfirst];
-    return clean || (unsigned)id < (unsigned)P.num_pages ? id : -1;
+  auto fetch_id = [&](int t) {                 // this wave's entry of tile t, as the table holds it
+    return btr[page_lim(t, w) > 0 ? ((kv_begin + t * kTileKeys) >> 4) + w : pfirst];
   };
+  // An entry is checked only when its page is staged, a tile after its load was issued, so that
+  // no stage waits for the table read.
+  auto usable = [&](int id) { return clean || (unsigned)id < (unsigned)P.num_pages ? id : -1; };
   int kpf, vpf;                                // entries of the next K / V tile to stage
   // Item with an entry outside the pool: tile t's key counts as its page owners published them
   // in stage_v (call after the barrier that follows).
@@ -1164,22 +1169,23 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
 
   // K(t): this wave stages page w of tile t into K buffer par = t & 1.
   auto stage_k = [&](auto par, int t) {
-    const int own = kpf, own_lim = own < 0 ? 0 : page_lim(t, w);
+    const int own = usable(kpf), own_lim = own < 0 ? 0 : page_lim(t, w);
     if constexpr (kF8) ks_own = own < 0 ? 1.f : ((CPTR(float))P.k_scale)[(size_t)own * P.hkv + head];
     kpf = fetch_id(t + 1);
     if (own_lim <= 0) return;                  // absent page: nothing is read
     char* dst = kbuf(par) + w * 1024;
-    stage_chunk<T, D, 0>(P.k, own, P.hkv, head, src_k, dst);
-    if constexpr (kKu > 1) stage_chunk<T, D, 1024>(P.k, own, P.hkv, head, src_k, dst + 4096);
-    if constexpr (kKu > 2) stage_chunk<T, D, 2048>(P.k, own, P.hkv, head, src_k, dst + 8192);
-    if constexpr (kKu > 3) stage_chunk<T, D, 3072>(P.k, own, P.hkv, head, src_k, dst + 12288);
+    const BufRsrc r = slab_rsrc<T, D>(P.k, own, P.hkv, head);
+    stage_chunk(r, 0, src_k, dst);
+    if constexpr (kKu > 1) stage_chunk(r, 1024, src_k, dst + 4096);
+    if constexpr (kKu > 2) stage_chunk(r, 2048, src_k, dst + 8192);
+    if constexpr (kKu > 3) stage_chunk(r, 3072, src_k, dst + 12288);
     static_assert(kKu <= 4, "K units per page");
   };
   // V(t): key counts of the tile's pages into lim (item with an entry outside the pool: complete
   // only after the next barrier, see lims_after_barrier); this wave stages page w; returns its
   // count.
   auto stage_v = [&](auto par, int t, int (&lim)[kTp]) -> int {
-    const int own = vpf, own_lim = own < 0 ? 0 : page_lim(t, w);
+    const int own = usable(vpf), own_lim = own < 0 ? 0 : page_lim(t, w);
 #pragma unroll
     for (int p = 0; p < kTp; ++p) lim[p] = page_lim(t, p);
     if (!clean && lane == 0) s_lims[t & 1][w] = own_lim;
@@ -1187,10 +1193,11 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
     vpf = fetch_id(t + 1);
     if (own_lim <= 0) return 0;
     char* dst = vbuf(par) + w * 1024;
-    stage_chunk<T, D, 0>(P.v, own, P.hkv, head, src_v, dst);
-    if constexpr (kVg > 1) stage_chunk<T, D, 1024>(P.v, own, P.hkv, head, src_v, dst + 4096);
-    if constexpr (kVg > 2) stage_chunk<T, D, 2048>(P.v, own, P.hkv, head, src_v, dst + 8192);
-    if constexpr (kVg > 3) stage_chunk<T, D, 3072>(P.v, own, P.hkv, head, src_v, dst + 12288);
+    const BufRsrc r = slab_rsrc<T, D>(P.v, own, P.hkv, head);
+    stage_chunk(r, 0, src_v, dst);
+    if constexpr (kVg > 1) stage_chunk(r, 1024, src_v, dst + 4096);
+    if constexpr (kVg > 2) stage_chunk(r, 2048, src_v, dst + 8192);
+    if constexpr (kVg > 3) stage_chunk(r, 3072, src_v, dst + 12288);
     static_assert(kVg <= 4, "V units per page");
     return own_lim;
   };
