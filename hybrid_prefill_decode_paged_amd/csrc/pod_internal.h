@@ -13,7 +13,6 @@ constexpr int kTileCols = 128;       // (query, head) columns of one prefill til
 constexpr int kMaxGroup = 16;        // decode-path columns: one 16-wide MFMA block
 constexpr int kExtendMaxQ = 16;      // default: prefill chunks of at most this many rows run on the decode path
 constexpr int kPrefillKvTile = 64;   // keys per prefill inner iteration (4 pages)
-constexpr int kDecodeStep = 32;      // keys per decode wave step (2 pages)
 constexpr int kCuSlots = 1024;       // hashed (XCC, SE, CU) slots for per-CU scheduler state
 constexpr int kXcds = 8;             // accelerator complex dies (one L2 each)
 constexpr int kPItemHeader = 16;     // prefill item table header: queue x = items [hdr[x], hdr[x+1])

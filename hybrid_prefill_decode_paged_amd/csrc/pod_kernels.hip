@@ -555,7 +555,12 @@ __device__ void decode_wave_item(const KernelParams& P, int item, float* sw) {
   const int st = dsc[kDSplitTok];
   const int kv_begin = split * st;
   const int kv_end = min(kv_len, kv_begin + st);
-  const int n_steps = (kv_end - kv_begin + kDecodeStep - 1) / kDecodeStep;
+  // Pages per step: 2 (the bf16 output product takes a page pair); 1 for an fp32 cache with
+  // 128-dim heads, whose double-buffered step registers would otherwise exceed the budget.
+  constexpr int kSp = (Gm::kBytes == 4 && D == 128) ? 1 : 2;
+  constexpr int kStepTok = kSp * kPage;
+  static_assert(kSp == 2 || Gm::kBytes == 4, "only the fp32 product takes single pages");
+  const int n_steps = (kv_end - kv_begin + kStepTok - 1) / kStepTok;
   CPTR(int32_t) btr = (CPTR(int32_t))P.bt + (size_t)seq * P.bt_stride;
   const float sl2 = P.scale_log2;
 
@@ -578,15 +583,16 @@ __device__ void decode_wave_item(const KernelParams& P, int item, float* sw) {
   float m_run = kNegInf, l_run = 0.f;
 
   typedef typename Gm::KReg KR;
-  KR kA[2][Gm::kNs], kB[2][Gm::kNs];
-  VT vA[2][Gm::kDb], vB[2][Gm::kDb];
-  int limA[2], limB[2];
-  float scA[4], scB[4];                        // Fp8: K scales of the step's two pages, then V scales
+  KR kA[kSp][Gm::kNs], kB[kSp][Gm::kNs];
+  VT vA[kSp][Gm::kDb], vB[kSp][Gm::kDb];
+  int limA[kSp], limB[kSp];
+  float scA[2 * kSp], scB[2 * kSp];            // Fp8: K scales of the step's pages, then V scales
 
-  auto load_step = [&](int step, KR (&kr)[2][Gm::kNs], VT (&vr)[2][Gm::kDb], int (&lim)[2], float (&sc)[4]) {
-    const int tok0 = kv_begin + step * kDecodeStep;
+  auto load_step = [&](int step, KR (&kr)[kSp][Gm::kNs], VT (&vr)[kSp][Gm::kDb], int (&lim)[kSp],
+                       float (&sc)[2 * kSp]) {
+    const int tok0 = kv_begin + step * kStepTok;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
+    for (int p = 0; p < kSp; ++p) {
       const int pi = (tok0 >> 4) + p;
       int l = min(kPage, kv_end - pi * kPage);
       const int pg = __builtin_amdgcn_readfirstlane(page_or_empty(btr, pi, l, P.num_pages, P.ctrl + kCStatus));
@@ -598,7 +604,7 @@ __device__ void decode_wave_item(const KernelParams& P, int item, float* sw) {
 #pragma unroll
         for (int s = 0; s < Gm::kNs; ++s) kr[p][s] = ld_stream<u32x2>(kp + k_chunk_off(2 * s + (q >> 1), n) + 8 * (q & 1));
         sc[p] = ((CPTR(float))P.k_scale)[(size_t)pg * P.hkv + head];
-        sc[2 + p] = ((CPTR(float))P.v_scale)[(size_t)pg * P.hkv + head];
+        sc[kSp + p] = ((CPTR(float))P.v_scale)[(size_t)pg * P.hkv + head];
       } else {
 #pragma unroll
         for (int s = 0; s < Gm::kNs; ++s) kr[p][s] = ld_stream<u32x4>(kp + k_chunk_off(4 * s + q, n));
@@ -608,31 +614,36 @@ __device__ void decode_wave_item(const KernelParams& P, int item, float* sw) {
     }
   };
 
-  auto compute_step = [&](KR (&kr)[2][Gm::kNs], VT (&vr)[2][Gm::kDb], const int (&lim)[2], const float (&sc)[4], int tok0) {
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  auto compute_step = [&](KR (&kr)[kSp][Gm::kNs], VT (&vr)[kSp][Gm::kDb], const int (&lim)[kSp],
+                          const float (&sc)[2 * kSp], int tok0) {
+    f32x4 sp[kSp];
+#pragma unroll
+    for (int p = 0; p < kSp; ++p) sp[p] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < Gm::kNs; ++s) {
-      s0 = mfma_chunk(k_operand(kr[0][s]), qop[s], s0, T());
-      s1 = mfma_chunk(k_operand(kr[1][s]), qop[s], s1, T());
+#pragma unroll
+      for (int p = 0; p < kSp; ++p) sp[p] = mfma_chunk(k_operand(kr[p][s]), qop[s], sp[p], T());
     }
     if constexpr (kIsFp8<T>) {                 // the K scale of each page multiplies its scores
-      s0 *= sc[0];
-      s1 *= sc[1];
-    }
-    float x[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = (4 * q + i < lim[0]) ? s0[i] : kNegInf;
-      x[4 + i] = (4 * q + i < lim[1]) ? s1[i] : kNegInf;
+      for (int p = 0; p < kSp; ++p) sp[p] *= sc[p];
     }
-    if (n_q > 1 && tok0 + kDecodeStep - 1 > q_pos) {   // extend rows: causal limit per column
+    float x[4 * kSp];                          // key slot 4p + i: token 4q + i of page p
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (tok0 + 4 * q + i > cmax) x[i] = kNegInf;
-        if (tok0 + kPage + 4 * q + i > cmax) x[4 + i] = kNegInf;
+    for (int p = 0; p < kSp; ++p) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[4 * p + i] = (4 * q + i < lim[p]) ? sp[p][i] : kNegInf;
+    }
+    if (n_q > 1 && tok0 + kStepTok - 1 > q_pos) {   // extend rows: causal limit per column
+#pragma unroll
+      for (int p = 0; p < kSp; ++p) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (tok0 + kPage * p + 4 * q + i > cmax) x[4 * p + i] = kNegInf;
+        }
       }
     }
-    rescale(o, softmax_update<8>(x, sl2, m_run, l_run));
+    rescale(o, softmax_update<4 * kSp>(x, sl2, m_run, l_run));
     if constexpr (kIsFp8<T>) {
       // V codes -> bf16; the V scale of each page multiplies its probabilities in the product
       // only (the row sum already has them unscaled)
@@ -649,29 +660,28 @@ __device__ void decode_wave_item(const KernelParams& P, int item, float* sw) {
           v8[1][b] = mask_vop(v8[1][b], q, lim[1]);
         }
       }
-      const u32x4 pb = {pack_bf16(x[0] * sc[2], x[1] * sc[2]), pack_bf16(x[2] * sc[2], x[3] * sc[2]),
-                        pack_bf16(x[4] * sc[3], x[5] * sc[3]), pack_bf16(x[6] * sc[3], x[7] * sc[3])};
+      const u32x4 pb = {pack_bf16(x[0] * sc[kSp], x[1] * sc[kSp]), pack_bf16(x[2] * sc[kSp], x[3] * sc[kSp]),
+                        pack_bf16(x[4] * sc[kSp + 1], x[5] * sc[kSp + 1]), pack_bf16(x[6] * sc[kSp + 1], x[7] * sc[kSp + 1])};
 #pragma unroll
       for (int b = 0; b < Gm::kDb; ++b) o[b] = pv_pair(v8[0][b], v8[1][b], pb, o[b]);
     } else {
-      if (lim[0] < kPage || lim[1] < kPage) {
 #pragma unroll
-        for (int b = 0; b < Gm::kDb; ++b) {
-          vr[0][b] = mask_vop(vr[0][b], q, lim[0]);
-          vr[1][b] = mask_vop(vr[1][b], q, lim[1]);
+      for (int p = 0; p < kSp; ++p) {
+        if (lim[p] < kPage) {
+#pragma unroll
+          for (int b = 0; b < Gm::kDb; ++b) vr[p][b] = mask_vop(vr[p][b], q, lim[p]);
         }
       }
       if constexpr (Gm::kBytes == 2) {
-        const u32x4 pb = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]),
-                          pack_bf16(x[6], x[7])};
+        const u32x4 pb = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])};
 #pragma unroll
         for (int b = 0; b < Gm::kDb; ++b) o[b] = pv_pair(vr[0][b], vr[1][b], pb, o[b]);
       } else {
-        const f32x4 p0 = {x[0], x[1], x[2], x[3]}, p1 = {x[4], x[5], x[6], x[7]};
 #pragma unroll
-        for (int b = 0; b < Gm::kDb; ++b) {
-          o[b] = pv_page_f32(vr[0][b], p0, o[b]);
-          o[b] = pv_page_f32(vr[1][b], p1, o[b]);
+        for (int p = 0; p < kSp; ++p) {
+          const f32x4 pw = {x[4 * p], x[4 * p + 1], x[4 * p + 2], x[4 * p + 3]};
+#pragma unroll
+          for (int b = 0; b < Gm::kDb; ++b) o[b] = pv_page_f32(vr[p][b], pw, o[b]);
         }
       }
     }
@@ -684,12 +694,12 @@ __device__ void decode_wave_item(const KernelParams& P, int item, float* sw) {
   for (;;) {
     int nxt = step + 1;
     load_step(nxt < n_steps ? nxt : step, kB, vB, limB, scB);
-    compute_step(kA, vA, limA, scA, kv_begin + step * kDecodeStep);
+    compute_step(kA, vA, limA, scA, kv_begin + step * kStepTok);
     if (nxt >= n_steps) break;
     step = nxt;
     nxt = step + 1;
     load_step(nxt < n_steps ? nxt : step, kA, vA, limA, scA);
-    compute_step(kB, vB, limB, scB, kv_begin + step * kDecodeStep);
+    compute_step(kB, vB, limB, scB, kv_begin + step * kStepTok);
     if (nxt >= n_steps) break;
     step = nxt;
   }
