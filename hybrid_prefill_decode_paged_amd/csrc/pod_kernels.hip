@@ -241,6 +241,15 @@ __device__ __forceinline__ int find_desc(CPTR(int32_t) descs, int n, int field, 
 }
 
 __device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+// This lane's index within its wave, through an empty asm statement (no instruction) that the
+// compiler cannot see through: per-lane addresses derived from it are recomputed in each work item
+// instead of being hoisted above a persistent kernel's claim loop and kept live (and spilled)
+// across every item.
+__device__ __forceinline__ int item_lane() {
+  int l = threadIdx.x & 63;
+  asm volatile("" : "+v"(l));
+  return l;
+}
 
 // The four LDS objects of a kernel (see Geo::kObjBytes): K and V staging buffers 0 and 1 of the
 // prefill tile, and, for the decode role and the split merge, one combine table per wave.  The
@@ -548,7 +557,7 @@ __device__ void decode_wave_item(const KernelParams& P, int item, float* sw) {
   const int local = item - dsc[kDItemBegin];
   const int split = local / P.hkv, head = local - split * P.hkv;   // adjacent items: adjacent heads
 
-  const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+  const int lane = item_lane(), n = lane & 15, q = lane >> 4;
   const int G = P.group;
   const int seq = dsc[kDSeq], q_row = dsc[kDQRow], kv_len = dsc[kDKvLen];
   const int n_q = dsc[kDNq], ncols = dsc[kDNcols], q_pos = dsc[kDQPos];
@@ -741,7 +750,7 @@ __device__ void decode_wave_item(const KernelParams& P, int item, float* sw) {
 template <typename T, int D>
 __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head, int split, const Stage& LB) {
   using Gm = Geo<T, D>;
-  const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, q = lane >> 4;
+  const int tid = threadIdx.x, lane = item_lane(), n = lane & 15, q = lane >> 4;
   const int w = wave_index();
   const int G = P.group;
   const int seq = dsc[kDSeq], q_row = dsc[kDQRow], n_q = dsc[kDNq], q_pos = dsc[kDQPos];
@@ -1072,7 +1081,7 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
   constexpr int kBufBytes = kKBytes + kTp * kVg * 1024;
   static_assert(kBufBytes * 2 == Geo<T, D>::kPrefillLds, "two staged tiles fill the prefill LDS");
   static_assert(kKBytes <= Geo<T, D>::kObjBytes && kTp * kVg * 1024 <= Geo<T, D>::kObjBytes, "a staged half fits its object");
-  const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+  const int lane = item_lane(), n = lane & 15, q = lane >> 4;
   const int w = wave_index();
   const int G = P.group;
   const int seq = dsc[kDSeq], q_row = dsc[kDQRow], n_q = dsc[kDNq], q_pos = dsc[kDQPos];
