@@ -32,6 +32,7 @@ constexpr double kPrefillFlopsPerSec = 0.85e15;
 constexpr double kDecodeBytesPerSec = 6.5e12;
 constexpr double kPrefillHeavyRatio = 0.75;   // prefill share >= 3/4 of the decode share
 constexpr int kOneRoundMaxSplit = 8192;       // longest decode split of the prefill-heavy fused plan
+constexpr int kMinPrefillSplit = 4096;        // shortest key split of a prefill tile
 int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 int round_up_int(int a, int m) { return ceil_div(a, m) * m; }
 }  // namespace
@@ -165,13 +166,51 @@ pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus
   const double qo_row_bytes = 2.0 * c.hq * c.d * c.q_elem_bytes();  // q in and out of one row
   const double page_bytes = 4.0 + (c.dtype == POD_ATTN_FP8_E4M3 ? 8.0 * c.hkv : 0.0);   // table entry (+ FP8 scales)
   std::vector<int> small_chunks;
+  auto is_small = [&](int L) { return L <= emax && L * G <= kMaxGroup; };
+  // Key splits of a chunk's tiles.  A split costs a partial write, its read-back in the merge and
+  // a pipeline fill, so tiles are split only as far as the workgroups that run them need: pieces
+  // of at least kMinPrefillSplit keys, at most `cap` per tile.  When the tiles run beside a longer
+  // decode stream (fused and two-stream modes, a batch that is not prefill-heavy by the estimate
+  // below), about one workgroup per CU runs them, so a piece is also about the prefill share's
+  // keys (all tiles, all KV heads) over the CUs: about one item per CU.  Measured (kernel us,
+  // split caps 8 / 2 / 1): Llama-3-8B-shaped fused 1626 / 1563 / 1559, two-stream 1824 / 1731 /
+  // 1696; long-context fused 5016 / 4987 / 5029, two-stream 5566 / 5130 / 5078.  A prefill-heavy
+  // batch keeps the floor: its decode share ends early and every workgroup then runs tiles (the
+  // Yi-6B-shaped batch, two-stream 587 / 607 / 888 us, and 573 -> 595 fused with an FP8 cache),
+  // and so does separate mode, which runs tiles on every workgroup slot (Yi-6B-shaped: 695 us
+  // against 818 at a cap of 2).
+  double beside_split = 0.0;
+  {
+    double tile_keys = 0.0, pf_flops = 0.0, dc_bytes = 0.0;
+    for (int i = 0; i < b->num_prefill; ++i) {
+      const int L = b->prefill_q_start[i + 1] - b->prefill_q_start[i];
+      const double ctx = b->prefill_ctx_len[i];
+      if (L == 0) continue;
+      if (is_small(L)) {
+        dc_bytes += ctx * kv_tok_bytes + L * qo_row_bytes + page_bytes * ceil_div((int)ctx, kPage);
+        continue;
+      }
+      for (int t = 0; t < L; t += p.tile_queries) {
+        const double nq = std::min(p.tile_queries, L - t), qpos = ctx - L + t;
+        tile_keys += qpos + nq;
+        pf_flops += 4.0 * c.d * G * c.hkv * (nq * qpos + nq * (nq + 1) / 2.0);
+      }
+    }
+    for (int i = 0; i < b->num_decode; ++i)
+      dc_bytes += (double)b->decode_ctx_len[i] * kv_tok_bytes + qo_row_bytes + page_bytes * ceil_div(b->decode_ctx_len[i], kPage);
+    const bool prefill_heavy = pf_flops / kPrefillFlopsPerSec >= kPrefillHeavyRatio * dc_bytes / kDecodeBytesPerSec;
+    if (dc_bytes > 0.0 && !prefill_heavy && (c.mode == POD_ATTN_MODE_FUSED || c.mode == POD_ATTN_MODE_STREAMS))
+      beside_split = tile_keys * c.hkv / num_cus;
+  }
   for (int i = 0; i < b->num_prefill; ++i) {
     const int L = b->prefill_q_start[i + 1] - b->prefill_q_start[i];
     const int ctx = b->prefill_ctx_len[i];
     if (L == 0) continue;
-    if (L <= emax && L * G <= kMaxGroup) { small_chunks.push_back(i); continue; }
+    if (is_small(L)) { small_chunks.push_back(i); continue; }
     p.prefill_bytes += (double)ctx * kv_tok_bytes + (double)L * qo_row_bytes + page_bytes * ceil_div(ctx, kPage);
-    int ns_c = std::max(1, std::min(std::min(cap, kMaxCombineSplits), ceil_div(ctx, 4096)));
+    int ns_c = std::max(1, std::min(std::min(cap, kMaxCombineSplits), ceil_div(ctx, kMinPrefillSplit)));
+    if (beside_split > kMinPrefillSplit)       // pieces of about beside_split keys (rounded)
+      ns_c = std::max(1, std::min(ns_c, (int)std::lround(ctx / beside_split)));
     const int st = round_up_int(ceil_div(ctx, ns_c), kPrefillKvTile);
     ns_c = ceil_div(ctx, st);
     std::vector<Tile> tiles;

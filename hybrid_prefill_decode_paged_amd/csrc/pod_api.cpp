@@ -81,7 +81,6 @@ struct pod_attn_handle {
   hipEvent_t prof_start = nullptr, prof_end = nullptr;   // one-shot profiling events
   TimingSlot timing[kRing];         // kernel time of the last runs (one slot per run, round robin)
   int timing_next = 0;
-  int role_prio = 0;                // POD_ATTN_ROLE_PRIO (decode | prefill << 2)
   void* scratch = nullptr;          // pod_attn_run_noalloc's device scratch on this handle's device
 };
 
@@ -124,7 +123,6 @@ pod_attn_status pod_attn_create(const pod_attn_config* cfg, pod_attn_handle** ou
   h->cfg.append_token_heads = std::max(1, env_int("POD_ATTN_APPEND_TOKEN_HEADS", kAppendTokenHeads));
   h->cfg.decode_taper = env_int("POD_ATTN_DECODE_TAPER", h->cfg.decode_taper);
   h->cfg.decode_items_per_wave = std::max(0, env_int("POD_ATTN_DECODE_ITEMS_PER_WAVE", h->cfg.decode_items_per_wave));
-  h->role_prio = env_int("POD_ATTN_ROLE_PRIO", 0) & 15;
   if (const char* m = std::getenv("POD_ATTN_MODE")) {
     if (!std::strcmp(m, "fused")) h->mode_env = POD_ATTN_MODE_FUSED;
     else if (!std::strcmp(m, "separate")) h->mode_env = POD_ATTN_MODE_SEPARATE;
@@ -185,11 +183,21 @@ void pod_attn_destroy(pod_attn_handle* h) {
   delete h;
 }
 
+// The configuration a batch is planned with: the handle's, in the mode its runs will launch
+// (POD_ATTN_MODE, and separate kernels when the fused kernel cannot be resident), so that
+// pod_attn_workspace_size and pod_attn_run plan alike.
+static Config planning_config(const pod_attn_handle* h) {
+  Config c = h->cfg;
+  if (h->mode_env >= 0) c.mode = h->mode_env;
+  if (c.mode == POD_ATTN_MODE_FUSED && h->fused_occupancy < 1) c.mode = POD_ATTN_MODE_SEPARATE;
+  return c;
+}
+
 pod_attn_status pod_attn_workspace_size(pod_attn_handle* h, const pod_attn_batch* b, size_t* bytes) {
   if (!h || !bytes) return fail(POD_ATTN_ERR_INVALID_ARG, "null handle or output");
   Plan p;
   std::string err;
-  pod_attn_status st = plan_batch(h->cfg, b, h->num_cus, h->wgs_per_cu, &p, &err);
+  pod_attn_status st = plan_batch(planning_config(h), b, h->num_cus, h->wgs_per_cu, &p, &err);
   if (st != POD_ATTN_OK) return fail(st, err);
   *bytes = p.map.total;
   return POD_ATTN_OK;
@@ -234,7 +242,7 @@ static pod_attn_status run_impl(pod_attn_handle* h, const void* q, const void* k
   const auto t0 = std::chrono::steady_clock::now();
   Plan p;
   std::string err;
-  pod_attn_status st = plan_batch(h->cfg, b, h->num_cus, h->wgs_per_cu, &p, &err);
+  pod_attn_status st = plan_batch(planning_config(h), b, h->num_cus, h->wgs_per_cu, &p, &err);
   if (st != POD_ATTN_OK) return fail(st, err);
   const double plan_us = std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t0).count();
   if (p.total_q == 0) return POD_ATTN_OK;
@@ -309,7 +317,6 @@ static pod_attn_status run_impl(pod_attn_handle* h, const void* q, const void* k
   kp.hq = h->cfg.hq; kp.hkv = h->cfg.hkv; kp.group = h->cfg.group();
   kp.bt_stride = b->block_table_stride; kp.num_pages = b->num_pages_in_pool;
   kp.scale_log2 = h->cfg.scale * 1.4426950408889634f;
-  kp.role_prio = h->role_prio;
 
   // Plan upload (and, in fused mode, the KV append in the same launch).
   stage_plan(p, h->cfg, (uint8_t*)slot.host, append);

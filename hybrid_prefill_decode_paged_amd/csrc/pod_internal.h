@@ -94,7 +94,6 @@ struct KernelParams {
   int hq, hkv, group, bt_stride, num_pages;
   float scale_log2;          // softmax scale * log2(e)
   int inline_combine;        // 1: the last-arriving decode split merges its group in-kernel (fused)
-  int role_prio;             // fused: wave priority (0..3) of decode-role (low 2 bits) and prefill-role (next 2) waves
   int group_begin, group_end;// combine kernel range
   int combine_col_blocks;     // combine kernel: workgroups per group (16 columns each)
 };

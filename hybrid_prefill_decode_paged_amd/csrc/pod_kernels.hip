@@ -750,7 +750,7 @@ __device__ void decode_wave_item(const KernelParams& P, int item, float* sw) {
 template <typename T, int D>
 __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head, int split, const Stage& LB) {
   using Gm = Geo<T, D>;
-  const int tid = threadIdx.x, lane = item_lane(), n = lane & 15, q = lane >> 4;
+  const int lane = item_lane(), n = lane & 15, q = lane >> 4;
   const int w = wave_index();
   const int G = P.group;
   const int seq = dsc[kDSeq], q_row = dsc[kDQRow], n_q = dsc[kDNq], q_pos = dsc[kDQPos];
@@ -1528,16 +1528,6 @@ __device__ void run_prefill_item(const KernelParams& P, int item, const Stage& L
   __syncthreads();   // LDS is reused by the next item
 }
 
-// Wave priority for the instruction arbiter of a SIMD shared by a decode and a prefill wave.
-__device__ __forceinline__ void set_prio(int p) {
-  switch (p & 3) {
-    case 0: __builtin_amdgcn_s_setprio(0); break;
-    case 1: __builtin_amdgcn_s_setprio(1); break;
-    case 2: __builtin_amdgcn_s_setprio(2); break;
-    default: __builtin_amdgcn_s_setprio(3); break;
-  }
-}
-
 __device__ __forceinline__ int cu_slot() {
   const unsigned hw = __builtin_amdgcn_s_getreg((4) | (0 << 6) | (31 << 11));     // HW_ID
   const unsigned xcc = __builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11));    // XCC_ID[3:0]
@@ -1627,7 +1617,6 @@ __global__ __launch_bounds__(kThreads, 2) void pod_fused_kernel(KernelParams P) 
     int item = s_item;
     __syncthreads();
     if (role < 0) break;
-    if (P.role_prio) set_prio(role == 1 ? P.role_prio : P.role_prio >> 2);
     if (role == 1) {
       // The workgroup claims 4 consecutive items (adjacent KV heads of one key range) and each
       // wave streams one of them; the next block is claimed once the current one is done.

@@ -319,21 +319,6 @@ def test_run_to_run_bitwise_determinism(mode):
     assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
 
 
-@pytest.mark.parametrize("prio", [2, 8, 14])
-def test_role_priority_leaves_results_unchanged(prio, monkeypatch):
-    """POD_ATTN_ROLE_PRIO (wave priority of the decode and prefill roles in the fused kernel)
-    changes only which instructions issue first: every item computes the same arithmetic and the
-    split merge order is fixed, so the output is bitwise that of the default schedule."""
-    spec = gen.custom_spec("bf16", Hq=32, Hkv=8, D=128, prefill=[(256, 2000)],
-                           decode=[3000, 1500, 700, 40], seed=22)
-    b = gen.make_batch(spec, "cuda")
-    _say(f"role priority {prio}")
-    ref, _, _ = run_library(b, mode="fused", decode_split_tokens=256)
-    monkeypatch.setenv("POD_ATTN_ROLE_PRIO", str(prio))   # read when a handle is created
-    got, _, _ = run_library(b, mode="fused", decode_split_tokens=256)
-    assert torch.equal(ref.view(torch.int16), got.view(torch.int16))
-
-
 def test_out_of_pool_page_id_is_reported_not_read():
     """A used block-table entry outside the pool is never dereferenced: the kernels flag it in
     the workspace status word and treat that page as holding no keys."""
