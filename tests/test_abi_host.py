@@ -119,12 +119,44 @@ def _check_coverage(spec, items, G):
 
 
 @pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
-def test_plan_covers_every_row_head_key_once(idx):
+@pytest.mark.parametrize("mode", ["fused", "separate", "streams"])
+def test_plan_covers_every_row_head_key_once(idx, mode):
     spec = gen.config_spec(idx)
-    cfg = B.make_config(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.dtype)
+    cfg = B.make_config(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.dtype, mode)
     items, st = B.plan_inspect(cfg, _meta(spec), 256, 2)
     assert st["num_prefill_items"] + st["num_decode_items"] == len(items)
     _check_coverage(spec, items, spec.num_q_heads // spec.num_kv_heads)
+
+
+def _prefill_splits(spec, mode, cus=256):
+    cfg = B.make_config(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.dtype, mode)
+    items, st = B.plan_inspect(cfg, _meta(spec), cus, 2)
+    return st["prefill_max_splits"], st["num_prefill_items"]
+
+
+def test_prefill_splits_follow_the_decode_share():
+    """Tiles beside a longer decode stream (fused and two-stream plans of a batch that is not
+    prefill-heavy) are cut into pieces of about the prefill share's keys over the CUs; separate
+    plans and prefill-heavy batches keep pieces of at least 4096 keys (at most 8 per tile)."""
+    w3, w4, w5 = gen.config_spec(3), gen.config_spec(4), gen.config_spec(5)
+    # Llama-3-8B-shaped (decode-heavy): 64 tiles x 8 KV heads, ~15.4K keys each -> ~31K keys a
+    # piece over 256 CUs: unsplit; separate: 16384 / 4096 = 4 pieces.
+    assert _prefill_splits(w3, "fused") == (1, 512)
+    assert _prefill_splits(w3, "streams") == (1, 512)
+    assert _prefill_splits(w3, "separate") == (4, 2048)
+    # long-context (decode-heavy): 128 tiles of ~32.5K keys -> ~16.3K a piece: 2 pieces
+    assert _prefill_splits(w5, "fused") == (2, 256)
+    assert _prefill_splits(w5, "separate") == (8, 1024)
+    # on fewer CUs a piece is longer: 64 CUs -> ~65K keys a piece, every tile whole
+    assert _prefill_splits(w5, "fused", cus=64)[0] == 1
+    # Yi-6B-shaped (prefill-heavy by the planner's estimate): the 4096-key floor in every mode
+    for mode in ("fused", "streams", "separate"):
+        assert _prefill_splits(w4, mode) == (7, 1408)
+    # FP8 halves the decode bytes: the Llama-3-8B-shaped batch becomes prefill-heavy
+    assert _prefill_splits(gen.fp8_spec(3), "fused") == (4, 2048)
+    # no decode work: the floor
+    only = gen.custom_spec("bf16", Hq=32, Hkv=8, D=128, prefill=[(2048, 16384)], decode=[])
+    assert _prefill_splits(only, "fused")[0] == 4
 
 
 @pytest.mark.parametrize("G,D,split,cap", [(1, 128, 0, 0), (2, 64, 128, 1), (3, 128, 256, 3),
