@@ -743,12 +743,14 @@ __device__ void decode_wave_item(const KernelParams& P, int item, float* sw) {
     combine_block_wave<T, D>(P, dsc, head, 0, sw);
 }
 
-// ------------------------------------------------------------------ prefill tile item
+// ------------------------------------------------------------------ prefill item, fp32 cache
 // One (query tile, KV head, key split): 128 columns = floor(128/G) queries x G heads; wave w
 // owns columns 32w .. 32w+31 (two 16-wide blocks).  Keys advance 64 (or 32) at a time,
-// staged in LDS by all 256 threads with the next tile's global loads in flight.
+// staged in LDS by all 256 threads with the next tile's loads in flight.  (bf16 and FP8 caches
+// take prefill_item_tile.)
 template <typename T, int D>
 __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head, int split, const Stage& LB) {
+  static_assert(sizeof(T) == 4 && !kIsFp8<T>, "the fp32 prefill item");
   using Gm = Geo<T, D>;
   const int lane = item_lane(), n = lane & 15, q = lane >> 4;
   const int w = wave_index();
@@ -792,12 +794,11 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
     for (int b = 0; b < Gm::kDb; ++b) o[nb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run[2] = {kNegInf, kNegInf}, l_run[2] = {0.f, 0.f};
 
-  // ---- staging: K and V pages of a key tile go HBM -> LDS directly (global_load_lds, no
-  // registers); instruction r of wave w moves linear chunks r*256 + 64w .. +63 of
-  // [K pages][V pages], one 16-byte chunk per lane, into consecutive LDS.
+  // ---- staging: K and V pages of a key tile go HBM -> LDS directly (LDS-DMA, no registers);
+  // instruction r of wave w moves linear chunks r*256 + 64w .. +63 of [K pages][V pages], one
+  // 16-byte chunk per lane, into consecutive LDS.
   int lim_cur[Gm::kTp], lim_nxt[Gm::kTp];
-  float sc_cur[2 * Gm::kTp], sc_nxt[2 * Gm::kTp];     // Fp8: K then V scale of each page of the tile
-  auto tile_pages = [&](int j, int (&lim)[Gm::kTp], int (&pg)[Gm::kTp], float (&sc)[2 * Gm::kTp]) {
+  auto tile_pages = [&](int j, int (&lim)[Gm::kTp], int (&pg)[Gm::kTp]) {
     const int tb = kv_begin + j * Gm::kTileKeys;
 #pragma unroll
     for (int p = 0; p < Gm::kTp; ++p) {
@@ -805,30 +806,13 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
       int l = min(kPage, kv_end - pi * kPage);
       pg[p] = __builtin_amdgcn_readfirstlane(page_or_empty(btr, pi, l, P.num_pages, P.ctrl + kCStatus));
       lim[p] = __builtin_amdgcn_readfirstlane(l);
-      if constexpr (kIsFp8<T>) {
-        sc[p] = ((CPTR(float))P.k_scale)[(size_t)pg[p] * P.hkv + head];
-        sc[Gm::kTp + p] = ((CPTR(float))P.v_scale)[(size_t)pg[p] * P.hkv + head];
-      } else {
-        sc[p] = sc[Gm::kTp + p] = 1.f;
-      }
     }
   };
   auto kbuf = [&](auto par) { return kbuf_of<decltype(par)::value>(LB); };
   auto vbuf = [&](auto par) { return vbuf_of<decltype(par)::value>(LB); };
-  // bf16 V rows are 32 bytes (two 16-byte halves); rows 8..15 of each 16-row block swap their
-  // halves so that a wave's 8-byte reads of 16 consecutive rows spread over all LDS banks.
-  // The swap is its own inverse, so LDS chunk c is loaded from source chunk vswz(c).
-  auto vswz = [&](int c) {
-    if constexpr (Gm::kBytes == 2) {
-      const int d = c >> 1, h = c & 1;
-      return d * 2 + (h ^ ((d >> 3) & 1));
-    } else {
-      return c;
-    }
-  };
-  auto issue_tile = [&](int j, auto b, int (&lim)[Gm::kTp], float (&sc)[2 * Gm::kTp]) {
+  auto issue_tile = [&](int j, auto b, int (&lim)[Gm::kTp]) {
     int pg[Gm::kTp];
-    tile_pages(j, lim, pg, sc);
+    tile_pages(j, lim, pg);
 #pragma unroll
     for (int r = 0; r < Gm::kStageR; ++r) {
       const int L0 = r * kThreads + 64 * w;                 // wave-uniform first chunk
@@ -840,11 +824,11 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
       for (int pp = 1; pp < Gm::kTp; ++pp) page = p == pp ? pg[pp] : page;
       const int c = c0 + lane;
       char* dst = (half ? vbuf(b) : kbuf(b)) + p * Gm::kSlab + c0 * 16;
-      stage_chunk(slab_rsrc<T, D>(half ? P.v : P.k, page, P.hkv, head), 0, (half ? vswz(c) : c) * 16, dst);
+      stage_chunk(slab_rsrc<T, D>(half ? P.v : P.k, page, P.hkv, head), 0, c * 16, dst);
     }
   };
 
-  auto compute_tile = [&](auto b, int j, const int (&lim)[Gm::kTp], const float (&sc)[2 * Gm::kTp]) {
+  auto compute_tile = [&](auto b, int j, const int (&lim)[Gm::kTp]) {
     const int tb = kv_begin + j * Gm::kTileKeys;
     if (!wave_active || tb > pmax) return;                    // every key after every query
     bool full = tb + Gm::kTileKeys - 1 <= pmin;
@@ -857,18 +841,12 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
     for (int mb = 0; mb < Gm::kTp; ++mb) {
       u32x4 kop[Gm::kNs];
 #pragma unroll
-      for (int s = 0; s < Gm::kNs; ++s) {
-        if constexpr (kIsFp8<T>)   // dims 32s+8q .. +7: 16-code chunk 2s + q/2, half q%2
-          kop[s] = e4m3x8_to_bf16(*(const u32x2*)(kb + mb * Gm::kSlab + k_chunk_off(2 * s + (q >> 1), n) + 8 * (q & 1)));
-        else
-          kop[s] = *(const u32x4*)(kb + mb * Gm::kSlab + k_chunk_off(4 * s + q, n));
-      }
+      for (int s = 0; s < Gm::kNs; ++s) kop[s] = *(const u32x4*)(kb + mb * Gm::kSlab + k_chunk_off(4 * s + q, n));
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < Gm::kNs; ++s) acc = mfma_chunk(kop[s], qop[nb][s], acc, T());
-        if constexpr (kIsFp8<T>) acc *= sc[mb];   // the page's K scale
         S[nb][mb] = acc;
       }
     }
@@ -898,81 +876,30 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
     bool vmask = false;
 #pragma unroll
     for (int p = 0; p < Gm::kTp; ++p) vmask = vmask || lim[p] < kPage;
-    if constexpr (kIsFp8<T>) {
-      // V codes of 4 slots -> bf16; each page's V scale multiplies its probabilities here only
 #pragma unroll
-      for (int pp = 0; pp < Gm::kTp / 2; ++pp) {
-        u32x4 pb[2];
+    for (int mb = 0; mb < Gm::kTp; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const f32x4 a = S[nb][2 * pp] * sc[Gm::kTp + 2 * pp], c = S[nb][2 * pp + 1] * sc[Gm::kTp + 2 * pp + 1];
-          pb[nb] = u32x4{pack_bf16(a.x, a.y), pack_bf16(a.z, a.w), pack_bf16(c.x, c.y), pack_bf16(c.z, c.w)};
-        }
+      for (int b2 = 0; b2 < Gm::kDb; ++b2) {
+        const int d = 16 * b2 + n;
+        u32x4 v = *(const u32x4*)(vb + mb * Gm::kSlab + v_elem_off<T>(d, 4 * q));
+        if (vmask) v = mask_vop(v, q, lim[mb]);
 #pragma unroll
-        for (int b2 = 0; b2 < Gm::kDb; ++b2) {
-          const int d = 16 * b2 + n;
-          u32x2 va = e4m3x4_to_bf16(*(const uint32_t*)(vb + (2 * pp) * Gm::kSlab + v_elem_off<T>(d, 4 * q)));
-          u32x2 vc = e4m3x4_to_bf16(*(const uint32_t*)(vb + (2 * pp + 1) * Gm::kSlab + v_elem_off<T>(d, 4 * q)));
-          if (vmask) {
-            va = mask_vop(va, q, lim[2 * pp]);
-            vc = mask_vop(vc, q, lim[2 * pp + 1]);
-          }
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb) o[nb][b2] = pv_pair(va, vc, pb[nb], o[nb][b2]);
-        }
+        for (int nb = 0; nb < 2; ++nb) o[nb][b2] = pv_page_f32(v, S[nb][mb], o[nb][b2]);
       }
-    } else if constexpr (Gm::kBytes == 2) {
-#pragma unroll
-      for (int pp = 0; pp < Gm::kTp / 2; ++pp) {
-        u32x4 pb[2];
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const f32x4 a = S[nb][2 * pp], c = S[nb][2 * pp + 1];
-          pb[nb] = u32x4{pack_bf16(a.x, a.y), pack_bf16(a.z, a.w), pack_bf16(c.x, c.y), pack_bf16(c.z, c.w)};
-        }
-#pragma unroll
-        for (int b2 = 0; b2 < Gm::kDb; ++b2) {
-          const int d = 16 * b2 + n;
-          const int off = vswz(d * 2 + (q >> 1)) * 16 + (q & 1) * 8;
-          u32x2 va = *(const u32x2*)(vb + (2 * pp) * Gm::kSlab + off);
-          u32x2 vc = *(const u32x2*)(vb + (2 * pp + 1) * Gm::kSlab + off);
-          if (vmask) {
-            va = mask_vop(va, q, lim[2 * pp]);
-            vc = mask_vop(vc, q, lim[2 * pp + 1]);
-          }
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb) o[nb][b2] = pv_pair(va, vc, pb[nb], o[nb][b2]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int mb = 0; mb < Gm::kTp; ++mb)
-#pragma unroll
-        for (int b2 = 0; b2 < Gm::kDb; ++b2) {
-          const int d = 16 * b2 + n;
-          u32x4 v = *(const u32x4*)(vb + mb * Gm::kSlab + v_elem_off<T>(d, 4 * q));
-          if (vmask) v = mask_vop(v, q, lim[mb]);
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb) o[nb][b2] = pv_page_f32(v, S[nb][mb], o[nb][b2]);
-        }
-    }
   };
-
   // Tile j is staged in buffer j & 1 while tile j - 1 is computed; the loop is unrolled by two so
   // that each step names its buffers at compile time.
   auto step = [&](auto par, int j) {
     constexpr int PAR = decltype(par)::value;
-    if (j + 1 < n_tiles) issue_tile(j + 1, Par<1 - PAR>(), lim_nxt, sc_nxt);
-    compute_tile(par, j, lim_cur, sc_cur);
+    if (j + 1 < n_tiles) issue_tile(j + 1, Par<1 - PAR>(), lim_nxt);
+    compute_tile(par, j, lim_cur);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
 #pragma unroll
     for (int p = 0; p < Gm::kTp; ++p) lim_cur[p] = lim_nxt[p];
-#pragma unroll
-    for (int p = 0; p < 2 * Gm::kTp; ++p) sc_cur[p] = sc_nxt[p];
   };
   if (n_tiles > 0) {
-    issue_tile(0, Par<0>(), lim_cur, sc_cur);
+    issue_tile(0, Par<0>(), lim_cur);
     __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): this wave's LDS loads landed
     __syncthreads();
     for (int j = 0; j < n_tiles; j += 2) {
