@@ -157,10 +157,10 @@ def summarize(t, t_roof_s=None):
 
 def measured_peaks(torch, B):
     """This GPU's HBM read rate and dense bf16 MFMA rate, from the library's probes
-    (pod_attn_probe_hbm_read over a 2 GiB buffer, pod_attn_probe_mfma), timed with HIP events
+    (pod_attn_probe_hbm_read over an 8 GiB buffer, pod_attn_probe_mfma), timed with HIP events
     on the launch stream after one untimed call each."""
     stream = torch.cuda.current_stream()
-    nbytes = 2 << 30
+    nbytes = 8 << 30
     buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
     isink = torch.empty(B.PROBE_WGS, dtype=torch.int32, device="cuda")
     fsink = torch.empty(4 * B.PROBE_WGS, dtype=torch.float32, device="cuda")
@@ -182,7 +182,7 @@ def measured_peaks(torch, B):
     t_mfma = timed(lambda: B.probe_mfma(iters, fsink, stream), 5)
     del buf
     return {"hbm_read_gbps": round(nbytes / t_hbm / 1e9, 1), "mfma_bf16_tflops": round(flops / t_mfma / 1e12, 1),
-            "how": "library probes: streaming read of 2 GiB in 16 KiB blocks; 4096x4 waves x 4 chains of bf16 32x32x16 MFMA"}
+            "how": "library probes: streaming read of 8 GiB in 16 KiB blocks, two in flight per wave; 4096x4 waves x 8 chains of bf16 32x32x16 MFMA"}
 
 
 def measured_traffic(kernel_name, workload_name):
@@ -316,7 +316,19 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (counter calibration)")
+    ap.add_argument("--calibrate-mfma", action="store_true",
+                    help="only run the library's dense bf16 MFMA probe 3 times (counter calibration)")
     args = ap.parse_args()
+    if args.calibrate_mfma:
+        import torch
+        from hybrid_prefill_decode_paged_amd import binding
+        binding.load()
+        sink = torch.empty(4 * binding.PROBE_WGS, dtype=torch.float32, device="cuda")
+        for _ in range(3):
+            flops = binding.probe_mfma(2048, sink)
+        torch.cuda.synchronize()
+        print(f"mfma probe 3 x {flops:.4g} FLOP", flush=True)
+        return
     if args.calibrate_copy:
         import torch
         x = torch.full((1 << 30,), 3, dtype=torch.uint8, device="cuda")
@@ -456,6 +468,10 @@ def main():
     if not args.no_peaks:
         say("measuring this GPU's HBM read and MFMA rates")
         peaks = measured_peaks(torch, binding)
+        # the dominant kernel's rate against this GPU's own ceiling (context beside frac)
+        if bound == "hbm" or spec.dtype != "fp32":
+            measured = peaks["hbm_read_gbps"] if bound == "hbm" else peaks["mfma_bf16_tflops"]
+            peaks["dominant_kernel_fraction_of_measured"] = round(achieved / measured, 4)
     line = {
         "metric": METRIC,
         "value": round(statistics.median(head["wall_ms"]) * 1e3, 2),

@@ -205,7 +205,7 @@ def probe_hbm_read(buf, sink, stream=None) -> None:
 
 def probe_mfma(iters: int, sink, stream=None) -> float:
     """pod_attn_probe_mfma: dense bf16 MFMA work; sink is a device float tensor of 4*PROBE_WGS
-    elements (each receives 4*iters).  Returns the FLOPs performed."""
+    elements (each receives 8*iters).  Returns the FLOPs performed."""
     flops = C.c_double(0.0)
     _check(load().pod_attn_probe_mfma(int(iters), _ptr(sink), C.byref(flops), _stream_handle(stream)))
     return flops.value

@@ -22,7 +22,7 @@ KernelSet kernel_set(int dtype, int head_dim);
 
 // Measurement probes (peaks on the machine at hand).
 constexpr int kProbeWgs = 4096;    // workgroups of either probe
-constexpr int kProbeChains = 4;    // independent 32x32x16 MFMA chains per wave
+constexpr int kProbeChains = 8;    // independent 32x32x16 MFMA chains per wave
 struct ProbeKernels {
   const void* hbm_read = nullptr;  // (const u32x4* buf, size_t n16, uint32_t* sink)
   const void* mfma = nullptr;      // (int iters, float* sink)

@@ -1762,25 +1762,46 @@ KernelSet make_set() {
 
 // ------------------------------------------------------------------ measurement probes
 // Streaming read of n16 16-byte chunks in 16 KiB blocks: wave v of the grid reads blocks v,
-// v + waves, ..., all 16 loads of a block in flight (16 per lane, consecutive lanes on consecutive
-// chunks); each workgroup writes the XOR of its words to sink[wg] (so the read cannot be dropped,
-// and a test can check that every byte was read).
+// v + waves, ..., with two blocks in flight (the next block's 16 loads per lane are issued before
+// the current block is folded; consecutive lanes on consecutive chunks); each workgroup writes the
+// XOR of its words to sink[wg] (so the read cannot be dropped, and a test can check that every
+// byte was read).
 __global__ __launch_bounds__(kThreads) void pod_probe_hbm_read_kernel(const u32x4* buf, size_t n16, uint32_t* sink) {
   constexpr int kPer = 16;                     // loads per lane per block
   constexpr size_t kBlock = 64 * kPer;         // chunks per block (16 KiB)
   const size_t nwaves = (size_t)gridDim.x * kWaves;
   const size_t lane = threadIdx.x & 63;
   uint32_t x = 0;
-  for (size_t blk = (size_t)blockIdx.x * kWaves + (threadIdx.x >> 6); blk * kBlock < n16; blk += nwaves) {
+  auto load = [&](size_t blk, u32x4 (&v)[kPer]) {
     const size_t base = blk * kBlock + lane;
-    u32x4 v[kPer];
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const size_t i = base + (size_t)j * 64;
       v[j] = i < n16 ? __builtin_nontemporal_load(buf + i) : u32x4{0u, 0u, 0u, 0u};
     }
+  };
+  auto fold = [&](const u32x4 (&v)[kPer]) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) x ^= v[j][0] ^ v[j][1] ^ v[j][2] ^ v[j][3];
+  };
+  size_t blk = (size_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  u32x4 a[kPer], b[kPer];
+  if (blk * kBlock < n16) {
+    load(blk, a);
+    for (;;) {                                 // a holds block blk (in flight)
+      size_t nx = blk + nwaves;
+      const bool more = nx * kBlock < n16;
+      if (more) load(nx, b);
+      fold(a);
+      if (!more) break;
+      blk = nx;                                // b holds block blk
+      nx = blk + nwaves;
+      const bool more2 = nx * kBlock < n16;
+      if (more2) load(nx, a);
+      fold(b);
+      if (!more2) break;
+      blk = nx;
+    }
   }
   for (int o = 32; o >= 1; o >>= 1) x ^= (uint32_t)__shfl_xor((int)x, o);
   __shared__ uint32_t s_x[kWaves];
@@ -1790,8 +1811,8 @@ __global__ __launch_bounds__(kThreads) void pod_probe_hbm_read_kernel(const u32x
 }
 
 // Dense bf16 MFMA: every wave runs kProbeChains independent 32x32x16 accumulation chains for
-// `iters` rounds (the 32x32 form keeps the matrix unit busy with few chains; the 16x16x32 form
-// needs about 16).  A is all ones and B all 2^-4, so each product adds exactly 1.0 to every
+// `iters` rounds (measured on gfx950 with 4096 x 4 waves: 8 chains of the 32x32 form reach 96% of
+// the 2.5 PFLOP/s peak, 4 chains 90%; the 16x16x32 form needs 16 chains for 93%).  A is all ones and B all 2^-4, so each product adds exactly 1.0 to every
 // accumulator element; lane 0 of each wave writes the sum of its chains' first elements
 // (kProbeChains * iters) to sink[4 * wg + wave].
 typedef float f32x16 __attribute__((ext_vector_type(16)));

@@ -371,13 +371,14 @@ pod_attn_status pod_attn_set_kernel_events(pod_attn_handle* h, void* ev_start, v
  * beside the vendor figures.  No handle; asynchronous on `stream`.
  *
  * pod_attn_probe_hbm_read: one streaming read of `bytes` bytes at `buf` (device, 16-byte aligned,
- * bytes a positive multiple of 16), 4096 workgroups of 256 threads reading 16-byte chunks in
- * address order across the grid.  sink (device, 4096 uint32) receives per workgroup the XOR of
+ * bytes a positive multiple of 16), 4096 workgroups of 256 threads; wave v of the grid reads the
+ * 16 KiB blocks v, v + 16384, ... (16-byte chunks, consecutive lanes on consecutive chunks) with
+ * two blocks in flight.  sink (device, 4096 uint32) receives per workgroup the XOR of
  * the 32-bit words it read, so the XOR of all of sink equals the XOR of the buffer's words.
  *
  * pod_attn_probe_mfma: dense bf16 32x32x16 MFMA work, 4096 workgroups of 4 waves, each wave
- * running 4 independent accumulation chains for `iters` rounds (1 <= iters <= 2^20) on operands
- * whose products add exactly 1.0 per round; sink (device, 4 * 4096 floats) receives 4 * iters per
+ * running 8 independent accumulation chains for `iters` rounds (1 <= iters <= 2^20) on operands
+ * whose products add exactly 1.0 per round; sink (device, 4 * 4096 floats) receives 8 * iters per
  * wave.  *flops (may be NULL) receives the FLOPs performed (2*32*32*16 per MFMA).
  *
  * Errors: POD_ATTN_ERR_INVALID_ARG for null or misaligned arguments and out-of-range sizes;

@@ -39,14 +39,38 @@ def test_hbm_read_probe_reads_every_word(n16):
     assert got == want
 
 
+def _xor_all(t):
+    """XOR of every 32-bit word of an int32 device tensor, by halving on the device."""
+    t = t.flatten()
+    while t.numel() > 1:
+        h = t.numel() // 2
+        r = t[:h] ^ t[h:2 * h]
+        t = torch.cat([r, t[2 * h:]]) if t.numel() % 2 else r
+    return int(t.item()) & 0xFFFFFFFF
+
+
+def test_hbm_read_probe_reads_every_word_with_several_blocks_per_wave():
+    """Every wave of the 4096 x 4 grid reads two or three 16 KiB blocks, the last one partial for
+    some waves: the two-blocks-in-flight loop and its tail."""
+    n16 = 4096 * 4 * 1024 * 2 + 4096 * 4 * 512 + 5
+    _say(f"hbm read probe n16={n16}")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    buf = torch.randint(-2**31, 2**31 - 1, (n16 * 4,), dtype=torch.int32, device="cuda", generator=g)
+    sink = torch.zeros(B.PROBE_WGS, dtype=torch.int32, device="cuda")
+    B.probe_hbm_read(buf, sink)
+    torch.cuda.synchronize()
+    assert _xor_all(sink) == _xor_all(buf)
+
+
 @pytest.mark.parametrize("iters", [1, 5, 1000])
 def test_mfma_probe_result_is_exact(iters):
     _say(f"mfma probe iters={iters}")
     sink = torch.full((4 * B.PROBE_WGS,), -1.0, dtype=torch.float32, device="cuda")
     flops = B.probe_mfma(iters, sink)
     torch.cuda.synchronize()
-    assert torch.all(sink == 4.0 * iters)
-    assert flops == B.PROBE_WGS * 4 * 4 * iters * 2 * 32 * 32 * 16
+    assert torch.all(sink == 8.0 * iters)
+    assert flops == B.PROBE_WGS * 4 * 8 * iters * 2 * 32 * 32 * 16
 
 
 def test_probes_reject_bad_arguments():
