@@ -20,6 +20,7 @@ struct Config {
   int group() const { return hq / hkv; }
   int elem_bytes() const { return dtype == POD_ATTN_FP32 ? 4 : dtype == POD_ATTN_BF16 ? 2 : 1; }   // cache element
   int q_elem_bytes() const { return dtype == POD_ATTN_FP32 ? 4 : 2; }                           // q and out
+  int lds_elem_bytes() const { return dtype == POD_ATTN_FP32 ? 4 : 2; }                         // prefill tile in LDS
 };
 
 struct Plan {

@@ -650,7 +650,7 @@ pod_attn_status pod_attn_batch_signals(const pod_attn_config* cfg, const pod_att
   s.combine_groups = p.n_groups;
   s.small_extends = p.num_small_extends;
   s.grid_wgs = num_cus * wgs_per_cu;
-  s.lds_bytes_per_wg = fused_lds_bytes(c.elem_bytes(), c.d);
+  s.lds_bytes_per_wg = fused_lds_bytes(c.lds_elem_bytes(), c.d);
   s.fallback_reason = p.n_pf_items == 0 ? POD_ATTN_FALLBACK_NO_PREFILL
                       : p.n_dc_items == 0 ? POD_ATTN_FALLBACK_NO_DECODE : POD_ATTN_FALLBACK_NONE;
   s.workspace_bytes = p.map.total;

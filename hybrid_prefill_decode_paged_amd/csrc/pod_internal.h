@@ -110,10 +110,12 @@ struct StageArgs {
 
 // LDS of one fused workgroup: four objects (K and V staging buffers 0 and 1 of the prefill tile,
 // each also one wave's combine table), each the larger of a staged half (4 pages per buffer when
-// a (page, head) slab is at most 4 KiB, else 2) and a combine table.  The kernels' geometry uses
-// the same formula.
-constexpr int fused_lds_bytes(int elem_bytes, int d) {
-  const int slab = kPage * d * elem_bytes;
+// a (page, head) slab of the tile's element type is at most 4 KiB, else 2) and a combine table.
+// lds_elem_bytes is the tile's element size in LDS: 4 for fp32, 2 for bf16 and for the FP8
+// cache (its codes are converted to bf16 when staged).  The kernels' geometry uses the same
+// formula.
+constexpr int fused_lds_bytes(int lds_elem_bytes, int d) {
+  const int slab = kPage * d * lds_elem_bytes;
   const int half = (slab <= 4096 ? 4 : 2) * slab;
   return 4 * (half > kCombineLdsPerWave ? half : kCombineLdsPerWave);
 }

@@ -75,19 +75,22 @@ template <typename T, int D> struct Geo {
   typedef typename std::conditional<kIsFp8<T>, u32x2, u32x4>::type KReg;   // K operand as loaded, per step
   static constexpr int kSlab = kPage * D * kBytes;      // bytes of one (page, KV head) slab
   static constexpr int kCps = kSlab / 16;               // 16-byte chunks per slab
-  static constexpr int kTp = kSlab <= 4096 ? 4 : 2;     // pages per prefill KV tile
+  // The prefill tile in LDS: FP8 codes are converted to bf16 when staged.
+  static constexpr int kLdsBytes = kIsFp8<T> ? 2 : kBytes;
+  static constexpr int kLdsSlab = kPage * D * kLdsBytes;                 // one staged (page, head)
+  static constexpr int kTp = kLdsSlab <= 4096 ? 4 : 2;  // pages per prefill KV tile
   static constexpr int kTileKeys = kTp * kPage;
   static constexpr int kDb = D / 16;                    // 16-row blocks of O^T
   static constexpr int kStageChunks = 2 * kTp * kCps;   // K + V chunks of one prefill tile
   static constexpr int kStageR = kStageChunks / kThreads;
-  static constexpr int kPrefillLds = 2 * 2 * kTp * kSlab;              // 2 buffers x (K, V)
+  static constexpr int kPrefillLds = 2 * 2 * kTp * kLdsSlab;           // 2 buffers x (K, V)
   // LDS is four separate objects: K and V staging buffers 0 and 1 of the prefill tile, each also
   // one wave's combine table.  Separate objects let the compiler's wait-count pass tell a read of
   // one buffer from the LDS-DMA loads in flight into another, so a tile's operand reads do not
   // wait for the next tile's staging loads.
-  static constexpr int kObjBytes = kTp * kSlab > kCombineLdsPerWave ? kTp * kSlab : kCombineLdsPerWave;
+  static constexpr int kObjBytes = kTp * kLdsSlab > kCombineLdsPerWave ? kTp * kLdsSlab : kCombineLdsPerWave;
   static constexpr int kFusedLds = 4 * kObjBytes;
-  static_assert(kFusedLds == fused_lds_bytes(kBytes, D), "host-side LDS figure matches the kernels");
+  static_assert(kFusedLds == fused_lds_bytes(kLdsBytes, D), "host-side LDS figure matches the kernels");
   static_assert(kStageChunks % kThreads == 0, "tile must split evenly over the workgroup");
   static_assert(kTp % 2 == 0, "bf16 PV pairs pages");
 };
@@ -975,33 +978,19 @@ __device__ __forceinline__ u32x4 mask_v8(u32x4 v, int lt) {
   return r;
 }
 
-// Zero the E4M3 codes of token slots >= lt in one 16-byte V row chunk (one dim, 16 slots).
-__device__ __forceinline__ u32x4 mask_v16_codes(u32x4 v, int lt) {
-  u32x4 r;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    uint32_t m = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) m |= (4 * k + b < lt ? 0xFFu : 0u) << (8 * b);
-    r[k] = v[k] & m;
-  }
-  return r;
-}
-// FP8 K slots in LDS: page parity par swaps slot bit 2, so that the b64 operand reads of the two
-// pages of a pair (rows 0..7 and 8..15 of a block) fall on different LDS banks.
-__device__ __forceinline__ int kslot8(int par, int t) { return t ^ (par << 2); }
-
-// The same tile for the bf16 cache (T = __bf16) and the FP8 cache (T = Fp8: E4M3 codes staged
-// as they are, half the bytes; operands converted to bf16 as they are read from LDS, the page's K
-// scale applied to its scores and its V scale to its probabilities in the output product).
-// FP8 LDS units are 1 KB as well: a K unit holds 4 chunks of 16 dims (64 dims) for the page's 16
-// slots, a V unit 64 dims x 16 slots.
+// The same tile for the bf16 cache (T = __bf16) and the FP8 cache (T = Fp8).  FP8: each wave
+// stages its page's E4M3 codes (half the bytes) by LDS-DMA into the first units of the page's
+// place, and once they have landed converts them in place into the bf16 layout above (every code
+// converted once per workgroup, exactly: E4M3 values are bf16 values); the products then read bf16
+// operands as for the bf16 cache, the page's K scale applied to its scores and its V scale to its
+// probabilities in the output product.
 template <typename T, int D>
 __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int head, int split, const Stage& LB) {
   constexpr bool kF8 = kIsFp8<T>;
   constexpr int kNs = D / 32;                  // QK steps of 32 dims
-  constexpr int kKu = kF8 ? D / 64 : D / 32;   // K units per page
-  constexpr int kVg = kF8 ? D / 64 : D / 32;   // V units per page
+  constexpr int kKu = D / 32;                  // K units (1 KB) per page in LDS, bf16 layout
+  constexpr int kVg = D / 32;                  // V units per page
+  constexpr int kDma = Geo<T, D>::kSlab / 1024;   // 1 KB LDS-DMA pieces of a staged page
   constexpr int kDb = D / 16;                  // 16-dim blocks of O^T
   constexpr int kTp = 4, kTileKeys = kTp * kPage;
   constexpr int kKBytes = kTp * kKu * 1024;
@@ -1056,15 +1045,13 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
   // lane-constant LDS offsets of the operand reads and of the staging sources
   const int par = n >> 3;
   const int t_a = 8 * ((n >> 2) & 1) + (n & 3);
-  // bf16: K read = chunk q of the unit, 16 bytes; FP8: chunk (2(s&1) + q/2) of unit s/2, the
-  // half q%2 (8 codes), the s-dependent part added at the read
-  const int koff_a = kF8 ? par * 1024 + ((q >> 1) * 16 + kslot8(par, t_a)) * 16 + 8 * (q & 1)
-                         : par * 1024 + (q * 16 + kslot(par, t_a)) * 16;
-  const int koff_b = kF8 ? par * 1024 + ((q >> 1) * 16 + kslot8(par, t_a + 4)) * 16 + 8 * (q & 1)
-                         : par * 1024 + (q * 16 + kslot(par, t_a + 4)) * 16;
-  const int voff = kF8 ? (q >> 1) * 1024 + n * 16 + 8 * (q & 1) : (q >> 1) * 1024 + (2 * n + (q & 1)) * 16;
-  const int src_k = kF8 ? ((lane >> 4) * 16 + kslot8(w & 1, lane & 15)) * 16
-                        : ((lane >> 4) * 16 + kslot(w & 1, lane & 15)) * 16;
+  // K read = chunk q of the unit, 16 bytes
+  const int koff_a = par * 1024 + (q * 16 + kslot(par, t_a)) * 16;
+  const int koff_b = par * 1024 + (q * 16 + kslot(par, t_a + 4)) * 16;
+  const int voff = (q >> 1) * 1024 + (2 * n + (q & 1)) * 16;
+  // staging sources: bf16 K with the slot permutation; FP8 pages are copied in their own order
+  // and permuted by the conversion
+  const int src_k = kF8 ? lane * 16 : ((lane >> 4) * 16 + kslot(w & 1, lane & 15)) * 16;
   const int src_v = lane * 16;
   // FP8: K and V scales of the tiles' pages, [K, V][tile parity][page], each published by the
   // page's owner (the wave that stages it) before the barrier that precedes their use
@@ -1113,19 +1100,21 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
     }
   };
 
-  // K(t): this wave stages page w of tile t into K buffer par = t & 1.
-  auto stage_k = [&](auto par, int t) {
+  // K(t): this wave stages page w of tile t into K buffer par = t & 1; returns whether it read
+  // the page.
+  auto stage_k = [&](auto par, int t) -> bool {
     const int own = usable(kpf), own_lim = own < 0 ? 0 : page_lim(t, w);
     if constexpr (kF8) ks_own = own < 0 ? 1.f : ((CPTR(float))P.k_scale)[(size_t)own * P.hkv + head];
     kpf = fetch_id(t + 1);
-    if (own_lim <= 0) return;                  // absent page: nothing is read
+    if (own_lim <= 0) return false;            // absent page: nothing is read
     char* dst = kbuf(par) + w * 1024;
     const BufRsrc r = slab_rsrc<T, D>(P.k, own, P.hkv, head);
     stage_chunk(r, 0, src_k, dst);
-    if constexpr (kKu > 1) stage_chunk(r, 1024, src_k, dst + 4096);
-    if constexpr (kKu > 2) stage_chunk(r, 2048, src_k, dst + 8192);
-    if constexpr (kKu > 3) stage_chunk(r, 3072, src_k, dst + 12288);
-    static_assert(kKu <= 4, "K units per page");
+    if constexpr (kDma > 1) stage_chunk(r, 1024, src_k, dst + 4096);
+    if constexpr (kDma > 2) stage_chunk(r, 2048, src_k, dst + 8192);
+    if constexpr (kDma > 3) stage_chunk(r, 3072, src_k, dst + 12288);
+    static_assert(kDma <= kKu && kKu <= 4, "K units per page");
+    return true;
   };
   // V(t): key counts of the tile's pages into lim (item with an entry outside the pool: complete
   // only after the next barrier, see lims_after_barrier); this wave stages page w; returns its
@@ -1141,11 +1130,44 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
     char* dst = vbuf(par) + w * 1024;
     const BufRsrc r = slab_rsrc<T, D>(P.v, own, P.hkv, head);
     stage_chunk(r, 0, src_v, dst);
-    if constexpr (kVg > 1) stage_chunk(r, 1024, src_v, dst + 4096);
-    if constexpr (kVg > 2) stage_chunk(r, 2048, src_v, dst + 8192);
-    if constexpr (kVg > 3) stage_chunk(r, 3072, src_v, dst + 12288);
-    static_assert(kVg <= 4, "V units per page");
+    if constexpr (kDma > 1) stage_chunk(r, 1024, src_v, dst + 4096);
+    if constexpr (kDma > 2) stage_chunk(r, 2048, src_v, dst + 8192);
+    if constexpr (kDma > 3) stage_chunk(r, 3072, src_v, dst + 12288);
+    static_assert(kDma <= kVg && kVg <= 4, "V units per page");
     return own_lim;
+  };
+  // FP8, after this wave's staging loads have landed: convert its page of K buffer par in place
+  // from the page's own order (FP8 chunk c of token t at byte (16c + t) * 16 of the staged
+  // copy, 1 KB per unit) into the bf16 layout (bf16 chunks 2c and 2c+1 of that token, at the slot
+  // whose source is t).  Every lane reads all of its codes before any lane writes.
+  auto convert_k = [&](auto par) {
+    char* kb = kbuf(par) + w * 1024;
+    const int t = kslot(w & 1, lane & 15);     // source token of this lane's slot
+    u32x4 c[kDma];
+#pragma unroll
+    for (int j = 0; j < kDma; ++j) c[j] = *(const u32x4*)(kb + j * 4096 + ((lane >> 4) * 16 + t) * 16);
+#pragma unroll
+    for (int j = 0; j < kDma; ++j) {
+      const int c16 = 4 * j + (lane >> 4);     // FP8 chunk: dims 16 c16 .. 16 c16 + 15
+      char* u = kb + (c16 >> 1) * 4096 + (2 * (c16 & 1) * 16 + (lane & 15)) * 16;
+      *(u32x4*)u = e4m3x8_to_bf16(u32x2{c[j][0], c[j][1]});
+      *(u32x4*)(u + 256) = e4m3x8_to_bf16(u32x2{c[j][2], c[j][3]});
+    }
+  };
+  // FP8: the same for this wave's page of V buffer par: dim d's 16 codes (byte 16d of the staged
+  // copy) become its two 16-byte halves (tokens 0..7, 8..15) at unit d/32, byte (d%32) * 32.
+  auto convert_v = [&](auto par) {
+    char* vb = vbuf(par) + w * 1024;
+    u32x4 c[kDma];
+#pragma unroll
+    for (int j = 0; j < kDma; ++j) c[j] = *(const u32x4*)(vb + j * 4096 + lane * 16);
+#pragma unroll
+    for (int j = 0; j < kDma; ++j) {
+      const int d = 64 * j + lane;
+      char* u = vb + (d >> 5) * 4096 + (d & 31) * 32;
+      *(u32x4*)u = e4m3x8_to_bf16(u32x2{c[j][0], c[j][1]});
+      *(u32x4*)(u + 16) = e4m3x8_to_bf16(u32x2{c[j][2], c[j][3]});
+    }
   };
   // After this wave's staging loads have landed: zero the V slots of tokens >= lim of its page
   // (all of them for an absent page), so that a zero probability never meets a NaN or stale
@@ -1156,12 +1178,8 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
     for (int g = 0; g < kVg; ++g) {
       u32x4* cp = (u32x4*)(vu + g * 4096 + lane * 16);
       const u32x4 v = lim_own > 0 ? *cp : u32x4{0u, 0u, 0u, 0u};
-      if constexpr (kF8) {
-        *cp = mask_v16_codes(v, lim_own);      // the chunk holds the 16 slots of one dim
-      } else {
-        const int h = lane & 1;                // the chunk holds tokens 8h .. 8h+7
-        *cp = mask_v8(v, lim_own - 8 * h);
-      }
+      const int h = lane & 1;                  // the chunk holds tokens 8h .. 8h+7
+      *cp = mask_v8(v, lim_own - 8 * h);
     }
   };
 
@@ -1173,12 +1191,7 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
     auto kread = [&](int k, u32x4 (&kop)[kNs]) {
       const int pp = k >> 1, blk = k & 1;
 #pragma unroll
-      for (int s = 0; s < kNs; ++s) {
-        if constexpr (kF8)
-          kop[s] = e4m3x8_to_bf16(*(const u32x2*)(kb + ((s >> 1) * 4 + 2 * pp) * 1024 + (s & 1) * 512 + (blk ? koff_b : koff_a)));
-        else
-          kop[s] = *(const u32x4*)(kb + (s * 4 + 2 * pp) * 1024 + (blk ? koff_b : koff_a));
-      }
+      for (int s = 0; s < kNs; ++s) kop[s] = *(const u32x4*)(kb + (s * 4 + 2 * pp) * 1024 + (blk ? koff_b : koff_a));
     };
     u32x4 kop0[kNs], kop1[kNs];
     kread(0, kop0);
@@ -1292,10 +1305,7 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
   auto pv = [&](const char* vb, const u32x4 (&pb)[2][2]) {
     auto vread = [&](int k) {
       const int pp = k / kDb, b2 = k % kDb;
-      if constexpr (kF8)                       // dims 16b2 .. +15: unit b2/4, rows 16(b2%4) ..
-        return e4m3x8_to_bf16(*(const u32x2*)(vb + ((b2 >> 2) * 4 + 2 * pp) * 1024 + (b2 & 3) * 256 + voff));
-      else
-        return *(const u32x4*)(vb + ((b2 >> 1) * 4 + 2 * pp) * 1024 + (b2 & 1) * 512 + voff);
+      return *(const u32x4*)(vb + ((b2 >> 1) * 4 + 2 * pp) * 1024 + (b2 & 1) * 512 + voff);
     };
     constexpr int kPv = 2 * kDb;
     u32x4 vq[3];
@@ -1337,7 +1347,7 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
     constexpr int PAR = decltype(par)::value;     // j & 1
     const int tb = kv_begin + j * kTileKeys;
     const bool more1 = j + 1 < n_tiles;
-    if (j + 2 < n_tiles) stage_k(par, j + 2);
+    const bool k_staged = j + 2 < n_tiles && stage_k(par, j + 2);
     int own_nv = kPage;
     if (more1) own_nv = stage_v(Par<1 - PAR>(), j + 1, lim_nxt);
     if (wave_active && tb <= pmax) {          // else every key follows every query of the wave
@@ -1362,6 +1372,10 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
     if (j + 2 < n_tiles) publish_k(j + 2);
     if (more1) publish_v(j + 1);
     __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): this wave's staging loads landed
+    if constexpr (kF8) {
+      if (k_staged) convert_k(par);
+      if (more1 && own_nv > 0) convert_v(Par<1 - PAR>());
+    }
     if (own_nv < kPage) zero_v_tail(Par<1 - PAR>(), own_nv);
     __syncthreads();
 #pragma unroll
@@ -1372,15 +1386,21 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
   if (n_tiles > 0) {
     Scores SA, SB;
     kpf = vpf = fetch_id(0);
-    stage_k(Par<0>(), 0);
+    const bool k0 = stage_k(Par<0>(), 0);
     publish_k(0);
+    bool k1 = false;
     if (n_tiles > 1) {
-      stage_k(Par<1>(), 1);
+      k1 = stage_k(Par<1>(), 1);
       publish_k(1);
     }
     const int own0 = stage_v(Par<0>(), 0, lim_cur);
     publish_v(0);
     __builtin_amdgcn_s_waitcnt(0x0F70);
+    if constexpr (kF8) {
+      if (k0) convert_k(Par<0>());
+      if (k1) convert_k(Par<1>());
+      if (own0 > 0) convert_v(Par<0>());
+    }
     if (own0 < kPage) zero_v_tail(Par<0>(), own0);
     __syncthreads();
     lims_after_barrier(0, lim_cur);
