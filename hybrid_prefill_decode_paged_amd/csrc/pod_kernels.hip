@@ -1237,32 +1237,26 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
   // or a column with none yet), and then `settle` takes the tile's per-column maxima, moves the
   // references that grew by more than the bound, rescales those columns' running output and sum by
   // 2^(m_old - m_new), and recomputes the probabilities.
-  typedef float Probs[2][16];                  // [nb][key slot k = 8pp + 4blk + i]
   auto sval = [&](const Scores& S, int nb, int k) { return S[nb][k >> 3][(k >> 2) & 1][k & 3]; };
-  auto exps = [&](const Scores& S, int nb, Probs& x) {
-    const float mu = m_run[nb] == kNegInf ? 0.f : m_run[nb];
+  auto col_max = [&](const Scores& S, int nb) {
+    float m = fmaxf(sval(S, nb, 0), sval(S, nb, 1));
 #pragma unroll
-    for (int k = 0; k < 16; ++k) x[nb][k] = exp2_fast(__builtin_fmaf(sval(S, nb, k), sl2, -mu));
+    for (int k = 2; k < 16; ++k) m = fmaxf(m, sval(S, nb, k));
+    return m;
   };
-  auto probs = [&](const Scores& S, Probs& x) -> bool {
+  // whether some column's scores (raw, before the mask: a masked score only lowers a maximum)
+  // exceed its reference by more than the bound, or a column has no reference yet
+  auto needs_settle = [&](const Scores& S) -> bool {
     bool slow = false;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      exps(S, nb, x);
-      float xm = fmaxf(x[nb][0], x[nb][1]);
-#pragma unroll
-      for (int k = 2; k < 16; ++k) xm = fmaxf(xm, x[nb][k]);
-      slow = slow | (xm > kRescaleBound) | (m_run[nb] == kNegInf);
-    }
+    for (int nb = 0; nb < 2; ++nb) slow = slow | (col_max(S, nb) * sl2 > m_run[nb] + kRescaleLog2) | (m_run[nb] == kNegInf);
     return __any(slow);
   };
-  auto settle = [&](const Scores& S, Probs& x) {
+  // masked scores: move the references that grew past the bound, rescale those columns
+  auto settle = [&](const Scores& S) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      float m = fmaxf(sval(S, nb, 0), sval(S, nb, 1));
-#pragma unroll
-      for (int k = 2; k < 16; ++k) m = fmaxf(m, sval(S, nb, k));
-      const float mx = max_over_groups(m) * sl2;
+      const float mx = max_over_groups(col_max(S, nb)) * sl2;
       const bool grow = mx > m_run[nb] + kRescaleLog2;
       const float alpha = grow ? exp2_fast(m_run[nb] - mx) : 1.f;
       m_run[nb] = grow ? mx : m_run[nb];
@@ -1270,24 +1264,36 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
       for (int b = 0; b < kDb; ++b) o[nb][b] *= alpha;
       if constexpr (kF8) lrow[nb] *= alpha;
       else lsum[nb] *= alpha;
-      exps(S, nb, x);
+    }
+  };
+  auto exps = [&](Scores& S) {                 // in place
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const float mu = m_run[nb] == kNegInf ? 0.f : m_run[nb];
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) S[nb][pp][blk][i] = exp2_fast(__builtin_fmaf(S[nb][pp][blk][i], sl2, -mu));
     }
   };
   // Product operands of the probabilities: bf16 pairs, keys 8q .. 8q+7 of a page pair per lane;
   // with an FP8 cache each page's V scale multiplies its probabilities here, and the row sums are
   // taken from the unscaled fp32 probabilities (xsum: this lane's keys).
-  auto pack = [&](const Probs& x, const float (&vs)[kTp], u32x4 (&pb)[2][2], float (&xsum)[2]) {
+  auto pack = [&](const Scores& X, const float (&vs)[kTp], u32x4 (&pb)[2][2], float (&xsum)[2]) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp) {
+        float xp[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) xp[k] = sval(X, nb, 8 * pp + k);
         if constexpr (kF8) {                   // keys 8q .. 8q+7 of the pair lie in page 2pp + q/2
           const float c = (q >> 1) ? vs[2 * pp + 1] : vs[2 * pp];
-          const float* xp = &x[nb][8 * pp];
           pb[nb][pp] = u32x4{pack_bf16(xp[0] * c, xp[1] * c), pack_bf16(xp[2] * c, xp[3] * c),
                              pack_bf16(xp[4] * c, xp[5] * c), pack_bf16(xp[6] * c, xp[7] * c)};
         } else {
-          const float* xp = &x[nb][8 * pp];
           pb[nb][pp] = u32x4{pack_bf16(xp[0], xp[1]), pack_bf16(xp[2], xp[3]), pack_bf16(xp[4], xp[5]),
                              pack_bf16(xp[6], xp[7])};
         }
@@ -1295,7 +1301,7 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
       if constexpr (kF8) {
         float t = 0.f;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) t += x[nb][k];
+        for (int k = 0; k < 16; ++k) t += sval(X, nb, k);
         xsum[nb] = t;
       }
     }
@@ -1340,6 +1346,7 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
   };
 
   int lim_cur[kTp], lim_nxt[kTp];
+  bool slow = true;                            // tile j's scores need a settle (always tile 0)
   // Iteration j: stage K(j+2) and V(j+1); QK(j+1) beside softmax(j) (one basic block, so the
   // matrix and vector units overlap); PV(j).  The product for tile j+1 past the last tile reads
   // a stale buffer and is discarded.
@@ -1357,17 +1364,25 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
       float ks[kTp], vs[kTp];
       read_scales(0, j + 1, ks);
       read_scales(1, j, vs);
+      if (slow) settle(Sc);
       qk(kbuf(Par<1 - PAR>()), Sn, ks);
-      Probs x;
-      if (probs(Sc, x)) settle(Sc, x);
+      exps(Sc);
       u32x4 pb[2][2];
       float xsum[2];
-      pack(x, vs, pb, xsum);
+      pack(Sc, vs, pb, xsum);
       if constexpr (kF8) {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) lrow[nb] += xsum[nb];
       }
       pv(vbuf(par), pb);
+      slow = needs_settle(Sn);
+    } else {
+      // never read again (the wave's keys are done), but defined on this path too, so that no
+      // tile's scores stay live across the loop's back edge
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) Sn[nb][pp][0] = Sn[nb][pp][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     if (j + 2 < n_tiles) publish_k(j + 2);
     if (more1) publish_v(j + 1);
