@@ -157,8 +157,10 @@ def summarize(t, t_roof_s=None):
 
 def measured_peaks(torch, B):
     """This GPU's HBM read rate and dense bf16 MFMA rate, from the library's probes
-    (pod_attn_probe_hbm_read over an 8 GiB buffer, pod_attn_probe_mfma), timed with HIP events
-    on the launch stream after one untimed call each."""
+    (pod_attn_probe_hbm_read over an 8 GiB buffer, pod_attn_probe_mfma): each probe runs untimed
+    for at least 0.2 s, then the median of individually timed launches (HIP events on the launch
+    stream).  Called before any workload is allocated: measured, an 8 GiB buffer allocated right
+    after tens of GiB were returned to the driver reads about 4% slower, warm-up or not."""
     stream = torch.cuda.current_stream()
     nbytes = 8 << 30
     buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
@@ -166,23 +168,26 @@ def measured_peaks(torch, B):
     fsink = torch.empty(4 * B.PROBE_WGS, dtype=torch.float32, device="cuda")
     iters = 2048
 
-    def timed(fn, reps):
-        fn()
-        torch.cuda.synchronize()
-        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(reps):
+    def timed(fn, reps, warm_s=0.2):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < warm_s:
             fn()
-        z.record(stream)
+            torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, z in ev:
+            a.record(stream)
+            fn()
+            z.record(stream)
         torch.cuda.synchronize()
-        return a.elapsed_time(z) / 1e3 / reps
+        return statistics.median(a.elapsed_time(z) for a, z in ev) / 1e3
 
-    t_hbm = timed(lambda: B.probe_hbm_read(buf, isink, stream), 10)
+    t_hbm = timed(lambda: B.probe_hbm_read(buf, isink, stream), 15)
     flops = B.probe_mfma(iters, fsink, stream)
-    t_mfma = timed(lambda: B.probe_mfma(iters, fsink, stream), 5)
+    t_mfma = timed(lambda: B.probe_mfma(iters, fsink, stream), 9)
     del buf
     return {"hbm_read_gbps": round(nbytes / t_hbm / 1e9, 1), "mfma_bf16_tflops": round(flops / t_mfma / 1e12, 1),
-            "how": "library probes: streaming read of 8 GiB in 16 KiB blocks, two in flight per wave; 4096x4 waves x 8 chains of bf16 32x32x16 MFMA"}
+            "how": "library probes, median of timed launches after 0.2 s of untimed ones: streaming read of 8 GiB "
+                   "in 16 KiB blocks, two in flight per wave; 4096x4 waves x 8 chains of bf16 32x32x16 MFMA"}
 
 
 def measured_traffic(kernel_name, workload_name):
@@ -353,6 +358,11 @@ def main():
 
     binding.load()
     torch.cuda.set_device(0)
+    # the probes run first, before the workloads' tens of GiB are allocated
+    peaks = None
+    if not args.no_peaks:
+        say("measuring this GPU's HBM read and MFMA rates")
+        peaks = measured_peaks(torch, binding)
     spec = gen.config_spec(args.workload)
     say(f"generating {spec.name}: {spec.num_pages} pages")
     b = gen.make_batch(spec, "cuda")
@@ -464,10 +474,7 @@ def main():
     st = stats[args.mode]
     kernel_name = "pod_fused_kernel" if args.mode == "fused" else f"{args.mode} kernels"
     traffic = measured_traffic(kernel_name, spec.name)
-    peaks = None
-    if not args.no_peaks:
-        say("measuring this GPU's HBM read and MFMA rates")
-        peaks = measured_peaks(torch, binding)
+    if peaks is not None:
         # the dominant kernel's rate against this GPU's own ceiling (context beside frac)
         if bound == "hbm" or spec.dtype != "fp32":
             measured = peaks["hbm_read_gbps"] if bound == "hbm" else peaks["mfma_bf16_tflops"]
