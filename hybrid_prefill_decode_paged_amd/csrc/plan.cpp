@@ -32,6 +32,7 @@ constexpr double kPrefillFlopsPerSec = 0.85e15;
 constexpr double kDecodeBytesPerSec = 6.5e12;
 constexpr double kPrefillHeavyRatio = 0.75;   // prefill share >= 3/4 of the decode share
 constexpr int kOneRoundMaxSplit = 8192;       // longest decode split of the prefill-heavy fused plan
+constexpr int kOneRoundMaxSplitFp8 = 5120;    // the same with an FP8 cache
 constexpr int kMinPrefillSplit = 4096;        // shortest key split of a prefill tile
 int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 int round_up_int(int a, int m) { return ceil_div(a, m) * m; }
@@ -318,10 +319,13 @@ pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus
     // (q load, partial store, merge).  Measured on the Llama-2-7B-shaped FP8 batch: 2048-token
     // items 496 us, 4096-token items 418 us; the bf16 batch is flat between the two.
     if (!one_round) st = st * 2 / c.elem_bytes();
-    // The one-item-per-slot plan stops at 8192 tokens: longer items outlast the prefill share
-    // (FP8 cache, Llama-3-8B-shaped batch: 32768-token items 1503 us, 16384: 1347, 8192: 1302,
-    // 4096: 1320; the Yi-6B-shaped bf16 batch is best at 8192 too).
-    if (one_round) st = std::min(st, (long)kOneRoundMaxSplit);
+    // The one-item-per-slot plan stops at 8192 tokens (5120 with an FP8 cache): the longest
+    // items end the launch (Yi-6B-shaped batch, fused kernel us, bf16 cap 8192 / 6144 / 5120:
+    // 540.9 / 546.7 / 553.6; FP8 cap 8192 / 6144 / 5120 / 4096: 579.8 / 561.2 / 544.5 / 571.7,
+    // and the FP8 Llama-3-8B-shaped batch 1248.8 / 1230.6 / 1250.5 / 1249.7; earlier, that FP8
+    // batch: 32768-token items 1503 us, 16384: 1347).
+    if (one_round)
+      st = std::min(st, (long)(c.dtype == POD_ATTN_FP8_E4M3 ? kOneRoundMaxSplitFp8 : kOneRoundMaxSplit));
     st = std::max(512L, std::min(32768L, st));
     st_target = round_up_int((int)st, 128);
   }

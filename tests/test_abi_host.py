@@ -205,7 +205,7 @@ def test_decode_items_sized_by_bytes():
     """Decode items are sized by the bytes they stream: the FP8 cache's items hold twice the
     tokens of the bf16 cache's on the same batch, and the prefill-heavy fused plan (here the
     FP8 Llama-3-8B-shaped batch, whose halved decode bytes make it prefill-heavy) stops at
-    8192-token splits."""
+    5120-token splits with an FP8 cache (8192 with bf16)."""
     for idx in (2, 5):
         bf, f8 = gen.config_spec(idx), gen.fp8_spec(idx)
         st = {}
@@ -217,7 +217,7 @@ def test_decode_items_sized_by_bytes():
     spec = gen.fp8_spec(3)
     cfg = B.make_config(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.dtype, "fused")
     items, s_ = B.plan_inspect(cfg, _meta(spec), 256, 2)
-    assert s_["decode_split_tokens"] == 8192
+    assert s_["decode_split_tokens"] == 5120
     _check_coverage(spec, items, spec.num_q_heads // spec.num_kv_heads)
 
 
