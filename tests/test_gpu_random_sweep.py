@@ -1,6 +1,6 @@
 """Randomized parity sweep: seeded random hybrid batches against the fp64 oracle on the whole
-output.  Each case draws a dtype (bf16 or the FP8 cache with scales that are not powers of two),
-head_dim, KV heads, group size, prefill chunks (lengths and offsets around tile, page and split
+output.  Each case draws a dtype (bf16, fp32, or the FP8 cache with scales that are not powers
+of two), head_dim, KV heads, group size, prefill chunks (lengths and offsets around tile, page and split
 edges), decode contexts (page edges), a mode, and sometimes forced decode splits or a prefill
 split cap; unused cache slots hold NaN.  Fusion must not change the result (POD-Attention
 digest, "Virtual CTAs and per-SM balance"), whatever the shape.
@@ -28,7 +28,7 @@ def _need_gpu():
 
 
 def _draw(rng: random.Random):
-    dtype = rng.choice(["bf16", "bf16", "fp8"])
+    dtype = rng.choice(["bf16", "bf16", "fp8", "fp32"])
     D = rng.choice([64, 128])
     hkv = rng.choice([1, 2, 4])
     G = rng.choice([1, 2, 4, 8, 16])
