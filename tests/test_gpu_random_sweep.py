@@ -69,3 +69,45 @@ def test_random_batches_match_the_oracle(chunk):
         torch.cuda.synchronize()
         check_close(to_f64(out), problem(b).full_output(), dtype, what)
         h.close()
+
+
+@pytest.mark.parametrize("chunk", range(2))
+def test_random_appends_match_the_oracle(chunk):
+    """The same draw through pod_attn_run_append (bf16 and fp32 caches; writing FP8 is not
+    built): the new tokens' K/V land bit-exactly where the oracle's append puts them, no other
+    cache byte changes, and the output over the updated cache matches the oracle."""
+    from oracle import attention as orc
+
+    def raw(t, dt):
+        t = t.cpu()
+        return t.view(torch.int16).numpy().copy() if dt == "bf16" else t.numpy().copy()
+
+    rng = random.Random(20261204 + chunk)
+    for i in range(CASES_PER_CHUNK):
+        dtype, D, hkv, hq, pre, dec, mode, kw, seed = _draw(rng)
+        if dtype == "fp8":
+            dtype = "bf16"
+        what = (f"append chunk {chunk} case {i}: {dtype} Hq={hq} Hkv={hkv} D={D} prefill={pre} "
+                f"decode={dec} mode={mode} {kw} seed={seed}")
+        print(what, flush=True)
+        spec = gen.custom_spec(dtype, Hq=hq, Hkv=hkv, D=D, prefill=pre, decode=dec, seed=seed)
+        b = gen.make_batch(spec, "cuda")
+        rows = orc.row_positions(b.prefill_q_start, b.prefill_ctx_len, b.decode_ctx_len)
+        k_new, v_new = gen.new_tokens(spec, seed + 1, "cuda")
+        kr, vr = gen.k_rows_view(b.k_pool), gen.v_rows_view(b.v_pool)
+        for s, pos in rows:                      # a slot the append misses shows as NaN
+            p = int(b.block_tables_host[s][pos // 16])
+            kr[p, :, pos % 16] = float("nan")
+            vr[p, :, pos % 16] = float("nan")
+        want_k, want_v = raw(b.k_pool, dtype), raw(b.v_pool, dtype)
+        orc.append_tokens(want_k, want_v, b.block_tables_host, rows, raw(k_new, dtype), raw(v_new, dtype))
+        h = B.PodAttention(hq, hkv, D, dtype, mode, scale=spec.softmax_scale, **kw)
+        meta = B.BatchMeta.from_batch(b)
+        ws = torch.empty(h.workspace_size(meta), dtype=torch.uint8, device="cuda")
+        out = torch.full_like(b.q, float("nan"))
+        h.run_append(b.q, k_new, v_new, b.k_pool, b.v_pool, b.block_tables, meta, out, ws)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(raw(b.k_pool, dtype), want_k, err_msg=what)
+        np.testing.assert_array_equal(raw(b.v_pool, dtype), want_v, err_msg=what)
+        check_close(to_f64(out), problem(b).full_output(), dtype, what)
+        h.close()
