@@ -88,3 +88,26 @@ def test_noalloc_rejects_a_batch_beyond_the_scratch_and_fp8():
         hf.run_noalloc(fbb.q, fbb.k_pool, fbb.v_pool, fbb.block_tables, B.BatchMeta.from_batch(fbb),
                        torch.empty_like(fbb.q))
     assert e.value.status == -1
+
+
+@pytest.mark.parametrize("mode", ["fused", "separate", "streams"])
+def test_noalloc_random_sequence_matches_run(mode):
+    """Twelve seeded random batches in a row on one handle, larger and smaller in turn, with and
+    without splits: every call bitwise equal to pod_attn_run, so nothing the scratch keeps from
+    the call before leaks into the next."""
+    import random
+    rng = random.Random(7300 + ["fused", "separate", "streams"].index(mode))
+    h = B.PodAttention(16, 4, 128, "bf16", mode, decode_split_tokens=rng.choice([256, 512]), prefill_split_cap=4)
+    for i in range(12):
+        pre = [(rng.choice([1, 3, 17, 128, 129, 300]), 0) for _ in range(rng.randint(0, 2))]
+        pre = [(L, L + rng.choice([0, 15, 700, 4000])) for L, _ in pre]
+        dec = [rng.choice([1, 16, 17, 255, 1000, 6000]) for _ in range(rng.randint(0 if pre else 1, 5))]
+        spec = gen.custom_spec("bf16", Hq=16, Hkv=4, D=128, prefill=pre, decode=dec, seed=7400 + i)
+        b = gen.make_batch(spec, "cuda")
+        meta = B.BatchMeta.from_batch(b)
+        _say(f"noalloc sequence mode={mode} call {i}: prefill={pre} decode={dec}")
+        ref, _, _ = run_library(b, handle=h)
+        out = torch.full_like(b.q, float("nan"))
+        h.run_noalloc(b.q, b.k_pool, b.v_pool, b.block_tables, meta, out)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"{mode}/call {i}: differs from pod_attn_run"
