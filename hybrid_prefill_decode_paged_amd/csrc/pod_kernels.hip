@@ -961,8 +961,7 @@ __device__ void prefill_item(const KernelParams& P, CPTR(int32_t) dsc, int head,
 // its own inverse, so the staging lane at slot i fetches source chunk kslot(p&1, i); the V
 // operand read is conflict-free unpermuted.  Wave w stages page w of every tile: contiguous
 // 1 KB HBM reads straight into LDS.
-constexpr float kRescaleLog2 = 8.f;   // keep a stale running max while scores exceed it by < 2^8
-constexpr float kRescaleBound = 256.f; // 2^kRescaleLog2: the largest probability the stale max allows
+constexpr float kRescaleLog2 = 8.f;   // keep a stale running max while no probability exceeds 2^8
 
 __device__ __forceinline__ int kslot(int par, int t) { return t ^ ((((t >> 3) & 1) ^ par) << 2); }
 
