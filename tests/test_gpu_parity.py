@@ -393,6 +393,44 @@ def test_workspace_too_small_is_rejected():
     assert e.value.status == -3
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_million_token_contexts(dtype):
+    """Contexts far past the measured workloads' 32K: a decode over 2^20 keys (a block-table row
+    of 65,536 pages, split at most 128 ways) and a 64-row chunk at 300,000 keys, beside a
+    17-key decode; every output element against the oracle, fused and separate."""
+    spec = gen.custom_spec(dtype, Hq=8, Hkv=1, D=128, prefill=[(64, 300000)], decode=[1 << 20, 17], seed=77)
+    _say(f"million-token contexts {dtype}: {spec.num_pages} pages")
+    b = gen.make_batch(spec, "cuda")
+    want = problem(b).full_output()
+    for mode in ("fused", "separate"):
+        _say(f"million-token contexts {dtype} mode={mode}")
+        out, h, ws = run_library(b, mode=mode)
+        check_close(to_f64(out), want, dtype, f"million/{dtype}/{mode}")
+        st = h.stats()
+        assert 1 < st["decode_max_splits"] <= 128 and st["prefill_max_splits"] <= 128, st
+        h.close()
+        del ws
+    del b
+    torch.cuda.empty_cache()
+
+
+def test_thousands_of_short_sequences():
+    """4,000 decodes of 1 to 300 keys beside three prefill chunks: far more sequences than
+    workgroup slots, most of them a single partial page; every output element against the
+    oracle in every mode."""
+    rng = np.random.Generator(np.random.PCG64(88))
+    dec = rng.integers(1, 300, size=4000, endpoint=True).tolist()
+    spec = gen.custom_spec("bf16", Hq=8, Hkv=2, D=64, prefill=[(100, 100), (37, 5000), (300, 1200)],
+                           decode=dec, seed=88)
+    b = gen.make_batch(spec, "cuda")
+    want = problem(b).full_output()
+    for mode in MODES:
+        _say(f"4000 short sequences mode={mode}")
+        out, h, ws = run_library(b, mode=mode)
+        check_close(to_f64(out), want, "bf16", f"many-seqs/{mode}")
+        h.close()
+
+
 # ------------------------------------------------------------------ full-size workloads
 # Every mode against the fp64 oracle at the workloads' full sizes, in the launch configuration
 # the bench times: every decode row (every 8th of the 256 long-context ones) and the first and
