@@ -14,7 +14,7 @@ data in this library's buffer formats, ``steps`` times, and records the step's w
 and maximum), the fused kernel's own time, and the batch's signals (``pod_attn_batch_signals``).
 A bucket is validated when its runs took the fused path, reported no device error, wrote a
 finite output, and its output matched an independent reference within the library's stated
-tolerance (bf16: max abs 2e-2, mean abs 2e-3; fp32: 1e-5) on the sampled rows of
+tolerance (bf16 and the FP8 cache: max abs 2e-2, mean abs 2e-3; fp32: 1e-5) on the sampled rows of
 ``checked_rows`` (every head of the first and last prefill row and of the first and last decode
 row).  The reference is the caller's (``calibrate(reference=...)``): this module computes no
 attention itself, and a table calibrated without one publishes no validated bucket.  ``CostTable.lookup`` rounds each axis of a batch up to the table's next grid
@@ -99,7 +99,7 @@ def bucket_batch(chunk_len: int, chunk_ctx: int, n_decode: int, decode_ctx: int)
     return np.asarray(q_start, np.int32), np.asarray(p_ctx, np.int32), np.full(n_decode, decode_ctx, np.int32)
 
 
-TOLERANCE = {"bf16": (2e-2, 2e-3), "fp32": (1e-5, 1e-5)}   # (max abs, mean abs) of a validated bucket
+TOLERANCE = {"bf16": (2e-2, 2e-3), "fp8": (2e-2, 2e-3), "fp32": (1e-5, 1e-5)}   # (max abs, mean abs) of a validated bucket
 
 
 @dataclass
@@ -119,6 +119,8 @@ class BucketRun:
     scale: float
     out: object
     rows: List[int]
+    k_scale: object = None      # FP8 cache: float32 [pages, Hkv] scale of each K slab
+    v_scale: object = None
 
 
 def checked_rows(chunk_len: int, n_decode: int) -> List[int]:
@@ -138,8 +140,9 @@ def calibrate(num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: str,
     against an independent reference; without it no bucket is validated."""
     import torch
 
-    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
-    x = 16 // (2 if dtype == "bf16" else 4)
+    fp8 = dtype == "fp8"
+    tdt = torch.float32 if dtype == "fp32" else torch.bfloat16     # q and out (bf16 beside an FP8 cache)
+    x = 16 // {"bf16": 2, "fp32": 4, "fp8": 1}[dtype]               # elements per 16-byte K chunk
     grid = [(L, C if L else 0, n, Dc if n else 0) for L in chunk_lens for C in chunk_ctxs
             for n in decode_counts for Dc in decode_ctxs if (L == 0 or C >= L)]
     grid = sorted(set(g for g in grid if g[0] or g[2]))
@@ -149,8 +152,25 @@ def calibrate(num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: str,
     gen = torch.Generator(device="cuda")
     gen.manual_seed(seed)
     q = (torch.randn(max_rows, num_q_heads, head_dim, generator=gen, device="cuda") * 0.5).to(tdt)
-    k_pool = (torch.randn(max_pages, num_kv_heads, head_dim // x, PAGE, x, generator=gen, device="cuda") * 0.5).to(tdt)
-    v_pool = (torch.randn(max_pages, num_kv_heads, head_dim, PAGE, generator=gen, device="cuda") * 0.5).to(tdt)
+    k_scale = v_scale = None
+    if fp8:
+        # one scale per (page, KV head) slab, uniform in [0.5, 2); the slab holds the E4M3 codes
+        # (round to nearest even) of N(0,1) * 0.5 / scale
+        k_scale = torch.rand(max_pages, num_kv_heads, generator=gen, device="cuda") * 1.5 + 0.5
+        v_scale = torch.rand(max_pages, num_kv_heads, generator=gen, device="cuda") * 1.5 + 0.5
+        k_pool = (torch.randn(max_pages, num_kv_heads, head_dim // x, PAGE, x, generator=gen, device="cuda") * 0.5
+                  / k_scale[:, :, None, None, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+        v_pool = (torch.randn(max_pages, num_kv_heads, head_dim, PAGE, generator=gen, device="cuda") * 0.5
+                  / v_scale[:, :, None, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+    else:
+        k_pool = (torch.randn(max_pages, num_kv_heads, head_dim // x, PAGE, x, generator=gen, device="cuda") * 0.5).to(tdt)
+        v_pool = (torch.randn(max_pages, num_kv_heads, head_dim, PAGE, generator=gen, device="cuda") * 0.5).to(tdt)
+
+    def run(qv, bt_dev, meta, out, ws):
+        if fp8:
+            h.run_scaled(qv, k_pool, v_pool, k_scale, v_scale, bt_dev, meta, out, ws)
+        else:
+            h.run(qv, k_pool, v_pool, bt_dev, meta, out, ws)
     perm = np.random.Generator(np.random.PCG64(seed)).permutation(max_pages).astype(np.int32)
     h = binding.PodAttention(num_q_heads, num_kv_heads, head_dim, dtype, "fused")
     stream = torch.cuda.current_stream()
@@ -172,7 +192,7 @@ def calibrate(num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: str,
         out = torch.empty_like(qv)
         ws = torch.empty(h.workspace_size(meta), dtype=torch.uint8, device="cuda")
         for _ in range(warmup):
-            h.run(qv, k_pool, v_pool, bt_dev, meta, out, ws)
+            run(qv, bt_dev, meta, out, ws)
         torch.cuda.synchronize()
         walls, kerns = [], []
         for _ in range(steps):
@@ -183,7 +203,7 @@ def calibrate(num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: str,
             torch.cuda.synchronize()
             a.record(stream)
             h.set_kernel_events(ka, kz)
-            h.run(qv, k_pool, v_pool, bt_dev, meta, out, ws)
+            run(qv, bt_dev, meta, out, ws)
             z.record(stream)
             torch.cuda.synchronize()
             walls.append(a.elapsed_time(z) * 1e3)
@@ -195,7 +215,8 @@ def calibrate(num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: str,
         if reference is not None:
             max_err, mean_err = reference(BucketRun(qv, k_pool, v_pool, bt, q_start, p_ctx, d_ctx, num_q_heads,
                                                     num_kv_heads, dtype, h.cfg.scale if h.cfg.scale > 0
-                                                    else 1.0 / head_dim ** 0.5, out, checked_rows(L, n)))
+                                                    else 1.0 / head_dim ** 0.5, out, checked_rows(L, n),
+                                                    k_scale, v_scale))
             max_err, mean_err = float(max_err), float(mean_err)
         tol = TOLERANCE[dtype]
         ok = ok and max_err is not None and max_err <= tol[0] and mean_err <= tol[1]

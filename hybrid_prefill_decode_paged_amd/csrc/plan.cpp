@@ -314,11 +314,13 @@ pod_attn_status plan_batch(const Config& c, const pod_attn_batch* b, int num_cus
       one_round = true;
     }
     long st = (total_tok + target_items - 1) / std::max(1L, target_items);
-    // Items are sized by what they stream: an FP8 token is half a bf16 token's bytes, so it
-    // takes twice the tokens for an item to last as long and to amortise the same fixed costs
-    // (q load, partial store, merge).  Measured on the Llama-2-7B-shaped FP8 batch: 2048-token
-    // items 496 us, 4096-token items 418 us; the bf16 batch is flat between the two.
-    if (!one_round) st = st * 2 / c.elem_bytes();
+    // The same token count for every cache: an FP8 item streams half the bytes of a bf16 one,
+    // but doubling its tokens to make it last as long halves the number of items, and a batch
+    // whose items are not already capped by their sequences then leaves half the decode waves
+    // idle (FP8 decode-only batches at Llama-3-8B heads, fused kernel us, doubled -> not:
+    // 32 x 4K 98.9 -> 67.9, 128 x 32K 2558 -> 1406; the Llama-2-7B-, Llama-3-8B-shaped and
+    // long-context FP8 batches within 0.5% fused, the Llama-3-8B-shaped one 1624 -> 1548
+    // separate).
     // The one-item-per-slot plan stops at 8192 tokens (5120 with an FP8 cache): the longest
     // items end the launch (Yi-6B-shaped batch, fused kernel us, bf16 cap 8192 / 6144 / 5120:
     // 540.9 / 546.7 / 553.6; FP8 cap 8192 / 6144 / 5120 / 4096: 579.8 / 561.2 / 544.5 / 571.7,

@@ -206,9 +206,15 @@ def bucket_reference(run):
     (all heads), returning the (max, mean) absolute error of the library's output there."""
     q = run.q.cpu()
     qraw = q.view(torch.int16).numpy() if q.dtype == torch.bfloat16 else q.numpy()
-    prob = orc.HybridProblem(qraw, DevicePages(run.k_pool, run.dtype), DevicePages(run.v_pool, run.dtype),
-                             run.block_tables_host, run.prefill_q_start, run.prefill_ctx_len, run.decode_ctx_len,
-                             run.num_q_heads, run.num_kv_heads, run.dtype, run.scale)
+    meta = (run.block_tables_host, run.prefill_q_start, run.prefill_ctx_len, run.decode_ctx_len,
+            run.num_q_heads, run.num_kv_heads)
+    if run.dtype == "fp8":
+        prob = orc.HybridProblem(qraw, DevicePages(run.k_pool, "fp8"), DevicePages(run.v_pool, "fp8"), *meta,
+                                 "bf16", run.scale, kv_dtype="fp8", k_scale=run.k_scale.cpu().numpy(),
+                                 v_scale=run.v_scale.cpu().numpy())
+    else:
+        prob = orc.HybridProblem(qraw, DevicePages(run.k_pool, run.dtype), DevicePages(run.v_pool, run.dtype), *meta,
+                                 run.dtype, run.scale)
     errs = []
     for r in run.rows:
         s, _, _ = prob.row_info(int(r))

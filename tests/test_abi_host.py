@@ -3,6 +3,7 @@ function, the planner covers every (query row, head, visible key) exactly once, 
 validator rejects bad metadata with the documented status codes, and a host model of the
 fused kernel's claim policy terminates with every item claimed once."""
 import heapq
+from dataclasses import replace
 
 import numpy as np
 import pytest
@@ -201,19 +202,23 @@ def test_decode_split_length_follows_the_share_balance(idx):
         assert st["num_decode_items"] >= 4 * slots
 
 
-def test_decode_items_sized_by_bytes():
-    """Decode items are sized by the bytes they stream: the FP8 cache's items hold twice the
-    tokens of the bf16 cache's on the same batch, and the prefill-heavy fused plan (here the
-    FP8 Llama-3-8B-shaped batch, whose halved decode bytes make it prefill-heavy) stops at
-    5120-token splits with an FP8 cache (8192 with bf16)."""
-    for idx in (2, 5):
-        bf, f8 = gen.config_spec(idx), gen.fp8_spec(idx)
+def test_decode_items_fill_the_grid_for_every_cache():
+    """Decode items hold the same number of tokens for the FP8 and the bf16 cache on the same
+    batch, so a batch too small to be capped by its sequences still has about one item per
+    decode wave with an FP8 cache (here 32 decodes at 4K: 2048 items on 256 CUs x 2 x 4 waves).
+    The prefill-heavy fused plan (here the FP8 Llama-3-8B-shaped batch, whose halved decode
+    bytes make it prefill-heavy) stops at 5120-token splits with an FP8 cache (8192 with bf16)."""
+    small = gen.custom_spec("bf16", Hq=32, Hkv=8, D=128, prefill=[], decode=[4096] * 32, seed=1)
+    for bf, f8 in ((gen.config_spec(2), gen.fp8_spec(2)), (gen.config_spec(5), gen.fp8_spec(5)),
+                   (small, replace(small, dtype="fp8"))):
         st = {}
         for spec in (bf, f8):
-            cfg = B.make_config(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.dtype, "separate")
-            _, s_ = B.plan_inspect(cfg, _meta(spec), 256, 2)
-            st[spec.dtype] = s_["decode_split_tokens"]
-        assert st["fp8"] == min(32768, 2 * st["bf16"]), (idx, st)
+            for mode in ("fused", "separate"):
+                cfg = B.make_config(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.dtype, mode)
+                _, s_ = B.plan_inspect(cfg, _meta(spec), 256, 2)
+                st[spec.dtype, mode] = (s_["decode_split_tokens"], s_["num_decode_items"])
+        assert st["fp8", "fused"] == st["bf16", "fused"] and st["fp8", "separate"] == st["bf16", "separate"], st
+    assert st["fp8", "fused"][1] == 2048, st
     spec = gen.fp8_spec(3)
     cfg = B.make_config(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.dtype, "fused")
     items, s_ = B.plan_inspect(cfg, _meta(spec), 256, 2)

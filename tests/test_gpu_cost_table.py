@@ -1,8 +1,9 @@
 """GPU check of the measured cost table: every bucket of a small grid runs on the fused path with
 no device error and a finite output and matches the fp64 oracle on its sampled rows (so it is
 validated, with its errors recorded), its timings are positive and ordered (max >= median), its
-signals are the host's for that bucket, and lookups round batches up to the right bucket.  A
-reference that disagrees, or none, leaves every bucket unvalidated and lookups empty."""
+signals are the host's for that bucket, and lookups round batches up to the right bucket; the
+same for an FP8 cache.  A reference that disagrees, or none, leaves every bucket unvalidated and
+lookups empty."""
 import sys
 
 import pytest
@@ -43,6 +44,19 @@ def test_small_grid_calibrates_and_looks_up():
     assert t.lookup(65, 100, 0, 0) is None
     assert t.lookup(10, 100, 0, 0).key() == (64, 1024, 0, 0)
     assert CostTable.from_json(t.to_json()).lookup(30, 900, 5, 600).key() == (64, 1024, 8, 2048)
+
+
+def test_fp8_cache_grid_is_validated():
+    """The same calibration for an FP8 E4M3 cache (per-slab scales that are not powers of two):
+    every bucket validated against the oracle's decoded cache at the bf16 tolerance."""
+    print("[gpu-test] cost table 8/2/128 fp8, 2x1x2x1 grid", flush=True)
+    sys.stdout.flush()
+    t = calibrate(8, 2, 128, "fp8", [0, 64], [1024], [0, 8], [2048], steps=2, reference=bucket_reference)
+    assert t.dtype == "fp8" and len(t.entries) == 3
+    for e in t.entries:
+        assert e.validated, e
+        assert e.max_abs_err <= 2e-2 and e.mean_abs_err <= 2e-3
+    assert t.lookup(30, 900, 5, 600).key() == (64, 1024, 8, 2048)
 
 
 def test_buckets_that_disagree_with_the_reference_are_not_validated():
