@@ -190,9 +190,9 @@ def test_decode_split_length_follows_the_share_balance(idx):
         cfg = B.make_config(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.dtype, mode)
         _, st = B.plan_inspect(cfg, meta, 256, 2)
         per_wave = -(-tok // (slots * 4))
-        expect = -(-min(32768, max(512, per_wave)) // 128) * 128
+        expect = -(-min(32768, max(256, per_wave)) // 128) * 128
         if mode == "fused" and idx == 4:
-            expect = -(-min(32768, max(512, -(-tok // slots))) // 128) * 128
+            expect = -(-min(32768, max(256, -(-tok // slots))) // 128) * 128
         assert st["decode_split_tokens"] == expect, (idx, mode)
     cfg = B.make_config(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.dtype, "fused")
     _, st = B.plan_inspect(cfg, meta, 256, 2)
