@@ -186,6 +186,17 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16(u32x2 v) {
   const u32x2 lo = e4m3x4_to_bf16(v.x), hi = e4m3x4_to_bf16(v.y);
   return u32x4{lo.x, lo.y, hi.x, hi.y};
 }
+// Eight E4M3 codes (lowest byte first) decoded exactly, times s, rounded to bf16 (nearest even):
+// the values of an FP8 slab with its scale applied, as the bf16 tile takes them.
+__device__ __forceinline__ uint32_t e4m3x2_scaled_bf16(uint32_t v, bool hi, float s) {
+  const f32x2 x = hi ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v, 1.0f, true)
+                     : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v, 1.0f, false);
+  return pack_bf16(x.x * s, x.y * s);
+}
+__device__ __forceinline__ u32x4 e4m3x8_scaled_bf16(u32x2 v, float s) {
+  return u32x4{e4m3x2_scaled_bf16(v.x, false, s), e4m3x2_scaled_bf16(v.x, true, s),
+               e4m3x2_scaled_bf16(v.y, false, s), e4m3x2_scaled_bf16(v.y, true, s)};
+}
 // The K operand of one MFMA step as the matrix unit takes it.
 __device__ __forceinline__ u32x4 k_operand(u32x4 k) { return k; }
 __device__ __forceinline__ u32x4 k_operand(u32x2 k) { return e4m3x8_to_bf16(k); }
@@ -979,10 +990,10 @@ __device__ __forceinline__ u32x4 mask_v8(u32x4 v, int lt) {
 
 // The same tile for the bf16 cache (T = __bf16) and the FP8 cache (T = Fp8).  FP8: each wave
 // stages its page's E4M3 codes (half the bytes) by LDS-DMA into the first units of the page's
-// place, and once they have landed converts them in place into the bf16 layout above (every code
-// converted once per workgroup, exactly: E4M3 values are bf16 values); the products then read bf16
-// operands as for the bf16 cache, the page's K scale applied to its scores and its V scale to its
-// probabilities in the output product.
+// place, and once they have landed converts them in place into the bf16 layout above: each code
+// decoded exactly, times the page's scale (K or V), rounded to bf16, once per workgroup.  From
+// there on the tile is the bf16 one: no scale appears in the products, the softmax or the row
+// sums.
 template <typename T, int D>
 __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int head, int split, const Stage& LB) {
   constexpr bool kF8 = kIsFp8<T>;
@@ -1032,7 +1043,6 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
   const int pmax = q_pos + (min(ncols, wc0 + 32) - 1) / G;
 
   f32x4 o[2][kDb], lsum[2];
-  float lrow[2] = {0.f, 0.f};                  // FP8: this lane's share of the row sums
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     lsum[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1052,10 +1062,15 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
   // and permuted by the conversion
   const int src_k = kF8 ? lane * 16 : ((lane >> 4) * 16 + kslot(w & 1, lane & 15)) * 16;
   const int src_v = lane * 16;
-  // FP8: K and V scales of the tiles' pages, [K, V][tile parity][page], each published by the
-  // page's owner (the wave that stages it) before the barrier that precedes their use
-  __shared__ float s_scale[2][2][kTp];
-  float ks_own = 1.f, vs_own = 1.f;            // this wave's page of the tile just staged
+  // FP8: the scale of this wave's page in each K buffer and in the V buffer being staged,
+  // loaded with the staging (a vector load, counted with the LDS-DMA loads, so that no scalar
+  // load is in flight beside the LDS reads) and applied when the page is converted
+  float ks_own[2] = {1.f, 1.f}, vs_own = 1.f;
+  auto scale_load = [&](const float* base, int page) {
+    const BufRsrc r = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base) + (size_t)page * P.hkv, (short)0,
+                                                        P.hkv * 4, 0x00020000);
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, head * 4, 0, 0));
+  };
 
   // LDS: K buffers 0 and 1, V buffers 0 and 1, four separate objects.  K(t) (tile t) lives in K
   // buffer t&1 and is staged two tiles ahead of the QK product that reads it, V(t) in V buffer
@@ -1103,7 +1118,7 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
   // the page.
   auto stage_k = [&](auto par, int t) -> bool {
     const int own = usable(kpf), own_lim = own < 0 ? 0 : page_lim(t, w);
-    if constexpr (kF8) ks_own = own < 0 ? 1.f : ((CPTR(float))P.k_scale)[(size_t)own * P.hkv + head];
+    if constexpr (kF8) ks_own[decltype(par)::value] = scale_load(P.k_scale, own < 0 ? 0 : own);
     kpf = fetch_id(t + 1);
     if (own_lim <= 0) return false;            // absent page: nothing is read
     char* dst = kbuf(par) + w * 1024;
@@ -1123,7 +1138,7 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
 #pragma unroll
     for (int p = 0; p < kTp; ++p) lim[p] = page_lim(t, p);
     if (!clean && lane == 0) s_lims[t & 1][w] = own_lim;
-    if constexpr (kF8) vs_own = own < 0 ? 1.f : ((CPTR(float))P.v_scale)[(size_t)own * P.hkv + head];
+    if constexpr (kF8) vs_own = scale_load(P.v_scale, own < 0 ? 0 : own);
     vpf = fetch_id(t + 1);
     if (own_lim <= 0) return 0;
     char* dst = vbuf(par) + w * 1024;
@@ -1138,8 +1153,10 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
   // FP8, after this wave's staging loads have landed: convert its page of K buffer par in place
   // from the page's own order (FP8 chunk c of token t at byte (16c + t) * 16 of the staged
   // copy, 1 KB per unit) into the bf16 layout (bf16 chunks 2c and 2c+1 of that token, at the slot
-  // whose source is t).  Every lane reads all of its codes before any lane writes.
+  // whose source is t), each value decoded, times the page's K scale, rounded to bf16.  Every
+  // lane reads all of its codes before any lane writes.
   auto convert_k = [&](auto par) {
+    const float sc = ks_own[decltype(par)::value];
     char* kb = kbuf(par) + w * 1024;
     const int t = kslot(w & 1, lane & 15);     // source token of this lane's slot
     u32x4 c[kDma];
@@ -1149,13 +1166,15 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
     for (int j = 0; j < kDma; ++j) {
       const int c16 = 4 * j + (lane >> 4);     // FP8 chunk: dims 16 c16 .. 16 c16 + 15
       char* u = kb + (c16 >> 1) * 4096 + (2 * (c16 & 1) * 16 + (lane & 15)) * 16;
-      *(u32x4*)u = e4m3x8_to_bf16(u32x2{c[j][0], c[j][1]});
-      *(u32x4*)(u + 256) = e4m3x8_to_bf16(u32x2{c[j][2], c[j][3]});
+      *(u32x4*)u = e4m3x8_scaled_bf16(u32x2{c[j][0], c[j][1]}, sc);
+      *(u32x4*)(u + 256) = e4m3x8_scaled_bf16(u32x2{c[j][2], c[j][3]}, sc);
     }
   };
-  // FP8: the same for this wave's page of V buffer par: dim d's 16 codes (byte 16d of the staged
-  // copy) become its two 16-byte halves (tokens 0..7, 8..15) at unit d/32, byte (d%32) * 32.
+  // FP8: the same for this wave's page of V buffer par (times the page's V scale): dim d's 16
+  // codes (byte 16d of the staged copy) become its two 16-byte halves (tokens 0..7, 8..15) at
+  // unit d/32, byte (d%32) * 32.
   auto convert_v = [&](auto par) {
+    const float sc = vs_own;
     char* vb = vbuf(par) + w * 1024;
     u32x4 c[kDma];
 #pragma unroll
@@ -1164,8 +1183,8 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
     for (int j = 0; j < kDma; ++j) {
       const int d = 64 * j + lane;
       char* u = vb + (d >> 5) * 4096 + (d & 31) * 32;
-      *(u32x4*)u = e4m3x8_to_bf16(u32x2{c[j][0], c[j][1]});
-      *(u32x4*)(u + 16) = e4m3x8_to_bf16(u32x2{c[j][2], c[j][3]});
+      *(u32x4*)u = e4m3x8_scaled_bf16(u32x2{c[j][0], c[j][1]}, sc);
+      *(u32x4*)(u + 16) = e4m3x8_scaled_bf16(u32x2{c[j][2], c[j][3]}, sc);
     }
   };
   // After this wave's staging loads have landed: zero the V slots of tokens >= lim of its page
@@ -1186,7 +1205,7 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
   typedef f32x4 Scores[2][2][2];               // S^T blocks [nb][pp][blk]
 
   // QK of one staged tile; the K operands of step k+1 are read while step k multiplies.
-  auto qk = [&](const char* kb, Scores& S, const float (&ks)[kTp]) {
+  auto qk = [&](const char* kb, Scores& S) {
     auto kread = [&](int k, u32x4 (&kop)[kNs]) {
       const int pp = k >> 1, blk = k & 1;
 #pragma unroll
@@ -1204,7 +1223,6 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < kNs; ++s) acc = mfma_chunk(cur[s], qop[nb][s], acc, __bf16());
-        if constexpr (kF8) acc *= (q >> 1) ? ks[2 * (k >> 1) + 1] : ks[2 * (k >> 1)];   // rows of page 2pp + q/2
         S[nb][k >> 1][k & 1] = acc;
       }
     }
@@ -1261,8 +1279,7 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
       m_run[nb] = grow ? mx : m_run[nb];
 #pragma unroll
       for (int b = 0; b < kDb; ++b) o[nb][b] *= alpha;
-      if constexpr (kF8) lrow[nb] *= alpha;
-      else lsum[nb] *= alpha;
+      lsum[nb] *= alpha;
     }
   };
   auto exps = [&](Scores& S) {                 // in place
@@ -1277,10 +1294,8 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
           for (int i = 0; i < 4; ++i) S[nb][pp][blk][i] = exp2_fast(__builtin_fmaf(S[nb][pp][blk][i], sl2, -mu));
     }
   };
-  // Product operands of the probabilities: bf16 pairs, keys 8q .. 8q+7 of a page pair per lane;
-  // with an FP8 cache each page's V scale multiplies its probabilities here, and the row sums are
-  // taken from the unscaled fp32 probabilities (xsum: this lane's keys).
-  auto pack = [&](const Scores& X, const float (&vs)[kTp], u32x4 (&pb)[2][2], float (&xsum)[2]) {
+  // Product operands of the probabilities: bf16 pairs, keys 8q .. 8q+7 of a page pair per lane.
+  auto pack = [&](const Scores& X, u32x4 (&pb)[2][2]) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
@@ -1288,25 +1303,13 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
         float xp[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) xp[k] = sval(X, nb, 8 * pp + k);
-        if constexpr (kF8) {                   // keys 8q .. 8q+7 of the pair lie in page 2pp + q/2
-          const float c = (q >> 1) ? vs[2 * pp + 1] : vs[2 * pp];
-          pb[nb][pp] = u32x4{pack_bf16(xp[0] * c, xp[1] * c), pack_bf16(xp[2] * c, xp[3] * c),
-                             pack_bf16(xp[4] * c, xp[5] * c), pack_bf16(xp[6] * c, xp[7] * c)};
-        } else {
-          pb[nb][pp] = u32x4{pack_bf16(xp[0], xp[1]), pack_bf16(xp[2], xp[3]), pack_bf16(xp[4], xp[5]),
-                             pack_bf16(xp[6], xp[7])};
-        }
-      }
-      if constexpr (kF8) {
-        float t = 0.f;
-#pragma unroll
-        for (int k = 0; k < 16; ++k) t += sval(X, nb, k);
-        xsum[nb] = t;
+        pb[nb][pp] = u32x4{pack_bf16(xp[0], xp[1]), pack_bf16(xp[2], xp[3]), pack_bf16(xp[4], xp[5]),
+                           pack_bf16(xp[6], xp[7])};
       }
     }
   };
-  // PV of one staged tile: V^T operands two blocks ahead of the products that use them; for the
-  // bf16 cache the row sums come from the same P^T against a ones operand.
+  // PV of one staged tile: V^T operands two blocks ahead of the products that use them; the row
+  // sums come from the same P^T against a ones operand.
   auto pv = [&](const char* vb, const u32x4 (&pb)[2][2]) {
     auto vread = [&](int k) {
       const int pp = k / kDb, b2 = k % kDb;
@@ -1322,7 +1325,7 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
       if (k + 2 < kPv) vq[(k + 2) % 3] = vread(k + 2);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) o[nb][b2] = mfma_chunk(vq[k % 3], pb[nb][pp], o[nb][b2], __bf16());
-      if (!kF8 && b2 == kDb - 1) {
+      if (b2 == kDb - 1) {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) lsum[nb] = mfma_chunk(ones, pb[nb][pp], lsum[nb], __bf16());
       }
@@ -1331,19 +1334,6 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
 
   // FP8: publish this wave's page scales of the tiles it just staged (lane 0; read by every wave
   // after the next barrier).  Deferred to the end of the iteration, when their loads are done.
-  auto publish_k = [&](int t) {
-    if constexpr (kF8) { if (lane == 0) s_scale[0][t & 1][w] = ks_own; }
-  };
-  auto publish_v = [&](int t) {
-    if constexpr (kF8) { if (lane == 0) s_scale[1][t & 1][w] = vs_own; }
-  };
-  auto read_scales = [&](int which, int t, float (&sc)[kTp]) {
-    if constexpr (kF8) {
-#pragma unroll
-      for (int p = 0; p < kTp; ++p) sc[p] = s_scale[which][t & 1][p];
-    }
-  };
-
   int lim_cur[kTp], lim_nxt[kTp];
   bool slow = true;                            // tile j's scores need a settle (always tile 0)
   // Iteration j: stage K(j+2) and V(j+1); QK(j+1) beside softmax(j) (one basic block, so the
@@ -1360,19 +1350,11 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
       const bool full = (tb + kTileKeys - 1 <= pmin) & (lim_cur[0] == kPage) & (lim_cur[1] == kPage) &
                         (lim_cur[2] == kPage) & (lim_cur[3] == kPage);
       if (!full) apply_mask(Sc, tb, lim_cur);
-      float ks[kTp], vs[kTp];
-      read_scales(0, j + 1, ks);
-      read_scales(1, j, vs);
       if (slow) settle(Sc);
-      qk(kbuf(Par<1 - PAR>()), Sn, ks);
+      qk(kbuf(Par<1 - PAR>()), Sn);
       exps(Sc);
       u32x4 pb[2][2];
-      float xsum[2];
-      pack(Sc, vs, pb, xsum);
-      if constexpr (kF8) {
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) lrow[nb] += xsum[nb];
-      }
+      pack(Sc, pb);
       pv(vbuf(par), pb);
       slow = needs_settle(Sn);
     } else {
@@ -1383,8 +1365,6 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) Sn[nb][pp][0] = Sn[nb][pp][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    if (j + 2 < n_tiles) publish_k(j + 2);
-    if (more1) publish_v(j + 1);
     __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): this wave's staging loads landed
     if constexpr (kF8) {
       if (k_staged) convert_k(par);
@@ -1401,14 +1381,9 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
     Scores SA, SB;
     kpf = vpf = fetch_id(0);
     const bool k0 = stage_k(Par<0>(), 0);
-    publish_k(0);
     bool k1 = false;
-    if (n_tiles > 1) {
-      k1 = stage_k(Par<1>(), 1);
-      publish_k(1);
-    }
+    if (n_tiles > 1) k1 = stage_k(Par<1>(), 1);
     const int own0 = stage_v(Par<0>(), 0, lim_cur);
-    publish_v(0);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     if constexpr (kF8) {
       if (k0) convert_k(Par<0>());
@@ -1418,9 +1393,7 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
     if (own0 < kPage) zero_v_tail(Par<0>(), own0);
     __syncthreads();
     lims_after_barrier(0, lim_cur);
-    float ks0[kTp];
-    read_scales(0, 0, ks0);
-    if (wave_active && kv_begin <= pmax) qk(kbuf(Par<0>()), SA, ks0);
+    if (wave_active && kv_begin <= pmax) qk(kbuf(Par<0>()), SA);
     __syncthreads();                           // K buffer 0 is restaged by the first iteration
     for (int j = 0; j < n_tiles; j += 2) {
       iteration(Par<0>(), j, SA, SB);
@@ -1431,11 +1404,7 @@ __device__ void prefill_item_tile(const KernelParams& P, CPTR(int32_t) dsc, int 
   // ---- epilogue: normalise and write the output, or the split partial (o, lse)
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    float l_tot = lsum[nb][0];                 // every row of the ones-product holds the column sum
-    if constexpr (kF8) {                       // the four lanes of a column hold a quarter each
-      l_tot = lrow[nb] + __shfl_xor(lrow[nb], 16);
-      l_tot += __shfl_xor(l_tot, 32);
-    }
+    const float l_tot = lsum[nb][0];           // every row of the ones-product holds the column sum
     if (!cval[nb]) continue;
     const int c = 32 * w + 16 * nb + n;
     const int qi = c / G, hh = c - qi * G;

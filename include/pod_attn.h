@@ -201,12 +201,14 @@ pod_attn_status pod_attn_run(pod_attn_handle* h, const void* q, const void* k_ca
 
 /* pod_attn_run for an FP8_E4M3 handle: k_scale and v_scale are device float arrays
  * [num_pages_in_pool][Hkv], the scale of each (page, KV head) slab of k_cache / v_cache.  The
- * scores of a key are multiplied by its page's K scale before the softmax and its probability by
- * its page's V scale in the output sum (the row sum takes it unscaled), which is attention over
- * the decoded, scaled cache.  Other handles: POD_ATTN_ERR_INVALID_ARG.  Everything else as
- * pod_attn_run; pod_attn_run on an FP8_E4M3 handle returns POD_ATTN_ERR_INVALID_ARG (the scales
- * are required) and pod_attn_run_append POD_ATTN_ERR_UNSUPPORTED (writing FP8 needs a
- * quantizer, which stays with the cache's producer). */
+ * result is attention over the decoded, scaled cache (value = decode(code) * scale, any finite
+ * scale).  Decode rows multiply their fp32 scores by the K scale and their probabilities by the
+ * V scale (the row sum takes them unscaled); prefill tiles round each decoded, scaled value to
+ * bf16 when they stage it, as a bf16 cache holds it.  Other handles: POD_ATTN_ERR_INVALID_ARG.
+ * Everything else as pod_attn_run; pod_attn_run on an FP8_E4M3 handle returns
+ * POD_ATTN_ERR_INVALID_ARG (the scales are required) and pod_attn_run_append
+ * POD_ATTN_ERR_UNSUPPORTED (writing FP8 needs a quantizer, which stays with the cache's
+ * producer). */
 pod_attn_status pod_attn_run_scaled(pod_attn_handle* h, const void* q, const void* k_cache,
                                     const void* v_cache, const float* k_scale, const float* v_scale,
                                     const int32_t* block_tables, const pod_attn_batch* batch,

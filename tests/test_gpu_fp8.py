@@ -112,6 +112,30 @@ def test_fp8_general_scales(mode):
     check_close(to_f64(out), problem(b).full_output(), "fp8", f"fp8-scales/{mode}")
 
 
+@pytest.mark.parametrize("mode", MODES)
+def test_fp8_scales_outside_the_usual_range(mode):
+    """Page scales a quantiser would not produce -- zero, negative and 1.3 * 2^-70 -- on about a
+    fifth of the pages, K and V drawn apart: the prefill tile multiplies such a scale into its
+    page's bf16 values when it converts them (instead of folding it into the exponent), the
+    decode path multiplies scores and probabilities by it; both against the oracle on every
+    output element.  (Scales above 2^64 take the same path; they make every softmax one-hot
+    with outputs too large for an absolute tolerance, so they are not drawn here.)"""
+    spec = gen.custom_spec("fp8", Hq=8, Hkv=2, D=128, prefill=[(150, 1500), (40, 900), (3, 70)],
+                           decode=[1, 37, 900, 2500], seed=74)
+    b = gen.make_batch(spec, "cuda")
+    gen.poison_unused(b)
+    rng = np.random.Generator(np.random.PCG64(740))
+    odd = np.array([0.0, -0.75, 1.3 * 2.0 ** -70], dtype=np.float32)
+    for t in (b.k_scale, b.v_scale):
+        sc = t.cpu().numpy()
+        pick = rng.random(sc.shape) < 0.2
+        sc[pick] = odd[rng.integers(0, len(odd), size=int(pick.sum()))]
+        t.copy_(torch.from_numpy(sc))
+    _say(f"fp8 scales outside the usual range mode={mode}")
+    out, _, _ = run_library(b, mode=mode, decode_split_tokens=256, prefill_split_cap=4)
+    check_close(to_f64(out), problem(b).full_output(), "fp8", f"fp8-odd-scales/{mode}")
+
+
 def test_fp8_entry_points_reject_what_they_cannot_do():
     spec = gen.custom_spec("fp8", Hq=4, Hkv=2, D=128, prefill=[(8, 40)], decode=[9], seed=71)
     b = gen.make_batch(spec, "cuda")
