@@ -305,11 +305,12 @@ def test_trace_records_every_item(mode):
 
 
 @pytest.mark.parametrize("mode", MODES)
-def test_run_to_run_bitwise_determinism(mode):
-    spec = gen.custom_spec("bf16", Hq=32, Hkv=8, D=128, prefill=[(256, 2000)],
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_run_to_run_bitwise_determinism(mode, dtype):
+    spec = gen.custom_spec(dtype, Hq=32, Hkv=8, D=128, prefill=[(256, 2000)],
                            decode=[3000, 1500, 700, 40], seed=21)
     b = gen.make_batch(spec, "cuda")
-    _say(f"determinism mode={mode}")
+    _say(f"determinism mode={mode} {dtype}")
     o1, h, ws = run_library(b, mode=mode, decode_split_tokens=256)
     o2 = torch.empty_like(o1)
     run_library(b, handle=h, out=o2, workspace=ws)
