@@ -345,7 +345,7 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
-              "(the hybrid batch shards by sequence or KV head with no exchange; see DESIGN.md)",
+              "(a hybrid batch would shard by sequence or KV head, one process per GPU, with no exchange)",
               file=sys.stderr)
         sys.exit(2)
 
